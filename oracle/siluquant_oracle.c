@@ -1,0 +1,198 @@
+/*
+ * CPU oracle for silu_dot_fwd_bwd_quant_fuse -- TEST INFRASTRUCTURE ONLY.
+ *
+ * This file is the plain, slow, single-threaded definition that the HIP path
+ * is checked against.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load it; the product library never does,
+ * and this file shares no code, header, table or constant with it.
+ *
+ * What it computes (page "kernelgen-challenge-9-task3-silu-quant" on
+ * githubhelp.com, the entry-point listing and the two output bullets that
+ * follow it):
+ *   x = [gate | up]            bf16 [T, 2H]   (gate = cols [0,H), up = [H,2H))
+ *   grad_y                     bf16 [T, H]
+ *   y      = silu(gate) * up                       (forward recompute)
+ *   d_gate = grad_y * up * s * (1 + gate*(1 - s))  (s = sigmoid(gate))
+ *   d_up   = grad_y * silu(gate)
+ *   grad_input_q/_s : [d_gate, d_up] quantised to int8, one fp32 scale per
+ *                     `group` contiguous channels of each 2H-long row.
+ *   y_q_t/_s_t      : y transposed to [H, T], int8, one fp32 scale per
+ *                     `group` consecutive tokens of each row of y^T.
+ * The same page's list of design constraints fixes two more points used here:
+ * every value is rounded through bf16 before it is quantised, and the
+ * quantiser multiplies by a precomputed inverse scale.
+ *
+ * Readings taken where the page is silent (each is listed in the design notes):
+ *   - arithmetic is fp32, evaluated strictly left to right in the order
+ *     written below, with no fused multiply-add (build with -ffp-contract=off);
+ *   - exp(-g) is the correctly rounded fp32 value, obtained from the double
+ *     exp and rounded once to float;
+ *   - bf16 rounding is round-to-nearest-even on the fp32 bit pattern, with
+ *     subnormals kept;
+ *   - the group maximum is taken over the bf16-rounded values;
+ *   - scale = amax / 127 (1.0 when amax == 0), inv = 1 / scale,
+ *     q = clamp(rne(v * inv), -127, 127), and q = 0 whenever v == 0 (this
+ *     avoids 0 * inf when a group's scale is so small that 1/scale overflows);
+ *   - a trailing group shorter than `group` (T or 2H not a multiple of it) is
+ *     quantised over the elements it has.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_API __attribute__((visibility("default")))
+
+/* ---- bf16 <-> fp32 --------------------------------------------------------- */
+
+/* bf16 widens to fp32 exactly: its 16 bits are the top half of the fp32. */
+ORACLE_API float oracle_bf16_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* fp32 -> bf16, round to nearest, ties to even, on the bit pattern.
+ * Adding 0x7FFF plus the lowest kept bit carries into the kept half exactly
+ * when the dropped half is above the midpoint, or at it with an odd kept half.
+ * Subnormals round the same way; NaN is outside the domain. */
+ORACLE_API uint16_t oracle_f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+static float bf16_round(float f) { return oracle_bf16_to_f32(oracle_f32_to_bf16(f)); }
+
+/* ---- the elementwise part -------------------------------------------------- */
+
+/* Sigmoid as 1 / (1 + exp(-g)).  The intermediate e and den are returned too so
+ * that tests can pin each rounding step separately. */
+ORACLE_API float oracle_sigmoid_parts(float g, float* e_out, float* den_out) {
+  float e = (float)exp(-(double)g); /* one rounding of the (double) exp to fp32 */
+  float den = 1.0f + e;
+  float s = 1.0f / den;
+  if (e_out) *e_out = e;
+  if (den_out) *den_out = den;
+  return s;
+}
+
+ORACLE_API float oracle_sigmoid(float g) { return oracle_sigmoid_parts(g, NULL, NULL); }
+
+/* One (t, h) position before the bf16 round trip: gate g, up u, grad_y d.
+ * Order of operations: silu = g*s; y = silu*u;
+ * d_gate = ((d*u)*s) * (1 + g*(1 - s)); d_up = d*silu. */
+ORACLE_API void oracle_pair_f32(float g, float u, float d, float* y, float* d_gate, float* d_up) {
+  float s = oracle_sigmoid(g);
+  float silu = g * s;
+  *y = silu * u;
+  float a = d * u;
+  float b = a * s;
+  float c = 1.0f - s;
+  float k = g * c;
+  float m = 1.0f + k;
+  *d_gate = b * m;
+  *d_up = d * silu;
+}
+
+/* ---- the quantiser --------------------------------------------------------- */
+
+/* Quantise n values v[0], v[stride], ... into q[0], q[qstride], ... and return
+ * the group's scale.  v holds bf16-representable values. */
+ORACLE_API float oracle_quant_group(const float* v, int64_t n, int64_t stride, int8_t* q, int64_t qstride) {
+  float amax = 0.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    float a = fabsf(v[i * stride]);
+    if (a > amax) amax = a;
+  }
+  float scale = (amax == 0.0f) ? 1.0f : amax / 127.0f;
+  float inv = 1.0f / scale;
+  for (int64_t i = 0; i < n; ++i) {
+    float x = v[i * stride];
+    int8_t out = 0;
+    if (x != 0.0f) {
+      float t = x * inv;
+      float r = nearbyintf(t); /* default rounding mode: to nearest, ties to even */
+      if (r > 127.0f) r = 127.0f;
+      if (r < -127.0f) r = -127.0f;
+      out = (int8_t)r;
+    }
+    q[i * qstride] = out;
+  }
+  return scale;
+}
+
+/* ---- the whole pass -------------------------------------------------------- */
+
+enum {
+  ORACLE_OK = 0,
+  ORACLE_BAD_ARG = 1,
+  ORACLE_NO_MEMORY = 2,
+};
+
+/* The bf16-rounded intermediates: Y [T, H] (y) and D [T, 2H] ([d_gate, d_up]),
+ * stored as float. */
+ORACLE_API int oracle_intermediates(const uint16_t* x, const uint16_t* grad_y, float* Y, float* D,
+                                    int64_t T, int64_t H) {
+  if (T < 0 || H < 0) return ORACLE_BAD_ARG;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t h = 0; h < H; ++h) {
+      float g = oracle_bf16_to_f32(x[t * 2 * H + h]);
+      float u = oracle_bf16_to_f32(x[t * 2 * H + H + h]);
+      float d = oracle_bf16_to_f32(grad_y[t * H + h]);
+      float y, dg, du;
+      oracle_pair_f32(g, u, d, &y, &dg, &du);
+      Y[t * H + h] = bf16_round(y);
+      D[t * 2 * H + h] = bf16_round(dg);
+      D[t * 2 * H + H + h] = bf16_round(du);
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* Quantise the intermediates: row groups of D, then column groups of Y. */
+ORACLE_API int oracle_quantise(const float* Y, const float* D, int8_t* grad_input_q, float* grad_input_s,
+                               int8_t* y_q_t, float* y_s_t, int64_t T, int64_t H, int64_t group) {
+  if (T < 0 || H < 0 || group <= 0) return ORACLE_BAD_ARG;
+  int64_t row_groups = (2 * H + group - 1) / group;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t j = 0; j < row_groups; ++j) {
+      int64_t c0 = j * group;
+      int64_t n = (2 * H - c0 < group) ? 2 * H - c0 : group;
+      grad_input_s[t * row_groups + j] =
+          oracle_quant_group(&D[t * 2 * H + c0], n, 1, &grad_input_q[t * 2 * H + c0], 1);
+    }
+  }
+  int64_t col_groups = (T + group - 1) / group;
+  for (int64_t h = 0; h < H; ++h) {
+    for (int64_t j = 0; j < col_groups; ++j) {
+      int64_t t0 = j * group;
+      int64_t n = (T - t0 < group) ? T - t0 : group;
+      /* column h of Y, tokens t0.., goes to row h of y^T */
+      y_s_t[h * col_groups + j] = oracle_quant_group(&Y[t0 * H + h], n, H, &y_q_t[h * T + t0], 1);
+    }
+  }
+  return ORACLE_OK;
+}
+
+ORACLE_API int oracle_silu_dot_fwd_bwd_quant_fuse(const uint16_t* x, const uint16_t* grad_y, int8_t* grad_input_q,
+                                                  float* grad_input_s, int8_t* y_q_t, float* y_s_t, int64_t T,
+                                                  int64_t H, int64_t group) {
+  if (T < 0 || H < 0 || group <= 0) return ORACLE_BAD_ARG;
+  if (T == 0 || H == 0) return ORACLE_OK;
+  float* Y = (float*)malloc((size_t)(T * H) * sizeof(float));
+  float* D = (float*)malloc((size_t)(T * 2 * H) * sizeof(float));
+  if (!Y || !D) {
+    free(Y);
+    free(D);
+    return ORACLE_NO_MEMORY;
+  }
+  int rc = oracle_intermediates(x, grad_y, Y, D, T, H);
+  if (rc == ORACLE_OK) rc = oracle_quantise(Y, D, grad_input_q, grad_input_s, y_q_t, y_s_t, T, H, group);
+  free(Y);
+  free(D);
+  return rc;
+}

@@ -1,0 +1,54 @@
+"""The oracle's pins must catch plausible mistakes (CPU only).
+
+Each case below plants one mistake in a private copy of the oracle's C source
+(a dropped term, a wrong sign, a swapped operand, a transposed store, a wrong
+rounding rule ...), builds it, and runs the pin tests against it in a child
+process.  The pins pass on the real oracle; every mutant must make at least
+one of them fail.
+"""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "siluquant_oracle.c")
+PINS = ["tests/test_oracle_pipeline.py", "tests/test_oracle_quant.py",
+        "tests/test_oracle_elementwise.py", "tests/test_oracle_sigmoid.py"]
+
+MUTANTS = {
+    "sigmoid_sign": ("exp(-(double)g)", "exp((double)g)"),
+    "dgate_one_minus_s": ("float c = 1.0f - s;", "float c = s;"),
+    "dgate_dropped_term": ("float m = 1.0f + k;", "float m = 1.0f;"),
+    "dup_uses_up": ("*d_up = d * silu;", "*d_up = d * u;"),
+    "y_missing_up": ("*y = silu * u;", "*y = silu;"),
+    "bf16_truncates": ("u += 0x7FFFu + lsb;", "u += 0u * lsb;"),
+    "no_bf16_round_trip": ("Y[t * H + h] = bf16_round(y);", "Y[t * H + h] = y;"),
+    "ties_away_from_zero": ("nearbyintf(t)", "roundf(t)"),
+    "scale_over_128": ("amax / 127.0f", "amax / 128.0f"),
+    "amax_without_abs": ("float a = fabsf(v[i * stride]);", "float a = v[i * stride];"),
+    "zero_group_scale_zero": ("(amax == 0.0f) ? 1.0f", "(amax == 0.0f) ? 0.0f"),
+    "gate_up_swapped": ("float g = oracle_bf16_to_f32(x[t * 2 * H + h]);",
+                        "float g = oracle_bf16_to_f32(x[t * 2 * H + H + h]);"),
+    "yqt_not_transposed": ("&y_q_t[h * T + t0], 1)", "&y_q_t[t0 * H + h], H)"),
+    "row_groups_skip_up_half": ("int64_t row_groups = (2 * H + group - 1) / group;",
+                                "int64_t row_groups = (H + group - 1) / group;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor not found once: %r" % old
+    mutant = tmp_path / "mutant.c"
+    mutant.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fPIC", "-shared",
+                    "-fvisibility=hidden", str(mutant), "-o", str(lib), "-lm"], check=True)
+    env = dict(os.environ, SILUQUANT_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] + PINS,
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, "mutant %s passed every pin:\n%s" % (name, r.stdout[-2000:])

@@ -1,0 +1,258 @@
+"""Pins for the whole oracle pass (CPU only).
+
+* Closed forms: a saturated gate (s == 1) turns d_gate into an exact copy of
+  grad_y * up, which drives the quantiser worked example (ties to even) through
+  the full pass; a very negative gate (s == 0) zeroes every output; a zero gate
+  gives y = d_up = 0 and d_gate = bf16(d * u / 2).
+* All-constant inputs: every group is constant, so every code is +-127 (or 0)
+  and every scale is |v| / 127 rounded, with v the bf16 rounding of the exact
+  value (computed here from 60-digit exponentials, away from rounding ties).
+* An fp64 error bound on random inputs: dequantised outputs sit within half a
+  scale step plus the bf16 rounding of the exact y, d_gate and d_up, and each
+  scale is within bf16 rounding of (exact group max) / 127.  A transposed
+  output, a wrong group index or a swapped half fails this.
+* Metamorphic: permuting tokens inside a 128-token group permutes the columns of
+  y_q_t and nothing else; permuting channels inside a 128-channel block permutes
+  codes and the per-channel rows of y_s_t, and leaves the row-group scales
+  alone; any sub-grid of 128 x 128 blocks, run on
+  its own, reproduces the matching slices of the full result.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact import bf16_bits_to_fraction, rn32, rnbf16, sigmoid_exact
+from swiglu_backward_int8_amd.inputs import make_inputs, random_inputs
+
+G = 128
+
+
+def _bits(vals, shape):
+    t = torch.tensor(np.asarray(vals, dtype=np.float32)).reshape(shape).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _const_inputs(T, H, g, u, d):
+    x = np.empty((T, 2 * H), dtype=np.float32)
+    x[:, :H] = g
+    x[:, H:] = u
+    return _bits(x, (T, 2 * H)), _bits(np.full((T, H), d, np.float32), (T, H))
+
+
+def test_saturated_gate_drives_quantiser_example():
+    # g = 100 gives s == 1 exactly, so d_gate = ((d*u)*1)*(1 + 100*0) = u for
+    # d = 1, y = bf16(100*u) and d_up = d*silu = 100.
+    T = H = 128
+    u = np.zeros((T, H), np.float32)
+    row = [127.0, 2.5, 0.5, -2.5, 126.5, 3.5, -0.5, 1.5]
+    u[:, : len(row)] = row
+    x = np.concatenate([np.full((T, H), 100.0, np.float32), u], axis=1)
+    xb = _bits(x, (T, 2 * H))
+    dyb = _bits(np.ones((T, H), np.float32), (T, H))
+    gq, gs, yq, ys = oracle.silu_dot_fwd_bwd_quant_fuse(xb, dyb)
+    assert np.all(gs[:, 0] == 1.0)  # d_gate group: amax 127
+    assert gq[0, : len(row)].tolist() == [127, 2, 0, -2, 126, 4, 0, 2]
+    assert np.all(gq[:, len(row):H] == 0)
+    # d_up = 100 everywhere: constant group
+    assert np.all(gq[:, H:] == 127)
+    assert np.all(gs[:, 1] == np.float32(float(rn32(Fraction(100, 127)))))
+    # y = bf16(100 * u); for u = 127: 12700 -> bf16 12672 (8 significant bits)
+    assert float(rnbf16(Fraction(12700))) == 12672.0
+
+
+def test_very_negative_gate_zeroes_everything():
+    xb, dyb = _const_inputs(256, 128, -100.0, 3.0, 0.5)
+    gq, gs, yq, ys = oracle.silu_dot_fwd_bwd_quant_fuse(xb, dyb)
+    assert not gq.any() and not yq.any()
+    assert np.all(gs == 1.0) and np.all(ys == 1.0)
+
+
+def test_zero_gate():
+    T, H = 128, 128
+    rng = np.random.default_rng(3)
+    u = rng.standard_normal((T, H)).astype(np.float32)
+    d = rng.standard_normal((T, H)).astype(np.float32)
+    xb = _bits(np.concatenate([np.zeros((T, H), np.float32), u], axis=1), (T, 2 * H))
+    dyb = _bits(d, (T, H))
+    Y, D = oracle.intermediates(xb, dyb)
+    assert not Y.any() and not D[:, H:].any()
+    ub = (xb[:, H:].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    db = (dyb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    want = np.array([float(rnbf16(Fraction(a) * Fraction(b) / 2)) for a, b in zip(ub.ravel(), db.ravel())])
+    assert np.array_equal(D[:, :H].ravel().astype(np.float64), want)
+
+
+# (gate, up, grad_y) constants
+CONSTANTS = [(0.0, 1.0, 1.0), (1.0, 1.0, 1.0), (20.0, 1.5, 0.25), (-2.0, 1.0, 1.0), (-100.0, 1.0, 1.0),
+             (0.5, -3.0, 0.01)]
+
+
+def _exact_values(g, u, d):
+    g, u, d = Fraction(g), Fraction(u), Fraction(d)
+    s = sigmoid_exact(g) if abs(g) < 120 else Fraction(int(g > 0))
+    y = g * s * u
+    dg = d * u * s * (1 + g * (1 - s))
+    du = d * g * s
+    return y, dg, du
+
+
+def _bf16_far_from_tie(v: Fraction) -> bool:
+    """True when fp32 rounding noise (a few 2^-24 relative) cannot move v across
+    a bf16 rounding midpoint."""
+    if v == 0:
+        return True
+    r = rnbf16(v)
+    return rnbf16(v * (1 + Fraction(1, 2**18))) == r == rnbf16(v * (1 - Fraction(1, 2**18)))
+
+
+@pytest.mark.parametrize("g,u,d", CONSTANTS)
+def test_constant_inputs(g, u, d):
+    T, H = 256, 256
+    xb, dyb = _const_inputs(T, H, g, u, d)
+    gq, gs, yq, ys = oracle.silu_dot_fwd_bwd_quant_fuse(xb, dyb)
+    y, dg, du = _exact_values(g, u, d)
+    for v, q, s in ((dg, gq[:, :H], gs[:, : H // G]), (du, gq[:, H:], gs[:, H // G:]), (y, yq, ys)):
+        assert _bf16_far_from_tie(v)
+        vb = rnbf16(v)
+        if vb == 0:
+            assert np.all(s == 1.0) and not q.any()
+            continue
+        assert np.all(s == np.float32(float(rn32(abs(vb) / 127))))
+        assert np.all(q == (127 if vb > 0 else -127))
+
+
+def _exact_f64(xb, dyb):
+    x = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    dy = (dyb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    H = dy.shape[1]
+    g, u = x[:, :H], x[:, H:]
+    with np.errstate(over="ignore"):  # exp(-g) = inf for g < -709 gives s = 0
+        s = 1.0 / (1.0 + np.exp(-g))
+    y = g * s * u
+    dg = dy * u * s * (1.0 + g * (1.0 - s))
+    du = dy * g * s
+    return y, np.concatenate([dg, du], axis=1)
+
+
+def _check_group_bound(q, s, exact, axis_len):
+    """q [.., n] codes, s [.., n/G] scales, exact [.., n] fp64 values; groups of G
+    along the last axis."""
+    n = q.shape[-1]
+    sc = np.repeat(s.astype(np.float64), G, axis=-1)[..., :n]
+    deq = q.astype(np.float64) * sc
+    # bf16 keeps 8 significant bits: rounding moves a value by at most 2^-8 of it
+    slack = sc * (0.5 + 2.0**-15) + np.abs(exact) * (2.0**-8 + 2.0**-20) + 1e-300
+    assert np.all(np.abs(deq - exact) <= slack), np.max(np.abs(deq - exact) - slack)
+    gmax = np.abs(exact).reshape(exact.shape[:-1] + (-1, G)).max(axis=-1)
+    nz = gmax > 1e-30
+    rel = np.abs(s.astype(np.float64)[nz] * 127.0 - gmax[nz]) / gmax[nz]
+    assert np.all(rel <= 2.0**-8 + 2.0**-20)
+
+
+@pytest.mark.parametrize("name", ["t256_h256"])
+def test_fp64_error_bound(name):
+    xt, dyt = make_inputs(name, device="cpu")
+    xb = xt.view(torch.int16).numpy().view(np.uint16)
+    dyb = dyt.view(torch.int16).numpy().view(np.uint16)
+    gq, gs, yq, ys = oracle.silu_dot_fwd_bwd_quant_fuse(xb, dyb)
+    y, d = _exact_f64(xb, dyb)
+    _check_group_bound(gq, gs, d, G)
+    _check_group_bound(yq, ys, np.ascontiguousarray(y.T), G)
+
+
+def test_fp64_error_bound_outlier_workload():
+    xt, dyt = make_inputs("t32768_h2048_outliers", device="cpu", T=512)
+    xt, dyt = xt[:, :].contiguous(), dyt.contiguous()
+    H = dyt.shape[1]
+    # take 256 channels of each half to keep it quick
+    x = torch.cat([xt[:, :256], xt[:, H:H + 256]], dim=1).contiguous()
+    dy = dyt[:, :256].contiguous()
+    xb = x.view(torch.int16).numpy().view(np.uint16)
+    dyb = dy.view(torch.int16).numpy().view(np.uint16)
+    gq, gs, yq, ys = oracle.silu_dot_fwd_bwd_quant_fuse(xb, dyb)
+    y, d = _exact_f64(xb, dyb)
+    _check_group_bound(gq, gs, d, G)
+    _check_group_bound(yq, ys, np.ascontiguousarray(y.T), G)
+    zero_rows = np.arange(512) % 97 == 96
+    assert np.all(gs[zero_rows] == 1.0) and not gq[zero_rows].any()
+
+
+def _np_bits(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def test_token_permutation_within_group():
+    xt, dyt = random_inputs(256, 256, seed=11)
+    xb, dyb = _np_bits(xt), _np_bits(dyt)
+    rng = np.random.default_rng(5)
+    perm = np.concatenate([rng.permutation(G), G + rng.permutation(G)])
+    base = oracle.silu_dot_fwd_bwd_quant_fuse(xb, dyb)
+    pm = oracle.silu_dot_fwd_bwd_quant_fuse(np.ascontiguousarray(xb[perm]), np.ascontiguousarray(dyb[perm]))
+    assert np.array_equal(pm[0], base[0][perm]) and np.array_equal(pm[1], base[1][perm])
+    assert np.array_equal(pm[2], base[2][:, perm])
+    assert np.array_equal(pm[3], base[3])
+
+
+def test_channel_permutation_within_block():
+    T, H = 128, 256
+    xt, dyt = random_inputs(T, H, seed=12)
+    xb, dyb = _np_bits(xt), _np_bits(dyt)
+    rng = np.random.default_rng(6)
+    p = np.concatenate([rng.permutation(G), G + rng.permutation(G)])  # within each 128-block
+    xp = np.ascontiguousarray(np.concatenate([xb[:, :H][:, p], xb[:, H:][:, p]], axis=1))
+    dyp = np.ascontiguousarray(dyb[:, p])
+    base = oracle.silu_dot_fwd_bwd_quant_fuse(xb, dyb)
+    pm = oracle.silu_dot_fwd_bwd_quant_fuse(xp, dyp)
+    full = np.concatenate([p, H + p])
+    assert np.array_equal(pm[0], base[0][:, full])
+    assert np.array_equal(pm[1], base[1])
+    assert np.array_equal(pm[2], base[2][p])
+    assert np.array_equal(pm[3], base[3][p])  # y^T rows are channels
+
+
+def test_sub_grid_reproduces_slices():
+    T, H = 512, 512
+    xt, dyt = random_inputs(T, H, seed=13, gate_std=2.0)
+    xb, dyb = _np_bits(xt), _np_bits(dyt)
+    gq, gs, yq, ys = oracle.silu_dot_fwd_bwd_quant_fuse(xb, dyb)
+    tb = [3, 1]  # token blocks, in this order
+    hb = [2, 0, 3]  # channel blocks
+    rows = np.concatenate([np.arange(b * G, (b + 1) * G) for b in tb])
+    cols = np.concatenate([np.arange(b * G, (b + 1) * G) for b in hb])
+    xs = np.ascontiguousarray(np.concatenate([xb[rows][:, cols], xb[rows][:, H + cols]], axis=1))
+    dys = np.ascontiguousarray(dyb[rows][:, cols])
+    sq, ss, syq, sys_ = oracle.silu_dot_fwd_bwd_quant_fuse(xs, dys)
+    assert np.array_equal(sq, gq[rows][:, np.concatenate([cols, H + cols])])
+    assert np.array_equal(ss, gs[rows][:, hb + [H // G + b for b in hb]])
+    assert np.array_equal(syq, yq[cols][:, rows])
+    assert np.array_equal(sys_, ys[cols][:, tb])
+
+
+def test_trailing_partial_token_group():
+    # 200 tokens: two token groups, the second of 72 tokens, quantised over what
+    # it has; cutting to the first 128 tokens reproduces the first group.
+    xt, dyt = random_inputs(200, 128, seed=14)
+    xb, dyb = _np_bits(xt), _np_bits(dyt)
+    gq, gs, yq, ys = oracle.silu_dot_fwd_bwd_quant_fuse(xb, dyb)
+    assert ys.shape == (128, 2) and yq.shape == (128, 200)
+    c = oracle.silu_dot_fwd_bwd_quant_fuse(np.ascontiguousarray(xb[:128]), np.ascontiguousarray(dyb[:128]))
+    assert np.array_equal(c[2], yq[:, :128]) and np.array_equal(c[3][:, 0], ys[:, 0])
+    assert np.array_equal(c[0], gq[:128]) and np.array_equal(c[1], gs[:128])
+    Y, _ = oracle.intermediates(xb, dyb)
+    tail = np.abs(Y[128:]).max(axis=0)
+    want = np.array([float(rn32(Fraction(float(a)) / 127)) if a > 0 else 1.0 for a in tail], np.float32)
+    assert np.array_equal(ys[:, 1], want)
+    assert np.all(np.abs(yq[:, 128:]).max(axis=1)[tail > 0] == 127)
+
+
+def test_empty_inputs():
+    for T, H in ((0, 128), (128, 0), (0, 0)):
+        xb = np.zeros((T, 2 * H), np.uint16)
+        dyb = np.zeros((T, H), np.uint16)
+        gq, gs, yq, ys = oracle.silu_dot_fwd_bwd_quant_fuse(xb, dyb)
+        assert gq.size == 0 or T == 0
+        assert yq.shape == (H, T)

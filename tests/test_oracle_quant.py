@@ -1,0 +1,112 @@
+"""Pins for the oracle's group quantiser (CPU only).
+
+The quantiser (scale = amax / 127, 1.0 for an all-zero group; inv = 1 / scale;
+q = clamp(rne(v * inv), -127, 127)) is pinned by:
+
+* hand-derived worked examples whose exact results are known without running
+  any float code (derivations in the comments);
+* brute-force rounding: with amax = 127 the scale and its inverse are exactly 1,
+  so every code must be the integer nearest to v (ties to even), found here by
+  comparing the two integer neighbours in exact arithmetic, for every bf16
+  value in [-127, 127];
+* invariants on random groups: |q| <= 127, some |q| == 127 in every group with
+  a normal-range scale, zero groups give scale 1.0 and zero codes, signs agree,
+  codes are monotone in v, and the dequantised error is at most half a scale
+  step plus the rounding slack of inv and v * inv.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from exact import all_finite_bf16, bf16_bits_to_fraction, f32_bits, rn32, rne_int
+
+
+def test_worked_example_amax_one():
+    # 1/127 = 0.0078740157...: fp32 exponent -7, significand 2^30/127 =
+    # 8454660.03 -> 8454660 = 0x810204 -> bits 0x3C010204.  1 / that value is
+    # 2^30 / 8454660 = 126.99999955, which is within half an ulp (2^-18) of 127,
+    # so inv == 127 exactly and q = rne(127 * v) for bf16 v (exact products).
+    v = [1.0, -0.5, 0.25, 0.00390625, 0.5, -1.0, 0.75, 0.0]
+    q, s = oracle.quant_group(v)
+    assert f32_bits(s) == 0x3C010204
+    # 127, -63.5 -> -64 (tie, even), 31.75 -> 32, 0.496 -> 0, 63.5 -> 64 (tie),
+    # -127, 95.25 -> 95, 0
+    assert q.tolist() == [127, -64, 32, 0, 64, -127, 95, 0]
+
+
+def test_worked_example_amax_127_ties_to_even():
+    # amax = 127 (a bf16 value): scale = 127/127 = 1 and inv = 1 exactly, so the
+    # codes are the values rounded half-to-even.  Half-away-from-zero would give
+    # 3, 1, -3, 127, 4 for the first five.
+    v = [2.5, 0.5, -2.5, 126.5, 3.5, 127.0, -0.5, 1.5, -126.5, 0.25]
+    q, s = oracle.quant_group(v)
+    assert s == 1.0
+    assert q.tolist() == [2, 0, -2, 126, 4, 127, 0, 2, -126, 0]
+
+
+def test_zero_group():
+    q, s = oracle.quant_group([0.0] * 128)
+    assert s == 1.0 and not q.any()
+    q, s = oracle.quant_group([-0.0] * 5)
+    assert s == 1.0 and not q.any()
+
+
+def test_brute_force_rounding_all_bf16_in_range():
+    bits = all_finite_bf16()
+    vals = np.array([float(bf16_bits_to_fraction(int(b))) for b in bits], dtype=np.float64)
+    vals = vals[np.abs(vals) <= 127.0]
+    group = np.concatenate([[127.0], vals]).astype(np.float32)
+    q, s = oracle.quant_group(group)
+    assert s == 1.0
+    for v, code in zip(group, q):
+        assert int(code) == rne_int(Fraction(float(v))), (float(v), int(code))
+
+
+def test_tiny_scale_overflowing_inverse():
+    # amax = 2^-130 (a bf16 subnormal): scale = 2^-130/127 is a subnormal fp32
+    # and 1/scale overflows to +inf.  Zeros stay 0, non-zeros clamp to +-127.
+    tiny = 2.0**-130
+    q, s = oracle.quant_group([tiny, -tiny, 0.0, tiny / 2])
+    assert Fraction(float(s)) == rn32(Fraction(tiny) / 127)
+    assert q.tolist() == [127, -127, 0, 127]
+
+
+def _random_groups(rng, n_groups=400):
+    groups = []
+    for i in range(n_groups):
+        n = int(rng.integers(1, 129))
+        mag = 10.0 ** rng.uniform(-30, 30)
+        v = rng.standard_normal(n) * mag
+        if i % 7 == 0:
+            v[rng.integers(0, n, size=max(1, n // 4))] = 0.0
+        # bf16-representable values, as the pass produces
+        v = np.array([float(bf16_bits_to_fraction(oracle.f32_to_bf16(float(x)))) for x in v])
+        groups.append(v.astype(np.float32))
+    return groups
+
+
+def test_invariants_random_groups():
+    rng = np.random.default_rng(7)
+    for v in _random_groups(rng):
+        q, s = oracle.quant_group(v)
+        qi = q.astype(np.int64)
+        amax = float(np.max(np.abs(v)))
+        assert np.all(np.abs(qi) <= 127)
+        if amax == 0.0:
+            assert s == 1.0 and not q.any()
+            continue
+        assert Fraction(float(s)) == rn32(Fraction(amax) / 127)
+        if float(s) >= 2.0**-126:
+            assert np.max(np.abs(qi)) == 127
+        # sign agreement and zeros
+        assert np.all((qi == 0) | (np.sign(qi) == np.sign(v)))
+        assert np.all(qi[v == 0] == 0)
+        # monotone in v
+        order = np.argsort(v, kind="stable")
+        assert np.all(np.diff(qi[order]) >= 0)
+        # dequantisation error bound, in double
+        err = np.abs(qi * float(s) - v.astype(np.float64))
+        assert np.all(err <= float(s) * (0.5 + 2.0**-15)), (err.max(), float(s))
