@@ -1,0 +1,170 @@
+"""Benchmark of the fused SwiGLU backward + two-axis int8 quantisation pass.
+
+One step = one call of silu_dot_fwd_bwd_quant_fuse over the whole workload
+(default: T = 16384 tokens, H = 11008 channels, the largest single-GPU
+workload), inputs already resident in HBM.  The metric is achieved HBM
+bandwidth: algorithmic bytes per call (reads of x and grad_y, writes of both
+code tensors and both scale tensors) divided by the time per call.
+
+Prints one JSON line.  Usage:
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+KERNEL_SRC = os.path.join(ROOT, "swiglu_backward_int8_amd", "csrc", "siluquant.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_source_sha") != kernel_source_digest():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, dy, w):
+    """The oracle, single-threaded, on the whole workload (one call)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    xb = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    db = dy.view(torch.int16).cpu().numpy().view(np.uint16)
+    oracle.build(force=False)
+    t = time.perf_counter()
+    oracle.silu_dot_fwd_bwd_quant_fuse(xb, db)
+    dt = time.perf_counter() - t
+    import swiglu_backward_int8_amd as sq
+
+    return {
+        "value": round(sq.algorithmic_bytes(w.T, w.H) / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "whole %s workload (T=%d, H=%d), one call, %.1f s" % (w.name, w.T, w.H, dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="t16384_h11008")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this pass runs on one GPU; --gpus %d is not supported (the tensors of a "
+              "multi-GPU job shard by tokens with no exchange, so per-GPU throughput is the "
+              "one-GPU figure)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import swiglu_backward_int8_amd as sq
+    from swiglu_backward_int8_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nbytes = sq.algorithmic_bytes(w.T, w.H)
+    # Rotate buffer sets so that one pass over them exceeds twice the 256 MB
+    # last-level cache: every step then reads its inputs from HBM.
+    sets = max(1, -(-512 * 2**20 // nbytes))
+    bufs = []
+    for r in range(sets):
+        x, dy = make_inputs(w, device=dev, seed=w.seed + 1000 * r)
+        bufs.append((x, dy, sq.empty_outputs(w.T, w.H, dev)))
+    sq.prepare()
+    torch.cuda.synchronize()
+
+    def step(i):
+        x, dy, outs = bufs[i % sets]
+        sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *outs)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)  # the stream every call is launched on
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+
+    per_launch_s = gpu_ms / 1e3 / args.steps
+    achieved = nbytes / per_launch_s / 1e9
+    value = nbytes * args.steps / wall / 1e9
+    out = {
+        "metric": "achieved HBM GB/s (+% of MI355X peak) for fused silu fwd/bwd+int8 quant",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "T": w.T, "H": w.H, "group": 128,
+            "bytes_per_step": nbytes, "pairs_per_s": round(w.T * w.H * args.steps / wall, 1),
+            "buffer_sets": sets,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic(w.name),
+            "kernel": "silu_quant_bwd_kernel",
+            "avg_launch_us": round(per_launch_s * 1e6, 3),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        x, dy, _ = bufs[0]
+        out["cpu_baseline"] = cpu_baseline(x, dy, w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

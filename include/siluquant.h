@@ -1,0 +1,108 @@
+/*
+ * libsiluquant -- fused SwiGLU forward recompute, SwiGLU backward and
+ * two-axis int8 quantisation for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one the page "kernelgen-challenge-9-task3-silu-quant"
+ * (githubhelp.com) defines: its entry-point listing gives the name and the
+ * argument order, its two output bullets give the outputs, and its list of
+ * design constraints gives the 128 x 128 tiling, the bf16 round trip before
+ * quantising and the multiplication by a precomputed inverse scale.
+ *
+ * Plain C ABI: pointers and sizes only.  Device pointers are HIP device (or
+ * managed) memory on the current HIP device; the stream is a hipStream_t
+ * passed as void* (NULL = the null stream).
+ */
+#ifndef SILUQUANT_H
+#define SILUQUANT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Every argument check runs on the host before any HIP call,
+ * so a call that returns one of the first five codes has touched neither the
+ * device nor any buffer. */
+enum siluquant_status {
+  SILUQUANT_OK = 0,
+  SILUQUANT_ERR_NULL_PTR = 1,      /* a buffer pointer is NULL while T*H > 0 */
+  SILUQUANT_ERR_BAD_SHAPE = 2,     /* T < 0, H < 0, T or H not a multiple of 128, or too large */
+  SILUQUANT_ERR_BAD_GROUP = 3,     /* group != 128 */
+  SILUQUANT_ERR_MISALIGNED = 4,    /* x, grad_y, grad_input_q, y_q_t not 16-byte aligned,
+                                      or a scale buffer not 4-byte aligned */
+  SILUQUANT_ERR_OVERLAP = 5,       /* two buffers share bytes */
+  SILUQUANT_ERR_DEVICE = 6,        /* a HIP runtime call failed (device query, the one-time
+                                      sigmoid table build) */
+  SILUQUANT_ERR_LAUNCH_FAILED = 7, /* the kernel launch reported an error */
+};
+
+/*
+ * silu_dot_fwd_bwd_quant_fuse -- one fused pass.
+ *
+ * Inputs (read only):
+ *   x       bf16 [T, 2H] row-major; columns [0, H) are gate, [H, 2H) are up.
+ *   grad_y  bf16 [T, H]  row-major; the gradient of y = silu(gate) * up.
+ * Outputs (fully overwritten; every element written):
+ *   grad_input_q  int8 [T, 2H]       [d_gate | d_up] quantised per row, in groups of
+ *                                    128 contiguous channels (d_gate groups first);
+ *   grad_input_s  fp32 [T, 2H/128]   one scale per such group;
+ *   y_q_t         int8 [H, T]        y transposed, quantised in groups of 128
+ *                                    consecutive tokens along each row;
+ *   y_s_t         fp32 [H, T/128]    one scale per such group.
+ * Arithmetic: fp32 throughout, no fused multiply-add.  s = 1 / (1 + exp(-g)) with
+ * exp(-g) correctly rounded to fp32; y = (g*s)*u;
+ * d_gate = ((d*u)*s) * (1 + g*(1 - s)); d_up = d*(g*s); each rounded to bf16
+ * (nearest, ties to even) before quantising.  Per group: amax over the bf16
+ * values, scale = amax/127 (1.0 when amax == 0), inv = 1/scale,
+ * q = clamp(rne(v*inv), -127, 127), with q = 0 for v == 0.
+ *   -128 is never produced.  Inputs must be finite and keep y, d_gate and d_up
+ *   finite.
+ * Sizes: T >= 0 and H >= 0 multiples of 128 (T == 0 or H == 0 is a no-op that
+ *   returns SILUQUANT_OK); T*2H < 2^62; group must be 128.
+ * Ownership: the caller allocates and owns every buffer; the library keeps no
+ *   pointer after the call returns.  Buffers must not overlap.
+ * Asynchrony: the work is enqueued on `stream` and the call returns without
+ *   waiting; outputs are valid once the stream reaches this point.  The first
+ *   call on each device also builds a 31 KB sigmoid table in device memory and
+ *   waits for that build (once per device, per process).
+ * Returns a siluquant_status code.
+ */
+int silu_dot_fwd_bwd_quant_fuse(const void* x, const void* grad_y, int8_t* grad_input_q, float* grad_input_s,
+                                int8_t* y_q_t, float* y_s_t, int64_t T, int64_t H, int64_t group,
+                                void* stream);
+
+/* Builds the sigmoid table on the current device now (otherwise the first
+ * silu_dot_fwd_bwd_quant_fuse call on the device does it).  Blocks until the
+ * table is in place.  Safe to call repeatedly and from several threads. */
+int siluquant_prepare(void);
+
+/* Static text for a status code (never NULL). */
+const char* siluquant_strerror(int status);
+
+/* Bytes the pass must move per call: reads 6*T*H (x, grad_y), writes 3*T*H
+ * int8 codes plus 4*(T*2H/128 + H*T/128) bytes of scales.  Host-only
+ * arithmetic; returns -1 for negative sizes or a group other than 128. */
+int64_t siluquant_algorithmic_bytes(int64_t T, int64_t H, int64_t group);
+
+/* Diagnostics.  They run the fused kernel's own device helpers on their own so
+ * that tests can compare intermediate values bit for bit; the pass itself
+ * never needs them.
+ *
+ * siluquant_eval_sigmoid: s[i] = sigmoid of the bf16 gate gate[i] exactly as the
+ *   fused kernel evaluates it.  gate: bf16 [n] (2-byte aligned), s: fp32 [n]
+ *   (4-byte aligned), both device memory.  Enqueued on `stream`.
+ * siluquant_eval_intermediates: the bf16 values the fused kernel quantises:
+ *   y_bf16 [T, H] = bf16(y) and dgdu_bf16 [T, 2H] = [bf16(d_gate) | bf16(d_up)],
+ *   from x [T, 2H] and grad_y [T, H] as above; any T, H >= 0; 2-byte aligned
+ *   device buffers that must not overlap.  Enqueued on `stream`.
+ * Both return siluquant_status codes with the same meanings as above. */
+int siluquant_eval_sigmoid(const void* gate, float* s, int64_t n, void* stream);
+int siluquant_eval_intermediates(const void* x, const void* grad_y, void* y_bf16, void* dgdu_bf16, int64_t T,
+                                 int64_t H, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SILUQUANT_H */

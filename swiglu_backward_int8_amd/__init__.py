@@ -1,0 +1,178 @@
+"""Python binding for libsiluquant (fused SwiGLU backward + two-axis int8 quantisation).
+
+Argument marshalling only: every step of the pass runs in the HIP kernel inside
+``libsiluquant.so``; PyTorch supplies device memory and the current stream.
+The binding has the name and argument order of the entry point listed on the
+page "kernelgen-challenge-9-task3-silu-quant" (githubhelp.com).  If the built
+library is missing the call raises; there is no other implementation behind it.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsiluquant.so")
+GROUP = 128
+
+SILUQUANT_OK = 0
+_ERRORS = {
+    1: (ValueError, "NULL_PTR"),
+    2: (ValueError, "BAD_SHAPE"),
+    3: (ValueError, "BAD_GROUP"),
+    4: (ValueError, "MISALIGNED"),
+    5: (ValueError, "OVERLAP"),
+    6: (RuntimeError, "DEVICE"),
+    7: (RuntimeError, "LAUNCH_FAILED"),
+}
+
+EXPORTED = ("silu_dot_fwd_bwd_quant_fuse", "siluquant_prepare", "siluquant_strerror",
+            "siluquant_algorithmic_bytes", "siluquant_eval_sigmoid", "siluquant_eval_intermediates")
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libsiluquant.so is not built (run swiglu_backward_int8_amd/_build.py or "
+                               "__graft_entry__.build()); there is no fallback implementation")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        L.silu_dot_fwd_bwd_quant_fuse.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
+        L.silu_dot_fwd_bwd_quant_fuse.restype = ctypes.c_int
+        L.siluquant_prepare.argtypes = []
+        L.siluquant_prepare.restype = ctypes.c_int
+        L.siluquant_strerror.argtypes = [ctypes.c_int]
+        L.siluquant_strerror.restype = ctypes.c_char_p
+        L.siluquant_algorithmic_bytes.argtypes = [i64, i64, i64]
+        L.siluquant_algorithmic_bytes.restype = i64
+        L.siluquant_eval_sigmoid.argtypes = [vp, vp, i64, vp]
+        L.siluquant_eval_sigmoid.restype = ctypes.c_int
+        L.siluquant_eval_intermediates.argtypes = [vp, vp, vp, vp, i64, i64, vp]
+        L.siluquant_eval_intermediates.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().siluquant_strerror(int(code)).decode()
+
+
+def algorithmic_bytes(T: int, H: int, group: int = GROUP) -> int:
+    """Bytes one call must move (reads + writes), as the library counts them."""
+    return int(lib().siluquant_algorithmic_bytes(int(T), int(H), int(group)))
+
+
+def _check(code: int, what: str):
+    if code != SILUQUANT_OK:
+        exc, name = _ERRORS.get(code, (RuntimeError, "UNKNOWN"))
+        raise exc("%s failed: %s (%s)" % (what, name, strerror(code)))
+
+
+def output_shapes(T: int, H: int, group: int = GROUP) -> dict:
+    return {
+        "grad_input_q": (T, 2 * H),
+        "grad_input_s": (T, 2 * H // group),
+        "y_q_t": (H, T),
+        "y_s_t": (H, T // group),
+    }
+
+
+def raw_call(x_ptr: int, grad_y_ptr: int, gq_ptr: int, gs_ptr: int, yq_ptr: int, ys_ptr: int, T: int, H: int,
+             group: int, stream: int) -> int:
+    """The C entry point with plain integers for pointers; returns the status code."""
+    return int(lib().silu_dot_fwd_bwd_quant_fuse(x_ptr, grad_y_ptr, gq_ptr, gs_ptr, yq_ptr, ys_ptr, int(T),
+                                                 int(H), int(group), stream))
+
+
+def silu_dot_fwd_bwd_quant_fuse(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size: int = GROUP):
+    """Recompute y = silu(gate) * up from x = [gate | up] and write the int8 codes
+    and fp32 scales of [d_gate, d_up] (per row, 128-channel groups) and of y^T
+    (128-token groups) into the given output tensors.  Enqueued on the current
+    stream of x's device; returns None."""
+    import torch
+
+    T, H = int(grad_y.shape[0]) if grad_y.dim() == 2 else -1, int(grad_y.shape[-1])
+    if x.dim() != 2 or grad_y.dim() != 2 or tuple(x.shape) != (T, 2 * H):
+        raise ValueError("x must be [T, 2H] and grad_y [T, H]; got %s and %s" % (tuple(x.shape), tuple(grad_y.shape)))
+    if group_size != GROUP:
+        raise ValueError("group_size must be 128")
+    want = output_shapes(T, H, group_size) if T % GROUP == 0 and H % GROUP == 0 else None
+    checks = [
+        ("x", x, torch.bfloat16, (T, 2 * H)),
+        ("grad_y", grad_y, torch.bfloat16, (T, H)),
+        ("grad_input_q", grad_input_q, torch.int8, want and want["grad_input_q"]),
+        ("grad_input_s", grad_input_s, torch.float32, want and want["grad_input_s"]),
+        ("y_q_t", y_q_t, torch.int8, want and want["y_q_t"]),
+        ("y_s_t", y_s_t, torch.float32, want and want["y_s_t"]),
+    ]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU; got %s" % dev)
+    for name, t, dt, shape in checks:
+        if t.dtype != dt:
+            raise ValueError("%s must be %s, got %s" % (name, dt, t.dtype))
+        if t.device != dev:
+            raise ValueError("%s is on %s, x on %s" % (name, t.device, dev))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        code = raw_call(x.data_ptr(), grad_y.data_ptr(), grad_input_q.data_ptr(), grad_input_s.data_ptr(),
+                        y_q_t.data_ptr(), y_s_t.data_ptr(), T, H, group_size, stream)
+    _check(code, "silu_dot_fwd_bwd_quant_fuse")
+
+
+def empty_outputs(T: int, H: int, device, group: int = GROUP):
+    """Freshly allocated (grad_input_q, grad_input_s, y_q_t, y_s_t) for a call."""
+    import torch
+
+    s = output_shapes(T, H, group)
+    return (torch.empty(s["grad_input_q"], dtype=torch.int8, device=device),
+            torch.empty(s["grad_input_s"], dtype=torch.float32, device=device),
+            torch.empty(s["y_q_t"], dtype=torch.int8, device=device),
+            torch.empty(s["y_s_t"], dtype=torch.float32, device=device))
+
+
+def prepare():
+    """Build the sigmoid table on the current device now (the first call does it otherwise)."""
+    _check(int(lib().siluquant_prepare()), "siluquant_prepare")
+
+
+def eval_sigmoid(gate):
+    """Diagnostic: the kernel's sigmoid of each bf16 gate (a 1-D CUDA bf16 tensor)."""
+    import torch
+
+    if gate.dtype != torch.bfloat16 or gate.device.type != "cuda" or not gate.is_contiguous():
+        raise ValueError("gate must be a contiguous bf16 GPU tensor")
+    out = torch.empty(gate.shape, dtype=torch.float32, device=gate.device)
+    with torch.cuda.device(gate.device):
+        code = lib().siluquant_eval_sigmoid(gate.data_ptr(), out.data_ptr(), gate.numel(),
+                                            torch.cuda.current_stream(gate.device).cuda_stream)
+    _check(code, "siluquant_eval_sigmoid")
+    return out
+
+
+def eval_intermediates(x, grad_y):
+    """Diagnostic: bf16 y [T, H] and [d_gate | d_up] [T, 2H] as the kernel computes them."""
+    import torch
+
+    T, H = grad_y.shape
+    for name, t in (("x", x), ("grad_y", grad_y)):
+        if t.dtype != torch.bfloat16 or t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous bf16 GPU tensor" % name)
+    if tuple(x.shape) != (T, 2 * H):
+        raise ValueError("x must be [T, 2H]")
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    d = torch.empty((T, 2 * H), dtype=torch.bfloat16, device=x.device)
+    with torch.cuda.device(x.device):
+        code = lib().siluquant_eval_intermediates(x.data_ptr(), grad_y.data_ptr(), y.data_ptr(), d.data_ptr(),
+                                                  T, H, torch.cuda.current_stream(x.device).cuda_stream)
+    _check(code, "siluquant_eval_intermediates")
+    return y, d

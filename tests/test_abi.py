@@ -1,0 +1,137 @@
+"""The C-ABI library: it loads, exports every entry point its header declares,
+and rejects bad arguments before touching any device (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import swiglu_backward_int8_amd as sq
+from swiglu_backward_int8_amd import _build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "siluquant.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sq.LIB_PATH):
+        _build.build()
+    return sq.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    assert "silu_dot_fwd_bwd_quant_fuse" in names
+    assert set(names) == set(sq.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_product_library_does_not_link_the_oracle():
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", sq.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert "oracle" not in out
+    deps = subprocess.run(["readelf", "-d", sq.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert "liboracle" not in deps
+
+
+# Fake, well-aligned, non-overlapping addresses: every call below must be
+# rejected by the host-side checks, so none of them is ever dereferenced.
+BASE = 1 << 40
+
+
+def _ptrs(T, H, misalign=None, null=None, overlap=False):
+    sizes = [4 * T * H, 2 * T * H, 2 * T * H, 4 * (2 * T * H // 128), T * H, 4 * (T * H // 128)]
+    ptrs, at = [], BASE
+    for s in sizes:
+        ptrs.append(at)
+        at += ((max(s, 1) + 4095) // 4096) * 4096
+    if misalign is not None:
+        ptrs[misalign] += 2
+    if null is not None:
+        ptrs[null] = 0
+    if overlap:
+        ptrs[4] = ptrs[2] + 64  # y_q_t inside grad_input_q
+    return ptrs
+
+
+@pytest.mark.parametrize("T,H,group,code", [
+    (256, 256, 64, 3), (256, 256, 0, 3), (256, 256, 256, 3),
+    (-128, 256, 128, 2), (256, -128, 128, 2), (200, 256, 128, 2), (256, 200, 128, 2), (256, 136, 128, 2),
+])
+def test_bad_shape_and_group(lib, T, H, group, code):
+    assert sq.raw_call(*_ptrs(abs(T), abs(H)), T, H, group, 0) == code
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_null_pointer(lib, which):
+    assert sq.raw_call(*_ptrs(256, 256, null=which), 256, 256, 128, 0) == 1
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_misaligned(lib, which):
+    assert sq.raw_call(*_ptrs(256, 256, misalign=which), 256, 256, 128, 0) == 4
+
+
+def test_overlap(lib):
+    assert sq.raw_call(*_ptrs(256, 256, overlap=True), 256, 256, 128, 0) == 5
+    p = _ptrs(256, 256)
+    p[1] = p[0]  # grad_y aliases x
+    assert sq.raw_call(*p, 256, 256, 128, 0) == 5
+
+
+def test_empty_is_a_no_op(lib):
+    # nothing to do: success without any pointer being looked at
+    assert sq.raw_call(0, 0, 0, 0, 0, 0, 0, 256, 128, 0) == 0
+    assert sq.raw_call(0, 0, 0, 0, 0, 0, 256, 0, 128, 0) == 0
+
+
+def test_diagnostics_reject_bad_arguments(lib):
+    assert lib.siluquant_eval_sigmoid(None, None, -1, None) == 2
+    assert lib.siluquant_eval_sigmoid(None, None, 0, None) == 0
+    assert lib.siluquant_eval_sigmoid(None, BASE, 10, None) == 1
+    assert lib.siluquant_eval_sigmoid(BASE + 1, BASE + 4096, 10, None) == 4
+    assert lib.siluquant_eval_sigmoid(BASE, BASE + 8, 10, None) == 5
+    assert lib.siluquant_eval_intermediates(None, None, None, None, 128, -1, None) == 2
+    assert lib.siluquant_eval_intermediates(BASE, None, BASE, BASE, 128, 128, None) == 1
+
+
+def test_strerror(lib):
+    for code in range(8):
+        assert sq.strerror(code)
+    assert sq.strerror(99) == "unknown status"
+
+
+# Algorithmic bytes per call: reads x (4 B) and grad_y (2 B) per (t, h) pair,
+# writes 2 + 1 code bytes and one fp32 scale per 128 codes on each axis.
+# Totals counted tensor by tensor for the five workloads.
+BYTES = {
+    (256, 256): 262_144 + 131_072 + 131_072 + 4_096 + 65_536 + 2_048,
+    (4096, 1408): 23_068_672 + 11_534_336 + 11_534_336 + 360_448 + 5_767_168 + 180_224,
+    (8192, 4096): 134_217_728 + 67_108_864 + 67_108_864 + 2_097_152 + 33_554_432 + 1_048_576,
+    (16384, 11008): 721_420_288 + 360_710_144 + 360_710_144 + 11_272_192 + 180_355_072 + 5_636_096,
+    (32768, 2048): 268_435_456 + 134_217_728 + 134_217_728 + 4_194_304 + 67_108_864 + 2_097_152,
+}
+
+
+@pytest.mark.parametrize("shape", sorted(BYTES))
+def test_algorithmic_bytes(lib, shape):
+    assert sq.algorithmic_bytes(*shape) == BYTES[shape]
+    assert BYTES[(16384, 11008)] == 1_640_103_936
+
+
+def test_algorithmic_bytes_rejects(lib):
+    assert sq.algorithmic_bytes(-1, 128) == -1
+    assert sq.algorithmic_bytes(128, 128, 64) == -1

@@ -1,0 +1,219 @@
+"""Parity of the HIP path with the CPU oracle (GPU).
+
+Every case generates seeded inputs, runs the library through its C ABI (via the
+thin binding), runs the oracle on the same bits, and compares element by
+element.  The bar: every scale within 1e-6 relative of the oracle's, every int8
+code equal except that |dq| == 1 is tolerated on at most 1e-4 of the codes of
+each output (never more than 1).  The cases report how many codes differ; the
+expected count is zero, because the kernel reproduces the oracle's arithmetic
+operation for operation.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import swiglu_backward_int8_amd as sq
+from exact import all_finite_bf16
+from swiglu_backward_int8_amd.inputs import WORKLOADS, make_inputs, random_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+SCALE_RTOL = 1e-6
+Q_FRACTION = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    sq.lib()
+    sq.prepare()
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_gpu(x, grad_y):
+    T, H = grad_y.shape
+    outs = sq.empty_outputs(T, H, x.device)
+    for o in outs:  # poison: every element must be written
+        o.fill_(-7 if o.dtype == torch.int8 else float("nan"))
+    sq.silu_dot_fwd_bwd_quant_fuse(x, grad_y, *outs)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in outs]
+
+
+def compare(got, want, label=""):
+    names = ("grad_input_q", "grad_input_s", "y_q_t", "y_s_t")
+    report = {}
+    for name, g, w in zip(names, got, want):
+        assert g.shape == w.shape, (name, g.shape, w.shape)
+        if g.dtype == np.float32:
+            assert not np.isnan(g).any(), "%s %s: unwritten scales" % (label, name)
+            rel = np.abs(g.astype(np.float64) - w.astype(np.float64)) / np.maximum(np.abs(w.astype(np.float64)),
+                                                                                1e-300)
+            bad = int((rel > SCALE_RTOL).sum())
+            report[name] = bad
+            assert bad == 0, "%s %s: %d scales off, worst rel %g" % (label, name, bad, rel.max())
+        else:
+            d = np.abs(g.astype(np.int16) - w.astype(np.int16))
+            n1 = int((d == 1).sum())
+            report[name] = n1
+            assert int(d.max(initial=0)) <= 1, "%s %s: |dq| up to %d" % (label, name, int(d.max()))
+            assert n1 <= Q_FRACTION * d.size, "%s %s: %d codes off by one" % (label, name, n1)
+    print("%s mismatches %s" % (label, report), flush=True)
+    return report
+
+
+def check(x, grad_y, label):
+    got = run_gpu(x, grad_y)
+    want = oracle.silu_dot_fwd_bwd_quant_fuse(_bits(x), _bits(grad_y))
+    return compare(got, want, label)
+
+
+def test_sigmoid_every_bf16_gate_bit_exact():
+    bits = all_finite_bf16()
+    gate = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    got = sq.eval_sigmoid(gate).cpu().numpy()
+    want = np.array([oracle.sigmoid(oracle.bf16_to_f32(int(b))) for b in bits], dtype=np.float32)
+    diff = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+    assert diff.size == 0, [(hex(int(bits[i])), float(got[i]), float(want[i])) for i in diff[:8]]
+
+
+@pytest.mark.parametrize("name", ["t256_h256", "t4096_h1408", "t32768_h2048_outliers"])
+def test_intermediates_bit_exact(name):
+    T = 1024 if WORKLOADS[name].T > 4096 else None
+    x, dy = make_inputs(name, device=DEV, T=T)
+    y, d = sq.eval_intermediates(x, dy)
+    Y, D = oracle.intermediates(_bits(x), _bits(dy))
+    gy = (_bits(y).astype(np.uint32) << 16).view(np.float32)
+    gd = (_bits(d).astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(gy.view(np.uint32), Y.view(np.uint32)), int((gy != Y).sum())
+    assert np.array_equal(gd.view(np.uint32), D.view(np.uint32)), int((gd != D).sum())
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_parity(name):
+    print("case", name, flush=True)
+    x, dy = make_inputs(name, device=DEV)
+    rep = check(x, dy, name)
+    assert sum(rep.values()) == 0  # the kernel is expected to be exact
+
+
+@pytest.mark.parametrize("name,seed", [("t4096_h1408", 1001), ("t8192_h4096", 1002),
+                                       ("t32768_h2048_outliers", 1004)])
+def test_workload_parity_second_seed(name, seed):
+    print("case", name, seed, flush=True)
+    x, dy = make_inputs(name, device=DEV, seed=seed)
+    check(x, dy, "%s seed %d" % (name, seed))
+
+
+@pytest.mark.parametrize("T,H", [(128, 128), (128, 1280), (1280, 128), (384, 640), (2048, 256)])
+def test_shapes(T, H):
+    x, dy = random_inputs(T, H, device=DEV, seed=T + H)
+    check(x, dy, "T=%d H=%d" % (T, H))
+
+
+def _const(T, H, g, u, d):
+    x = torch.empty((T, 2 * H), dtype=torch.bfloat16, device=DEV)
+    x[:, :H] = g
+    x[:, H:] = u
+    return x, torch.full((T, H), d, dtype=torch.bfloat16, device=DEV)
+
+
+@pytest.mark.parametrize("g,u,d", [(0.0, 1.0, 1.0), (1.0, 1.0, 1.0), (20.0, 1.5, 0.25), (-2.0, 1.0, 1.0),
+                                   (-100.0, 1.0, 1.0), (0.0, 0.0, 0.0)])
+def test_constant_inputs(g, u, d):
+    x, dy = _const(256, 256, g, u, d)
+    check(x, dy, "const %r" % ((g, u, d),))
+
+
+def test_saturated_gate_ties_to_even():
+    T = H = 128
+    x, dy = _const(T, H, 100.0, 0.0, 1.0)
+    row = torch.tensor([127.0, 2.5, 0.5, -2.5, 126.5, 3.5, -0.5, 1.5], dtype=torch.bfloat16, device=DEV)
+    x[:, H:H + 8] = row
+    got = run_gpu(x, dy)
+    assert got[0][0, :8].tolist() == [127, 2, 0, -2, 126, 4, 0, 2]
+    check(x, dy, "ties")
+
+
+@pytest.mark.parametrize("lo,hi", [(16.0, 17.5), (-90.0, -87.0), (-88.75, -87.5), (-1e-6, 1e-6)])
+def test_gate_edge_ranges(lo, hi):
+    # saturation edges, the subnormal-sigmoid band and the s == 1/2 band
+    T, H = 256, 256
+    gen = torch.Generator(device=DEV).manual_seed(99)
+    g = lo + (hi - lo) * torch.rand((T, H), generator=gen, device=DEV)
+    u = torch.randn((T, H), generator=gen, device=DEV)
+    d = torch.randn((T, H), generator=gen, device=DEV)
+    x = torch.cat([g, u], dim=1).to(torch.bfloat16).contiguous()
+    check(x, d.to(torch.bfloat16), "gates in [%g, %g]" % (lo, hi))
+
+
+def test_tiny_groups_overflowing_inverse():
+    # Groups whose maximum is below 127 * 2^-128: 1/scale overflows to inf and
+    # the clamp / zero rule decides the codes.  gate = 20 (s = 1), grad_y = 1,
+    # so d_gate = up exactly.
+    T = H = 128
+    x, dy = _const(T, H, 20.0, 0.0, 1.0)
+    tiny = torch.tensor([2.0**-130, -(2.0**-131), 0.0, 2.0**-133], dtype=torch.float32)
+    x[:, H:H + 4] = tiny.to(torch.bfloat16).to(DEV)
+    got = run_gpu(x, dy)
+    assert got[0][0, :4].tolist() == [127, -127, 0, 127]  # every non-zero clamps
+    check(x, dy, "tiny groups")
+
+
+def test_zero_rows_and_outliers_small():
+    x, dy = make_inputs("t32768_h2048_outliers", device=DEV, T=1024)
+    rep = check(x, dy, "outliers T=1024")
+    assert sum(rep.values()) == 0
+
+
+def test_deterministic():
+    x, dy = make_inputs("t4096_h1408", device=DEV)
+    a = run_gpu(x, dy)
+    b = run_gpu(x, dy)
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+def test_non_default_stream():
+    x, dy = make_inputs("t4096_h1408", device=DEV)
+    T, H = dy.shape
+    s = torch.cuda.Stream(device=DEV)
+    outs = sq.empty_outputs(T, H, DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *outs)
+    s.synchronize()
+    got = [o.cpu().numpy() for o in outs]
+    compare(got, oracle.silu_dot_fwd_bwd_quant_fuse(_bits(x), _bits(dy)), "side stream")
+
+
+def test_binding_rejects_bad_tensors():
+    x, dy = random_inputs(128, 128, device=DEV)
+    outs = list(sq.empty_outputs(128, 128, DEV))
+    with pytest.raises(ValueError):
+        sq.silu_dot_fwd_bwd_quant_fuse(x.float(), dy, *outs)
+    with pytest.raises(ValueError):
+        sq.silu_dot_fwd_bwd_quant_fuse(x, dy, outs[0], outs[1].double(), outs[2], outs[3])
+    with pytest.raises(ValueError):
+        sq.silu_dot_fwd_bwd_quant_fuse(x[:, :128], dy[:, :64], *outs)
+    with pytest.raises(ValueError):
+        x2, dy2 = random_inputs(200, 128, device=DEV)
+        sq.silu_dot_fwd_bwd_quant_fuse(x2, dy2, *sq.empty_outputs(128, 128, DEV))
+    with pytest.raises(ValueError):
+        sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *outs, group_size=64)
+
+
+def test_empty_inputs_are_no_ops():
+    for T, H in ((0, 128), (128, 0)):
+        x = torch.empty((T, 2 * H), dtype=torch.bfloat16, device=DEV)
+        dy = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+        sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *sq.empty_outputs(T, H, DEV))
+    torch.cuda.synchronize()
