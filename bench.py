@@ -72,6 +72,34 @@ def cpu_baseline(x, dy, w):
     }
 
 
+def stream_probes(dev, reps: int = 20):
+    """Plain streaming kernels of known size, for the attainable bandwidth and for
+    scaling hardware byte counters: a 1 GiB copy (1 GiB read + 1 GiB written) and
+    c = a + b on bf16 (2 reads : 1 write, close to this pass's 1.94 : 1)."""
+    import torch
+
+    n = 2**30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    a = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+    b = torch.ones_like(a)
+    c = torch.empty_like(a)
+    res = {}
+    for name, fn, nbytes in (("copy_1GiB", lambda: dst.copy_(src), 2 * n),
+                             ("add_bf16_2r1w", lambda: torch.add(a, b, out=c), 3 * n)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / reps
+        res[name] = {"bytes": nbytes, "us": round(sec * 1e6, 2), "GB/s": round(nbytes / sec / 1e9, 1)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -79,6 +107,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="t16384_h11008")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probes", action="store_true",
+                    help="also time a plain 1 GiB copy and a 2-read/1-write bf16 add (reference streams)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this pass runs on one GPU; --gpus %d is not supported (the tensors of a "
@@ -160,6 +190,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.probes:
+        out["probes"] = stream_probes(dev)
     if not args.no_cpu_baseline:
         x, dy, _ = bufs[0]
         out["cpu_baseline"] = cpu_baseline(x, dy, w)

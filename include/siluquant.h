@@ -54,8 +54,9 @@ enum siluquant_status {
  * exp(-g) correctly rounded to fp32; y = (g*s)*u;
  * d_gate = ((d*u)*s) * (1 + g*(1 - s)); d_up = d*(g*s); each rounded to bf16
  * (nearest, ties to even) before quantising.  Per group: amax over the bf16
- * values, scale = amax/127 (1.0 when amax == 0), inv = 1/scale,
- * q = clamp(rne(v*inv), -127, 127), with q = 0 for v == 0.
+ * values, scale = amax/127 (1.0 when amax == 0), inv = 1/scale (fp32),
+ * q = clamp(rne(v*inv), -127, 127) rounding the exact product of the bf16 value
+ * and the fp32 inverse (one rounding, ties to even), with q = 0 for v == 0.
  *   -128 is never produced.  Inputs must be finite and keep y, d_gate and d_up
  *   finite.
  * Sizes: T >= 0 and H >= 0 multiples of 128 (T == 0 or H == 0 is a no-op that

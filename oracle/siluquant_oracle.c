@@ -30,8 +30,11 @@
  *   - bf16 rounding is round-to-nearest-even on the fp32 bit pattern, with
  *     subnormals kept;
  *   - the group maximum is taken over the bf16-rounded values;
- *   - scale = amax / 127 (1.0 when amax == 0), inv = 1 / scale,
- *     q = clamp(rne(v * inv), -127, 127), and q = 0 whenever v == 0 (this
+ *   - scale = amax / 127 (1.0 when amax == 0), inv = 1 / scale (both fp32),
+ *     q = clamp(rne(v * inv), -127, 127) where v * inv is the exact product of
+ *     the bf16 value and the fp32 inverse (the page says to multiply by the
+ *     inverse and leaves the precision of that product open; the exact
+ *     product is what the formula states), and q = 0 whenever v == 0 (this
  *     avoids 0 * inf when a group's scale is so small that 1/scale overflows);
  *   - a trailing group shorter than `group` (T or 2H not a multiple of it) is
  *     quantised over the elements it has.
@@ -114,10 +117,11 @@ ORACLE_API float oracle_quant_group(const float* v, int64_t n, int64_t stride, i
     float x = v[i * stride];
     int8_t out = 0;
     if (x != 0.0f) {
-      float t = x * inv;
-      float r = nearbyintf(t); /* default rounding mode: to nearest, ties to even */
-      if (r > 127.0f) r = 127.0f;
-      if (r < -127.0f) r = -127.0f;
+      /* x has 8 significant bits and inv 24, so the double product is exact */
+      double t = (double)x * (double)inv;
+      double r = nearbyint(t); /* default rounding mode: to nearest, ties to even */
+      if (r > 127.0) r = 127.0;
+      if (r < -127.0) r = -127.0;
       out = (int8_t)r;
     }
     q[i * qstride] = out;

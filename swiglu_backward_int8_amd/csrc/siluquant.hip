@@ -39,7 +39,17 @@ namespace {
 
 constexpr int kGroup = 128;
 constexpr int kTile = 128;
-constexpr int kThreads = 512;
+// Lane (q, p) of a workgroup owns tokens kRows*q .. kRows*q + kRows - 1 and
+// channels 8p .. 8p+7 of the tile: 16 lanes span the tile's 128 channels and
+// 128 / kRows groups of 16 lanes span its 128 tokens.
+#ifndef SILUQUANT_ROWS_PER_LANE
+#define SILUQUANT_ROWS_PER_LANE 2
+#endif
+constexpr int kRows = SILUQUANT_ROWS_PER_LANE;
+static_assert(kRows == 2 || kRows == 4, "rows per lane");
+constexpr int kQ = kTile / kRows;        // lane groups along the tokens
+constexpr int kThreads = 16 * kQ;        // 1024 for two rows per lane
+constexpr int kWorkgroupsPerCU = 1;
 
 // Sigmoid table: entry k of half `sign` holds s(g) for the bf16 gate with bits
 // (sign << 15) | (kSigM0 + k).  Every magnitude at or below kSigM0 gives
@@ -52,16 +62,16 @@ static_assert(kSigEntries % 4 == 0, "table copied in 16-byte pieces");
 
 __device__ float g_sigma_tab[kSigEntries];
 
-// LDS layout (floats).  The table stays live through the elementwise phase;
-// the partial maxima and the transpose buffer follow it.
-constexpr int kRowPartStride = 2 * kTile + 4;  // 260: rows of 16-byte writes spread over banks
+// LDS layout (floats).  The table stays live for the workgroup's lifetime;
+// then come the partial maxima, the inverse scales and a flag.  The transposed
+// y codes reuse the row partials once those have been reduced.
+constexpr int kRowPartStride = 2 * kTile + 4;  // 260: a wave's writes spread over the banks
 constexpr int kRowPartFloats = 16 * kRowPartStride;
-constexpr int kColPartFloats = 32 * kTile;
+constexpr int kColPartFloats = kQ * kTile;
 constexpr int kInvFloats = 3 * kTile;  // 256 row groups + 128 column groups
 constexpr int kYqtBytes = kTile * kTile;
 static_assert(kYqtBytes <= kRowPartFloats * 4, "transpose buffer reuses the row partials");
-
-constexpr int kLdsFloats = kSigEntries + kRowPartFloats + kColPartFloats + kInvFloats;
+constexpr int kLdsFloats = kSigEntries + kRowPartFloats + kColPartFloats + kInvFloats + 4;
 
 __global__ void build_sigma_table_kernel() {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -74,54 +84,81 @@ __global__ void build_sigma_table_kernel() {
   g_sigma_tab[i] = 1.0f / den;
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Every input byte is read once and every output byte written once, so all
+// global traffic is marked non-temporal (streaming): it does not displace the
+// lines that neighbouring workgroups' scale writes are merging into.
+__device__ __forceinline__ uint4 load_stream(const void* ptr) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(void* ptr, uint4 v) {
+  __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(ptr));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Round to the nearest bf16 (ties to even) and return it widened to fp32.
-__device__ __forceinline__ float round_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u = u + 0x7fffu + ((u >> 16) & 1u);
-  return __uint_as_float(u & 0xffff0000u);
+// Two fp32 values -> two bf16 (round to nearest, ties to even, subnormals
+// kept; one v_cvt_pk_bf16_f32 on gfx950), a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
-__device__ __forceinline__ int sigma_index(uint32_t b16) {
-  int k = (int)(b16 & 0x7fffu) - (int)kSigM0;
-  k = min(max(k, 0), kSigL - 1);
-  return k + (int)(b16 >> 15) * kSigL;
+// Byte offsets into the table for the two bf16 gates packed in w, computed on
+// both halves at once with 16-bit packed integer instructions.
+__device__ __forceinline__ void sigma_offsets2(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  u16x2 v = __builtin_bit_cast(u16x2, w);
+  u16x2 k = __builtin_elementwise_sub_sat(v & (u16x2)(0x7fff), (u16x2)(kSigM0));
+  k = __builtin_elementwise_min(k, (u16x2)(kSigL - 1));
+  u16x2 idx = (v >> 15) * (u16x2)(kSigL) + k;  // < 2 * kSigL
+  uint32_t b = __builtin_bit_cast(uint32_t, (u16x2)(idx << 2));
+  lo = b & 0xffffu;
+  hi = b >> 16;
 }
 
-// One (t, h) position: gate g (bits gb), up u, grad_y d -> bf16-rounded
-// y, d_gate, d_up.  Operation order is fixed; no contraction (-ffp-contract=off).
-__device__ __forceinline__ void pair(const float* __restrict__ tab, uint32_t gb, float g, float u, float d,
-                                     float& y, float& dg, float& du) {
-  float s = tab[sigma_index(gb)];
+__device__ __forceinline__ float lds_f32(const float* base, uint32_t byte_off) {
+  return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+
+// One (t, h) position before rounding: gate g, up u, grad_y d, sigmoid s.
+// Operation order is fixed; no contraction (-ffp-contract=off).
+__device__ __forceinline__ void pair_f32(float s, float g, float u, float d, float& y, float& dg, float& du) {
   float silu = g * s;
-  float yv = silu * u;
+  y = silu * u;
   float a = d * u;
   float b = a * s;
   float c = 1.0f - s;
   float k = g * c;
   float m = 1.0f + k;
-  float dgv = b * m;
-  float duv = d * silu;
-  y = round_bf16(yv);
-  dg = round_bf16(dgv);
-  du = round_bf16(duv);
+  dg = b * m;
+  du = d * silu;
 }
 
-__device__ __forceinline__ float amax2(float a, float b) { return fmaxf(fabsf(a), fabsf(b)); }
+__device__ __forceinline__ float amax3(float m, float a, float b) { return fmaxf(m, fmaxf(fabsf(a), fabsf(b))); }
 
 // Quantise one value: the low byte of the returned word is the int8 code.
-// Adding 1.5 * 2^23 moves |t| <= 128 into the range where fp32 spacing is 1,
-// so the add itself rounds to the nearest integer, ties to even, and the
-// integer sits in the low mantissa bits in two's complement.  With a finite
-// inverse scale |v * inv| stays below 127.5, so no clamp is needed; kSafe adds
-// the clamp and the v == 0 rule for groups whose inverse overflowed.
+// One fused multiply-add forms v * inv + 1.5 * 2^23 with a single rounding.
+// For |v * inv| < 2^22 the sum lies where the fp32 spacing is 1, so that
+// rounding is the nearest integer to the exact product, ties to even (the
+// offset is even), and the integer sits in the low mantissa bits in two's
+// complement.  With a finite inverse scale |v * inv| <= 127 * (1 + 2^-22), so
+// the code is within [-127, 127] without a clamp.  kSafe serves groups whose
+// inverse overflowed to +inf: it clamps to +-127 and maps v == 0 to 0, and
+// gives the same word as the fast form for every finite inverse.
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 template <bool kSafe>
 __device__ __forceinline__ uint32_t code_word(float v, float inv) {
-  float t = v * inv;
-  if (kSafe) t = (v == 0.0f) ? 0.0f : fminf(fmaxf(t, -127.0f), 127.0f);
-  return __float_as_uint(t + 12582912.0f);
+  float r = __builtin_fmaf(v, inv, kMagic);
+  if (kSafe) {
+    r = __builtin_amdgcn_fmed3f(r, kMagic - 127.0f, kMagic + 127.0f);
+    r = (v == 0.0f) ? kMagic : r;
+  }
+  return __float_as_uint(r);
 }
 
 // Low bytes of four words -> one word, b0 in the lowest byte.
@@ -131,78 +168,214 @@ __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2,
   return (b3 << 24) | b;
 }
 
-__device__ __forceinline__ float group_scale(float amax) { return amax == 0.0f ? 1.0f : amax / 127.0f; }
+// Low bytes of two words -> the low half of one word, b0 first.
+__device__ __forceinline__ uint32_t pack2(uint32_t b0, uint32_t b1) {
+  return __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+}
 
+// Eight codes from four packed-bf16 words with one inverse scale.
 template <bool kSafe>
-__device__ __forceinline__ void quantise_tile(const float (&Y)[4][8], const float (&DG)[4][8],
-                                              const float (&DU)[4][8], const float4 inv_dg, const float4 inv_du,
-                                              const float4 inv_y0, const float4 inv_y1, int8_t* __restrict__ gq_row0,
-                                              int64_t two_h, int64_t H, uint32_t* __restrict__ yqt_words, int p,
-                                              int q) {
-  const float idg[4] = {inv_dg.x, inv_dg.y, inv_dg.z, inv_dg.w};
-  const float idu[4] = {inv_du.x, inv_du.y, inv_du.z, inv_du.w};
-  const float iy[8] = {inv_y0.x, inv_y0.y, inv_y0.z, inv_y0.w, inv_y1.x, inv_y1.y, inv_y1.z, inv_y1.w};
+__device__ __forceinline__ uint2 codes8(const uint32_t (&w)[4], float inv) {
+  return make_uint2(pack4(code_word<kSafe>(bf16_lo(w[0]), inv), code_word<kSafe>(bf16_hi(w[0]), inv),
+                          code_word<kSafe>(bf16_lo(w[1]), inv), code_word<kSafe>(bf16_hi(w[1]), inv)),
+                    pack4(code_word<kSafe>(bf16_lo(w[2]), inv), code_word<kSafe>(bf16_hi(w[2]), inv),
+                          code_word<kSafe>(bf16_lo(w[3]), inv), code_word<kSafe>(bf16_hi(w[3]), inv)));
+}
+
+// Scale of a group from the maximum of its unrounded values.  Rounding to
+// bf16 is monotone and odd, so the largest rounded magnitude is the rounding
+// of the largest unrounded magnitude.
+__device__ __forceinline__ float group_scale(float amax_unrounded) {
+  float amax = bf16_lo(pack_bf16(amax_unrounded, 0.0f));
+  return amax == 0.0f ? 1.0f : amax / 127.0f;
+}
+
+struct TileIn {
+  uint4 g[kRows], u[kRows], d[kRows];
+};
+
+// The tile base is uniform (scalar registers) and the lane's byte offset is a
+// fixed 32-bit value.
+__device__ __forceinline__ void load_tile(TileIn& in, const char* xt, const char* dyt, uint32_t lane_x,
+                                          uint32_t lane_dy, int64_t x_row_bytes, int64_t dy_row_bytes) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t w[8], v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      w[j] = code_word<kSafe>(DG[i][j], idg[i]);
-      v[j] = code_word<kSafe>(DU[i][j], idu[i]);
-    }
-    uint2 cg = make_uint2(pack4(w[0], w[1], w[2], w[3]), pack4(w[4], w[5], w[6], w[7]));
-    uint2 cu = make_uint2(pack4(v[0], v[1], v[2], v[3]), pack4(v[4], v[5], v[6], v[7]));
-    int8_t* row = gq_row0 + (int64_t)i * two_h;
-    *reinterpret_cast<uint2*>(row) = cg;
-    *reinterpret_cast<uint2*>(row + H) = cu;
-  }
-  // y codes, transposed: channel 8p + j gets tokens 4q..4q+3 as one word.
-  // Word q of transposed row h is stored at position q ^ (4 * ((h >> 3) & 7)),
-  // which spreads a wave's 64 writes evenly over the 32 banks and keeps every
-  // aligned group of four words (16 tokens) contiguous for the read-back.
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t word = pack4(code_word<kSafe>(Y[0][j], iy[j]), code_word<kSafe>(Y[1][j], iy[j]),
-                          code_word<kSafe>(Y[2][j], iy[j]), code_word<kSafe>(Y[3][j], iy[j]));
-    int h = 8 * p + j;
-    yqt_words[h * 32 + (q ^ ((p & 7) << 2))] = word;
+  for (int i = 0; i < kRows; ++i) {
+    in.g[i] = load_stream(xt + i * x_row_bytes + lane_x);
+    in.u[i] = load_stream(xt + i * x_row_bytes + (x_row_bytes >> 1) + lane_x);
+    in.d[i] = load_stream(dyt + i * dy_row_bytes + lane_dy);
   }
 }
 
-__global__ __launch_bounds__(kThreads) void silu_quant_bwd_kernel(
+struct Tile {
+  int tb, hb;
+  int64_t t0, h0;
+};
+
+__device__ __forceinline__ Tile tile_at(int tile, int tiles_h) {
+  Tile c;
+  c.tb = tile / tiles_h;
+  c.hb = tile - c.tb * tiles_h;
+  c.t0 = (int64_t)c.tb * kTile;
+  c.h0 = (int64_t)c.hb * kTile;
+  return c;
+}
+
+// The elementwise part of one tile for one lane: packed bf16 y, d_gate and
+// d_up ([row][word], channel pairs per word), plus the lane's partial maxima of
+// unrounded magnitudes per row of d_gate and d_up (rg, ru) and per channel of
+// y (cm).
+__device__ __forceinline__ void elementwise(const TileIn& in, const float* s_tab, uint32_t (&Yp)[kRows][4],
+                                            uint32_t (&Gp)[kRows][4], uint32_t (&Up)[kRows][4],
+                                            float (&rg)[kRows], float (&ru)[kRows], float (&cm)[8]) {
+#pragma unroll
+  for (int i = 0; i < kRows; i += 2) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float yv[2][2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const uint32_t gw = (&in.g[i + r].x)[k], uw = (&in.u[i + r].x)[k], dw = (&in.d[i + r].x)[k];
+        uint32_t olo, ohi;
+        sigma_offsets2(gw, olo, ohi);
+        const float s0 = lds_f32(s_tab, olo), s1 = lds_f32(s_tab, ohi);
+        float y0, dg0, du0, y1, dg1, du1;
+        pair_f32(s0, bf16_lo(gw), bf16_lo(uw), bf16_lo(dw), y0, dg0, du0);
+        pair_f32(s1, bf16_hi(gw), bf16_hi(uw), bf16_hi(dw), y1, dg1, du1);
+        Yp[i + r][k] = pack_bf16(y0, y1);
+        Gp[i + r][k] = pack_bf16(dg0, dg1);
+        Up[i + r][k] = pack_bf16(du0, du1);
+        if (k == 0) {
+          rg[i + r] = fmaxf(fabsf(dg0), fabsf(dg1));
+          ru[i + r] = fmaxf(fabsf(du0), fabsf(du1));
+        } else {
+          rg[i + r] = amax3(rg[i + r], dg0, dg1);
+          ru[i + r] = amax3(ru[i + r], du0, du1);
+        }
+        yv[r][0] = y0;
+        yv[r][1] = y1;
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if (i == 0)
+          cm[2 * k + c] = fmaxf(fabsf(yv[0][c]), fabsf(yv[1][c]));
+        else
+          cm[2 * k + c] = amax3(cm[2 * k + c], yv[0][c], yv[1][c]);
+      }
+    }
+  }
+}
+
+// Position of the kRows-byte piece q of transposed row h (128 bytes) in the
+// LDS transpose buffer.  16-byte chunks are swapped by (h >> 3) & 7: a wave's
+// writes (16 rows 8 apart) spread over the banks, and every chunk stays
+// contiguous for the 16-byte read-back.
+__device__ __forceinline__ int yqt_byte(int h, int q) {
+  const int b = kRows * q;
+  return h * kTile + ((((b >> 4) ^ ((h >> 3) & 7)) << 4) | (b & 15));
+}
+
+// Swap a value with the neighbouring lane (lanes 2m and 2m+1).
+__device__ __forceinline__ uint32_t swap_neighbour(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1 /* quad_perm [1,0,3,2] */, 0xf, 0xf, false);
+}
+
+// Codes of rows (r0, r1) for 8 channels each, held by lanes p (even) and p+1:
+// the even lane ends with row r0, channels 8p..8p+15, the odd lane with row r1,
+// channels 8(p-1)..8p+7 -- one whole 16-byte piece each.
+__device__ __forceinline__ uint4 pair_rows16(uint2 r0, uint2 r1, bool odd) {
+  const uint2 send = odd ? r0 : r1;
+  const uint2 recv = make_uint2(swap_neighbour(send.x), swap_neighbour(send.y));
+  return odd ? make_uint4(recv.x, recv.y, r1.x, r1.y) : make_uint4(r0.x, r0.y, recv.x, recv.y);
+}
+
+// lane_gq addresses row kRows*q + (p & 1), channel 8 * (p & ~1) of the tile.
+template <bool kSafe>
+__device__ __forceinline__ void quantise_rows_and_y(const uint32_t (&Gp)[kRows][4], const uint32_t (&Up)[kRows][4],
+                                                    const uint32_t (&Yp)[kRows][4], const float (&idg)[kRows],
+                                                    const float (&idu)[kRows], const float (&iy)[8], int8_t* gqt,
+                                                    uint32_t lane_gq, int64_t gq_row_bytes, int64_t H,
+                                                    char* s_yqt, int p, int q) {
+  const bool odd = p & 1;
+#pragma unroll
+  for (int i = 0; i < kRows; i += 2) {
+    int8_t* row = gqt + i * gq_row_bytes + lane_gq;
+    store_stream(row, pair_rows16(codes8<kSafe>(Gp[i], idg[i]), codes8<kSafe>(Gp[i + 1], idg[i + 1]), odd));
+    store_stream(row + H, pair_rows16(codes8<kSafe>(Up[i], idu[i]), codes8<kSafe>(Up[i + 1], idu[i + 1]), odd));
+  }
+  // y codes, transposed: channel 8p + j gets the lane's kRows tokens.
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t c[kRows];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      const float v = (j & 1) ? bf16_hi(Yp[i][j >> 1]) : bf16_lo(Yp[i][j >> 1]);
+      c[i] = code_word<kSafe>(v, iy[j]);
+    }
+    char* dst = s_yqt + yqt_byte(8 * p + j, q);
+    if constexpr (kRows == 4)
+      *reinterpret_cast<uint32_t*>(dst) = pack4(c[0], c[1], c[2], c[3]);
+    else
+      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)pack2(c[0], c[1]);
+  }
+}
+
+// Persistent kernel: workgroup b walks tiles first, first + stride, ... < end.
+// Workgroups are dealt to the 8 XCDs round-robin by index, so with a grid that
+// is a multiple of 8, the workgroups of one XCD take one contiguous eighth of
+// the tiles (row-major over 128 x 128 tiles) and walk it together: neighbouring
+// tiles, whose scale writes share cache lines, then meet in the same L2.
+// One workgroup per CU; the next tile's inputs are requested at the top of each
+// iteration and stay in flight while the current tile is processed.
+__global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void silu_quant_bwd_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ grad_y, int8_t* __restrict__ grad_input_q,
     float* __restrict__ grad_input_s, int8_t* __restrict__ y_q_t, float* __restrict__ y_s_t, int64_t T, int64_t H,
-    int tiles_h) {
+    int tiles_h, int tiles) {
   __shared__ __align__(16) float lds[kLdsFloats];
   float* s_tab = lds;
   float* s_rowpart = lds + kSigEntries;
   float* s_colpart = s_rowpart + kRowPartFloats;
   float* s_inv = s_colpart + kColPartFloats;
-  uint32_t* s_yqt = reinterpret_cast<uint32_t*>(s_rowpart);
+  char* s_yqt = reinterpret_cast<char*>(s_rowpart);
+  int* s_flag = reinterpret_cast<int*>(s_inv + kInvFloats);  // a group's inverse overflowed
 
   const int tid = threadIdx.x;
   const int p = tid & 15;
   const int q = tid >> 4;
-  const int tile = blockIdx.x;
-  const int tb = tile / tiles_h;
-  const int hb = tile - tb * tiles_h;
-  const int64_t t0 = (int64_t)tb * kTile;
-  const int64_t h0 = (int64_t)hb * kTile;
-  const int64_t two_h = 2 * H;
 
-  // Inputs: 4 rows x (gate, up, grad_y) x 8 channels, 16 bytes each.
-  uint4 gin[4], uin[4], din[4];
-  {
-    const uint16_t* xr = x + (t0 + 4 * q) * two_h + h0 + 8 * p;
-    const uint16_t* dr = grad_y + (t0 + 4 * q) * H + h0 + 8 * p;
+  // Row pitches in bytes and the lane's fixed byte offsets inside a tile.
+  const int64_t x_row_bytes = 4 * H, dy_row_bytes = 2 * H, gq_row_bytes = 2 * H;
+  const int64_t row_groups = 2 * H / kGroup, col_groups = T / kGroup;
+  const uint32_t lane_x = (uint32_t)(kRows * q * x_row_bytes + 16 * p);
+  const uint32_t lane_dy = (uint32_t)(kRows * q * dy_row_bytes + 16 * p);
+  const uint32_t lane_gq = (uint32_t)((kRows * q + (p & 1)) * gq_row_bytes + 8 * (p & ~1));
+  constexpr int kOutSteps = kTile * kTile / 16 / kThreads;  // 16-byte pieces of y_q_t per thread
+  uint32_t lane_yq[kOutSteps];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      gin[i] = *reinterpret_cast<const uint4*>(xr + i * two_h);
-      uin[i] = *reinterpret_cast<const uint4*>(xr + i * two_h + H);
-      din[i] = *reinterpret_cast<const uint4*>(dr + i * H);
-    }
+  for (int step = 0; step < kOutSteps; ++step) {
+    const int id = tid + step * kThreads;
+    lane_yq[step] = (uint32_t)((id >> 3) * T + 16 * (id & 7));
   }
-  // Sigmoid table into LDS.
+
+  int tile, end, stride;
+  if ((gridDim.x & 7) == 0) {
+    const int xcd = blockIdx.x & 7, per_xcd = gridDim.x >> 3;
+    const int begin = (int)(((int64_t)tiles * xcd) >> 3);
+    end = (int)(((int64_t)tiles * (xcd + 1)) >> 3);
+    tile = begin + (int)(blockIdx.x >> 3);
+    stride = per_xcd;
+  } else {
+    tile = blockIdx.x;
+    end = tiles;
+    stride = gridDim.x;
+  }
+
+  const char* xb = reinterpret_cast<const char*>(x);
+  const char* dyb = reinterpret_cast<const char*>(grad_y);
+  TileIn in, in_next;
+  Tile cur = tile_at(tile < end ? tile : 0, tiles_h);
+  if (tile < end)
+    load_tile(in, xb + (cur.t0 * x_row_bytes + 2 * cur.h0), dyb + (cur.t0 * dy_row_bytes + 2 * cur.h0), lane_x,
+              lane_dy, x_row_bytes, dy_row_bytes);
   {
     const float4* src = reinterpret_cast<const float4*>(g_sigma_tab);
     float4* dst = reinterpret_cast<float4*>(s_tab);
@@ -210,113 +383,125 @@ __global__ __launch_bounds__(kThreads) void silu_quant_bwd_kernel(
   }
   __syncthreads();
 
-  float Y[4][8], DG[4][8], DU[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t gw[4] = {gin[i].x, gin[i].y, gin[i].z, gin[i].w};
-    const uint32_t uw[4] = {uin[i].x, uin[i].y, uin[i].z, uin[i].w};
-    const uint32_t dw[4] = {din[i].x, din[i].y, din[i].z, din[i].w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      pair(s_tab, gw[k] & 0xffffu, bf16_lo(gw[k]), bf16_lo(uw[k]), bf16_lo(dw[k]), Y[i][2 * k], DG[i][2 * k],
-           DU[i][2 * k]);
-      pair(s_tab, gw[k] >> 16, bf16_hi(gw[k]), bf16_hi(uw[k]), bf16_hi(dw[k]), Y[i][2 * k + 1],
-           DG[i][2 * k + 1], DU[i][2 * k + 1]);
-    }
-  }
+  while (tile < end) {
+    // ---- the next tile's inputs stay in flight through this whole iteration --
+    const int next = tile + stride;
+    const Tile nxt = tile_at(next < end ? next : tile, tiles_h);
+    if (next < end)
+      load_tile(in_next, xb + (nxt.t0 * x_row_bytes + 2 * nxt.h0), dyb + (nxt.t0 * dy_row_bytes + 2 * nxt.h0),
+                lane_x, lane_dy, x_row_bytes, dy_row_bytes);
 
-  // Partial maxima.  Row groups: lane (q, p) covers 8 channels of rows 4q..4q+3.
-  // Column groups: the lane covers 4 tokens of channels 8p..8p+7.
-  {
-    float rg[4], ru[4], cm[8];
+    // ---- elementwise: packed bf16 results and partial maxima -------------
+    uint32_t Yp[kRows][4], Gp[kRows][4], Up[kRows][4];  // y, d_gate, d_up
+    float rg[kRows], ru[kRows], cm[8];
+    elementwise(in, s_tab, Yp, Gp, Up, rg, ru, cm);
+    if (tid == 0) s_flag[0] = 0;
+
+    // ---- partial maxima to LDS --------------------------------------------
+    {
+      float* rp = s_rowpart + p * kRowPartStride + kRows * q;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float a = amax2(DG[i][0], DG[i][1]), b = amax2(DU[i][0], DU[i][1]);
-#pragma unroll
-      for (int j = 2; j < 8; ++j) {
-        a = fmaxf(a, fabsf(DG[i][j]));
-        b = fmaxf(b, fabsf(DU[i][j]));
+      for (int i = 0; i < kRows; ++i) {
+        rp[i] = rg[i];
+        rp[kTile + i] = ru[i];
       }
-      rg[i] = a;
-      ru[i] = b;
+      // column partials: [q][half][4p + jj] for channel 8p + 4*half + jj
+      float4* cp = reinterpret_cast<float4*>(s_colpart + q * kTile + 4 * p);
+      cp[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
+      cp[16] = make_float4(cm[4], cm[5], cm[6], cm[7]);
     }
+    __syncthreads();
+
+    // ---- one thread per group: maximum, scale, inverse ---------------------
+    if (tid < 2 * kTile) {
+      const int g = tid;  // g < 128: d_gate of row g; else d_up of row g - 128
+      float m = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      cm[j] = fmaxf(amax2(Y[0][j], Y[1][j]), amax2(Y[2][j], Y[3][j]));
+      for (int pp = 0; pp < 16; ++pp) m = fmaxf(m, s_rowpart[pp * kRowPartStride + g]);
+      const float scale = group_scale(m);
+      const float inv = 1.0f / scale;
+      s_inv[g] = inv;
+      if (inv == __builtin_huge_valf()) s_flag[0] = 1;
+      const uint32_t off = (uint32_t)((g & (kTile - 1)) * row_groups + (g >> 7) * (H / kGroup));
+      grad_input_s[cur.t0 * row_groups + cur.hb + off] = scale;
+    } else if (tid < 3 * kTile) {
+      const int c = tid - 2 * kTile;  // channel within the tile
+      const int idx = ((c >> 2) & 1) * 64 + (c >> 3) * 4 + (c & 3);
+      float m = 0.0f;
+#pragma unroll 8
+      for (int qq = 0; qq < kQ; ++qq) m = fmaxf(m, s_colpart[qq * kTile + idx]);
+      const float scale = group_scale(m);
+      const float inv = 1.0f / scale;
+      s_inv[2 * kTile + c] = inv;
+      if (inv == __builtin_huge_valf()) s_flag[0] = 1;
+      y_s_t[cur.h0 * col_groups + cur.tb + (uint32_t)(c * col_groups)] = scale;
     }
-    float4* rp = reinterpret_cast<float4*>(s_rowpart + p * kRowPartStride + 4 * q);
-    rp[0] = make_float4(rg[0], rg[1], rg[2], rg[3]);
-    rp[kTile / 4] = make_float4(ru[0], ru[1], ru[2], ru[3]);
-    // column partials: [q][half][4p + jj] for channel 8p + 4*half + jj
-    float4* cp = reinterpret_cast<float4*>(s_colpart + q * kTile + 4 * p);
-    cp[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
-    cp[16] = make_float4(cm[4], cm[5], cm[6], cm[7]);
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // One thread per group: finish the maximum, compute scale and inverse.
-  if (tid < 2 * kTile) {
-    const int g = tid;  // g < 128: d_gate of row g; else d_up of row g - 128
-    float m = 0.0f;
+    // ---- codes: [d_gate | d_up] rows straight out, y via the LDS transpose --
+    {
+      float idg[kRows], idu[kRows], iy[8];
 #pragma unroll
-    for (int pp = 0; pp < 16; ++pp) m = fmaxf(m, s_rowpart[pp * kRowPartStride + g]);
-    float scale = group_scale(m);
-    s_inv[g] = 1.0f / scale;
-    const int r = g & (kTile - 1);
-    const int64_t row_groups = two_h / kGroup;
-    const int64_t col = (g >> 7) * (H / kGroup) + hb;
-    grad_input_s[(t0 + r) * row_groups + col] = scale;
-  } else if (tid < 3 * kTile) {
-    const int c = tid - 2 * kTile;  // channel within the tile
-    const int idx = ((c >> 2) & 1) * 64 + (c >> 3) * 4 + (c & 3);
-    float m = 0.0f;
-#pragma unroll
-    for (int qq = 0; qq < 32; ++qq) m = fmaxf(m, s_colpart[qq * kTile + idx]);
-    float scale = group_scale(m);
-    s_inv[2 * kTile + c] = 1.0f / scale;
-    y_s_t[(h0 + c) * (T / kGroup) + tb] = scale;
-  }
-  __syncthreads();
-
-  {
-    const float4 inv_dg = *reinterpret_cast<const float4*>(s_inv + 4 * q);
-    const float4 inv_du = *reinterpret_cast<const float4*>(s_inv + kTile + 4 * q);
-    const float4 inv_y0 = *reinterpret_cast<const float4*>(s_inv + 2 * kTile + 8 * p);
-    const float4 inv_y1 = *reinterpret_cast<const float4*>(s_inv + 2 * kTile + 8 * p + 4);
-    // An inverse scale overflows only for a group whose maximum is below
-    // 127 * 2^-128; such a group needs the clamp and the v == 0 rule.
-    const float big = fmaxf(fmaxf(fmaxf(inv_dg.x, inv_dg.y), fmaxf(inv_dg.z, inv_dg.w)),
-                            fmaxf(fmaxf(inv_du.x, inv_du.y), fmaxf(inv_du.z, inv_du.w)));
-    const float bigy = fmaxf(fmaxf(fmaxf(inv_y0.x, inv_y0.y), fmaxf(inv_y0.z, inv_y0.w)),
-                             fmaxf(fmaxf(inv_y1.x, inv_y1.y), fmaxf(inv_y1.z, inv_y1.w)));
-    int8_t* gq_row0 = grad_input_q + (t0 + 4 * q) * two_h + h0 + 8 * p;
-    if (__builtin_expect(fmaxf(big, bigy) == __builtin_huge_valf(), 0)) {
-      quantise_tile<true>(Y, DG, DU, inv_dg, inv_du, inv_y0, inv_y1, gq_row0, two_h, H, s_yqt, p, q);
-    } else {
-      quantise_tile<false>(Y, DG, DU, inv_dg, inv_du, inv_y0, inv_y1, gq_row0, two_h, H, s_yqt, p, q);
+      for (int i = 0; i < kRows; ++i) {
+        idg[i] = s_inv[kRows * q + i];
+        idu[i] = s_inv[kTile + kRows * q + i];
+      }
+      const float4 inv_y0 = *reinterpret_cast<const float4*>(s_inv + 2 * kTile + 8 * p);
+      const float4 inv_y1 = *reinterpret_cast<const float4*>(s_inv + 2 * kTile + 8 * p + 4);
+      iy[0] = inv_y0.x, iy[1] = inv_y0.y, iy[2] = inv_y0.z, iy[3] = inv_y0.w;
+      iy[4] = inv_y1.x, iy[5] = inv_y1.y, iy[6] = inv_y1.z, iy[7] = inv_y1.w;
+      int8_t* gqt = grad_input_q + (cur.t0 * gq_row_bytes + cur.h0);
+      quantise_rows_and_y<false>(Gp, Up, Yp, idg, idu, iy, gqt, lane_gq, gq_row_bytes, H, s_yqt, p, q);
+      __syncthreads();
+      // Rare: some group's inverse overflowed (its maximum is below
+      // 127 * 2^-128).  Recompute the tile from its inputs and rewrite every
+      // code with the clamped rule, which gives the same words for the other
+      // groups.
+      if (s_flag[0]) {
+        TileIn again;
+        load_tile(again, xb + (cur.t0 * x_row_bytes + 2 * cur.h0), dyb + (cur.t0 * dy_row_bytes + 2 * cur.h0),
+                  lane_x, lane_dy, x_row_bytes, dy_row_bytes);
+        float rg2[kRows], ru2[kRows], cm2[8];
+        elementwise(again, s_tab, Yp, Gp, Up, rg2, ru2, cm2);
+        quantise_rows_and_y<true>(Gp, Up, Yp, idg, idu, iy, gqt, lane_gq, gq_row_bytes, H, s_yqt, p, q);
+        __syncthreads();
+      }
     }
-  }
-  __syncthreads();
 
-  // Transposed codes out: 128 rows of y_q_t x 128 tokens, 16 bytes per thread
-  // per step; eight neighbouring threads write one whole 128-byte row segment.
+    // ---- transposed codes out: eight neighbouring threads per 128-byte row --
+    {
+      int8_t* yqt = y_q_t + (cur.h0 * T + cur.t0);
 #pragma unroll
-  for (int step = 0; step < 2; ++step) {
-    const int id = tid + step * kThreads;
-    const int h = id >> 3;
-    const int chunk = id & 7;
-    const int phys = chunk ^ ((h >> 3) & 7);
-    const uint4 v = *reinterpret_cast<const uint4*>(s_yqt + h * 32 + phys * 4);
-    *reinterpret_cast<uint4*>(y_q_t + (h0 + h) * T + t0 + 16 * chunk) = v;
+      for (int step = 0; step < kOutSteps; ++step) {
+        const int id = tid + step * kThreads;
+        const int h = id >> 3;
+        const int phys = (id & 7) ^ ((h >> 3) & 7);
+        const uint4 v = *reinterpret_cast<const uint4*>(s_yqt + h * kTile + phys * 16);
+        store_stream(yqt + lane_yq[step], v);
+      }
+    }
+
+    in = in_next;
+    tile = next;
+    cur = nxt;
+    if (tile < end) __syncthreads();  // the transpose buffer is read before it is rewritten
   }
 }
 
 // Diagnostics: the fused kernel's own sigmoid lookup and elementwise helpers,
-// run on their own so tests can compare them bit for bit.
+// run on their own so tests can compare them bit for bit.  Element i takes the
+// low half of the packed index path when i is even and the high half when odd,
+// so both halves of sigma_offsets2 are exercised.
+__device__ __forceinline__ float sigma_of(uint32_t gb, int64_t i) {
+  uint32_t lo, hi;
+  sigma_offsets2(gb | (gb << 16), lo, hi);
+  return g_sigma_tab[((i & 1) ? hi : lo) >> 2];
+}
+
 __global__ void eval_sigmoid_kernel(const uint16_t* __restrict__ gate, float* __restrict__ s, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  s[i] = g_sigma_tab[sigma_index(gate[i])];
+  s[i] = sigma_of(gate[i], i);
 }
 
 __global__ void eval_intermediates_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ grad_y,
@@ -326,18 +511,19 @@ __global__ void eval_intermediates_kernel(const uint16_t* __restrict__ x, const 
   if (i >= T * H) return;
   int64_t t = i / H, h = i - t * H;
   uint32_t gb = x[t * 2 * H + h];
-  float g = __uint_as_float(gb << 16);
-  float u = __uint_as_float((uint32_t)x[t * 2 * H + H + h] << 16);
-  float d = __uint_as_float((uint32_t)grad_y[i] << 16);
+  float g = bf16_lo(gb);
+  float u = bf16_lo(x[t * 2 * H + H + h]);
+  float d = bf16_lo(grad_y[i]);
   float y, dg, du;
-  pair(g_sigma_tab, gb, g, u, d, y, dg, du);
-  y_out[i] = (uint16_t)(__float_as_uint(y) >> 16);
-  dgdu_out[t * 2 * H + h] = (uint16_t)(__float_as_uint(dg) >> 16);
-  dgdu_out[t * 2 * H + H + h] = (uint16_t)(__float_as_uint(du) >> 16);
+  pair_f32(sigma_of(gb, i), g, u, d, y, dg, du);
+  y_out[i] = (uint16_t)pack_bf16(y, 0.0f);
+  dgdu_out[t * 2 * H + h] = (uint16_t)pack_bf16(dg, 0.0f);
+  dgdu_out[t * 2 * H + H + h] = (uint16_t)pack_bf16(du, 0.0f);
 }
 
 constexpr int kMaxDevices = 64;
 std::atomic<bool> g_table_ready[kMaxDevices];
+int g_cu_count[kMaxDevices];
 std::mutex g_table_mutex;
 
 int ensure_table(int* device_out) {
@@ -347,6 +533,10 @@ int ensure_table(int* device_out) {
   if (g_table_ready[dev].load(std::memory_order_acquire)) return SILUQUANT_OK;
   std::lock_guard<std::mutex> lock(g_table_mutex);
   if (g_table_ready[dev].load(std::memory_order_relaxed)) return SILUQUANT_OK;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return SILUQUANT_ERR_DEVICE;
+  g_cu_count[dev] = cus;
   hipStream_t s = nullptr;
   if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return SILUQUANT_ERR_DEVICE;
   hipLaunchKernelGGL(build_sigma_table_kernel, dim3((kSigEntries + 255) / 256), dim3(256), 0, s);
@@ -402,7 +592,10 @@ __attribute__((visibility("default"))) int silu_dot_fwd_bwd_quant_fuse(const voi
   if (T < 0 || H < 0 || T % kTile != 0 || H % kTile != 0) return SILUQUANT_ERR_BAD_SHAPE;
   if (T == 0 || H == 0) return SILUQUANT_OK;
   // Tile indices are int and byte offsets int64: bound both.
-  if (T > (int64_t(1) << 40) / H || (T / kTile) * (H / kTile) > 0x7fffffff) return SILUQUANT_ERR_BAD_SHAPE;
+  // Tile indices are int; a lane's byte offset inside a tile (< 512 * H for x,
+  // < 128 * T for y_q_t) must fit in 32 bits.
+  if (T > (int64_t(1) << 24) || H > (int64_t(1) << 22) || (T / kTile) * (H / kTile) > 0x7fffffff)
+    return SILUQUANT_ERR_BAD_SHAPE;
   if (!x || !grad_y || !grad_input_q || !grad_input_s || !y_q_t || !y_s_t) return SILUQUANT_ERR_NULL_PTR;
   auto mis16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; };
   auto mis4 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 3u) != 0; };
@@ -421,9 +614,14 @@ __attribute__((visibility("default"))) int silu_dot_fwd_bwd_quant_fuse(const voi
 
   const int tiles_h = (int)(H / kTile);
   const int tiles = (int)(T / kTile) * tiles_h;
-  hipLaunchKernelGGL(silu_quant_bwd_kernel, dim3(tiles), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+  // Persistent grid: as many workgroups as fit on the device at once (a
+  // multiple of 8, one share per XCD), or one per tile if there are fewer.
+  int grid = g_cu_count[dev] * kWorkgroupsPerCU;
+  grid = grid >= 8 ? grid - grid % 8 : grid;
+  if (tiles < grid) grid = tiles;
+  hipLaunchKernelGGL(silu_quant_bwd_kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(grad_y), grad_input_q,
-                     grad_input_s, y_q_t, y_s_t, T, H, tiles_h);
+                     grad_input_s, y_q_t, y_s_t, T, H, tiles_h, tiles);
   if (hipGetLastError() != hipSuccess) return SILUQUANT_ERR_LAUNCH_FAILED;
   return SILUQUANT_OK;
 }

@@ -3,6 +3,10 @@
 The quantiser (scale = amax / 127, 1.0 for an all-zero group; inv = 1 / scale;
 q = clamp(rne(v * inv), -127, 127)) is pinned by:
 
+* the rounding rule itself: each code is the integer nearest to the exact
+  rational product v * inv (ties to even), found by comparing the two integer
+  neighbours in exact arithmetic, including a group where rounding the fp32
+  product first would give a different code;
 * hand-derived worked examples whose exact results are known without running
   any float code (derivations in the comments);
 * brute-force rounding: with amax = 127 the scale and its inverse are exactly 1,
@@ -110,3 +114,44 @@ def test_invariants_random_groups():
         # dequantisation error bound, in double
         err = np.abs(qi * float(s) - v.astype(np.float64))
         assert np.all(err <= float(s) * (0.5 + 2.0**-15)), (err.max(), float(s))
+
+
+def _inv_of(scale) -> Fraction:
+    return rn32(1 / Fraction(float(scale)))
+
+
+def test_codes_round_the_exact_product():
+    rng = np.random.default_rng(11)
+    for v in _random_groups(rng, n_groups=150):
+        q, s = oracle.quant_group(v)
+        if float(np.max(np.abs(v))) == 0.0 or float(s) < 2.0**-126:
+            continue
+        inv = _inv_of(s)
+        for x, code in zip(v, q):
+            want = max(-127, min(127, rne_int(Fraction(float(x)) * inv)))
+            assert int(code) == want, (float(x), float(s), int(code), want)
+
+
+def _first_double_rounding_case():
+    """A group (amax, v) where rounding v * inv to fp32 first lands on a tie that
+    the exact product is not on, so the two rules give different codes."""
+    for num in range(129, 256):
+        amax = Fraction(num, 2)  # bf16-exact values in (64, 128)
+        inv = rn32(1 / rn32(amax / 127))
+        for vnum in range(1, 256):
+            v = Fraction(vnum, 4)
+            if v > amax:
+                break
+            exact = v * inv
+            via_f32 = rn32(exact)
+            if rne_int(exact) != rne_int(via_f32):
+                return amax, v, rne_int(exact), rne_int(via_f32)
+    return None
+
+
+def test_exact_product_differs_from_fp32_product_somewhere():
+    case = _first_double_rounding_case()
+    assert case is not None
+    amax, v, want, other = case
+    q, s = oracle.quant_group([float(amax), float(v)])
+    assert int(q[1]) == want != other
