@@ -60,7 +60,7 @@ enum siluquant_status {
  *   -128 is never produced.  Inputs must be finite and keep y, d_gate and d_up
  *   finite.
  * Sizes: T >= 0 and H >= 0 multiples of 128 (T == 0 or H == 0 is a no-op that
- *   returns SILUQUANT_OK); T*2H < 2^62; group must be 128.
+ *   returns SILUQUANT_OK), T <= 2^23, H <= 2^22; group must be 128.
  * Ownership: the caller allocates and owns every buffer; the library keeps no
  *   pointer after the call returns.  Buffers must not overlap.
  * Asynchrony: the work is enqueued on `stream` and the call returns without

@@ -96,8 +96,17 @@ __device__ __forceinline__ uint4 load_stream(const void* ptr) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
-__device__ __forceinline__ void store_stream(void* ptr, uint4 v) {
-  __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(ptr));
+// Code stores go through a buffer resource so they can carry the system-scope,
+// streaming cache policy (sc0 sc1 nt), which measured faster than plain
+// non-temporal stores for this pass.  The scale stores stay ordinary stores:
+// they are 4-byte pieces that merge into lines in L2, and streaming them
+// measured far slower.
+constexpr int kStreamStorePolicy = 1 | 2 | 16;  // sc0 | nt | sc1 on gfx950
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void store_stream(__amdgpu_buffer_rsrc_t buf, uint32_t offset, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128((u32x4){v.x, v.y, v.z, v.w}, buf, offset, 0, kStreamStorePolicy);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -288,19 +297,21 @@ __device__ __forceinline__ uint4 pair_rows16(uint2 r0, uint2 r1, bool odd) {
   return odd ? make_uint4(recv.x, recv.y, r1.x, r1.y) : make_uint4(r0.x, r0.y, recv.x, recv.y);
 }
 
-// lane_gq addresses row kRows*q + (p & 1), channel 8 * (p & ~1) of the tile.
+// gq_buf covers the tile's 128 rows of grad_input_q (its base is the tile's
+// first code); lane_gq addresses row kRows*q + (p & 1), channel 8 * (p & ~1).
 template <bool kSafe>
 __device__ __forceinline__ void quantise_rows_and_y(const uint32_t (&Gp)[kRows][4], const uint32_t (&Up)[kRows][4],
                                                     const uint32_t (&Yp)[kRows][4], const float (&idg)[kRows],
-                                                    const float (&idu)[kRows], const float (&iy)[8], int8_t* gqt,
-                                                    uint32_t lane_gq, int64_t gq_row_bytes, int64_t H,
-                                                    char* s_yqt, int p, int q) {
+                                                    const float (&idu)[kRows], const float (&iy)[8],
+                                                    __amdgpu_buffer_rsrc_t gq_buf, uint32_t lane_gq,
+                                                    uint32_t gq_row_bytes, uint32_t H, char* s_yqt, int p, int q) {
   const bool odd = p & 1;
 #pragma unroll
   for (int i = 0; i < kRows; i += 2) {
-    int8_t* row = gqt + i * gq_row_bytes + lane_gq;
-    store_stream(row, pair_rows16(codes8<kSafe>(Gp[i], idg[i]), codes8<kSafe>(Gp[i + 1], idg[i + 1]), odd));
-    store_stream(row + H, pair_rows16(codes8<kSafe>(Up[i], idu[i]), codes8<kSafe>(Up[i + 1], idu[i + 1]), odd));
+    const uint32_t row = i * gq_row_bytes + lane_gq;
+    store_stream(gq_buf, row, pair_rows16(codes8<kSafe>(Gp[i], idg[i]), codes8<kSafe>(Gp[i + 1], idg[i + 1]), odd));
+    store_stream(gq_buf, row + H,
+                 pair_rows16(codes8<kSafe>(Up[i], idu[i]), codes8<kSafe>(Up[i + 1], idu[i + 1]), odd));
   }
   // y codes, transposed: channel 8p + j gets the lane's kRows tokens.
 #pragma unroll
@@ -450,8 +461,10 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
       const float4 inv_y1 = *reinterpret_cast<const float4*>(s_inv + 2 * kTile + 8 * p + 4);
       iy[0] = inv_y0.x, iy[1] = inv_y0.y, iy[2] = inv_y0.z, iy[3] = inv_y0.w;
       iy[4] = inv_y1.x, iy[5] = inv_y1.y, iy[6] = inv_y1.z, iy[7] = inv_y1.w;
-      int8_t* gqt = grad_input_q + (cur.t0 * gq_row_bytes + cur.h0);
-      quantise_rows_and_y<false>(Gp, Up, Yp, idg, idu, iy, gqt, lane_gq, gq_row_bytes, H, s_yqt, p, q);
+      const __amdgpu_buffer_rsrc_t gq_buf =
+          buffer_of(grad_input_q + (cur.t0 * gq_row_bytes + cur.h0), (uint32_t)(kTile * gq_row_bytes));
+      quantise_rows_and_y<false>(Gp, Up, Yp, idg, idu, iy, gq_buf, lane_gq, (uint32_t)gq_row_bytes, (uint32_t)H,
+                                 s_yqt, p, q);
       __syncthreads();
       // Rare: some group's inverse overflowed (its maximum is below
       // 127 * 2^-128).  Recompute the tile from its inputs and rewrite every
@@ -463,21 +476,22 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
                   lane_x, lane_dy, x_row_bytes, dy_row_bytes);
         float rg2[kRows], ru2[kRows], cm2[8];
         elementwise(again, s_tab, Yp, Gp, Up, rg2, ru2, cm2);
-        quantise_rows_and_y<true>(Gp, Up, Yp, idg, idu, iy, gqt, lane_gq, gq_row_bytes, H, s_yqt, p, q);
+        quantise_rows_and_y<true>(Gp, Up, Yp, idg, idu, iy, gq_buf, lane_gq, (uint32_t)gq_row_bytes, (uint32_t)H,
+                                  s_yqt, p, q);
         __syncthreads();
       }
     }
 
     // ---- transposed codes out: eight neighbouring threads per 128-byte row --
     {
-      int8_t* yqt = y_q_t + (cur.h0 * T + cur.t0);
+      const __amdgpu_buffer_rsrc_t yq_buf = buffer_of(y_q_t + (cur.h0 * T + cur.t0), (uint32_t)(kTile * T));
 #pragma unroll
       for (int step = 0; step < kOutSteps; ++step) {
         const int id = tid + step * kThreads;
         const int h = id >> 3;
         const int phys = (id & 7) ^ ((h >> 3) & 7);
         const uint4 v = *reinterpret_cast<const uint4*>(s_yqt + h * kTile + phys * 16);
-        store_stream(yqt + lane_yq[step], v);
+        store_stream(yq_buf, lane_yq[step], v);
       }
     }
 
@@ -592,9 +606,11 @@ __attribute__((visibility("default"))) int silu_dot_fwd_bwd_quant_fuse(const voi
   if (T < 0 || H < 0 || T % kTile != 0 || H % kTile != 0) return SILUQUANT_ERR_BAD_SHAPE;
   if (T == 0 || H == 0) return SILUQUANT_OK;
   // Tile indices are int and byte offsets int64: bound both.
-  // Tile indices are int; a lane's byte offset inside a tile (< 512 * H for x,
-  // < 128 * T for y_q_t) must fit in 32 bits.
-  if (T > (int64_t(1) << 24) || H > (int64_t(1) << 22) || (T / kTile) * (H / kTile) > 0x7fffffff)
+  // Tile indices are int; a lane's byte offset inside a tile (< 512 * H for x)
+  // must fit in 32 bits, and a tile's output span (128 rows of 2H bytes of
+  // grad_input_q, 128 rows of T bytes of y_q_t) in a buffer resource's
+  // 31-bit record count.
+  if (T > (int64_t(1) << 23) || H > (int64_t(1) << 22) || (T / kTile) * (H / kTile) > 0x7fffffff)
     return SILUQUANT_ERR_BAD_SHAPE;
   if (!x || !grad_y || !grad_input_q || !grad_input_s || !y_q_t || !y_s_t) return SILUQUANT_ERR_NULL_PTR;
   auto mis16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; };
