@@ -112,6 +112,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="t16384_h11008")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", choices=["backward", "forward"], default="backward",
+                    help="backward: the fused SwiGLU backward + two-axis int8 pass (the headline); "
+                         "forward: SwiGLU forward + row-wise int8 quantisation")
     ap.add_argument("--probes", action="store_true",
                     help="also time a plain 1 GiB copy and a 2-read/1-write bf16 add (reference streams)")
     args = ap.parse_args()
@@ -129,20 +132,30 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    nbytes = sq.algorithmic_bytes(w.T, w.H)
+    forward = args.op == "forward"
+    nbytes = sq.forward_bytes(w.T, w.H) if forward else sq.algorithmic_bytes(w.T, w.H)
     # Rotate buffer sets so that one pass over them exceeds twice the 256 MB
     # last-level cache: every step then reads its inputs from HBM.
     sets = max(1, -(-512 * 2**20 // nbytes))
     bufs = []
     for r in range(sets):
         x, dy = make_inputs(w, device=dev, seed=w.seed + 1000 * r)
-        bufs.append((x, dy, sq.empty_outputs(w.T, w.H, dev)))
+        if forward:
+            del dy
+            outs = (torch.empty((w.T, w.H), dtype=torch.int8, device=dev),
+                    torch.empty((w.T, w.H // 128), dtype=torch.float32, device=dev))
+            bufs.append((x, None, outs))
+        else:
+            bufs.append((x, dy, sq.empty_outputs(w.T, w.H, dev)))
     sq.prepare()
     torch.cuda.synchronize()
 
     def step(i):
         x, dy, outs = bufs[i % sets]
-        sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *outs)
+        if forward:
+            sq.silu_fwd_quant(x, *outs)
+        else:
+            sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *outs)
 
     for i in range(args.warmup):
         step(i)
@@ -164,8 +177,11 @@ def main():
     per_launch_s = gpu_ms / 1e3 / args.steps
     achieved = nbytes / per_launch_s / 1e9
     value = nbytes * args.steps / wall / 1e9
+    metric = "achieved HBM GB/s (+% of MI355X peak) for fused silu fwd/bwd+int8 quant"
+    if forward:
+        metric = "achieved HBM GB/s (+% of MI355X peak) for fused silu forward + row-wise int8 quant"
     out = {
-        "metric": "achieved HBM GB/s (+% of MI355X peak) for fused silu fwd/bwd+int8 quant",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "GB/s",
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
@@ -189,15 +205,15 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic(w.name),
-            "kernel": "silu_quant_bwd_kernel",
+            "traffic": measured_traffic(("forward:" if forward else "") + w.name),
+            "kernel": "silu_fwd_quant_kernel" if forward else "silu_quant_bwd_kernel",
             "avg_launch_us": round(per_launch_s * 1e6, 3),
         },
         "cpu_baseline": None,
     }
     if args.probes:
         out["probes"] = stream_probes(dev)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not forward:
         x, dy, _ = bufs[0]
         out["cpu_baseline"] = cpu_baseline(x, dy, w)
     print(json.dumps(out), flush=True)

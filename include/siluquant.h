@@ -73,6 +73,28 @@ int silu_dot_fwd_bwd_quant_fuse(const void* x, const void* grad_y, int8_t* grad_
                                 int8_t* y_q_t, float* y_s_t, int64_t T, int64_t H, int64_t group,
                                 void* stream);
 
+/*
+ * silu_fwd_quant -- forward SwiGLU with row-wise int8 group quantisation.
+ *
+ * The fused launch shape of kquant_swiglu_q8_1_rows on the page "kquant_mmq.rs"
+ * (docs.atlascybernetics.ai): y = bf16((silu(gate) * up) * w[t]) rounded once to
+ * bf16 (nearest, ties to even), then quantised per row in groups of 128
+ * contiguous channels exactly as above (scale = amax/127, 1.0 for an all-zero
+ * group; q = clamp(rne(v * inv)), v == 0 -> 0).  With no row weight, y is the
+ * same bf16 value the backward pass recomputes.  The page's `limit` argument
+ * has no stated meaning and is not provided.
+ *
+ *   x           bf16 [T, 2H] as above (read only; 16-byte aligned)
+ *   row_weight  fp32 [T], or NULL for weight 1 (4-byte aligned)
+ *   y_q         int8 [T, H]       codes (16-byte aligned)
+ *   y_s         fp32 [T, H/128]   one scale per group (4-byte aligned)
+ *   y_bf16      bf16 [T, H] the rounded y, or NULL (16-byte aligned)
+ * Sizes: any T >= 0 (T <= 2^31), H a multiple of 128 (H <= 2^22), group 128.
+ * Same ownership, asynchrony and error conventions as above.
+ */
+int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q, float* y_s, void* y_bf16, int64_t T,
+                   int64_t H, int64_t group, void* stream);
+
 /* Builds the sigmoid table on the current device now (otherwise the first
  * silu_dot_fwd_bwd_quant_fuse call on the device does it).  Blocks until the
  * table is in place.  Safe to call repeatedly and from several threads. */

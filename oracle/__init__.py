@@ -85,6 +85,8 @@ def _load():
         lib.oracle_quantise.restype = ctypes.c_int
         lib.oracle_silu_dot_fwd_bwd_quant_fuse.argtypes = [u16p, u16p, i8p, f32p, i8p, f32p, i64, i64, i64]
         lib.oracle_silu_dot_fwd_bwd_quant_fuse.restype = ctypes.c_int
+        lib.oracle_silu_fwd_quant.argtypes = [u16p, f32p, i8p, f32p, u16p, i64, i64, i64]
+        lib.oracle_silu_fwd_quant.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -217,3 +219,26 @@ def quantise(Y: np.ndarray, D: np.ndarray, group_size: int = GROUP):
     if rc != 0:
         raise RuntimeError("oracle_quantise failed with code %d" % rc)
     return gq, gs, yq, ys
+
+
+def silu_fwd_quant(x, w=None, group_size: int = GROUP, want_bf16: bool = False):
+    """Forward quantiser on the CPU: y = bf16((silu(gate) * up) * w[t]) from
+    x = [gate | up] bf16 bits [T, 2H]; returns (y_q int8 [T, H], y_s fp32
+    [T, ceil(H/group)]) and, if want_bf16, the bf16 bits of y as uint16 [T, H]."""
+    x = _as_bits(x)
+    T, H2 = x.shape
+    H = H2 // 2
+    groups = -(-H // group_size)
+    yq = np.zeros((T, H), dtype=np.int8)
+    ys = np.zeros((T, groups), dtype=np.float32)
+    yb = np.zeros((T, H), dtype=np.uint16) if want_bf16 else None
+    wp = None
+    if w is not None:
+        w = np.ascontiguousarray(np.asarray(w, dtype=np.float32))
+        assert w.shape == (T,)
+        wp = _ptr(w, ctypes.c_float)
+    rc = _load().oracle_silu_fwd_quant(_ptr(x, ctypes.c_uint16), wp, _ptr(yq, ctypes.c_int8), _ptr(ys, ctypes.c_float),
+                                       _ptr(yb, ctypes.c_uint16) if yb is not None else None, T, H, group_size)
+    if rc != 0:
+        raise RuntimeError("oracle_silu_fwd_quant failed with code %d" % rc)
+    return (yq, ys, yb) if want_bf16 else (yq, ys)

@@ -38,6 +38,15 @@
  *     avoids 0 * inf when a group's scale is so small that 1/scale overflows);
  *   - a trailing group shorter than `group` (T or 2H not a multiple of it) is
  *     quantised over the elements it has.
+ *
+ * The forward quantiser (oracle_silu_fwd_quant) follows the fused launch the
+ * page "kquant_mmq.rs" (docs.atlascybernetics.ai) documents for
+ * kquant_swiglu_q8_1_rows: h = bf16(swiglu(gate, up) * w[row]), then group
+ * quantisation of those bf16 rows.  Readings: w is an optional fp32 weight per
+ * row (absent = 1); swiglu is (g * s) * u exactly as in the backward pass, the
+ * weight multiplies that fp32 product, and the result is rounded to bf16 once;
+ * groups are `group` contiguous channels of each row with the quantiser above.
+ * The page's `limit` argument has no stated meaning and is not modelled.
  */
 #include <math.h>
 #include <stdint.h>
@@ -179,6 +188,38 @@ ORACLE_API int oracle_quantise(const float* Y, const float* D, int8_t* grad_inpu
       y_s_t[h * col_groups + j] = oracle_quant_group(&Y[t0 * H + h], n, H, &y_q_t[h * T + t0], 1);
     }
   }
+  return ORACLE_OK;
+}
+
+/* Forward: y = bf16((silu(g) * u) * w[t]) for x = [gate | up] [T, 2H]; writes
+ * y_q [T, H] int8 and y_s [T, ceil(H/group)] fp32 (row groups), and, when
+ * y_bf16 is not NULL, the bf16 bits of y.  w may be NULL (weight 1). */
+ORACLE_API int oracle_silu_fwd_quant(const uint16_t* x, const float* w, int8_t* y_q, float* y_s, uint16_t* y_bf16,
+                                     int64_t T, int64_t H, int64_t group) {
+  if (T < 0 || H < 0 || group <= 0) return ORACLE_BAD_ARG;
+  if (T == 0 || H == 0) return ORACLE_OK;
+  float* Y = (float*)malloc((size_t)H * sizeof(float));
+  if (!Y) return ORACLE_NO_MEMORY;
+  int64_t groups = (H + group - 1) / group;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t h = 0; h < H; ++h) {
+      float g = oracle_bf16_to_f32(x[t * 2 * H + h]);
+      float u = oracle_bf16_to_f32(x[t * 2 * H + H + h]);
+      float s = oracle_sigmoid(g);
+      float silu = g * s;
+      float v = silu * u;
+      if (w) v = v * w[t];
+      uint16_t b = oracle_f32_to_bf16(v);
+      Y[h] = oracle_bf16_to_f32(b);
+      if (y_bf16) y_bf16[t * H + h] = b;
+    }
+    for (int64_t j = 0; j < groups; ++j) {
+      int64_t c0 = j * group;
+      int64_t n = (H - c0 < group) ? H - c0 : group;
+      y_s[t * groups + j] = oracle_quant_group(&Y[c0], n, 1, &y_q[t * H + c0], 1);
+    }
+  }
+  free(Y);
   return ORACLE_OK;
 }
 

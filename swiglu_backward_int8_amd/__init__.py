@@ -27,7 +27,7 @@ _ERRORS = {
     7: (RuntimeError, "LAUNCH_FAILED"),
 }
 
-EXPORTED = ("silu_dot_fwd_bwd_quant_fuse", "siluquant_prepare", "siluquant_strerror",
+EXPORTED = ("silu_dot_fwd_bwd_quant_fuse", "silu_fwd_quant", "siluquant_prepare", "siluquant_strerror",
             "siluquant_algorithmic_bytes", "siluquant_eval_sigmoid", "siluquant_eval_intermediates")
 
 _lib = None
@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
         L.siluquant_strerror.restype = ctypes.c_char_p
         L.siluquant_algorithmic_bytes.argtypes = [i64, i64, i64]
         L.siluquant_algorithmic_bytes.restype = i64
+        L.silu_fwd_quant.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+        L.silu_fwd_quant.restype = ctypes.c_int
         L.siluquant_eval_sigmoid.argtypes = [vp, vp, i64, vp]
         L.siluquant_eval_sigmoid.restype = ctypes.c_int
         L.siluquant_eval_intermediates.argtypes = [vp, vp, vp, vp, i64, i64, vp]
@@ -127,6 +129,44 @@ def silu_dot_fwd_bwd_quant_fuse(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_
         code = raw_call(x.data_ptr(), grad_y.data_ptr(), grad_input_q.data_ptr(), grad_input_s.data_ptr(),
                         y_q_t.data_ptr(), y_s_t.data_ptr(), T, H, group_size, stream)
     _check(code, "silu_dot_fwd_bwd_quant_fuse")
+
+
+def silu_fwd_quant(x, y_q, y_s, row_weight=None, y_bf16=None, group_size: int = GROUP):
+    """Forward SwiGLU with row-wise int8 quantisation: y = bf16((silu(gate) * up)
+    * row_weight[t]) from x = [gate | up] [T, 2H]; writes y_q int8 [T, H] and
+    y_s fp32 [T, H/128], and y_bf16 [T, H] if given.  Enqueued on the current
+    stream of x's device; returns None."""
+    import torch
+
+    if x.dim() != 2 or x.shape[1] % 2:
+        raise ValueError("x must be [T, 2H]")
+    T, H = int(x.shape[0]), int(x.shape[1]) // 2
+    if group_size != GROUP:
+        raise ValueError("group_size must be 128")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU; got %s" % dev)
+    checks = [("x", x, torch.bfloat16, (T, 2 * H)), ("y_q", y_q, torch.int8, (T, H)),
+              ("y_s", y_s, torch.float32, (T, H // GROUP))]
+    if row_weight is not None:
+        checks.append(("row_weight", row_weight, torch.float32, (T,)))
+    if y_bf16 is not None:
+        checks.append(("y_bf16", y_bf16, torch.bfloat16, (T, H)))
+    for name, t, dt, shape in checks:
+        if t.dtype != dt or t.device != dev or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+            raise ValueError("%s must be a contiguous %s tensor of shape %s on %s" % (name, dt, shape, dev))
+    with torch.cuda.device(dev):
+        code = int(lib().silu_fwd_quant(x.data_ptr(), row_weight.data_ptr() if row_weight is not None else None,
+                                        y_q.data_ptr(), y_s.data_ptr(),
+                                        y_bf16.data_ptr() if y_bf16 is not None else None, T, H, group_size,
+                                        torch.cuda.current_stream(dev).cuda_stream))
+    _check(code, "silu_fwd_quant")
+
+
+def forward_bytes(T: int, H: int, with_bf16: bool = False, with_weight: bool = False) -> int:
+    """Bytes the forward quantiser must move: x (4 per pair) in, codes (1) and
+    one fp32 scale per 128 codes out, plus bf16 y (2) and the row weights."""
+    return 5 * T * H + 4 * (T * H // GROUP) + (2 * T * H if with_bf16 else 0) + (4 * T if with_weight else 0)
 
 
 def empty_outputs(T: int, H: int, device, group: int = GROUP):

@@ -502,6 +502,137 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
   }
 }
 
+// ---------------------------------------------------------------------------
+// Forward quantiser: y = bf16((silu(gate) * up) * w[t]), quantised per row in
+// groups of 128 channels (y_q [T, H], y_s [T, H/128]), optionally also the
+// bf16 y itself.  The fused launch shape follows the page "kquant_mmq.rs"
+// (kquant_swiglu_q8_1_rows: swiglu times an optional row weight, rounded to
+// bf16, then group-quantised), with this library's 128-channel groups.
+//
+// A wave owns 4 rows x 128 channels per unit (16 lanes per row, 8 channels
+// per lane, 16-byte loads); the group maximum is a 4-step DPP butterfly inside
+// the 16-lane row, so no LDS and no barrier is needed beyond the sigmoid table.
+// Workgroups are persistent and each wave walks units w, w + waves, ... with
+// the next unit's inputs in flight.
+constexpr int kFwdThreads = 256;
+constexpr int kFwdWorkgroupsPerCU = 4;
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_max(float v) {
+  const int o = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), kCtrl, 0xf, 0xf, false);
+  return fmaxf(v, __int_as_float(o));
+}
+
+// Maximum over the 16 lanes of a DPP row: lane pairs, quads, half rows, row.
+__device__ __forceinline__ float row16_max(float v) {
+  v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max<0x141>(v);  // row_half_mirror
+  v = dpp_max<0x140>(v);  // row_mirror
+  return v;
+}
+
+struct FwdIn {
+  uint4 g, u;
+};
+
+__global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ row_weight, int8_t* __restrict__ y_q,
+    float* __restrict__ y_s, uint16_t* __restrict__ y_bf16, int64_t T, int64_t H, int tiles_h, int64_t units) {
+  __shared__ __align__(16) float s_tab[kSigEntries];
+  const int tid = threadIdx.x;
+  {
+    const float4* src = reinterpret_cast<const float4*>(g_sigma_tab);
+    float4* dst = reinterpret_cast<float4*>(s_tab);
+    for (int i = tid; i < kSigEntries / 4; i += kFwdThreads) dst[i] = src[i];
+  }
+  __syncthreads();
+
+  const int lane = tid & 63;
+  const int r = lane >> 4, p = lane & 15;
+  const bool odd = p & 1;
+  const int64_t waves = (int64_t)gridDim.x * (kFwdThreads / 64);
+  int64_t u = (int64_t)blockIdx.x * (kFwdThreads / 64) + (tid >> 6);
+  const int64_t groups = H / kGroup;
+
+  auto coords = [&](int64_t unit, int64_t& t, int64_t& h0, int64_t& hb) {
+    const int64_t rb = unit / tiles_h;
+    hb = unit - rb * tiles_h;
+    t = 4 * rb + r;
+    h0 = hb * kTile;
+  };
+  auto load = [&](FwdIn& in, int64_t t, int64_t h0) {
+    if (t < T) {
+      const uint16_t* xr = x + t * 2 * H + h0 + 8 * p;
+      in.g = load_stream(xr);
+      in.u = load_stream(xr + H);
+    } else {
+      in.g = make_uint4(0, 0, 0, 0);
+      in.u = in.g;
+    }
+  };
+
+  FwdIn in, in_next;
+  int64_t t = 0, h0 = 0, hb = 0;
+  if (u < units) {
+    coords(u, t, h0, hb);
+    load(in, t, h0);
+  }
+  while (u < units) {
+    const int64_t un = u + waves;
+    int64_t tn = 0, h0n = 0, hbn = 0;
+    if (un < units) {
+      coords(un, tn, h0n, hbn);
+      load(in_next, tn, h0n);
+    }
+    const float wt = (row_weight != nullptr && t < T) ? row_weight[t] : 1.0f;
+    uint32_t Yp[4];
+    float m = 0.0f;
+    const uint32_t gw[4] = {in.g.x, in.g.y, in.g.z, in.g.w};
+    const uint32_t uw[4] = {in.u.x, in.u.y, in.u.z, in.u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t olo, ohi;
+      sigma_offsets2(gw[k], olo, ohi);
+      const float s0 = lds_f32(s_tab, olo), s1 = lds_f32(s_tab, ohi);
+      float y0 = (bf16_lo(gw[k]) * s0) * bf16_lo(uw[k]);
+      float y1 = (bf16_hi(gw[k]) * s1) * bf16_hi(uw[k]);
+      if (row_weight != nullptr) {
+        y0 = y0 * wt;
+        y1 = y1 * wt;
+      }
+      Yp[k] = pack_bf16(y0, y1);
+      m = amax3(m, y0, y1);
+    }
+    m = row16_max(m);
+    const float scale = group_scale(m);
+    const float inv = 1.0f / scale;
+    uint2 c;
+    if (__builtin_expect(inv == __builtin_huge_valf(), 0))
+      c = codes8<true>(Yp, inv);
+    else
+      c = codes8<false>(Yp, inv);
+    // The even lane of each pair stores the pair's 16 codes.
+    const uint2 other = make_uint2(swap_neighbour(c.x), swap_neighbour(c.y));
+    if (t < T) {
+      if (!odd) {
+        const uint4 v = make_uint4(c.x, c.y, other.x, other.y);
+        __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w},
+                                    reinterpret_cast<u32x4*>(y_q + t * H + h0 + 8 * p));
+      }
+      if (y_bf16 != nullptr)
+        __builtin_nontemporal_store((u32x4){Yp[0], Yp[1], Yp[2], Yp[3]},
+                                    reinterpret_cast<u32x4*>(y_bf16 + t * H + h0 + 8 * p));
+      if (p == 0) y_s[t * groups + hb] = scale;
+    }
+    in = in_next;
+    u = un;
+    t = tn;
+    h0 = h0n;
+    hb = hbn;
+  }
+}
+
 // Diagnostics: the fused kernel's own sigmoid lookup and elementwise helpers,
 // run on their own so tests can compare them bit for bit.  Element i takes the
 // low half of the packed index path when i is even and the high half when odd,
@@ -640,6 +771,39 @@ __attribute__((visibility("default"))) int silu_dot_fwd_bwd_quant_fuse(const voi
                      grad_input_s, y_q_t, y_s_t, T, H, tiles_h, tiles);
   if (hipGetLastError() != hipSuccess) return SILUQUANT_ERR_LAUNCH_FAILED;
   return SILUQUANT_OK;
+}
+
+__attribute__((visibility("default"))) int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q,
+                                                          float* y_s, void* y_bf16, int64_t T, int64_t H,
+                                                          int64_t group, void* stream) {
+  if (group != kGroup) return SILUQUANT_ERR_BAD_GROUP;
+  if (T < 0 || H < 0 || H % kTile != 0) return SILUQUANT_ERR_BAD_SHAPE;
+  if (T == 0 || H == 0) return SILUQUANT_OK;
+  if (T > (int64_t(1) << 31) || H > (int64_t(1) << 22) || T > (int64_t(1) << 40) / H) return SILUQUANT_ERR_BAD_SHAPE;
+  if (!x || !y_q || !y_s) return SILUQUANT_ERR_NULL_PTR;
+  auto mis16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; };
+  auto mis4 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 3u) != 0; };
+  if (mis16(x) || mis16(y_q) || mis4(y_s) || (y_bf16 && mis16(y_bf16)) || (row_weight && mis4(row_weight)))
+    return SILUQUANT_ERR_MISALIGNED;
+  const int64_t pairs = T * H;
+  const void* bufs[5] = {x, row_weight, y_q, y_s, y_bf16};
+  const int64_t sizes[5] = {4 * pairs, 4 * T, pairs, 4 * (pairs / kGroup), 2 * pairs};
+  for (int i = 0; i < 5; ++i)
+    for (int j = i + 1; j < 5; ++j)
+      if (bufs[i] && bufs[j] && overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
+  int dev = 0;
+  int rc = ensure_table(&dev);
+  if (rc != SILUQUANT_OK) return rc;
+  const int tiles_h = (int)(H / kTile);
+  const int64_t units = ((T + 3) / 4) * tiles_h;
+  const int64_t waves_needed = units;
+  int64_t grid = (int64_t)g_cu_count[dev] * kFwdWorkgroupsPerCU;
+  const int64_t wg_needed = (waves_needed + kFwdThreads / 64 - 1) / (kFwdThreads / 64);
+  if (wg_needed < grid) grid = wg_needed;
+  hipLaunchKernelGGL(silu_fwd_quant_kernel, dim3((unsigned)grid), dim3(kFwdThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(x), row_weight, y_q, y_s,
+                     static_cast<uint16_t*>(y_bf16), T, H, tiles_h, units);
+  return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;
 }
 
 __attribute__((visibility("default"))) int siluquant_eval_sigmoid(const void* gate, float* s, int64_t n,

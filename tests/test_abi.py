@@ -135,3 +135,15 @@ def test_algorithmic_bytes(lib, shape):
 def test_algorithmic_bytes_rejects(lib):
     assert sq.algorithmic_bytes(-1, 128) == -1
     assert sq.algorithmic_bytes(128, 128, 64) == -1
+
+
+def test_forward_rejects_bad_arguments(lib):
+    f = lib.silu_fwd_quant
+    assert f(BASE, None, BASE + 2**24, BASE + 2**25, None, 8, 256, 64, None) == 3
+    assert f(BASE, None, BASE + 2**24, BASE + 2**25, None, 8, 200, 128, None) == 2
+    assert f(BASE, None, BASE + 2**24, BASE + 2**25, None, -1, 256, 128, None) == 2
+    assert f(None, None, BASE + 2**24, BASE + 2**25, None, 8, 256, 128, None) == 1
+    assert f(BASE + 8, None, BASE + 2**24, BASE + 2**25, None, 8, 256, 128, None) == 4
+    assert f(BASE, BASE + 2**26 + 2, BASE + 2**24, BASE + 2**25, None, 8, 256, 128, None) == 4
+    assert f(BASE, None, BASE + 1024, BASE + 2**25, None, 8, 256, 128, None) == 5
+    assert f(None, None, None, None, None, 0, 256, 128, None) == 0

@@ -1,0 +1,108 @@
+"""Parity of the forward quantiser (silu_fwd_quant) with the CPU oracle (GPU).
+
+Same bar as the backward pass: scales within 1e-6 relative, codes equal except
+|dq| <= 1 on at most 1e-4 of them; the cases assert exact equality, which holds.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import swiglu_backward_int8_amd as sq
+from swiglu_backward_int8_amd.inputs import WORKLOADS, make_inputs, random_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run(x, w=None, want_bf16=False):
+    T, H = x.shape[0], x.shape[1] // 2
+    yq = torch.full((T, H), -7, dtype=torch.int8, device=DEV)
+    ys = torch.full((T, H // 128), float("nan"), dtype=torch.float32, device=DEV)
+    yb = torch.empty((T, H), dtype=torch.bfloat16, device=DEV) if want_bf16 else None
+    sq.silu_fwd_quant(x, yq, ys, row_weight=w, y_bf16=yb)
+    torch.cuda.synchronize()
+    out = [yq.cpu().numpy(), ys.cpu().numpy()]
+    if want_bf16:
+        out.append(_bits(yb))
+    return out
+
+
+def check(x, w=None, want_bf16=False, label=""):
+    got = run(x, w, want_bf16)
+    want = oracle.silu_fwd_quant(_bits(x), None if w is None else w.cpu().numpy(), want_bf16=want_bf16)
+    assert np.array_equal(got[1].view(np.uint32), want[1].view(np.uint32)), "%s: scales differ" % label
+    d = np.abs(got[0].astype(np.int16) - want[0].astype(np.int16))
+    assert int(d.max(initial=0)) == 0, "%s: %d codes differ" % (label, int((d > 0).sum()))
+    if want_bf16:
+        assert np.array_equal(got[2], want[2]), "%s: bf16 y differs" % label
+    print("%s exact" % label, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available()
+    sq.prepare()
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workloads(name):
+    T = min(WORKLOADS[name].T, 8192)
+    x, _ = make_inputs(name, device=DEV, T=T)
+    check(x, want_bf16=True, label=name)
+
+
+@pytest.mark.parametrize("name", ["t4096_h1408", "t32768_h2048_outliers"])
+def test_row_weights(name):
+    x, _ = make_inputs(name, device=DEV, T=2048)
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    w = (torch.rand(x.shape[0], generator=gen, device=DEV) * 4 - 2).contiguous()
+    w[::17] = 0.0
+    check(x, w=w, want_bf16=True, label=name + " weighted")
+
+
+@pytest.mark.parametrize("T", [1, 3, 5, 127, 1000, 4097])
+def test_ragged_token_counts(T):
+    x, _ = random_inputs(T, 384, device=DEV, seed=T)
+    check(x, want_bf16=(T % 2 == 1), label="T=%d" % T)
+
+
+def test_without_bf16_output_matches():
+    x, _ = random_inputs(512, 256, device=DEV, seed=9)
+    a = run(x, want_bf16=False)
+    b = run(x, want_bf16=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_edge_values():
+    T, H = 64, 256
+    x = torch.zeros((T, 2 * H), dtype=torch.bfloat16, device=DEV)
+    x[:, :H] = torch.linspace(-100, 30, H, device=DEV).to(torch.bfloat16)
+    x[:, H:] = 1.0
+    x[1, :] = 0.0  # all-zero row: scale 1.0, codes 0
+    x[2, H:] = 2.0**-130  # tiny groups: inverse overflows
+    x[2, :H] = 20.0
+    check(x, want_bf16=True, label="edges")
+
+
+def test_empty_and_errors():
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    sq.silu_fwd_quant(x, torch.empty((0, 128), dtype=torch.int8, device=DEV),
+                      torch.empty((0, 1), dtype=torch.float32, device=DEV))
+    x, _ = random_inputs(8, 200, device=DEV)
+    with pytest.raises(ValueError):
+        sq.silu_fwd_quant(x, torch.empty((8, 200), dtype=torch.int8, device=DEV),
+                          torch.empty((8, 1), dtype=torch.float32, device=DEV))
+
+
+def test_forward_y_equals_backward_recompute():
+    # without a row weight the forward y is the y the backward pass quantises
+    x, dy = make_inputs("t4096_h1408", device=DEV, T=512)
+    yb = run(x, want_bf16=True)[2]
+    y, _ = sq.eval_intermediates(x, dy)
+    assert np.array_equal(yb, _bits(y))

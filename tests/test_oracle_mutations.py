@@ -16,7 +16,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "siluquant_oracle.c")
 PINS = ["tests/test_oracle_pipeline.py", "tests/test_oracle_quant.py",
-        "tests/test_oracle_elementwise.py", "tests/test_oracle_sigmoid.py"]
+        "tests/test_oracle_elementwise.py", "tests/test_oracle_sigmoid.py", "tests/test_oracle_forward.py"]
 
 MUTANTS = {
     "sigmoid_sign": ("exp(-(double)g)", "exp((double)g)"),
@@ -34,6 +34,10 @@ MUTANTS = {
     "gate_up_swapped": ("float g = oracle_bf16_to_f32(x[t * 2 * H + h]);",
                         "float g = oracle_bf16_to_f32(x[t * 2 * H + H + h]);"),
     "yqt_not_transposed": ("&y_q_t[h * T + t0], 1)", "&y_q_t[t0 * H + h], H)"),
+    "forward_missing_up": ("float v = silu * u;", "float v = silu;"),
+    "forward_ignores_weight": ("if (w) v = v * w[t];", "if (w) v = v + 0.0f * w[t];"),
+    "forward_weight_after_rounding": ("      Y[h] = oracle_bf16_to_f32(b);",
+                                      "      Y[h] = oracle_bf16_to_f32(b) * (w ? w[t] : 1.0f);"),
     "row_groups_skip_up_half": ("int64_t row_groups = (2 * H + group - 1) / group;",
                                 "int64_t row_groups = (H + group - 1) / group;"),
 }
