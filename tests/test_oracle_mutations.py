@@ -31,8 +31,14 @@ MUTANTS = {
     "scale_over_128": ("amax / 127.0f", "amax / 128.0f"),
     "amax_without_abs": ("float a = fabsf(v[i * stride]);", "float a = v[i * stride];"),
     "zero_group_scale_zero": ("(amax == 0.0f) ? 1.0f", "(amax == 0.0f) ? 0.0f"),
-    "gate_up_swapped": ("float g = oracle_bf16_to_f32(x[t * 2 * H + h]);",
-                        "float g = oracle_bf16_to_f32(x[t * 2 * H + H + h]);"),
+    "gate_up_swapped": ("float g = oracle_bf16_to_f32(x[t * 2 * H + h]);\n"
+                        "      float u = oracle_bf16_to_f32(x[t * 2 * H + H + h]);\n      float d",
+                        "float g = oracle_bf16_to_f32(x[t * 2 * H + H + h]);\n"
+                        "      float u = oracle_bf16_to_f32(x[t * 2 * H + h]);\n      float d"),
+    "forward_gate_up_swapped": ("float g = oracle_bf16_to_f32(x[t * 2 * H + h]);\n"
+                                "      float u = oracle_bf16_to_f32(x[t * 2 * H + H + h]);\n      float s",
+                                "float g = oracle_bf16_to_f32(x[t * 2 * H + H + h]);\n"
+                                "      float u = oracle_bf16_to_f32(x[t * 2 * H + h]);\n      float s"),
     "yqt_not_transposed": ("&y_q_t[h * T + t0], 1)", "&y_q_t[t0 * H + h], H)"),
     "forward_missing_up": ("float v = silu * u;", "float v = silu;"),
     "forward_ignores_weight": ("if (w) v = v * w[t];", "if (w) v = v + 0.0f * w[t];"),
