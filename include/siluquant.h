@@ -27,7 +27,7 @@ extern "C" {
 enum siluquant_status {
   SILUQUANT_OK = 0,
   SILUQUANT_ERR_NULL_PTR = 1,      /* a buffer pointer is NULL while T*H > 0 */
-  SILUQUANT_ERR_BAD_SHAPE = 2,     /* T < 0, H < 0, T or H not a multiple of 128, or too large */
+  SILUQUANT_ERR_BAD_SHAPE = 2,     /* T < 0, H < 0, H not a multiple of 128 (where required), or too large */
   SILUQUANT_ERR_BAD_GROUP = 3,     /* group != 128 */
   SILUQUANT_ERR_MISALIGNED = 4,    /* x, grad_y, grad_input_q, y_q_t not 16-byte aligned,
                                       or a scale buffer not 4-byte aligned */
@@ -48,8 +48,10 @@ enum siluquant_status {
  *                                    128 contiguous channels (d_gate groups first);
  *   grad_input_s  fp32 [T, 2H/128]   one scale per such group;
  *   y_q_t         int8 [H, T]        y transposed, quantised in groups of 128
- *                                    consecutive tokens along each row;
- *   y_s_t         fp32 [H, T/128]    one scale per such group.
+ *                                    consecutive tokens along each row (the last
+ *                                    group of a T that is not a multiple of 128
+ *                                    has the T % 128 tokens that remain);
+ *   y_s_t         fp32 [H, ceil(T/128)]  one scale per such group.
  * Arithmetic: fp32 throughout, no fused multiply-add.  s = 1 / (1 + exp(-g)) with
  * exp(-g) correctly rounded to fp32; y = (g*s)*u;
  * d_gate = ((d*u)*s) * (1 + g*(1 - s)); d_up = d*(g*s); each rounded to bf16
@@ -59,8 +61,10 @@ enum siluquant_status {
  * and the fp32 inverse (one rounding, ties to even), with q = 0 for v == 0.
  *   -128 is never produced.  Inputs must be finite and keep y, d_gate and d_up
  *   finite.
- * Sizes: T >= 0 and H >= 0 multiples of 128 (T == 0 or H == 0 is a no-op that
- *   returns SILUQUANT_OK), T <= 2^23, H <= 2^22; group must be 128.
+ * Sizes: any T >= 0, H >= 0 a multiple of 128 (T == 0 or H == 0 is a no-op that
+ *   returns SILUQUANT_OK), T <= 2^23, H <= 2^22; group must be 128.  y_q_t is
+ *   written with 16-byte stores when T % 16 == 0; other T work, with narrower
+ *   stores.
  * Ownership: the caller allocates and owns every buffer; the library keeps no
  *   pointer after the call returns.  Buffers must not overlap.
  * Asynchrony: the work is enqueued on `stream` and the call returns without

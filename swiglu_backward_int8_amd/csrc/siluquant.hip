@@ -204,29 +204,64 @@ struct TileIn {
 };
 
 // The tile base is uniform (scalar registers) and the lane's byte offset is a
-// fixed 32-bit value.
+// fixed 32-bit value.  In the last token block of a ragged T only `rows` of
+// the 128 rows exist; the lane's missing rows read as zeros, whose y, d_gate
+// and d_up are zero and so never raise a column maximum.
 __device__ __forceinline__ void load_tile(TileIn& in, const char* xt, const char* dyt, uint32_t lane_x,
-                                          uint32_t lane_dy, int64_t x_row_bytes, int64_t dy_row_bytes) {
+                                          uint32_t lane_dy, int64_t x_row_bytes, int64_t dy_row_bytes, int rows,
+                                          int q) {
+  const bool full = rows == kTile;
 #pragma unroll
   for (int i = 0; i < kRows; ++i) {
-    in.g[i] = load_stream(xt + i * x_row_bytes + lane_x);
-    in.u[i] = load_stream(xt + i * x_row_bytes + (x_row_bytes >> 1) + lane_x);
-    in.d[i] = load_stream(dyt + i * dy_row_bytes + lane_dy);
+    if (full || kRows * q + i < rows) {
+      in.g[i] = load_stream(xt + i * x_row_bytes + lane_x);
+      in.u[i] = load_stream(xt + i * x_row_bytes + (x_row_bytes >> 1) + lane_x);
+      in.d[i] = load_stream(dyt + i * dy_row_bytes + lane_dy);
+    } else {
+      in.g[i] = in.u[i] = in.d[i] = make_uint4(0, 0, 0, 0);
+    }
   }
 }
 
 struct Tile {
   int tb, hb;
+  int rows;  // tokens of this tile that exist: 128 except in the last block of a ragged T
   int64_t t0, h0;
 };
 
-__device__ __forceinline__ Tile tile_at(int tile, int tiles_h) {
+__device__ __forceinline__ Tile tile_at(int tile, int tiles_h, int64_t T) {
   Tile c;
   c.tb = tile / tiles_h;
   c.hb = tile - c.tb * tiles_h;
   c.t0 = (int64_t)c.tb * kTile;
   c.h0 = (int64_t)c.hb * kTile;
+  c.rows = (int)min<int64_t>(kTile, T - c.t0);
   return c;
+}
+
+// y_q_t piece out: 16 codes for tokens t0 + 16*chunk.. of one transposed row,
+// `bytes` of which exist (< 16 only in the last block of a ragged T).  Rows of
+// y_q_t are T bytes long, so the widest store the row alignment allows is
+// used: 16 bytes when T % 16 == 0, else 4 bytes when T % 4 == 0, else bytes.
+__device__ __forceinline__ void store_yq_piece(__amdgpu_buffer_rsrc_t buf, uint32_t off, uint4 v, int bytes,
+                                               int align) {
+  if (bytes == 16 && align == 16) {
+    store_stream(buf, off, v);
+    return;
+  }
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (4 * j + 4 <= bytes && align >= 4) {
+      __builtin_amdgcn_raw_buffer_store_b32(w[j], buf, off + 4 * j, 0, kStreamStorePolicy);
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (4 * j + b < bytes)
+          __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(w[j] >> (8 * b)), buf, off + 4 * j + b, 0,
+                                               kStreamStorePolicy);
+    }
+  }
 }
 
 // The elementwise part of one tile for one lane: packed bf16 y, d_gate and
@@ -355,7 +390,8 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
 
   // Row pitches in bytes and the lane's fixed byte offsets inside a tile.
   const int64_t x_row_bytes = 4 * H, dy_row_bytes = 2 * H, gq_row_bytes = 2 * H;
-  const int64_t row_groups = 2 * H / kGroup, col_groups = T / kGroup;
+  const int64_t row_groups = 2 * H / kGroup, col_groups = (T + kGroup - 1) / kGroup;
+  const int yq_align = (T & 15) == 0 ? 16 : (T & 3) == 0 ? 4 : 1;
   const uint32_t lane_x = (uint32_t)(kRows * q * x_row_bytes + 16 * p);
   const uint32_t lane_dy = (uint32_t)(kRows * q * dy_row_bytes + 16 * p);
   const uint32_t lane_gq = (uint32_t)((kRows * q + (p & 1)) * gq_row_bytes + 8 * (p & ~1));
@@ -383,10 +419,10 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
   const char* xb = reinterpret_cast<const char*>(x);
   const char* dyb = reinterpret_cast<const char*>(grad_y);
   TileIn in, in_next;
-  Tile cur = tile_at(tile < end ? tile : 0, tiles_h);
+  Tile cur = tile_at(tile < end ? tile : 0, tiles_h, T);
   if (tile < end)
     load_tile(in, xb + (cur.t0 * x_row_bytes + 2 * cur.h0), dyb + (cur.t0 * dy_row_bytes + 2 * cur.h0), lane_x,
-              lane_dy, x_row_bytes, dy_row_bytes);
+              lane_dy, x_row_bytes, dy_row_bytes, cur.rows, q);
   {
     const float4* src = reinterpret_cast<const float4*>(g_sigma_tab);
     float4* dst = reinterpret_cast<float4*>(s_tab);
@@ -397,10 +433,10 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
   while (tile < end) {
     // ---- the next tile's inputs stay in flight through this whole iteration --
     const int next = tile + stride;
-    const Tile nxt = tile_at(next < end ? next : tile, tiles_h);
+    const Tile nxt = tile_at(next < end ? next : tile, tiles_h, T);
     if (next < end)
       load_tile(in_next, xb + (nxt.t0 * x_row_bytes + 2 * nxt.h0), dyb + (nxt.t0 * dy_row_bytes + 2 * nxt.h0),
-                lane_x, lane_dy, x_row_bytes, dy_row_bytes);
+                lane_x, lane_dy, x_row_bytes, dy_row_bytes, nxt.rows, q);
 
     // ---- elementwise: packed bf16 results and partial maxima -------------
     uint32_t Yp[kRows][4], Gp[kRows][4], Up[kRows][4];  // y, d_gate, d_up
@@ -434,7 +470,7 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
       s_inv[g] = inv;
       if (inv == __builtin_huge_valf()) s_flag[0] = 1;
       const uint32_t off = (uint32_t)((g & (kTile - 1)) * row_groups + (g >> 7) * (H / kGroup));
-      grad_input_s[cur.t0 * row_groups + cur.hb + off] = scale;
+      if ((g & (kTile - 1)) < cur.rows) grad_input_s[cur.t0 * row_groups + cur.hb + off] = scale;
     } else if (tid < 3 * kTile) {
       const int c = tid - 2 * kTile;  // channel within the tile
       const int idx = ((c >> 2) & 1) * 64 + (c >> 3) * 4 + (c & 3);
@@ -461,8 +497,10 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
       const float4 inv_y1 = *reinterpret_cast<const float4*>(s_inv + 2 * kTile + 8 * p + 4);
       iy[0] = inv_y0.x, iy[1] = inv_y0.y, iy[2] = inv_y0.z, iy[3] = inv_y0.w;
       iy[4] = inv_y1.x, iy[5] = inv_y1.y, iy[6] = inv_y1.z, iy[7] = inv_y1.w;
+      // The record count covers the tile's existing rows only: the range check
+      // of the buffer unit drops the stores of missing rows of a ragged T.
       const __amdgpu_buffer_rsrc_t gq_buf =
-          buffer_of(grad_input_q + (cur.t0 * gq_row_bytes + cur.h0), (uint32_t)(kTile * gq_row_bytes));
+          buffer_of(grad_input_q + (cur.t0 * gq_row_bytes + cur.h0), (uint32_t)(cur.rows * gq_row_bytes));
       quantise_rows_and_y<false>(Gp, Up, Yp, idg, idu, iy, gq_buf, lane_gq, (uint32_t)gq_row_bytes, (uint32_t)H,
                                  s_yqt, p, q);
       __syncthreads();
@@ -473,7 +511,7 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
       if (s_flag[0]) {
         TileIn again;
         load_tile(again, xb + (cur.t0 * x_row_bytes + 2 * cur.h0), dyb + (cur.t0 * dy_row_bytes + 2 * cur.h0),
-                  lane_x, lane_dy, x_row_bytes, dy_row_bytes);
+                  lane_x, lane_dy, x_row_bytes, dy_row_bytes, cur.rows, q);
         float rg2[kRows], ru2[kRows], cm2[8];
         elementwise(again, s_tab, Yp, Gp, Up, rg2, ru2, cm2);
         quantise_rows_and_y<true>(Gp, Up, Yp, idg, idu, iy, gq_buf, lane_gq, (uint32_t)gq_row_bytes, (uint32_t)H,
@@ -491,7 +529,10 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
         const int h = id >> 3;
         const int phys = (id & 7) ^ ((h >> 3) & 7);
         const uint4 v = *reinterpret_cast<const uint4*>(s_yqt + h * kTile + phys * 16);
-        store_stream(yq_buf, lane_yq[step], v);
+        if (cur.rows == kTile && yq_align == 16)
+          store_stream(yq_buf, lane_yq[step], v);
+        else
+          store_yq_piece(yq_buf, lane_yq[step], v, min(16, max(0, cur.rows - 16 * (id & 7))), yq_align);
       }
     }
 
@@ -705,9 +746,10 @@ extern "C" {
 __attribute__((visibility("default"))) int64_t siluquant_algorithmic_bytes(int64_t T, int64_t H, int64_t group) {
   if (T < 0 || H < 0 || group != kGroup) return -1;
   const int64_t pairs = T * H;
-  // x (4) + grad_y (2) in; grad_input_q (2) + y_q_t (1) out, per pair;
-  // plus one fp32 scale per 128 codes on each axis.
-  return 9 * pairs + 4 * (2 * pairs / kGroup) + 4 * (pairs / kGroup);
+  // x (4) + grad_y (2) in; grad_input_q (2) + y_q_t (1) out, per pair; plus
+  // one fp32 scale per group on each axis (128 channels of a 2H row; 128
+  // tokens, or the shorter last group, of a row of y^T).
+  return 9 * pairs + 4 * T * ((2 * H + kGroup - 1) / kGroup) + 4 * H * ((T + kGroup - 1) / kGroup);
 }
 
 __attribute__((visibility("default"))) const char* siluquant_strerror(int status) {
@@ -734,14 +776,14 @@ __attribute__((visibility("default"))) int silu_dot_fwd_bwd_quant_fuse(const voi
                                                                        int8_t* y_q_t, float* y_s_t, int64_t T,
                                                                        int64_t H, int64_t group, void* stream) {
   if (group != kGroup) return SILUQUANT_ERR_BAD_GROUP;
-  if (T < 0 || H < 0 || T % kTile != 0 || H % kTile != 0) return SILUQUANT_ERR_BAD_SHAPE;
+  if (T < 0 || H < 0 || H % kTile != 0) return SILUQUANT_ERR_BAD_SHAPE;
   if (T == 0 || H == 0) return SILUQUANT_OK;
   // Tile indices are int and byte offsets int64: bound both.
   // Tile indices are int; a lane's byte offset inside a tile (< 512 * H for x)
   // must fit in 32 bits, and a tile's output span (128 rows of 2H bytes of
   // grad_input_q, 128 rows of T bytes of y_q_t) in a buffer resource's
   // 31-bit record count.
-  if (T > (int64_t(1) << 23) || H > (int64_t(1) << 22) || (T / kTile) * (H / kTile) > 0x7fffffff)
+  if (T > (int64_t(1) << 23) || H > (int64_t(1) << 22) || ((T + kTile - 1) / kTile) * (H / kTile) > 0x7fffffff)
     return SILUQUANT_ERR_BAD_SHAPE;
   if (!x || !grad_y || !grad_input_q || !grad_input_s || !y_q_t || !y_s_t) return SILUQUANT_ERR_NULL_PTR;
   auto mis16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; };
@@ -749,8 +791,9 @@ __attribute__((visibility("default"))) int silu_dot_fwd_bwd_quant_fuse(const voi
   if (mis16(x) || mis16(grad_y) || mis16(grad_input_q) || mis16(y_q_t) || mis4(grad_input_s) || mis4(y_s_t))
     return SILUQUANT_ERR_MISALIGNED;
   const int64_t pairs = T * H;
+  const int64_t col_groups = (T + kGroup - 1) / kGroup;
   const void* bufs[6] = {x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t};
-  const int64_t sizes[6] = {4 * pairs, 2 * pairs, 2 * pairs, 4 * (2 * pairs / kGroup), pairs, 4 * (pairs / kGroup)};
+  const int64_t sizes[6] = {4 * pairs, 2 * pairs, 2 * pairs, 4 * (2 * pairs / kGroup), pairs, 4 * H * col_groups};
   for (int i = 0; i < 6; ++i)
     for (int j = i + 1; j < 6; ++j)
       if (overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
@@ -760,7 +803,7 @@ __attribute__((visibility("default"))) int silu_dot_fwd_bwd_quant_fuse(const voi
   if (rc != SILUQUANT_OK) return rc;
 
   const int tiles_h = (int)(H / kTile);
-  const int tiles = (int)(T / kTile) * tiles_h;
+  const int tiles = (int)col_groups * tiles_h;
   // Persistent grid: as many workgroups as fit on the device at once (a
   // multiple of 8, one share per XCD), or one per tile if there are fewer.
   int grid = g_cu_count[dev] * kWorkgroupsPerCU;

@@ -53,7 +53,7 @@ BASE = 1 << 40
 
 
 def _ptrs(T, H, misalign=None, null=None, overlap=False):
-    sizes = [4 * T * H, 2 * T * H, 2 * T * H, 4 * (2 * T * H // 128), T * H, 4 * (T * H // 128)]
+    sizes = [4 * T * H, 2 * T * H, 2 * T * H, 4 * T * -(-2 * H // 128), T * H, 4 * H * -(-T // 128)]
     ptrs, at = [], BASE
     for s in sizes:
         ptrs.append(at)
@@ -69,7 +69,7 @@ def _ptrs(T, H, misalign=None, null=None, overlap=False):
 
 @pytest.mark.parametrize("T,H,group,code", [
     (256, 256, 64, 3), (256, 256, 0, 3), (256, 256, 256, 3),
-    (-128, 256, 128, 2), (256, -128, 128, 2), (200, 256, 128, 2), (256, 200, 128, 2), (256, 136, 128, 2),
+    (-128, 256, 128, 2), (256, -128, 128, 2), (256, 200, 128, 2), (256, 136, 128, 2), (100, 64, 128, 2),
 ])
 def test_bad_shape_and_group(lib, T, H, group, code):
     assert sq.raw_call(*_ptrs(abs(T), abs(H)), T, H, group, 0) == code
@@ -124,6 +124,12 @@ BYTES = {
     (16384, 11008): 721_420_288 + 360_710_144 + 360_710_144 + 11_272_192 + 180_355_072 + 5_636_096,
     (32768, 2048): 268_435_456 + 134_217_728 + 134_217_728 + 4_194_304 + 67_108_864 + 2_097_152,
 }
+
+
+def test_algorithmic_bytes_ragged_tokens(lib):
+    # T = 200: 2 token groups (128 + 72), 2H/128 = 4 row groups
+    T, H = 200, 256
+    assert sq.algorithmic_bytes(T, H) == 9 * T * H + 4 * T * 4 + 4 * H * 2
 
 
 @pytest.mark.parametrize("shape", sorted(BYTES))

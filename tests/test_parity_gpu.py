@@ -195,6 +195,22 @@ def test_non_default_stream():
     compare(got, oracle.silu_dot_fwd_bwd_quant_fuse(_bits(x), _bits(dy)), "side stream")
 
 
+@pytest.mark.parametrize("T,H", [(1, 128), (100, 256), (129, 128), (200, 384), (1000, 256), (1023, 128),
+                                 (4097, 384), (16380, 256), (333, 1408)])
+def test_ragged_token_counts(T, H):
+    # the last token group holds T % 128 tokens; y_q_t rows are T bytes, so
+    # T % 16 and T % 4 select the store width
+    x, dy = random_inputs(T, H, device=DEV, seed=T * 7 + H)
+    rep = check(x, dy, "ragged T=%d H=%d" % (T, H))
+    assert sum(rep.values()) == 0
+
+
+def test_ragged_tokens_outlier_workload():
+    x, dy = make_inputs("t32768_h2048_outliers", device=DEV, T=3001)
+    rep = check(x, dy, "outliers T=3001")
+    assert sum(rep.values()) == 0
+
+
 def test_binding_rejects_bad_tensors():
     x, dy = random_inputs(128, 128, device=DEV)
     outs = list(sq.empty_outputs(128, 128, DEV))
@@ -207,6 +223,9 @@ def test_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):
         x2, dy2 = random_inputs(200, 128, device=DEV)
         sq.silu_dot_fwd_bwd_quant_fuse(x2, dy2, *sq.empty_outputs(128, 128, DEV))
+    with pytest.raises(ValueError):  # H not a multiple of 128
+        x3, dy3 = random_inputs(128, 200, device=DEV)
+        sq.silu_dot_fwd_bwd_quant_fuse(x3, dy3, *sq.empty_outputs(128, 200, DEV))
     with pytest.raises(ValueError):
         sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *outs, group_size=64)
 
