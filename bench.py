@@ -8,7 +8,7 @@ code tensors and both scale tensors) divided by the time per call.
 
 Prints one JSON line.  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline]
+                    [--op backward|forward|fp8] [--no-cpu-baseline] [--probes]
 """
 
 from __future__ import annotations
@@ -48,7 +48,7 @@ def measured_traffic(workload: str):
     return entry.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x, dy, w, min_seconds: float = 10.0, max_calls: int = 5):
+def cpu_baseline(x, dy, w, min_seconds: float = 10.0, max_calls: int = 5, fp8: bool = False):
     """The oracle, single-threaded, on the whole workload: calls are repeated
     until at least min_seconds of CPU work (at most max_calls); the rate is the
     algorithmic bytes of all calls over their total time."""
@@ -64,7 +64,7 @@ def cpu_baseline(x, dy, w, min_seconds: float = 10.0, max_calls: int = 5):
     calls, total = 0, 0.0
     while calls < max_calls and (calls == 0 or total < min_seconds):
         t = time.perf_counter()
-        oracle.silu_dot_fwd_bwd_quant_fuse(xb, db)
+        (oracle.silu_dot_fwd_bwd_quant_fuse_fp8 if fp8 else oracle.silu_dot_fwd_bwd_quant_fuse)(xb, db)
         total += time.perf_counter() - t
         calls += 1
     return {
@@ -112,9 +112,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="t16384_h11008")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=["backward", "forward"], default="backward",
+    ap.add_argument("--op", choices=["backward", "forward", "fp8"], default="backward",
                     help="backward: the fused SwiGLU backward + two-axis int8 pass (the headline); "
-                         "forward: SwiGLU forward + row-wise int8 quantisation")
+                         "forward: SwiGLU forward + row-wise int8 quantisation; "
+                         "fp8: the backward pass with OCP FP8 E4M3 codes")
     ap.add_argument("--probes", action="store_true",
                     help="also time a plain 1 GiB copy and a 2-read/1-write bf16 add (reference streams)")
     args = ap.parse_args()
@@ -133,6 +134,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     forward = args.op == "forward"
+    fp8 = args.op == "fp8"
     nbytes = sq.forward_bytes(w.T, w.H) if forward else sq.algorithmic_bytes(w.T, w.H)
     # Rotate buffer sets so that one pass over them exceeds twice the 256 MB
     # last-level cache: every step then reads its inputs from HBM.
@@ -146,7 +148,7 @@ def main():
                     torch.empty((w.T, w.H // 128), dtype=torch.float32, device=dev))
             bufs.append((x, None, outs))
         else:
-            bufs.append((x, dy, sq.empty_outputs(w.T, w.H, dev)))
+            bufs.append((x, dy, sq.empty_outputs(w.T, w.H, dev, fp8=fp8)))
     sq.prepare()
     torch.cuda.synchronize()
 
@@ -154,6 +156,8 @@ def main():
         x, dy, outs = bufs[i % sets]
         if forward:
             sq.silu_fwd_quant(x, *outs)
+        elif fp8:
+            sq.silu_dot_fwd_bwd_quant_fuse_fp8(x, dy, *outs)
         else:
             sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *outs)
 
@@ -180,6 +184,8 @@ def main():
     metric = "achieved HBM GB/s (+% of MI355X peak) for fused silu fwd/bwd+int8 quant"
     if forward:
         metric = "achieved HBM GB/s (+% of MI355X peak) for fused silu forward + row-wise int8 quant"
+    elif fp8:
+        metric = "achieved HBM GB/s (+% of MI355X peak) for fused silu fwd/bwd+fp8 e4m3 quant"
     out = {
         "metric": metric,
         "value": round(value, 2),
@@ -205,8 +211,9 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic(("forward:" if forward else "") + w.name),
-            "kernel": "silu_fwd_quant_kernel" if forward else "silu_quant_bwd_kernel",
+            "traffic": measured_traffic({"forward": "forward:", "fp8": "fp8:"}.get(args.op, "") + w.name),
+            "kernel": {"forward": "silu_fwd_quant_kernel", "fp8": "silu_quant_bwd_kernel<Fmt::kFp8>"}.get(
+                args.op, "silu_quant_bwd_kernel<Fmt::kInt8>"),
             "avg_launch_us": round(per_launch_s * 1e6, 3),
         },
         "cpu_baseline": None,
@@ -215,7 +222,7 @@ def main():
         out["probes"] = stream_probes(dev)
     if not args.no_cpu_baseline and not forward:
         x, dy, _ = bufs[0]
-        out["cpu_baseline"] = cpu_baseline(x, dy, w)
+        out["cpu_baseline"] = cpu_baseline(x, dy, w, fp8=fp8)
     print(json.dumps(out), flush=True)
 
 

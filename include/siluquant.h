@@ -78,6 +78,30 @@ int silu_dot_fwd_bwd_quant_fuse(const void* x, const void* grad_y, int8_t* grad_
                                 void* stream);
 
 /*
+ * silu_dot_fwd_bwd_quant_fuse_fp8 -- the same pass with FP8 codes.
+ *
+ * The pages name an fp8 quantise kernel among the benchmarked ops (the AstrAI
+ * commit page, csrc/bench, its list of added benchmarks) without fixing its
+ * format; the format here is OCP FP8 E4M3 (the OCP 8-bit floating point
+ * specification: bias 7, no infinities, largest finite 448, subnormals
+ * k * 2^-9), which gfx950 converts to in hardware.
+ *
+ * Arguments, layouts, sizes, ownership, asynchrony and status codes are those
+ * of silu_dot_fwd_bwd_quant_fuse; the recomputation of y and of the gradients
+ * and the bf16 round trip are identical.  Only the code format differs:
+ *   grad_input_q  uint8 [T, 2H] E4M3 bit patterns, per-row 128-channel groups;
+ *   y_q_t         uint8 [H, T]  E4M3 bit patterns, 128-token groups;
+ *   scale = amax/448 (fp32 division; 1.0 when amax == 0), inv = 1/scale (fp32);
+ *   code = E4M3(v * inv) where v * inv is the fp32 product and the conversion
+ *   rounds to nearest, ties to even; magnitudes above 448 (only reachable when
+ *   inv overflows to infinity for a group of subnormal scale) saturate to
+ *   +-448 (0x7E / 0xFE); a zero v gives the zero of its own sign (0x00 / 0x80).
+ *   NaN codes (0x7F, 0xFF) are never produced.
+ */
+int silu_dot_fwd_bwd_quant_fuse_fp8(const void* x, const void* grad_y, void* grad_input_q, float* grad_input_s,
+                                    void* y_q_t, float* y_s_t, int64_t T, int64_t H, int64_t group, void* stream);
+
+/*
  * silu_fwd_quant -- forward SwiGLU with row-wise int8 group quantisation.
  *
  * The fused launch shape of kquant_swiglu_q8_1_rows on the page "kquant_mmq.rs"

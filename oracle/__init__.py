@@ -87,6 +87,15 @@ def _load():
         lib.oracle_silu_dot_fwd_bwd_quant_fuse.restype = ctypes.c_int
         lib.oracle_silu_fwd_quant.argtypes = [u16p, f32p, i8p, f32p, u16p, i64, i64, i64]
         lib.oracle_silu_fwd_quant.restype = ctypes.c_int
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        lib.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_e4m3.restype = ctypes.c_uint8
+        lib.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_to_f64.restype = ctypes.c_double
+        lib.oracle_quant_group_fp8.argtypes = [f32p, i64, i64, u8p, i64]
+        lib.oracle_quant_group_fp8.restype = ctypes.c_float
+        lib.oracle_silu_dot_fwd_bwd_quant_fuse_fp8.argtypes = [u16p, u16p, u8p, f32p, u8p, f32p, i64, i64, i64]
+        lib.oracle_silu_dot_fwd_bwd_quant_fuse_fp8.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -242,3 +251,41 @@ def silu_fwd_quant(x, w=None, group_size: int = GROUP, want_bf16: bool = False):
     if rc != 0:
         raise RuntimeError("oracle_silu_fwd_quant failed with code %d" % rc)
     return (yq, ys, yb) if want_bf16 else (yq, ys)
+
+
+def f32_to_e4m3(x: float) -> int:
+    return int(_load().oracle_f32_to_e4m3(float(np.float32(x))))
+
+
+def e4m3_to_float(c: int) -> float:
+    return float(_load().oracle_e4m3_to_f64(int(c) & 0xFF))
+
+
+def quant_group_fp8(v) -> tuple[np.ndarray, np.float32]:
+    """Quantise one group to E4M3 codes; returns (codes uint8, scale fp32)."""
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float32))
+    q = np.zeros(v.shape[0], dtype=np.uint8)
+    s = _load().oracle_quant_group_fp8(_ptr(v, ctypes.c_float), v.shape[0], 1, _ptr(q, ctypes.c_uint8), 1)
+    return q, np.float32(s)
+
+
+def silu_dot_fwd_bwd_quant_fuse_fp8(x, grad_y, group_size: int = GROUP):
+    """The FP8 (E4M3) variant of the whole pass; codes returned as uint8 bit patterns."""
+    x = _as_bits(x)
+    grad_y = _as_bits(grad_y)
+    T, H2 = x.shape
+    H = H2 // 2
+    if grad_y.shape != (T, H):
+        raise ValueError("grad_y must be [T, H]")
+    shp = output_shapes(T, H, group_size)
+    gq = np.zeros(shp["grad_input_q"], dtype=np.uint8)
+    gs = np.zeros(shp["grad_input_s"], dtype=np.float32)
+    yq = np.zeros(shp["y_q_t"], dtype=np.uint8)
+    ys = np.zeros(shp["y_s_t"], dtype=np.float32)
+    u8 = ctypes.c_uint8
+    rc = _load().oracle_silu_dot_fwd_bwd_quant_fuse_fp8(
+        _ptr(x, ctypes.c_uint16), _ptr(grad_y, ctypes.c_uint16), _ptr(gq, u8), _ptr(gs, ctypes.c_float),
+        _ptr(yq, u8), _ptr(ys, ctypes.c_float), T, H, group_size)
+    if rc != 0:
+        raise RuntimeError("oracle fp8 pass failed with code %d" % rc)
+    return gq, gs, yq, ys

@@ -47,6 +47,17 @@
  * weight multiplies that fp32 product, and the result is rounded to bf16 once;
  * groups are `group` contiguous channels of each row with the quantiser above.
  * The page's `limit` argument has no stated meaning and is not modelled.
+ *
+ * The FP8 variant (oracle_silu_dot_fwd_bwd_quant_fuse_fp8) writes the same two
+ * products with OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; largest finite value 448; subnormals k * 2^-9):
+ * scale = amax / 448 (1.0 when amax == 0), inv = 1 / scale, and the code is
+ * the e4m3 value nearest the fp32 product v * inv (ties to even), saturated to
+ * +-448; a zero v gives the zero code of its own sign (E4M3 has -0 = 0x80, and
+ * this also avoids 0 * inf).  Readings: the product is rounded to fp32 first,
+ * because the conversion takes an fp32 input; saturation only matters for
+ * groups whose inverse overflowed, since with a finite inverse |v * inv| stays
+ * within 448 * (1 + 2^-22).
  */
 #include <math.h>
 #include <stdint.h>
@@ -112,14 +123,20 @@ ORACLE_API void oracle_pair_f32(float g, float u, float d, float* y, float* d_ga
 
 /* ---- the quantiser --------------------------------------------------------- */
 
-/* Quantise n values v[0], v[stride], ... into q[0], q[qstride], ... and return
- * the group's scale.  v holds bf16-representable values. */
-ORACLE_API float oracle_quant_group(const float* v, int64_t n, int64_t stride, int8_t* q, int64_t qstride) {
+/* Largest magnitude of a group of n values spaced stride apart. */
+static float oracle_group_amax(const float* v, int64_t n, int64_t stride) {
   float amax = 0.0f;
   for (int64_t i = 0; i < n; ++i) {
     float a = fabsf(v[i * stride]);
     if (a > amax) amax = a;
   }
+  return amax;
+}
+
+/* Quantise n values v[0], v[stride], ... into q[0], q[qstride], ... and return
+ * the group's scale.  v holds bf16-representable values. */
+ORACLE_API float oracle_quant_group(const float* v, int64_t n, int64_t stride, int8_t* q, int64_t qstride) {
+  float amax = oracle_group_amax(v, n, stride);
   float scale = (amax == 0.0f) ? 1.0f : amax / 127.0f;
   float inv = 1.0f / scale;
   for (int64_t i = 0; i < n; ++i) {
@@ -134,6 +151,50 @@ ORACLE_API float oracle_quant_group(const float* v, int64_t n, int64_t stride, i
       out = (int8_t)r;
     }
     q[i * qstride] = out;
+  }
+  return scale;
+}
+
+/* ---- FP8 E4M3 ---------------------------------------------------------------- */
+
+/* Nearest E4M3 code of x (ties to even), saturating at +-448; NaN is outside
+ * the domain.  Works in double, where every step below is exact. */
+ORACLE_API uint8_t oracle_f32_to_e4m3(float x) {
+  uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  double a = fabs((double)x);
+  if (a >= 448.0) return sign | 0x7E; /* 448 = 1.75 * 2^8: exponent field 15, mantissa 6 */
+  if (a < 0.015625) {                 /* below 2^-6: subnormals k * 2^-9, k = 0..8 */
+    double k = nearbyint(a * 512.0);  /* k == 8 is the smallest normal, 2^-6 */
+    return sign | (uint8_t)k;         /* k == 8 encodes as exponent field 1, mantissa 0 */
+  }
+  int e;
+  double m = frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+  double mant = nearbyint(m * 16.0); /* 8 .. 16: the leading one plus 3 fraction bits */
+  if (mant == 16.0) {
+    mant = 8.0;
+    e += 1;
+  }
+  int efield = e - 1 + 7;
+  if (efield > 15 || (efield == 15 && mant > 14.0)) return sign | 0x7E; /* rounds above 448 */
+  return sign | (uint8_t)(efield << 3) | (uint8_t)((int)mant - 8);
+}
+
+ORACLE_API double oracle_e4m3_to_f64(uint8_t c) {
+  double sgn = (c & 0x80) ? -1.0 : 1.0;
+  int ef = (c >> 3) & 0xF, mf = c & 7;
+  if (ef == 15 && mf == 7) return NAN;
+  if (ef == 0) return sgn * mf * ldexp(1.0, -9);
+  return sgn * (1.0 + mf / 8.0) * ldexp(1.0, ef - 7);
+}
+
+/* Quantise one group to E4M3 codes; returns the scale. */
+ORACLE_API float oracle_quant_group_fp8(const float* v, int64_t n, int64_t stride, uint8_t* q, int64_t qstride) {
+  float amax = oracle_group_amax(v, n, stride);
+  float scale = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+  float inv = 1.0f / scale;
+  for (int64_t i = 0; i < n; ++i) {
+    float x = v[i * stride];
+    q[i * qstride] = (x == 0.0f) ? oracle_f32_to_e4m3(x) : oracle_f32_to_e4m3(x * inv);
   }
   return scale;
 }
@@ -221,6 +282,42 @@ ORACLE_API int oracle_silu_fwd_quant(const uint16_t* x, const float* w, int8_t* 
   }
   free(Y);
   return ORACLE_OK;
+}
+
+/* The FP8 variant of the whole pass: the same intermediates, E4M3 codes. */
+ORACLE_API int oracle_silu_dot_fwd_bwd_quant_fuse_fp8(const uint16_t* x, const uint16_t* grad_y, uint8_t* grad_input_q,
+                                                      float* grad_input_s, uint8_t* y_q_t, float* y_s_t, int64_t T,
+                                                      int64_t H, int64_t group) {
+  if (T < 0 || H < 0 || group <= 0) return ORACLE_BAD_ARG;
+  if (T == 0 || H == 0) return ORACLE_OK;
+  float* Y = (float*)malloc((size_t)(T * H) * sizeof(float));
+  float* D = (float*)malloc((size_t)(T * 2 * H) * sizeof(float));
+  if (!Y || !D) {
+    free(Y);
+    free(D);
+    return ORACLE_NO_MEMORY;
+  }
+  int rc = oracle_intermediates(x, grad_y, Y, D, T, H);
+  if (rc == ORACLE_OK) {
+    int64_t row_groups = (2 * H + group - 1) / group;
+    for (int64_t t = 0; t < T; ++t)
+      for (int64_t j = 0; j < row_groups; ++j) {
+        int64_t c0 = j * group;
+        int64_t n = (2 * H - c0 < group) ? 2 * H - c0 : group;
+        grad_input_s[t * row_groups + j] =
+            oracle_quant_group_fp8(&D[t * 2 * H + c0], n, 1, &grad_input_q[t * 2 * H + c0], 1);
+      }
+    int64_t col_groups = (T + group - 1) / group;
+    for (int64_t h = 0; h < H; ++h)
+      for (int64_t j = 0; j < col_groups; ++j) {
+        int64_t t0 = j * group;
+        int64_t n = (T - t0 < group) ? T - t0 : group;
+        y_s_t[h * col_groups + j] = oracle_quant_group_fp8(&Y[t0 * H + h], n, H, &y_q_t[h * T + t0], 1);
+      }
+  }
+  free(Y);
+  free(D);
+  return rc;
 }
 
 ORACLE_API int oracle_silu_dot_fwd_bwd_quant_fuse(const uint16_t* x, const uint16_t* grad_y, int8_t* grad_input_q,

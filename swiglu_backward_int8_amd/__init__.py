@@ -27,7 +27,7 @@ _ERRORS = {
     7: (RuntimeError, "LAUNCH_FAILED"),
 }
 
-EXPORTED = ("silu_dot_fwd_bwd_quant_fuse", "silu_fwd_quant", "siluquant_prepare", "siluquant_strerror",
+EXPORTED = ("silu_dot_fwd_bwd_quant_fuse", "silu_dot_fwd_bwd_quant_fuse_fp8", "silu_fwd_quant", "siluquant_prepare", "siluquant_strerror",
             "siluquant_algorithmic_bytes", "siluquant_eval_sigmoid", "siluquant_eval_intermediates")
 
 _lib = None
@@ -44,6 +44,8 @@ def lib() -> ctypes.CDLL:
         vp, i64 = ctypes.c_void_p, ctypes.c_int64
         L.silu_dot_fwd_bwd_quant_fuse.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
         L.silu_dot_fwd_bwd_quant_fuse.restype = ctypes.c_int
+        L.silu_dot_fwd_bwd_quant_fuse_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
+        L.silu_dot_fwd_bwd_quant_fuse_fp8.restype = ctypes.c_int
         L.siluquant_prepare.argtypes = []
         L.siluquant_prepare.restype = ctypes.c_int
         L.siluquant_strerror.argtypes = [ctypes.c_int]
@@ -87,10 +89,11 @@ def output_shapes(T: int, H: int, group: int = GROUP) -> dict:
 
 
 def raw_call(x_ptr: int, grad_y_ptr: int, gq_ptr: int, gs_ptr: int, yq_ptr: int, ys_ptr: int, T: int, H: int,
-             group: int, stream: int) -> int:
-    """The C entry point with plain integers for pointers; returns the status code."""
-    return int(lib().silu_dot_fwd_bwd_quant_fuse(x_ptr, grad_y_ptr, gq_ptr, gs_ptr, yq_ptr, ys_ptr, int(T),
-                                                 int(H), int(group), stream))
+             group: int, stream: int, fp8: bool = False) -> int:
+    """The C entry point (int8, or E4M3 with fp8=True) with plain integers for
+    pointers; returns the status code."""
+    fn = lib().silu_dot_fwd_bwd_quant_fuse_fp8 if fp8 else lib().silu_dot_fwd_bwd_quant_fuse
+    return int(fn(x_ptr, grad_y_ptr, gq_ptr, gs_ptr, yq_ptr, ys_ptr, int(T), int(H), int(group), stream))
 
 
 def silu_dot_fwd_bwd_quant_fuse(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size: int = GROUP):
@@ -98,8 +101,19 @@ def silu_dot_fwd_bwd_quant_fuse(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_
     and fp32 scales of [d_gate, d_up] (per row, 128-channel groups) and of y^T
     (128-token groups) into the given output tensors.  Enqueued on the current
     stream of x's device; returns None."""
+    _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size, fp8=False)
+
+
+def silu_dot_fwd_bwd_quant_fuse_fp8(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size: int = GROUP):
+    """The same pass with OCP FP8 E4M3 codes (scale = amax / 448).  The code
+    tensors are uint8 (the E4M3 bit patterns) or torch.float8_e4m3fn."""
+    _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size, fp8=True)
+
+
+def _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size: int, fp8: bool):
     import torch
 
+    code_types = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)) if fp8 else (torch.int8,)
     T, H = int(grad_y.shape[0]) if grad_y.dim() == 2 else -1, int(grad_y.shape[-1])
     if x.dim() != 2 or grad_y.dim() != 2 or tuple(x.shape) != (T, 2 * H):
         raise ValueError("x must be [T, 2H] and grad_y [T, H]; got %s and %s" % (tuple(x.shape), tuple(grad_y.shape)))
@@ -109,16 +123,16 @@ def silu_dot_fwd_bwd_quant_fuse(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_
     checks = [
         ("x", x, torch.bfloat16, (T, 2 * H)),
         ("grad_y", grad_y, torch.bfloat16, (T, H)),
-        ("grad_input_q", grad_input_q, torch.int8, want and want["grad_input_q"]),
+        ("grad_input_q", grad_input_q, code_types, want and want["grad_input_q"]),
         ("grad_input_s", grad_input_s, torch.float32, want and want["grad_input_s"]),
-        ("y_q_t", y_q_t, torch.int8, want and want["y_q_t"]),
+        ("y_q_t", y_q_t, code_types, want and want["y_q_t"]),
         ("y_s_t", y_s_t, torch.float32, want and want["y_s_t"]),
     ]
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU; got %s" % dev)
     for name, t, dt, shape in checks:
-        if t.dtype != dt:
+        if t.dtype not in (dt if isinstance(dt, tuple) else (dt,)):
             raise ValueError("%s must be %s, got %s" % (name, dt, t.dtype))
         if t.device != dev:
             raise ValueError("%s is on %s, x on %s" % (name, t.device, dev))
@@ -129,8 +143,8 @@ def silu_dot_fwd_bwd_quant_fuse(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         code = raw_call(x.data_ptr(), grad_y.data_ptr(), grad_input_q.data_ptr(), grad_input_s.data_ptr(),
-                        y_q_t.data_ptr(), y_s_t.data_ptr(), T, H, group_size, stream)
-    _check(code, "silu_dot_fwd_bwd_quant_fuse")
+                        y_q_t.data_ptr(), y_s_t.data_ptr(), T, H, group_size, stream, fp8=fp8)
+    _check(code, "silu_dot_fwd_bwd_quant_fuse_fp8" if fp8 else "silu_dot_fwd_bwd_quant_fuse")
 
 
 def silu_fwd_quant(x, y_q, y_s, row_weight=None, y_bf16=None, group_size: int = GROUP):
@@ -171,14 +185,16 @@ def forward_bytes(T: int, H: int, with_bf16: bool = False, with_weight: bool = F
     return 5 * T * H + 4 * (T * H // GROUP) + (2 * T * H if with_bf16 else 0) + (4 * T if with_weight else 0)
 
 
-def empty_outputs(T: int, H: int, device, group: int = GROUP):
-    """Freshly allocated (grad_input_q, grad_input_s, y_q_t, y_s_t) for a call."""
+def empty_outputs(T: int, H: int, device, group: int = GROUP, fp8: bool = False):
+    """Freshly allocated (grad_input_q, grad_input_s, y_q_t, y_s_t) for a call
+    (uint8 code tensors with fp8=True)."""
     import torch
 
     s = output_shapes(T, H, group)
-    return (torch.empty(s["grad_input_q"], dtype=torch.int8, device=device),
+    code = torch.uint8 if fp8 else torch.int8
+    return (torch.empty(s["grad_input_q"], dtype=code, device=device),
             torch.empty(s["grad_input_s"], dtype=torch.float32, device=device),
-            torch.empty(s["y_q_t"], dtype=torch.int8, device=device),
+            torch.empty(s["y_q_t"], dtype=code, device=device),
             torch.empty(s["y_s_t"], dtype=torch.float32, device=device))
 
 

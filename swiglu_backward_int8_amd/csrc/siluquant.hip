@@ -182,21 +182,62 @@ __device__ __forceinline__ uint32_t pack2(uint32_t b0, uint32_t b1) {
   return __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
 }
 
-// Eight codes from four packed-bf16 words with one inverse scale.
-template <bool kSafe>
-__device__ __forceinline__ uint2 codes8(const uint32_t (&w)[4], float inv) {
-  return make_uint2(pack4(code_word<kSafe>(bf16_lo(w[0]), inv), code_word<kSafe>(bf16_hi(w[0]), inv),
-                          code_word<kSafe>(bf16_lo(w[1]), inv), code_word<kSafe>(bf16_hi(w[1]), inv)),
-                    pack4(code_word<kSafe>(bf16_lo(w[2]), inv), code_word<kSafe>(bf16_hi(w[2]), inv),
-                          code_word<kSafe>(bf16_lo(w[3]), inv), code_word<kSafe>(bf16_hi(w[3]), inv)));
-}
+// Code formats of the two quantised products: int8 (largest code 127) or OCP
+// FP8 E4M3 (largest finite value 448).
+enum class Fmt { kInt8, kFp8 };
+template <Fmt F>
+constexpr float kQmax = F == Fmt::kInt8 ? 127.0f : 448.0f;
 
 // Scale of a group from the maximum of its unrounded values.  Rounding to
 // bf16 is monotone and odd, so the largest rounded magnitude is the rounding
 // of the largest unrounded magnitude.
+template <Fmt F = Fmt::kInt8>
 __device__ __forceinline__ float group_scale(float amax_unrounded) {
   float amax = bf16_lo(pack_bf16(amax_unrounded, 0.0f));
-  return amax == 0.0f ? 1.0f : amax / 127.0f;
+  return amax == 0.0f ? 1.0f : amax / kQmax<F>;
+}
+
+// E4M3 codes: the fp32 product v * inv converted by v_cvt_pk_fp8_f32 (nearest,
+// ties to even; a zero keeps its sign).  With a finite inverse |v * inv| stays
+// within 448 * (1 + 2^-22), which converts to +-448; kSafe serves groups whose
+// inverse overflowed: it clamps to +-448 (the conversion gives NaN beyond the
+// E4M3 range) and keeps a zero v as the zero of its sign.
+template <bool kSafe>
+__device__ __forceinline__ float fp8_input(float v, float inv) {
+  float t = v * inv;
+  if (kSafe) t = (v == 0.0f) ? v : __builtin_amdgcn_fmed3f(t, -448.0f, 448.0f);
+  return t;
+}
+
+// Four codes -> one word (a in the lowest byte).
+template <Fmt F, bool kSafe>
+__device__ __forceinline__ uint32_t codes4(float a, float b, float c, float d, float inv) {
+  if constexpr (F == Fmt::kInt8) {
+    return pack4(code_word<kSafe>(a, inv), code_word<kSafe>(b, inv), code_word<kSafe>(c, inv),
+                 code_word<kSafe>(d, inv));
+  } else {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_input<kSafe>(a, inv), fp8_input<kSafe>(b, inv), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_input<kSafe>(c, inv), fp8_input<kSafe>(d, inv), w, true);
+    return (uint32_t)w;
+  }
+}
+
+// Two codes -> the low half of a word.
+template <Fmt F, bool kSafe>
+__device__ __forceinline__ uint32_t codes2(float a, float b, float inv) {
+  if constexpr (F == Fmt::kInt8) {
+    return pack2(code_word<kSafe>(a, inv), code_word<kSafe>(b, inv));
+  } else {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fp8_input<kSafe>(a, inv), fp8_input<kSafe>(b, inv), 0,
+                                                      false) & 0xffffu;
+  }
+}
+
+// Eight codes from four packed-bf16 words with one inverse scale.
+template <bool kSafe, Fmt F = Fmt::kInt8>
+__device__ __forceinline__ uint2 codes8(const uint32_t (&w)[4], float inv) {
+  return make_uint2(codes4<F, kSafe>(bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1]), inv),
+                    codes4<F, kSafe>(bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3]), inv));
 }
 
 struct TileIn {
@@ -334,7 +375,7 @@ __device__ __forceinline__ uint4 pair_rows16(uint2 r0, uint2 r1, bool odd) {
 
 // gq_buf covers the tile's 128 rows of grad_input_q (its base is the tile's
 // first code); lane_gq addresses row kRows*q + (p & 1), channel 8 * (p & ~1).
-template <bool kSafe>
+template <Fmt F, bool kSafe>
 __device__ __forceinline__ void quantise_rows_and_y(const uint32_t (&Gp)[kRows][4], const uint32_t (&Up)[kRows][4],
                                                     const uint32_t (&Yp)[kRows][4], const float (&idg)[kRows],
                                                     const float (&idu)[kRows], const float (&iy)[8],
@@ -344,24 +385,22 @@ __device__ __forceinline__ void quantise_rows_and_y(const uint32_t (&Gp)[kRows][
 #pragma unroll
   for (int i = 0; i < kRows; i += 2) {
     const uint32_t row = i * gq_row_bytes + lane_gq;
-    store_stream(gq_buf, row, pair_rows16(codes8<kSafe>(Gp[i], idg[i]), codes8<kSafe>(Gp[i + 1], idg[i + 1]), odd));
+    store_stream(gq_buf, row,
+                 pair_rows16(codes8<kSafe, F>(Gp[i], idg[i]), codes8<kSafe, F>(Gp[i + 1], idg[i + 1]), odd));
     store_stream(gq_buf, row + H,
-                 pair_rows16(codes8<kSafe>(Up[i], idu[i]), codes8<kSafe>(Up[i + 1], idu[i + 1]), odd));
+                 pair_rows16(codes8<kSafe, F>(Up[i], idu[i]), codes8<kSafe, F>(Up[i + 1], idu[i + 1]), odd));
   }
   // y codes, transposed: channel 8p + j gets the lane's kRows tokens.
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    uint32_t c[kRows];
+    float v[kRows];
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) {
-      const float v = (j & 1) ? bf16_hi(Yp[i][j >> 1]) : bf16_lo(Yp[i][j >> 1]);
-      c[i] = code_word<kSafe>(v, iy[j]);
-    }
+    for (int i = 0; i < kRows; ++i) v[i] = (j & 1) ? bf16_hi(Yp[i][j >> 1]) : bf16_lo(Yp[i][j >> 1]);
     char* dst = s_yqt + yqt_byte(8 * p + j, q);
     if constexpr (kRows == 4)
-      *reinterpret_cast<uint32_t*>(dst) = pack4(c[0], c[1], c[2], c[3]);
+      *reinterpret_cast<uint32_t*>(dst) = codes4<F, kSafe>(v[0], v[1], v[2], v[3], iy[j]);
     else
-      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)pack2(c[0], c[1]);
+      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)codes2<F, kSafe>(v[0], v[1], iy[j]);
   }
 }
 
@@ -372,6 +411,7 @@ __device__ __forceinline__ void quantise_rows_and_y(const uint32_t (&Gp)[kRows][
 // tiles, whose scale writes share cache lines, then meet in the same L2.
 // One workgroup per CU; the next tile's inputs are requested at the top of each
 // iteration and stay in flight while the current tile is processed.
+template <Fmt F>
 __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void silu_quant_bwd_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ grad_y, int8_t* __restrict__ grad_input_q,
     float* __restrict__ grad_input_s, int8_t* __restrict__ y_q_t, float* __restrict__ y_s_t, int64_t T, int64_t H,
@@ -465,7 +505,7 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
       float m = 0.0f;
 #pragma unroll
       for (int pp = 0; pp < 16; ++pp) m = fmaxf(m, s_rowpart[pp * kRowPartStride + g]);
-      const float scale = group_scale(m);
+      const float scale = group_scale<F>(m);
       const float inv = 1.0f / scale;
       s_inv[g] = inv;
       if (inv == __builtin_huge_valf()) s_flag[0] = 1;
@@ -477,7 +517,7 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
       float m = 0.0f;
 #pragma unroll 8
       for (int qq = 0; qq < kQ; ++qq) m = fmaxf(m, s_colpart[qq * kTile + idx]);
-      const float scale = group_scale(m);
+      const float scale = group_scale<F>(m);
       const float inv = 1.0f / scale;
       s_inv[2 * kTile + c] = inv;
       if (inv == __builtin_huge_valf()) s_flag[0] = 1;
@@ -501,7 +541,7 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
       // of the buffer unit drops the stores of missing rows of a ragged T.
       const __amdgpu_buffer_rsrc_t gq_buf =
           buffer_of(grad_input_q + (cur.t0 * gq_row_bytes + cur.h0), (uint32_t)(cur.rows * gq_row_bytes));
-      quantise_rows_and_y<false>(Gp, Up, Yp, idg, idu, iy, gq_buf, lane_gq, (uint32_t)gq_row_bytes, (uint32_t)H,
+      quantise_rows_and_y<F, false>(Gp, Up, Yp, idg, idu, iy, gq_buf, lane_gq, (uint32_t)gq_row_bytes, (uint32_t)H,
                                  s_yqt, p, q);
       __syncthreads();
       // Rare: some group's inverse overflowed (its maximum is below
@@ -514,7 +554,7 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
                   lane_x, lane_dy, x_row_bytes, dy_row_bytes, cur.rows, q);
         float rg2[kRows], ru2[kRows], cm2[8];
         elementwise(again, s_tab, Yp, Gp, Up, rg2, ru2, cm2);
-        quantise_rows_and_y<true>(Gp, Up, Yp, idg, idu, iy, gq_buf, lane_gq, (uint32_t)gq_row_bytes, (uint32_t)H,
+        quantise_rows_and_y<F, true>(Gp, Up, Yp, idg, idu, iy, gq_buf, lane_gq, (uint32_t)gq_row_bytes, (uint32_t)H,
                                   s_yqt, p, q);
         __syncthreads();
       }
@@ -741,6 +781,54 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 
 }  // namespace
 
+namespace {
+
+template <Fmt F>
+int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float* grad_input_s, void* y_q_t,
+                    float* y_s_t, int64_t T, int64_t H, int64_t group, void* stream) {
+  if (group != kGroup) return SILUQUANT_ERR_BAD_GROUP;
+  if (T < 0 || H < 0 || H % kTile != 0) return SILUQUANT_ERR_BAD_SHAPE;
+  if (T == 0 || H == 0) return SILUQUANT_OK;
+  // Tile indices are int; a lane's byte offset inside a tile (< 512 * H for x)
+  // must fit in 32 bits, and a tile's output span (128 rows of 2H bytes of
+  // grad_input_q, 128 rows of T bytes of y_q_t) in a buffer resource's
+  // 31-bit record count.
+  if (T > (int64_t(1) << 23) || H > (int64_t(1) << 22) || ((T + kTile - 1) / kTile) * (H / kTile) > 0x7fffffff)
+    return SILUQUANT_ERR_BAD_SHAPE;
+  if (!x || !grad_y || !grad_input_q || !grad_input_s || !y_q_t || !y_s_t) return SILUQUANT_ERR_NULL_PTR;
+  auto mis16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; };
+  auto mis4 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 3u) != 0; };
+  if (mis16(x) || mis16(grad_y) || mis16(grad_input_q) || mis16(y_q_t) || mis4(grad_input_s) || mis4(y_s_t))
+    return SILUQUANT_ERR_MISALIGNED;
+  const int64_t pairs = T * H;
+  const int64_t col_groups = (T + kGroup - 1) / kGroup;
+  const void* bufs[6] = {x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t};
+  const int64_t sizes[6] = {4 * pairs, 2 * pairs, 2 * pairs, 4 * (2 * pairs / kGroup), pairs, 4 * H * col_groups};
+  for (int i = 0; i < 6; ++i)
+    for (int j = i + 1; j < 6; ++j)
+      if (overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
+
+  int dev = 0;
+  int rc = ensure_table(&dev);
+  if (rc != SILUQUANT_OK) return rc;
+
+  const int tiles_h = (int)(H / kTile);
+  const int tiles = (int)col_groups * tiles_h;
+  // Persistent grid: as many workgroups as fit on the device at once (a
+  // multiple of 8, one share per XCD), or one per tile if there are fewer.
+  int grid = g_cu_count[dev] * kWorkgroupsPerCU;
+  grid = grid >= 8 ? grid - grid % 8 : grid;
+  if (tiles < grid) grid = tiles;
+  hipLaunchKernelGGL(silu_quant_bwd_kernel<F>, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(grad_y),
+                     static_cast<int8_t*>(grad_input_q), grad_input_s, static_cast<int8_t*>(y_q_t), y_s_t, T, H,
+                     tiles_h, tiles);
+  if (hipGetLastError() != hipSuccess) return SILUQUANT_ERR_LAUNCH_FAILED;
+  return SILUQUANT_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 __attribute__((visibility("default"))) int64_t siluquant_algorithmic_bytes(int64_t T, int64_t H, int64_t group) {
@@ -775,45 +863,14 @@ __attribute__((visibility("default"))) int silu_dot_fwd_bwd_quant_fuse(const voi
                                                                        int8_t* grad_input_q, float* grad_input_s,
                                                                        int8_t* y_q_t, float* y_s_t, int64_t T,
                                                                        int64_t H, int64_t group, void* stream) {
-  if (group != kGroup) return SILUQUANT_ERR_BAD_GROUP;
-  if (T < 0 || H < 0 || H % kTile != 0) return SILUQUANT_ERR_BAD_SHAPE;
-  if (T == 0 || H == 0) return SILUQUANT_OK;
-  // Tile indices are int and byte offsets int64: bound both.
-  // Tile indices are int; a lane's byte offset inside a tile (< 512 * H for x)
-  // must fit in 32 bits, and a tile's output span (128 rows of 2H bytes of
-  // grad_input_q, 128 rows of T bytes of y_q_t) in a buffer resource's
-  // 31-bit record count.
-  if (T > (int64_t(1) << 23) || H > (int64_t(1) << 22) || ((T + kTile - 1) / kTile) * (H / kTile) > 0x7fffffff)
-    return SILUQUANT_ERR_BAD_SHAPE;
-  if (!x || !grad_y || !grad_input_q || !grad_input_s || !y_q_t || !y_s_t) return SILUQUANT_ERR_NULL_PTR;
-  auto mis16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; };
-  auto mis4 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 3u) != 0; };
-  if (mis16(x) || mis16(grad_y) || mis16(grad_input_q) || mis16(y_q_t) || mis4(grad_input_s) || mis4(y_s_t))
-    return SILUQUANT_ERR_MISALIGNED;
-  const int64_t pairs = T * H;
-  const int64_t col_groups = (T + kGroup - 1) / kGroup;
-  const void* bufs[6] = {x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t};
-  const int64_t sizes[6] = {4 * pairs, 2 * pairs, 2 * pairs, 4 * (2 * pairs / kGroup), pairs, 4 * H * col_groups};
-  for (int i = 0; i < 6; ++i)
-    for (int j = i + 1; j < 6; ++j)
-      if (overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
+  return launch_backward<Fmt::kInt8>(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, T, H, group, stream);
+}
 
-  int dev = 0;
-  int rc = ensure_table(&dev);
-  if (rc != SILUQUANT_OK) return rc;
-
-  const int tiles_h = (int)(H / kTile);
-  const int tiles = (int)col_groups * tiles_h;
-  // Persistent grid: as many workgroups as fit on the device at once (a
-  // multiple of 8, one share per XCD), or one per tile if there are fewer.
-  int grid = g_cu_count[dev] * kWorkgroupsPerCU;
-  grid = grid >= 8 ? grid - grid % 8 : grid;
-  if (tiles < grid) grid = tiles;
-  hipLaunchKernelGGL(silu_quant_bwd_kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(grad_y), grad_input_q,
-                     grad_input_s, y_q_t, y_s_t, T, H, tiles_h, tiles);
-  if (hipGetLastError() != hipSuccess) return SILUQUANT_ERR_LAUNCH_FAILED;
-  return SILUQUANT_OK;
+__attribute__((visibility("default"))) int silu_dot_fwd_bwd_quant_fuse_fp8(const void* x, const void* grad_y,
+                                                                           void* grad_input_q, float* grad_input_s,
+                                                                           void* y_q_t, float* y_s_t, int64_t T,
+                                                                           int64_t H, int64_t group, void* stream) {
+  return launch_backward<Fmt::kFp8>(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, T, H, group, stream);
 }
 
 __attribute__((visibility("default"))) int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q,

@@ -71,31 +71,36 @@ def _ptrs(T, H, misalign=None, null=None, overlap=False):
     (256, 256, 64, 3), (256, 256, 0, 3), (256, 256, 256, 3),
     (-128, 256, 128, 2), (256, -128, 128, 2), (256, 200, 128, 2), (256, 136, 128, 2), (100, 64, 128, 2),
 ])
-def test_bad_shape_and_group(lib, T, H, group, code):
-    assert sq.raw_call(*_ptrs(abs(T), abs(H)), T, H, group, 0) == code
+@pytest.mark.parametrize("fp8", [False, True])
+def test_bad_shape_and_group(lib, T, H, group, code, fp8):
+    assert sq.raw_call(*_ptrs(abs(T), abs(H)), T, H, group, 0, fp8=fp8) == code
 
 
 @pytest.mark.parametrize("which", range(6))
-def test_null_pointer(lib, which):
-    assert sq.raw_call(*_ptrs(256, 256, null=which), 256, 256, 128, 0) == 1
+@pytest.mark.parametrize("fp8", [False, True])
+def test_null_pointer(lib, which, fp8):
+    assert sq.raw_call(*_ptrs(256, 256, null=which), 256, 256, 128, 0, fp8=fp8) == 1
 
 
 @pytest.mark.parametrize("which", range(6))
-def test_misaligned(lib, which):
-    assert sq.raw_call(*_ptrs(256, 256, misalign=which), 256, 256, 128, 0) == 4
+@pytest.mark.parametrize("fp8", [False, True])
+def test_misaligned(lib, which, fp8):
+    assert sq.raw_call(*_ptrs(256, 256, misalign=which), 256, 256, 128, 0, fp8=fp8) == 4
 
 
-def test_overlap(lib):
-    assert sq.raw_call(*_ptrs(256, 256, overlap=True), 256, 256, 128, 0) == 5
+@pytest.mark.parametrize("fp8", [False, True])
+def test_overlap(lib, fp8):
+    assert sq.raw_call(*_ptrs(256, 256, overlap=True), 256, 256, 128, 0, fp8=fp8) == 5
     p = _ptrs(256, 256)
     p[1] = p[0]  # grad_y aliases x
-    assert sq.raw_call(*p, 256, 256, 128, 0) == 5
+    assert sq.raw_call(*p, 256, 256, 128, 0, fp8=fp8) == 5
 
 
-def test_empty_is_a_no_op(lib):
+@pytest.mark.parametrize("fp8", [False, True])
+def test_empty_is_a_no_op(lib, fp8):
     # nothing to do: success without any pointer being looked at
-    assert sq.raw_call(0, 0, 0, 0, 0, 0, 0, 256, 128, 0) == 0
-    assert sq.raw_call(0, 0, 0, 0, 0, 0, 256, 0, 128, 0) == 0
+    assert sq.raw_call(0, 0, 0, 0, 0, 0, 0, 256, 128, 0, fp8=fp8) == 0
+    assert sq.raw_call(0, 0, 0, 0, 0, 0, 256, 0, 128, 0, fp8=fp8) == 0
 
 
 def test_diagnostics_reject_bad_arguments(lib):

@@ -16,7 +16,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "siluquant_oracle.c")
 PINS = ["tests/test_oracle_pipeline.py", "tests/test_oracle_quant.py",
-        "tests/test_oracle_elementwise.py", "tests/test_oracle_sigmoid.py", "tests/test_oracle_forward.py"]
+        "tests/test_oracle_elementwise.py", "tests/test_oracle_sigmoid.py", "tests/test_oracle_forward.py",
+        "tests/test_oracle_fp8.py"]
 
 MUTANTS = {
     "sigmoid_sign": ("exp(-(double)g)", "exp((double)g)"),
@@ -30,7 +31,8 @@ MUTANTS = {
     "fp32_product_before_rounding": ("double t = (double)x * (double)inv;", "double t = (double)(x * inv);"),
     "scale_over_128": ("amax / 127.0f", "amax / 128.0f"),
     "amax_without_abs": ("float a = fabsf(v[i * stride]);", "float a = v[i * stride];"),
-    "zero_group_scale_zero": ("(amax == 0.0f) ? 1.0f", "(amax == 0.0f) ? 0.0f"),
+    "zero_group_scale_zero": ("(amax == 0.0f) ? 1.0f : amax / 127.0f", "(amax == 0.0f) ? 0.0f : amax / 127.0f"),
+    "fp8_zero_group_scale_zero": ("(amax == 0.0f) ? 1.0f : amax / 448.0f", "(amax == 0.0f) ? 0.0f : amax / 448.0f"),
     "gate_up_swapped": ("float g = oracle_bf16_to_f32(x[t * 2 * H + h]);\n"
                         "      float u = oracle_bf16_to_f32(x[t * 2 * H + H + h]);\n      float d",
                         "float g = oracle_bf16_to_f32(x[t * 2 * H + H + h]);\n"
@@ -39,13 +41,24 @@ MUTANTS = {
                                 "      float u = oracle_bf16_to_f32(x[t * 2 * H + H + h]);\n      float s",
                                 "float g = oracle_bf16_to_f32(x[t * 2 * H + H + h]);\n"
                                 "      float u = oracle_bf16_to_f32(x[t * 2 * H + h]);\n      float s"),
-    "yqt_not_transposed": ("&y_q_t[h * T + t0], 1)", "&y_q_t[t0 * H + h], H)"),
+    "yqt_not_transposed": ("oracle_quant_group(&Y[t0 * H + h], n, H, &y_q_t[h * T + t0], 1)",
+                           "oracle_quant_group(&Y[t0 * H + h], n, H, &y_q_t[t0 * H + h], H)"),
+    "fp8_yqt_not_transposed": ("oracle_quant_group_fp8(&Y[t0 * H + h], n, H, &y_q_t[h * T + t0], 1)",
+                               "oracle_quant_group_fp8(&Y[t0 * H + h], n, H, &y_q_t[t0 * H + h], H)"),
     "forward_missing_up": ("float v = silu * u;", "float v = silu;"),
     "forward_ignores_weight": ("if (w) v = v * w[t];", "if (w) v = v + 0.0f * w[t];"),
     "forward_weight_after_rounding": ("      Y[h] = oracle_bf16_to_f32(b);",
                                       "      Y[h] = oracle_bf16_to_f32(b) * (w ? w[t] : 1.0f);"),
-    "row_groups_skip_up_half": ("int64_t row_groups = (2 * H + group - 1) / group;",
-                                "int64_t row_groups = (H + group - 1) / group;"),
+    "fp8_scale_over_127": ("(amax == 0.0f) ? 1.0f : amax / 448.0f", "(amax == 0.0f) ? 1.0f : amax / 127.0f"),
+    "fp8_truncates": ("double mant = nearbyint(m * 16.0);", "double mant = floor(m * 16.0);"),
+    "fp8_subnormal_step": ("double k = nearbyint(a * 512.0);", "double k = nearbyint(a * 256.0);"),
+    "fp8_exponent_bias": ("int efield = e - 1 + 7;", "int efield = e - 1 + 8;"),
+    "row_groups_skip_up_half": ("  int64_t row_groups = (2 * H + group - 1) / group;\n  for (int64_t t = 0; t < T; ++t) {",
+                                "  int64_t row_groups = (H + group - 1) / group;\n  for (int64_t t = 0; t < T; ++t) {"),
+    "fp8_row_groups_skip_up_half": ("    int64_t row_groups = (2 * H + group - 1) / group;\n    for (int64_t t = 0; t < T; ++t)\n",
+                                    "    int64_t row_groups = (H + group - 1) / group;\n    for (int64_t t = 0; t < T; ++t)\n"),
+    "fp8_zero_loses_sign": ("(x == 0.0f) ? oracle_f32_to_e4m3(x)", "(x == 0.0f) ? 0"),
+    "fp8_nan_beyond_range": ("if (a >= 448.0) return sign | 0x7E;", "if (a >= 464.0) return sign | 0x7F;"),
 }
 
 
