@@ -96,6 +96,9 @@ def _load():
         lib.oracle_quant_group_fp8.restype = ctypes.c_float
         lib.oracle_silu_dot_fwd_bwd_quant_fuse_fp8.argtypes = [u16p, u16p, u8p, f32p, u8p, f32p, i64, i64, i64]
         lib.oracle_silu_dot_fwd_bwd_quant_fuse_fp8.restype = ctypes.c_int
+        i8p, f64p = ctypes.POINTER(ctypes.c_int8), ctypes.POINTER(ctypes.c_double)
+        lib.oracle_i8_gemm_group_scaled.argtypes = [i8p, f32p, i8p, f32p, f64p, f64p, i64, i64, i64, i64, i64]
+        lib.oracle_i8_gemm_group_scaled.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -289,3 +292,30 @@ def silu_dot_fwd_bwd_quant_fuse_fp8(x, grad_y, group_size: int = GROUP):
     if rc != 0:
         raise RuntimeError("oracle fp8 pass failed with code %d" % rc)
     return gq, gs, yq, ys
+
+
+def i8_gemm_group_scaled(A, sA, B, sB, group_size: int = GROUP, b_rows_per_scale: int = 1):
+    """C = A . B^T of group-scaled int8 operands, exactly: returns (C, C_abs) in
+    float64, where C_abs[m, n] is the sum over groups of |term| (a bound for the
+    rounding of any fp32 evaluation).  A int8 [M, K], sA fp32 [M, K/group];
+    B int8 [N, K], sB fp32 [ceil(N / b_rows_per_scale), K/group]."""
+    A = np.ascontiguousarray(A, dtype=np.int8)
+    B = np.ascontiguousarray(B, dtype=np.int8)
+    sA = np.ascontiguousarray(sA, dtype=np.float32)
+    sB = np.ascontiguousarray(sB, dtype=np.float32)
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or K % group_size:
+        raise ValueError("A [M, K] and B [N, K] with K a multiple of the group size")
+    groups = K // group_size
+    if sA.shape != (M, groups) or sB.shape != (-(-N // b_rows_per_scale), groups):
+        raise ValueError("scale shapes: sA %s, sB %s" % (sA.shape, sB.shape))
+    C = np.zeros((M, N), dtype=np.float64)
+    C_abs = np.zeros((M, N), dtype=np.float64)
+    i8 = ctypes.c_int8
+    rc = _load().oracle_i8_gemm_group_scaled(_ptr(A, i8), _ptr(sA, ctypes.c_float), _ptr(B, i8),
+                                             _ptr(sB, ctypes.c_float), _ptr(C, ctypes.c_double),
+                                             _ptr(C_abs, ctypes.c_double), M, N, K, group_size, b_rows_per_scale)
+    if rc != 0:
+        raise RuntimeError("oracle GEMM failed with code %d" % rc)
+    return C, C_abs

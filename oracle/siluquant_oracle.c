@@ -58,6 +58,20 @@
  * because the conversion takes an fp32 input; saturation only matters for
  * groups whose inverse overflowed, since with a finite inverse |v * inv| stays
  * within 448 * (1 + 2^-22).
+ *
+ * The group-scaled int8 product (oracle_i8_gemm_group_scaled) is the consumer
+ * of the two quantised layouts: the same page's fusion bullet names the
+ * K-group and M-group quantisations, i.e. groups of 128 along the contraction
+ * axis of the GEMM that reads them.  The page gives no formula for the GEMM;
+ * the plain reading is the product of the dequantised operands,
+ *   C[m, n] = sum_k (sA[m, k/G] * A[m, k]) * (sB[n/Bb, k/G] * B[n, k])
+ *           = sum_g sA[m, g] * sB[n/Bb, g] * (sum_{k in g} A[m, k] * B[n, k]),
+ * with A [M, K] and B [N, K] int8 row-major (C = A . B^T), G = group and Bb
+ * the number of B rows sharing one scale (1: one scale per row and group, as
+ * y_s_t; 128: one per 128 x 128 block, a weight's usual layout).  The integer
+ * dot of each group is exact (int64) and the sum over groups is taken in
+ * double; the result is reported with the sum of the absolute values of the
+ * group terms, which bounds the rounding of any fp32 evaluation order.
  */
 #include <math.h>
 #include <stdint.h>
@@ -318,6 +332,30 @@ ORACLE_API int oracle_silu_dot_fwd_bwd_quant_fuse_fp8(const uint16_t* x, const u
   free(Y);
   free(D);
   return rc;
+}
+
+/* ---- the group-scaled int8 product ------------------------------------------ */
+
+ORACLE_API int oracle_i8_gemm_group_scaled(const int8_t* A, const float* sA, const int8_t* B, const float* sB,
+                                           double* C, double* C_abs, int64_t M, int64_t N, int64_t K,
+                                           int64_t group, int64_t b_rows_per_scale) {
+  if (M < 0 || N < 0 || K < 0 || group <= 0 || K % group != 0 || b_rows_per_scale <= 0) return ORACLE_BAD_ARG;
+  const int64_t groups = K / group;
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t n = 0; n < N; ++n) {
+      double sum = 0.0, sum_abs = 0.0;
+      for (int64_t g = 0; g < groups; ++g) {
+        int64_t dot = 0;
+        for (int64_t k = g * group; k < (g + 1) * group; ++k) dot += (int64_t)A[m * K + k] * (int64_t)B[n * K + k];
+        double term = (double)sA[m * groups + g] * (double)sB[(n / b_rows_per_scale) * groups + g] * (double)dot;
+        sum += term;
+        sum_abs += fabs(term);
+      }
+      C[m * N + n] = sum;
+      if (C_abs) C_abs[m * N + n] = sum_abs;
+    }
+  }
+  return ORACLE_OK;
 }
 
 ORACLE_API int oracle_silu_dot_fwd_bwd_quant_fuse(const uint16_t* x, const uint16_t* grad_y, int8_t* grad_input_q,

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "siluquant_oracle.c")
 PINS = ["tests/test_oracle_pipeline.py", "tests/test_oracle_quant.py",
         "tests/test_oracle_elementwise.py", "tests/test_oracle_sigmoid.py", "tests/test_oracle_forward.py",
-        "tests/test_oracle_fp8.py"]
+        "tests/test_oracle_fp8.py", "tests/test_oracle_gemm.py"]
 
 MUTANTS = {
     "sigmoid_sign": ("exp(-(double)g)", "exp((double)g)"),
@@ -58,6 +58,12 @@ MUTANTS = {
     "fp8_row_groups_skip_up_half": ("    int64_t row_groups = (2 * H + group - 1) / group;\n    for (int64_t t = 0; t < T; ++t)\n",
                                     "    int64_t row_groups = (H + group - 1) / group;\n    for (int64_t t = 0; t < T; ++t)\n"),
     "fp8_zero_loses_sign": ("(x == 0.0f) ? oracle_f32_to_e4m3(x)", "(x == 0.0f) ? 0"),
+    "gemm_drops_a_scale": ("double term = (double)sA[m * groups + g] * (double)sB",
+                           "double term = (double)sB"),
+    "gemm_b_scale_group_zero": ("sB[(n / b_rows_per_scale) * groups + g]", "sB[(n / b_rows_per_scale) * groups + 0]"),
+    "gemm_b_scale_row_zero": ("sB[(n / b_rows_per_scale) * groups + g]", "sB[g]"),
+    "gemm_b_not_transposed": ("(int64_t)B[n * K + k]", "(int64_t)B[k * N + n]"),
+    "gemm_group_offset": ("for (int64_t k = g * group; k < (g + 1) * group; ++k)", "for (int64_t k = 0; k < group; ++k)"),
     "fp8_nan_beyond_range": ("if (a >= 448.0) return sign | 0x7E;", "if (a >= 464.0) return sign | 0x7F;"),
 }
 
