@@ -8,7 +8,8 @@ code tensors and both scale tensors) divided by the time per call.
 
 Prints one JSON line.  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--op backward|forward|fp8] [--no-cpu-baseline] [--probes]
+                    [--op backward|forward|fp8|gemm_dgrad|gemm_wgrad]
+                    [--no-cpu-baseline] [--probes]
 """
 
 from __future__ import annotations
@@ -105,6 +106,115 @@ def stream_probes(dev, reps: int = 20):
     return res
 
 
+# The two consumers of the pass's outputs at the largest workload (T = 16384,
+# H = 11008; D = 4096, the model width that goes with an 11008-wide SwiGLU):
+#   dgrad: dX[T, D] = grad_input_q[T, 2H] . Wt[D, 2H]^T, weight scales per 128 x 128 block;
+#   wgrad: dW[D, H] = go_q_t[D, T] . y_q_t[H, T]^T, a scale per row of y_q_t and token group.
+GEMMS = {
+    "gemm_dgrad": dict(M=16384, N=4096, K=22016, b_rows=128, out="bf16"),
+    "gemm_wgrad": dict(M=4096, N=11008, K=16384, b_rows=1, out="f32"),
+}
+PEAK_INT8_TOPS = 5000.0  # MI355X dense int8 matrix peak, published
+
+
+def gemm_cpu_baseline(A, sA, B, sB, b_rows, min_seconds: float = 10.0):
+    """The oracle, single-threaded, on a sample of output rows and columns
+    (full K), repeated until at least min_seconds; rate in TOP/s."""
+    import numpy as np
+
+    import oracle
+
+    oracle.build(force=False)
+    rows, cols = 32, 32
+    An, sAn = A[:rows].cpu().numpy(), sA[:rows].cpu().numpy()
+    Bn = B[:cols].cpu().numpy()
+    sBn = sB.cpu().numpy()[np.arange(cols) // b_rows]
+    K = An.shape[1]
+    calls, total = 0, 0.0
+    while calls == 0 or total < min_seconds:
+        t = time.perf_counter()
+        oracle.i8_gemm_group_scaled(An, sAn, Bn, sBn)
+        total += time.perf_counter() - t
+        calls += 1
+    return {
+        "value": round(calls * 2.0 * rows * cols * K / total / 1e12, 6),
+        "unit": "TOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d x %d outputs over the full K = %d, %d call(s), %.1f s single-threaded" % (
+            rows, cols, K, calls, total),
+    }
+
+
+def run_gemm(args):
+    import torch
+
+    import swiglu_backward_int8_amd as sq
+
+    g = GEMMS[args.op]
+    M, N, K, b_rows = g["M"], g["N"], g["K"], g["b_rows"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev).manual_seed(7)
+    A = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=gen)
+    B = torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev, generator=gen)
+    sA = torch.rand((M, K // 128), device=dev, generator=gen) * 1e-3
+    sB = torch.rand((-(-N // b_rows), K // 128), device=dev, generator=gen) * 1e-2
+    C = torch.empty((M, N), dtype=torch.bfloat16 if g["out"] == "bf16" else torch.float32, device=dev)
+
+    def step():
+        sq.i8_gemm_group_scaled(A, sA, B, sB, C, b_rows_per_scale=b_rows)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    ops = 2.0 * M * N * K
+    achieved = ops / per_launch_s / 1e12
+    value = ops * args.steps / wall / 1e12
+    out = {
+        "metric": "achieved int8 TOP/s (+% of MI355X dense int8 peak) for the group-scaled GEMM ("
+                  + args.op[5:] + ")",
+        "value": round(value, 2),
+        "unit": "TOP/s",
+        "pct_of_peak": round(100.0 * value / PEAK_INT8_TOPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "t16384_h11008_d4096_" + args.op[5:], "M": M, "N": N, "K": K,
+                   "b_rows_per_scale": b_rows, "out": g["out"]},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TOP/s",
+            "frac": round(achieved / PEAK_INT8_TOPS, 4),
+            "traffic": measured_traffic(args.op + ":t16384_h11008"),
+            "kernel": "i8_gemm_kernel",
+            "avg_launch_us": round(per_launch_s * 1e6, 3),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = gemm_cpu_baseline(A, sA, B, sB, b_rows)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,10 +222,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="t16384_h11008")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=["backward", "forward", "fp8"], default="backward",
+    ap.add_argument("--op", choices=["backward", "forward", "fp8"] + sorted(GEMMS), default="backward",
                     help="backward: the fused SwiGLU backward + two-axis int8 pass (the headline); "
                          "forward: SwiGLU forward + row-wise int8 quantisation; "
-                         "fp8: the backward pass with OCP FP8 E4M3 codes")
+                         "fp8: the backward pass with OCP FP8 E4M3 codes; "
+                         "gemm_dgrad / gemm_wgrad: the group-scaled int8 GEMMs that consume its outputs")
     ap.add_argument("--probes", action="store_true",
                     help="also time a plain 1 GiB copy and a 2-read/1-write bf16 add (reference streams)")
     args = ap.parse_args()
@@ -124,6 +235,9 @@ def main():
               "multi-GPU job shard by tokens with no exchange, so per-GPU throughput is the "
               "one-GPU figure)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+
+    if args.op in GEMMS:
+        return run_gemm(args)
 
     import torch
 

@@ -123,6 +123,34 @@ int silu_dot_fwd_bwd_quant_fuse_fp8(const void* x, const void* grad_y, void* gra
 int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q, float* y_s, void* y_bf16, int64_t T,
                    int64_t H, int64_t group, void* stream);
 
+/*
+ * i8_gemm_group_scaled -- the consumer of the two quantised layouts.
+ *
+ * The fusion bullet of the page "kernelgen-challenge-9-task3-silu-quant"
+ * names the K-group and M-group quantisations: groups of 128 along the
+ * contraction axis of the GEMM that reads each product.  This is that GEMM, on
+ * the matrix cores (v_mfma_i32_32x32x32_i8):
+ *   C[m, n] = sum_g sA[m, g] * sB[n / Bb, g] * sum_{k in group g} A[m, k] * B[n, k]
+ *   A  int8 [M, K] row-major (16-byte aligned), sA fp32 [M, K/128];
+ *   B  int8 [N, K] row-major (16-byte aligned), sB fp32 [ceil(N/Bb), K/128];
+ *   Bb = b_rows_per_scale: 1 (a scale per row of B and group, as y_s_t) or 128
+ *        (one per 128 x 128 block of B, a pre-quantised weight);
+ *   C  [M, N] row-major, fp32 (c_dtype SILUQUANT_GEMM_OUT_F32, 4-byte aligned)
+ *      or bf16 (SILUQUANT_GEMM_OUT_BF16, 2-byte aligned), fully overwritten.
+ * Uses: dgrad dX[T, D] = grad_input_q[T, 2H] . Wt[D, 2H]^T (sA = grad_input_s,
+ *   Wt the gate/up weight transposed and quantised in 128 x 128 blocks, Bb =
+ *   128); wgrad dW[D, H] = go_q_t[D, T] . y_q_t[H, T]^T (sB = y_s_t, Bb = 1).
+ * Arithmetic: each group's integer dot is exact (int32); the groups are
+ *   accumulated in ascending order as acc = fma(float(dot), sA * sB, acc) in
+ *   fp32; bf16 output rounds that once (nearest, ties to even).
+ * Sizes: any M, N >= 0 (M == 0 or N == 0 is a no-op), K >= 0 a multiple of 128
+ *   (K == 0 writes zeros), group must be 128.  Same ownership, asynchrony and
+ *   status conventions as above; C must not overlap an input.
+ */
+enum siluquant_gemm_out { SILUQUANT_GEMM_OUT_F32 = 0, SILUQUANT_GEMM_OUT_BF16 = 1 };
+int i8_gemm_group_scaled(const int8_t* A, const float* sA, const int8_t* B, const float* sB, void* C, int64_t M,
+                         int64_t N, int64_t K, int64_t group, int64_t b_rows_per_scale, int c_dtype, void* stream);
+
 /* Builds the sigmoid table on the current device now (otherwise the first
  * silu_dot_fwd_bwd_quant_fuse call on the device does it).  Blocks until the
  * table is in place.  Safe to call repeatedly and from several threads. */

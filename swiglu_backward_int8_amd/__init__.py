@@ -27,7 +27,7 @@ _ERRORS = {
     7: (RuntimeError, "LAUNCH_FAILED"),
 }
 
-EXPORTED = ("silu_dot_fwd_bwd_quant_fuse", "silu_dot_fwd_bwd_quant_fuse_fp8", "silu_fwd_quant", "siluquant_prepare", "siluquant_strerror",
+EXPORTED = ("silu_dot_fwd_bwd_quant_fuse", "silu_dot_fwd_bwd_quant_fuse_fp8", "silu_fwd_quant", "i8_gemm_group_scaled", "siluquant_prepare", "siluquant_strerror",
             "siluquant_algorithmic_bytes", "siluquant_eval_sigmoid", "siluquant_eval_intermediates")
 
 _lib = None
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L.siluquant_algorithmic_bytes.restype = i64
         L.silu_fwd_quant.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
         L.silu_fwd_quant.restype = ctypes.c_int
+        L.i8_gemm_group_scaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, vp]
+        L.i8_gemm_group_scaled.restype = ctypes.c_int
         L.siluquant_eval_sigmoid.argtypes = [vp, vp, i64, vp]
         L.siluquant_eval_sigmoid.restype = ctypes.c_int
         L.siluquant_eval_intermediates.argtypes = [vp, vp, vp, vp, i64, i64, vp]
@@ -177,6 +179,45 @@ def silu_fwd_quant(x, y_q, y_s, row_weight=None, y_bf16=None, group_size: int = 
                                         y_bf16.data_ptr() if y_bf16 is not None else None, T, H, group_size,
                                         torch.cuda.current_stream(dev).cuda_stream))
     _check(code, "silu_fwd_quant")
+
+
+GEMM_OUT_F32, GEMM_OUT_BF16 = 0, 1
+
+
+def i8_gemm_group_scaled(A, sA, B, sB, C, b_rows_per_scale: int = 1, group_size: int = GROUP):
+    """C = A . B^T of group-scaled int8 operands on the matrix cores:
+    C[m, n] = sum_g sA[m, g] * sB[n // b_rows_per_scale, g] * (A[m, g-th 128] . B[n, g-th 128]).
+    A int8 [M, K], sA fp32 [M, K/128], B int8 [N, K], sB fp32
+    [ceil(N / b_rows_per_scale), K/128] (b_rows_per_scale 1 or 128); C fp32 or
+    bf16 [M, N] is overwritten.  Enqueued on the current stream of A's device."""
+    import torch
+
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1]:
+        raise ValueError("A must be [M, K] and B [N, K]")
+    M, K = int(A.shape[0]), int(A.shape[1])
+    N = int(B.shape[0])
+    if group_size != GROUP or K % GROUP:
+        raise ValueError("K must be a multiple of 128 and group_size 128")
+    if b_rows_per_scale not in (1, 128):
+        raise ValueError("b_rows_per_scale must be 1 or 128")
+    dev = A.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU; got %s" % dev)
+    groups = K // GROUP
+    if C.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("C must be float32 or bfloat16")
+    checks = [("A", A, torch.int8, (M, K)), ("sA", sA, torch.float32, (M, groups)),
+              ("B", B, torch.int8, (N, K)), ("sB", sB, torch.float32, (-(-N // b_rows_per_scale), groups)),
+              ("C", C, C.dtype, (M, N))]
+    for name, t, dt, shape in checks:
+        if t.dtype != dt or t.device != dev or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+            raise ValueError("%s must be a contiguous %s tensor of shape %s on %s" % (name, dt, shape, dev))
+    out = GEMM_OUT_F32 if C.dtype == torch.float32 else GEMM_OUT_BF16
+    with torch.cuda.device(dev):
+        code = int(lib().i8_gemm_group_scaled(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(),
+                                              C.data_ptr(), M, N, K, group_size, b_rows_per_scale, out,
+                                              torch.cuda.current_stream(dev).cuda_stream))
+    _check(code, "i8_gemm_group_scaled")
 
 
 def forward_bytes(T: int, H: int, with_bf16: bool = False, with_weight: bool = False) -> int:

@@ -1,6 +1,7 @@
 """Build step for libsiluquant.so (in-tree, for gfx950).
 
-hipcc compiles the single HIP source into a shared library next to this file.
+hipcc compiles the HIP sources (the fused SwiGLU passes and the group-scaled
+int8 GEMM) into one shared library next to this file.
 Flags that matter for the numbers the library produces:
   -ffp-contract=off                  no fused multiply-add: the arithmetic order
                                      is the one written in the source;
@@ -16,7 +17,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "siluquant.hip")
+SRCS = [os.path.join(PKG, "csrc", "siluquant.hip"), os.path.join(PKG, "csrc", "i8gemm.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsiluquant.so")
 ARCH = "gfx950"
@@ -38,7 +39,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     """Compile libsiluquant.so for gfx950 and return its path."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I" + INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-I" + INCLUDE] + SRCS + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature and says so; harmless
     noise = "is not a recognized feature for this target"

@@ -158,3 +158,26 @@ def test_forward_rejects_bad_arguments(lib):
     assert f(BASE, BASE + 2**26 + 2, BASE + 2**24, BASE + 2**25, None, 8, 256, 128, None) == 4
     assert f(BASE, None, BASE + 1024, BASE + 2**25, None, 8, 256, 128, None) == 5
     assert f(None, None, None, None, None, 0, 256, 128, None) == 0
+
+
+def test_gemm_rejects_bad_arguments(lib):
+    f = lib.i8_gemm_group_scaled
+    A, sA, B, sB, C = BASE, BASE + 2**26, BASE + 2**27, BASE + 2**28, BASE + 2**29
+    ok = (A, sA, B, sB, C, 256, 256, 512, 128, 1, 0, None)
+
+    def call(**kw):
+        args = list(ok)
+        for k, v in kw.items():
+            args[["A", "sA", "B", "sB", "C", "M", "N", "K", "group", "bb", "out", "stream"].index(k)] = v
+        return f(*args)
+
+    assert call(group=64) == 3
+    assert call(K=200) == 2 and call(M=-1) == 2 and call(N=-5) == 2 and call(K=-128) == 2
+    assert call(bb=64) == 2 and call(out=2) == 2
+    assert call(A=None) == 1 and call(sB=None) == 1 and call(C=None) == 1
+    assert call(A=A + 8) == 4 and call(B=B + 4) == 4 and call(sA=sA + 2) == 4 and call(C=C + 2) == 4
+    assert call(C=C + 1, out=1) == 4
+    assert call(C=A + 64) == 5 and call(C=sB) == 5
+    # nothing to do: success without looking at any pointer
+    assert call(M=0, A=None, sA=None, B=None, sB=None, C=None) == 0
+    assert call(N=0, A=None, sA=None, B=None, sB=None, C=None) == 0
