@@ -23,9 +23,7 @@
 // wave owns 64 x 64 = 2 x 2 MFMA blocks of 32 x 32.  Per group the A and B
 // tiles (128 x 128 bytes each) and their 256 scales are staged in LDS, double
 // buffered: the global loads of group g + 1 are in flight while the matrix
-// cores work on group g.  LDS rows are 128 bytes of 16-byte chunks stored at a
-// position XOR-swizzled by the row, so that both the staging writes and the
-// MFMA operand reads (32 rows, one chunk each) hit distinct banks.  Tiles are
+// cores work on group g.  Tiles are
 // handed out in groups of 8 tile-rows, and each XCD takes a contiguous range
 // of that order, so that the workgroups resident on one XCD share A and B
 // tiles in its L2.
@@ -36,17 +34,30 @@
 
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kBK = 128;  // tile of C and the K step (one group)
-constexpr int kGemmThreads = 256;
-constexpr int kGroupM = 8;                    // tile-rows per raster group
-constexpr int kStageBytes = (kBM + kBN) * kBK;  // A and B tiles of one group
+constexpr int kBK = 128;                  // the K step: one group
+constexpr int kWavesM = 4, kWavesN = 2;   // wave grid of a workgroup
+constexpr int kBM = 64 * kWavesM, kBN = 64 * kWavesN;  // tile of C: 256 x 128
+constexpr int kGemmThreads = 64 * kWavesM * kWavesN;   // 512
+constexpr int kGroupM = 8;                // tile-rows per raster group
+constexpr int kStageBytes = (kBM + kBN) * kBK;         // A and B tiles of one group
+constexpr int kChunksPerThread = kStageBytes / 16 / kGemmThreads;  // 16-byte chunks staged per thread
+constexpr int kAChunks = kBM * kBK / 16;  // chunk ids below this are A's, the rest B's
+static_assert(kStageBytes % (16 * kGemmThreads) == 0, "whole chunks per thread");
+static_assert(kAChunks % kGemmThreads == 0, "a thread's chunks are all A or all B per step");
+static_assert(kBM + kBN <= kGemmThreads, "one scale per thread");
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Byte offset of logical 16-byte chunk c of row r inside a 128-byte-row tile.
-__device__ __forceinline__ int swz(int r, int c) { return r * kBK + 16 * (c ^ ((r ^ (r >> 3)) & 7)); }
+// LDS layout of a tile of `rows` rows of 128 bytes: four slabs, one per MFMA
+// k-step (32 bytes of K each), each holding the rows' 32-byte pieces; the two
+// 16-byte halves of a piece swap places on rows with bit 2 set, so that eight
+// consecutive rows reading the same half cover all banks once.  Byte offset of
+// logical 16-byte chunk c (0..7) of row r:
+template <int kRows>
+__device__ __forceinline__ int lds_at(int r, int c) {
+  return (c >> 1) * (kRows * 32) + r * 32 + 16 * ((c & 1) ^ ((r >> 2) & 1));
+}
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -54,8 +65,19 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-template <bool kBf16Out>
-__global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* __restrict__ A,
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One group's operands in flight: kChunksPerThread 16-byte chunks and one scale.
+struct Stage {
+  i32x4 v[kChunksPerThread];
+  float sc;
+};
+
+// kBlockScale: B's scale rows cover 128 rows (constant over a wave's 64 columns).
+template <bool kBf16Out, bool kBlockScale>
+__global__ __launch_bounds__(kGemmThreads, 1) void i8_gemm_kernel(const int8_t* __restrict__ A,
                                                                   const float* __restrict__ sA,
                                                                   const int8_t* __restrict__ B,
                                                                   const float* __restrict__ sB, void* __restrict__ C,
@@ -75,35 +97,45 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
   const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;  // the wave's 64 x 64 corner
+  const int wm = (wave / kWavesN) * 64, wn = (wave % kWavesN) * 64;  // the wave's 64 x 64 corner
   const int groups = (int)(K / kBK);
 
-  // Staging: 16-byte chunk ids tid + 256 i, i = 0..3, for each of A and B.
-  const int64_t a_rows_left = M - m0, b_rows_left = N - n0;
-  auto load_stage = [&](int g, u32x4 (&ra)[4], u32x4 (&rb)[4], float& sc) {
-    const int64_t k0 = (int64_t)g * kBK;
+  // Rows past M or N read as zeros: the buffer's record count ends at the last row.
+  const int a_rows = M - m0 < kBM ? (int)(M - m0) : kBM;
+  const int b_rows_here = N - n0 < kBN ? (int)(N - n0) : kBN;
+  const __amdgpu_buffer_rsrc_t ra = rsrc(A + m0 * K, (int64_t)a_rows * K);
+  const __amdgpu_buffer_rsrc_t rb = rsrc(B + n0 * K, (int64_t)b_rows_here * K);
+  // this thread's scale: A rows for tid < kBM, then B rows
+  const bool sc_is_a = tid < kBM;
+  const int sc_row = sc_is_a ? tid : tid - kBM;
+  const bool sc_live = tid < kBM + kBN && (sc_is_a ? sc_row < a_rows : sc_row < b_rows_here);
+  const float* sc_ptr = sc_is_a ? sA + (m0 + sc_row) * groups : sB + ((n0 + sc_row) / b_rows) * groups;
+
+  auto load_stage = [&](int g, Stage& st) {
+    const int k0 = g * kBK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + kGemmThreads * i, r = id >> 3, c = id & 7;
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      ra[i] = r < a_rows_left ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(A + (m0 + r) * K + k0 + 16 * c))
-                              : zero;
-      rb[i] = r < b_rows_left ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(B + (n0 + r) * K + k0 + 16 * c))
-                              : zero;
+    for (int i = 0; i < kChunksPerThread; ++i) {
+      const int id = tid + kGemmThreads * i;
+      if (i < kAChunks / kGemmThreads) {  // uniform: the first chunks of every thread are A's
+        const int r = id >> 3, c = id & 7;
+        st.v[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, r * (int)K + 16 * c, k0, 0));
+      } else {
+        const int idb = id - kAChunks, r = idb >> 3, c = idb & 7;
+        st.v[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, r * (int)K + 16 * c, k0, 0));
+      }
     }
-    if (tid < kBM)
-      sc = tid < a_rows_left ? sA[(m0 + tid) * groups + g] : 0.0f;
-    else
-      sc = tid - kBM < b_rows_left ? sB[((n0 + tid - kBM) / b_rows) * groups + g] : 0.0f;
+    st.sc = sc_live ? sc_ptr[g] : 0.0f;
   };
-  auto store_stage = [&](int buf, const u32x4 (&ra)[4], const u32x4 (&rb)[4], float sc) {
+  auto store_stage = [&](int buf, const Stage& st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + kGemmThreads * i, r = id >> 3, c = id & 7;
-      *reinterpret_cast<u32x4*>(&s_tile[buf][swz(r, c)]) = ra[i];
-      *reinterpret_cast<u32x4*>(&s_tile[buf][kBM * kBK + swz(r, c)]) = rb[i];
+    for (int i = 0; i < kChunksPerThread; ++i) {
+      const int id = tid + kGemmThreads * i;
+      if (i < kAChunks / kGemmThreads)
+        *reinterpret_cast<i32x4*>(&s_tile[buf][lds_at<kBM>(id >> 3, id & 7)]) = st.v[i];
+      else
+        *reinterpret_cast<i32x4*>(&s_tile[buf][kBM * kBK + lds_at<kBN>((id - kAChunks) >> 3, id & 7)]) = st.v[i];
     }
-    s_scale[buf][tid] = sc;
+    if (tid < kBM + kBN) s_scale[buf][tid] = st.sc;
   };
 
   float acc[2][2][16];
@@ -114,19 +146,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  u32x4 ra[4], rb[4];
-  float sc = 0.0f;
-  if (groups > 0) {
-    load_stage(0, ra, rb, sc);
-    store_stage(0, ra, rb, sc);
-  }
-  __syncthreads();
-
   const int lrow = lane & 31, lhalf = lane >> 5;
-  for (int g = 0; g < groups; ++g) {
-    const int buf = g & 1;
-    if (g + 1 < groups) load_stage(g + 1, ra, rb, sc);
-
+  // One group from LDS buffer buf: 4 k-steps of 2 x 2 MFMAs, then promotion.
+  auto compute = [&](int buf) {
     const char* ta = s_tile[buf];
     const char* tb = s_tile[buf] + kBM * kBK;
     i32x16 I[2][2];
@@ -139,9 +161,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
       const int c = 2 * s + lhalf;
       i32x4 fa[2], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const i32x4*>(ta + swz(wm + 32 * i + lrow, c));
+      for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const i32x4*>(ta + lds_at<kBM>(wm + 32 * i + lrow, c));
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const i32x4*>(tb + swz(wn + 32 * j + lrow, c));
+      for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const i32x4*>(tb + lds_at<kBN>(wn + 32 * j + lrow, c));
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -151,8 +173,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
     // 8 q + 4 lhalf + e (q = r / 4, e = r % 4) of each 32-row block, its
     // column lrow of each 32-column block
     float sb[2];
+    if constexpr (kBlockScale) {
+      sb[0] = sb[1] = s_scale[buf][kBM + wn];
+    } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) sb[j] = s_scale[buf][kBM + wn + 32 * j + lrow];
+      for (int j = 0; j < 2; ++j) sb[j] = s_scale[buf][kBM + wn + 32 * j + lrow];
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -160,17 +186,33 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
         const float4 sa = *reinterpret_cast<const float4*>(&s_scale[buf][wm + 32 * i + 8 * q + 4 * lhalf]);
         const float sav[4] = {sa.x, sa.y, sa.z, sa.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q + e;
+          if constexpr (kBlockScale) {
+            const float s = sav[e] * sb[0];
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int r = 4 * q + e;
-            acc[i][j][r] = __builtin_fmaf((float)I[i][j][r], sav[e] * sb[j], acc[i][j][r]);
+            for (int j = 0; j < 2; ++j) acc[i][j][r] = __builtin_fmaf((float)I[i][j][r], s, acc[i][j][r]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j][r] = __builtin_fmaf((float)I[i][j][r], sav[e] * sb[j], acc[i][j][r]);
           }
+        }
       }
     }
-    if (g + 1 < groups) {
-      store_stage(buf ^ 1, ra, rb, sc);
-    }
+  };
+
+  // The next group's operands are loaded into registers while this group is
+  // computed from LDS, then written to the other LDS buffer.
+  Stage st;
+  if (groups > 0) {
+    load_stage(0, st);
+    store_stage(0, st);
+  }
+  __syncthreads();
+  for (int g = 0; g < groups; ++g) {
+    if (g + 1 < groups) load_stage(g + 1, st);
+    compute(g & 1);
+    if (g + 1 < groups) store_stage((g + 1) & 1, st);
     __syncthreads();
   }
 
@@ -213,8 +255,9 @@ __attribute__((visibility("default"))) int i8_gemm_group_scaled(const int8_t* A,
     return SILUQUANT_ERR_BAD_SHAPE;
   if (M == 0 || N == 0) return SILUQUANT_OK;
   const int64_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
-  // int tile indices; 32-bit K per row is ample, but row offsets are int64
-  if (tiles_m * tiles_n > (int64_t(1) << 30) || K > (int64_t(1) << 30)) return SILUQUANT_ERR_BAD_SHAPE;
+  // int tile indices; a tile's rows of A or B (at most 256 x K bytes) must fit
+  // a buffer resource's 31-bit record count
+  if (tiles_m * tiles_n > (int64_t(1) << 30) || K > (int64_t(1) << 22)) return SILUQUANT_ERR_BAD_SHAPE;
   if (!C || (K > 0 && (!A || !sA || !B || !sB))) return SILUQUANT_ERR_NULL_PTR;
   auto mis = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
   if (mis(A, 16) || mis(B, 16) || mis(sA, 4) || mis(sB, 4) || mis(C, c_dtype == SILUQUANT_GEMM_OUT_F32 ? 4 : 2))
@@ -230,12 +273,11 @@ __attribute__((visibility("default"))) int i8_gemm_group_scaled(const int8_t* A,
   const int per_xcd = (tiles + 7) / 8;
   const dim3 grid(8 * per_xcd), block(kGemmThreads);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (c_dtype == SILUQUANT_GEMM_OUT_BF16)
-    hipLaunchKernelGGL(i8_gemm_kernel<true>, grid, block, 0, s, A, sA, B, sB, C, M, N, K, (int)b_rows_per_scale,
-                       (int)tiles_m, (int)tiles_n, per_xcd);
-  else
-    hipLaunchKernelGGL(i8_gemm_kernel<false>, grid, block, 0, s, A, sA, B, sB, C, M, N, K, (int)b_rows_per_scale,
-                       (int)tiles_m, (int)tiles_n, per_xcd);
+  const bool bf16 = c_dtype == SILUQUANT_GEMM_OUT_BF16, blk = b_rows_per_scale == kBN;
+  auto kernel = bf16 ? (blk ? i8_gemm_kernel<true, true> : i8_gemm_kernel<true, false>)
+                     : (blk ? i8_gemm_kernel<false, true> : i8_gemm_kernel<false, false>);
+  hipLaunchKernelGGL(kernel, grid, block, 0, s, A, sA, B, sB, C, M, N, K, (int)b_rows_per_scale, (int)tiles_m,
+                     (int)tiles_n, per_xcd);
   if (hipGetLastError() != hipSuccess) return SILUQUANT_ERR_LAUNCH_FAILED;
   return SILUQUANT_OK;
 }
