@@ -19,14 +19,14 @@
 // by group in ascending order.  The result is C in fp32 or rounded once to
 // bf16 (nearest, ties to even).
 //
-// Kernel: 256 threads (4 waves in a 2 x 2 grid) per 128 x 128 tile of C; each
-// wave owns 64 x 64 = 2 x 2 MFMA blocks of 32 x 32.  Per group the A and B
-// tiles (128 x 128 bytes each) and their 256 scales are staged in LDS, double
-// buffered: the global loads of group g + 1 are in flight while the matrix
-// cores work on group g.  Tiles are
-// handed out in groups of 8 tile-rows, and each XCD takes a contiguous range
-// of that order, so that the workgroups resident on one XCD share A and B
-// tiles in its L2.
+// Kernel: 256 threads (4 waves in a 2 x 2 grid) per 128 x 128 tile of C, and
+// two workgroups per CU, so that one's loads and promotion overlap the other's
+// MFMAs.  Each wave owns 64 x 64 = 2 x 2 MFMA blocks of 32 x 32.  Per group,
+// the A and B tiles (128 x 128 bytes each) and their scales are staged in LDS,
+// double buffered: the next group is loaded into registers while the matrix
+// cores work on this one.  Tiles are handed out in groups of 8 tile-rows, and
+// each XCD takes a contiguous range of that order, so that the workgroups
+// resident on one XCD share A and B tiles in its L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,9 +35,9 @@
 namespace {
 
 constexpr int kBK = 128;                  // the K step: one group
-constexpr int kWavesM = 4, kWavesN = 2;   // wave grid of a workgroup
-constexpr int kBM = 64 * kWavesM, kBN = 64 * kWavesN;  // tile of C: 256 x 128
-constexpr int kGemmThreads = 64 * kWavesM * kWavesN;   // 512
+constexpr int kWavesM = 2, kWavesN = 2;   // wave grid of a workgroup
+constexpr int kBM = 64 * kWavesM, kBN = 64 * kWavesN;  // tile of C: 128 x 128
+constexpr int kGemmThreads = 64 * kWavesM * kWavesN;   // 256
 constexpr int kGroupM = 8;                // tile-rows per raster group
 constexpr int kStageBytes = (kBM + kBN) * kBK;         // A and B tiles of one group
 constexpr int kChunksPerThread = kStageBytes / 16 / kGemmThreads;  // 16-byte chunks staged per thread
@@ -49,15 +49,12 @@ static_assert(kBM + kBN <= kGemmThreads, "one scale per thread");
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
-// LDS layout of a tile of `rows` rows of 128 bytes: four slabs, one per MFMA
-// k-step (32 bytes of K each), each holding the rows' 32-byte pieces; the two
-// 16-byte halves of a piece swap places on rows with bit 2 set, so that eight
-// consecutive rows reading the same half cover all banks once.  Byte offset of
-// logical 16-byte chunk c (0..7) of row r:
-template <int kRows>
-__device__ __forceinline__ int lds_at(int r, int c) {
-  return (c >> 1) * (kRows * 32) + r * 32 + 16 * ((c & 1) ^ ((r >> 2) & 1));
-}
+// LDS layout of a tile: rows of 128 bytes, whose eight 16-byte chunks are
+// stored at positions XOR-permuted by the row.  Staging writes (eight lanes
+// per row, one chunk each) and MFMA operand reads (32 consecutive rows, one
+// chunk each) then both fall on distinct banks, for 32 or 64 banks.  Byte
+// offset of logical chunk c (0..7) of row r:
+__device__ __forceinline__ int lds_at(int r, int c) { return r * kBK + 16 * (c ^ ((r ^ (r >> 3)) & 7)); }
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -72,12 +69,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
 // One group's operands in flight: kChunksPerThread 16-byte chunks and one scale.
 struct Stage {
   i32x4 v[kChunksPerThread];
-  float sc;
+  float sc, sb;
 };
 
 // kBlockScale: B's scale rows cover 128 rows (constant over a wave's 64 columns).
 template <bool kBf16Out, bool kBlockScale>
-__global__ __launch_bounds__(kGemmThreads, 1) void i8_gemm_kernel(const int8_t* __restrict__ A,
+__global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* __restrict__ A,
                                                                   const float* __restrict__ sA,
                                                                   const int8_t* __restrict__ B,
                                                                   const float* __restrict__ sB, void* __restrict__ C,
@@ -110,32 +107,39 @@ __global__ __launch_bounds__(kGemmThreads, 1) void i8_gemm_kernel(const int8_t* 
   const int sc_row = sc_is_a ? tid : tid - kBM;
   const bool sc_live = tid < kBM + kBN && (sc_is_a ? sc_row < a_rows : sc_row < b_rows_here);
   const float* sc_ptr = sc_is_a ? sA + (m0 + sc_row) * groups : sB + ((n0 + sc_row) / b_rows) * groups;
+  // with block scales one B scale covers the whole tile (n0 is a multiple of
+  // 128): it is folded into the A scales when they are staged
+  const float* sb_blk = sB + (n0 / kBN) * groups;
 
+  // Chunk i of this thread is row (tid >> 3) + d of A or of B (d a multiple
+  // of 32), 16-byte chunk tid & 7: one byte offset per thread, the row step in
+  // the scalar offset.  In LDS, row r + d (r < 32 or d a multiple of 64) has
+  // the swizzle of row r XOR (d / 8) mod 8, so the store offsets are the
+  // thread's offset XOR a constant plus a constant.
+  constexpr int kAPer = kAChunks / kGemmThreads;  // A chunks per thread
+  const int g_off = (tid >> 3) * (int)K + 16 * (tid & 7);
+  const int l_off = lds_at(tid >> 3, tid & 7);
   auto load_stage = [&](int g, Stage& st) {
     const int k0 = g * kBK;
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
-      const int id = tid + kGemmThreads * i;
-      if (i < kAChunks / kGemmThreads) {  // uniform: the first chunks of every thread are A's
-        const int r = id >> 3, c = id & 7;
-        st.v[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, r * (int)K + 16 * c, k0, 0));
-      } else {
-        const int idb = id - kAChunks, r = idb >> 3, c = idb & 7;
-        st.v[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, r * (int)K + 16 * c, k0, 0));
-      }
+      const int row_step = (i < kAPer ? i : i - kAPer) * (kGemmThreads / 8);
+      st.v[i] = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(i < kAPer ? ra : rb, g_off, k0 + row_step * (int)K, 0));
     }
     st.sc = sc_live ? sc_ptr[g] : 0.0f;
+    if constexpr (kBlockScale) st.sb = sb_blk[g];
   };
   auto store_stage = [&](int buf, const Stage& st) {
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
-      const int id = tid + kGemmThreads * i;
-      if (i < kAChunks / kGemmThreads)
-        *reinterpret_cast<i32x4*>(&s_tile[buf][lds_at<kBM>(id >> 3, id & 7)]) = st.v[i];
-      else
-        *reinterpret_cast<i32x4*>(&s_tile[buf][kBM * kBK + lds_at<kBN>((id - kAChunks) >> 3, id & 7)]) = st.v[i];
+      const int row_step = (i < kAPer ? i : i - kAPer) * (kGemmThreads / 8);
+      *reinterpret_cast<i32x4*>(&s_tile[buf][(i < kAPer ? 0 : kBM * kBK) + row_step * kBK +
+                                            (l_off ^ (16 * ((row_step >> 3) & 7)))]) = st.v[i];
     }
-    if (tid < kBM + kBN) s_scale[buf][tid] = st.sc;
+    float sc = st.sc;
+    if constexpr (kBlockScale) sc = sc_is_a ? sc * st.sb : 0.0f;
+    if (tid < kBM + kBN) s_scale[buf][tid] = sc;
   };
 
   float acc[2][2][16];
@@ -147,35 +151,38 @@ __global__ __launch_bounds__(kGemmThreads, 1) void i8_gemm_kernel(const int8_t* 
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int lrow = lane & 31, lhalf = lane >> 5;
-  // One group from LDS buffer buf: 4 k-steps of 2 x 2 MFMAs, then promotion.
+  // This lane's operand rows are wm + 32 i + lrow (A) and wn + 32 j + lrow
+  // (B); k-step s reads logical chunk 2 s + lhalf.  Since wm and wn are
+  // multiples of 64 and lrow < 32, the swizzled chunk position of block i is
+  // that of block 0 with bit 2 flipped, and k-step s flips bits 1-2 by s: the
+  // offset of (i, s) is the (0, 0) offset XOR 32 s XOR 64 i, plus 4096 i.
+  const int a_base = lds_at(wm + lrow, lhalf);
+  const int b_base = kBM * kBK + lds_at(wn + lrow, lhalf);
+  auto off = [](int base, int blk, int s) { return (base ^ (32 * s) ^ (64 * blk)) + 32 * kBK * blk; };
+
+  // One group from LDS buffer buf: 4 k-steps of 2 x 2 MFMAs into exact int32
+  // sums, then acc += float(I) * (sA[m] * sB[n]).  The lane's rows are
+  // 8 q + 4 lhalf + e (q = r / 4, e = r % 4) of each 32-row block, its column
+  // lrow of each 32-column block.  With block scales the staged A scale
+  // already holds the product.
   auto compute = [&](int buf) {
-    const char* ta = s_tile[buf];
-    const char* tb = s_tile[buf] + kBM * kBK;
+    const char* t = s_tile[buf];
     i32x16 I[2][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) I[i][j] = (i32x16){};
-#pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int c = 2 * s + lhalf;
       i32x4 fa[2], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const i32x4*>(ta + lds_at<kBM>(wm + 32 * i + lrow, c));
+      for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const i32x4*>(t + off(a_base, i, s));
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const i32x4*>(tb + lds_at<kBN>(wn + 32 * j + lrow, c));
+      for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const i32x4*>(t + off(b_base, j, s));
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) I[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], I[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j)
+          I[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], s == 0 ? (i32x16){} : I[i][j], 0, 0, 0);
     }
-    // promotion: acc += float(I) * (sA[m] * sB[n]); the lane's rows are
-    // 8 q + 4 lhalf + e (q = r / 4, e = r % 4) of each 32-row block, its
-    // column lrow of each 32-column block
     float sb[2];
-    if constexpr (kBlockScale) {
-      sb[0] = sb[1] = s_scale[buf][kBM + wn];
-    } else {
+    if constexpr (!kBlockScale) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) sb[j] = s_scale[buf][kBM + wn + 32 * j + lrow];
     }
@@ -188,13 +195,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void i8_gemm_kernel(const int8_t* 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * q + e;
-          if constexpr (kBlockScale) {
-            const float s = sav[e] * sb[0];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j][r] = __builtin_fmaf((float)I[i][j][r], s, acc[i][j][r]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j][r] = __builtin_fmaf((float)I[i][j][r], sav[e] * sb[j], acc[i][j][r]);
+          for (int j = 0; j < 2; ++j) {
+            const float sc = kBlockScale ? sav[e] : sav[e] * sb[j];
+            acc[i][j][r] = __builtin_fmaf((float)I[i][j][r], sc, acc[i][j][r]);
           }
         }
       }
@@ -209,12 +213,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void i8_gemm_kernel(const int8_t* 
     store_stage(0, st);
   }
   __syncthreads();
-  for (int g = 0; g < groups; ++g) {
+  // The fence keeps the LDS writes (which wait for the loads) after the whole
+  // group's compute, so that the loads have that long to arrive.
+  auto group_step = [&](int g, int buf) {
     if (g + 1 < groups) load_stage(g + 1, st);
-    compute(g & 1);
-    if (g + 1 < groups) store_stage((g + 1) & 1, st);
+    compute(buf);
+    __builtin_amdgcn_sched_barrier(0);
+    if (g + 1 < groups) store_stage(buf ^ 1, st);
     __syncthreads();
-  }
+  };
+  for (int g = 0; g < groups; ++g) group_step(g, g & 1);
 
   // epilogue: row m0 + wm + 32 i + 8 q + 4 lhalf + e, column n0 + wn + 32 j + lrow
 #pragma unroll
