@@ -27,8 +27,8 @@ extern "C" {
 enum siluquant_status {
   SILUQUANT_OK = 0,
   SILUQUANT_ERR_NULL_PTR = 1,      /* a buffer pointer is NULL while T*H > 0 */
-  SILUQUANT_ERR_BAD_SHAPE = 2,     /* T < 0, H < 0, H not a multiple of 128 (where required), or too large */
-  SILUQUANT_ERR_BAD_GROUP = 3,     /* group != 128 */
+  SILUQUANT_ERR_BAD_SHAPE = 2,     /* T < 0, H < 0, H not a multiple of the group, or too large */
+  SILUQUANT_ERR_BAD_GROUP = 3,     /* a group size the entry point does not take */
   SILUQUANT_ERR_MISALIGNED = 4,    /* x, grad_y, grad_input_q, y_q_t not 16-byte aligned,
                                       or a scale buffer not 4-byte aligned */
   SILUQUANT_ERR_OVERLAP = 5,       /* two buffers share bytes */
@@ -61,10 +61,13 @@ enum siluquant_status {
  * and the fp32 inverse (one rounding, ties to even), with q = 0 for v == 0.
  *   -128 is never produced.  Inputs must be finite and keep y, d_gate and d_up
  *   finite.
- * Sizes: any T >= 0, H >= 0 a multiple of 128 (T == 0 or H == 0 is a no-op that
- *   returns SILUQUANT_OK), T <= 2^23, H <= 2^22; group must be 128.  y_q_t is
- *   written with 16-byte stores when T % 16 == 0; other T work, with narrower
- *   stores.
+ * Group size: `group` is 128 (the page's default), 64 or 32; the scale tensors
+ *   are then grad_input_s fp32 [T, 2H/group] and y_s_t fp32 [H, ceil(T/group)].
+ *   Groups of 2H-row channels never straddle d_gate and d_up because H must be
+ *   a multiple of `group`.  Any other group returns SILUQUANT_ERR_BAD_GROUP.
+ * Sizes: any T >= 0, H >= 0 a multiple of `group` (T == 0 or H == 0 is a
+ *   no-op that returns SILUQUANT_OK), T <= 2^23, H <= 2^22.  y_q_t is written
+ *   with 16-byte stores when T % 16 == 0; other T work, with narrower stores.
  * Ownership: the caller allocates and owns every buffer; the library keeps no
  *   pointer after the call returns.  Buffers must not overlap.
  * Asynchrony: the work is enqueued on `stream` and the call returns without
@@ -160,8 +163,9 @@ int siluquant_prepare(void);
 const char* siluquant_strerror(int status);
 
 /* Bytes the pass must move per call: reads 6*T*H (x, grad_y), writes 3*T*H
- * int8 codes plus 4*(T*2H/128 + H*T/128) bytes of scales.  Host-only
- * arithmetic; returns -1 for negative sizes or a group other than 128. */
+ * int8 codes plus 4*(T*ceil(2H/group) + H*ceil(T/group)) bytes of scales.
+ * Host-only arithmetic; returns -1 for negative sizes or a group other than
+ * 32, 64 or 128. */
 int64_t siluquant_algorithmic_bytes(int64_t T, int64_t H, int64_t group);
 
 /* Diagnostics.  They run the fused kernel's own device helpers on their own so

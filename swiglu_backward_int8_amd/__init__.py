@@ -15,6 +15,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsiluquant.so")
 GROUP = 128
+GROUPS = (32, 64, 128)  # group sizes of the backward pass (they divide its 128 x 128 tiles)
 
 SILUQUANT_OK = 0
 _ERRORS = {
@@ -100,9 +101,10 @@ def raw_call(x_ptr: int, grad_y_ptr: int, gq_ptr: int, gs_ptr: int, yq_ptr: int,
 
 def silu_dot_fwd_bwd_quant_fuse(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size: int = GROUP):
     """Recompute y = silu(gate) * up from x = [gate | up] and write the int8 codes
-    and fp32 scales of [d_gate, d_up] (per row, 128-channel groups) and of y^T
-    (128-token groups) into the given output tensors.  Enqueued on the current
-    stream of x's device; returns None."""
+    and fp32 scales of [d_gate, d_up] (per row, groups of group_size channels)
+    and of y^T (groups of group_size tokens) into the given output tensors.
+    group_size is 128 (the default), 64 or 32, and H must be a multiple of it.
+    Enqueued on the current stream of x's device; returns None."""
     _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size, fp8=False)
 
 
@@ -119,9 +121,9 @@ def _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size: i
     T, H = int(grad_y.shape[0]) if grad_y.dim() == 2 else -1, int(grad_y.shape[-1])
     if x.dim() != 2 or grad_y.dim() != 2 or tuple(x.shape) != (T, 2 * H):
         raise ValueError("x must be [T, 2H] and grad_y [T, H]; got %s and %s" % (tuple(x.shape), tuple(grad_y.shape)))
-    if group_size != GROUP:
-        raise ValueError("group_size must be 128")
-    want = output_shapes(T, H, group_size) if H % GROUP == 0 else None
+    if group_size not in GROUPS:
+        raise ValueError("group_size must be one of %s" % (GROUPS,))
+    want = output_shapes(T, H, group_size) if H % group_size == 0 else None
     checks = [
         ("x", x, torch.bfloat16, (T, 2 * H)),
         ("grad_y", grad_y, torch.bfloat16, (T, H)),

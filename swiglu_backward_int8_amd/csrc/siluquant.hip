@@ -68,7 +68,8 @@ __device__ float g_sigma_tab[kSigEntries];
 constexpr int kRowPartStride = 2 * kTile + 4;  // 260: a wave's writes spread over the banks
 constexpr int kRowPartFloats = 16 * kRowPartStride;
 constexpr int kColPartFloats = kQ * kTile;
-constexpr int kInvFloats = 3 * kTile;  // 256 row groups + 128 column groups
+constexpr int kMinGroup = 32;          // group sizes 32, 64 and 128 divide the tile
+constexpr int kInvFloats = 3 * kTile * (kTile / kMinGroup);  // row and column inverses of the smallest groups
 constexpr int kYqtBytes = kTile * kTile;
 static_assert(kYqtBytes <= kRowPartFloats * 4, "transpose buffer reuses the row partials");
 constexpr int kLdsFloats = kSigEntries + kRowPartFloats + kColPartFloats + kInvFloats + 4;
@@ -246,15 +247,17 @@ struct TileIn {
 
 // The tile base is uniform (scalar registers) and the lane's byte offset is a
 // fixed 32-bit value.  In the last token block of a ragged T only `rows` of
-// the 128 rows exist; the lane's missing rows read as zeros, whose y, d_gate
-// and d_up are zero and so never raise a column maximum.
+// the 128 rows exist, and in the last channel block of an H that is not a
+// multiple of 128 only `cols` channels (lane_live: 8 p < cols); the missing
+// values read as zeros, whose y, d_gate and d_up are zero and so never raise
+// a maximum.
 __device__ __forceinline__ void load_tile(TileIn& in, const char* xt, const char* dyt, uint32_t lane_x,
                                           uint32_t lane_dy, int64_t x_row_bytes, int64_t dy_row_bytes, int rows,
-                                          int q) {
+                                          bool lane_live, int q) {
   const bool full = rows == kTile;
 #pragma unroll
   for (int i = 0; i < kRows; ++i) {
-    if (full || kRows * q + i < rows) {
+    if (lane_live && (full || kRows * q + i < rows)) {
       in.g[i] = load_stream(xt + i * x_row_bytes + lane_x);
       in.u[i] = load_stream(xt + i * x_row_bytes + (x_row_bytes >> 1) + lane_x);
       in.d[i] = load_stream(dyt + i * dy_row_bytes + lane_dy);
@@ -267,16 +270,18 @@ __device__ __forceinline__ void load_tile(TileIn& in, const char* xt, const char
 struct Tile {
   int tb, hb;
   int rows;  // tokens of this tile that exist: 128 except in the last block of a ragged T
+  int cols;  // channels that exist: 128 except in the last block of a ragged H
   int64_t t0, h0;
 };
 
-__device__ __forceinline__ Tile tile_at(int tile, int tiles_h, int64_t T) {
+__device__ __forceinline__ Tile tile_at(int tile, int tiles_h, int64_t T, int64_t H) {
   Tile c;
   c.tb = tile / tiles_h;
   c.hb = tile - c.tb * tiles_h;
   c.t0 = (int64_t)c.tb * kTile;
   c.h0 = (int64_t)c.hb * kTile;
-  c.rows = (int)min<int64_t>(kTile, T - c.t0);
+  c.rows = T - c.t0 < kTile ? (int)(T - c.t0) : kTile;
+  c.cols = H - c.h0 < kTile ? (int)(H - c.h0) : kTile;
   return c;
 }
 
@@ -384,6 +389,7 @@ __device__ __forceinline__ void quantise_rows_and_y(const uint32_t (&Gp)[kRows][
   const bool odd = p & 1;
 #pragma unroll
   for (int i = 0; i < kRows; i += 2) {
+    // lane_gq is past the buffer's records for channels past H: those stores drop
     const uint32_t row = i * gq_row_bytes + lane_gq;
     store_stream(gq_buf, row,
                  pair_rows16(codes8<kSafe, F>(Gp[i], idg[i]), codes8<kSafe, F>(Gp[i + 1], idg[i + 1]), odd));
@@ -411,11 +417,22 @@ __device__ __forceinline__ void quantise_rows_and_y(const uint32_t (&Gp)[kRows][
 // tiles, whose scale writes share cache lines, then meet in the same L2.
 // One workgroup per CU; the next tile's inputs are requested at the top of each
 // iteration and stay in flight while the current tile is processed.
-template <Fmt F>
+template <Fmt F, int kG>
 __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void silu_quant_bwd_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ grad_y, int8_t* __restrict__ grad_input_q,
     float* __restrict__ grad_input_s, int8_t* __restrict__ y_q_t, float* __restrict__ y_s_t, int64_t T, int64_t H,
     int tiles_h, int tiles) {
+  // kG-wide groups: kSub of them per 128 channels of a row and per 128 tokens
+  // of a channel.  Row group (half, sub, row) and column group (sub, channel)
+  // keep their inverses at s_inv[(half * kSub + sub) * 128 + row] and
+  // s_inv[kRowGroups + sub * 128 + channel].
+  static_assert(kG == 32 || kG == 64 || kG == 128, "group sizes that divide the tile");
+  constexpr int kSub = kTile / kG;
+  constexpr int kRowGroups = 2 * kTile * kSub, kColGroups = kTile * kSub;
+  constexpr int kLanesPerRowGroup = kG / 8;   // lanes p of 8 channels each
+  constexpr int kPairsPerColGroup = kG / kRows;  // lane groups q of kRows tokens each
+  static_assert(kRowGroups + kColGroups <= kInvFloats, "inverse slots");
+
   __shared__ __align__(16) float lds[kLdsFloats];
   float* s_tab = lds;
   float* s_rowpart = lds + kSigEntries;
@@ -430,11 +447,12 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
 
   // Row pitches in bytes and the lane's fixed byte offsets inside a tile.
   const int64_t x_row_bytes = 4 * H, dy_row_bytes = 2 * H, gq_row_bytes = 2 * H;
-  const int64_t row_groups = 2 * H / kGroup, col_groups = (T + kGroup - 1) / kGroup;
+  const int64_t row_groups = 2 * H / kG, col_groups = (T + kG - 1) / kG;
   const int yq_align = (T & 15) == 0 ? 16 : (T & 3) == 0 ? 4 : 1;
   const uint32_t lane_x = (uint32_t)(kRows * q * x_row_bytes + 16 * p);
   const uint32_t lane_dy = (uint32_t)(kRows * q * dy_row_bytes + 16 * p);
   const uint32_t lane_gq = (uint32_t)((kRows * q + (p & 1)) * gq_row_bytes + 8 * (p & ~1));
+  constexpr uint32_t kDropped = 0x80000000u;  // past any record count: the store is dropped
   constexpr int kOutSteps = kTile * kTile / 16 / kThreads;  // 16-byte pieces of y_q_t per thread
   uint32_t lane_yq[kOutSteps];
 #pragma unroll
@@ -442,6 +460,8 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
     const int id = tid + step * kThreads;
     lane_yq[step] = (uint32_t)((id >> 3) * T + 16 * (id & 7));
   }
+  // this lane's row and column groups: channels 8p.. and tokens kRows q..
+  const int sub_row = p / kLanesPerRowGroup, sub_col = q / kPairsPerColGroup;
 
   int tile, end, stride;
   if ((gridDim.x & 7) == 0) {
@@ -459,10 +479,10 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
   const char* xb = reinterpret_cast<const char*>(x);
   const char* dyb = reinterpret_cast<const char*>(grad_y);
   TileIn in, in_next;
-  Tile cur = tile_at(tile < end ? tile : 0, tiles_h, T);
+  Tile cur = tile_at(tile < end ? tile : 0, tiles_h, T, H);
   if (tile < end)
     load_tile(in, xb + (cur.t0 * x_row_bytes + 2 * cur.h0), dyb + (cur.t0 * dy_row_bytes + 2 * cur.h0), lane_x,
-              lane_dy, x_row_bytes, dy_row_bytes, cur.rows, q);
+              lane_dy, x_row_bytes, dy_row_bytes, cur.rows, 8 * p < cur.cols, q);
   {
     const float4* src = reinterpret_cast<const float4*>(g_sigma_tab);
     float4* dst = reinterpret_cast<float4*>(s_tab);
@@ -473,10 +493,10 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
   while (tile < end) {
     // ---- the next tile's inputs stay in flight through this whole iteration --
     const int next = tile + stride;
-    const Tile nxt = tile_at(next < end ? next : tile, tiles_h, T);
+    const Tile nxt = tile_at(next < end ? next : tile, tiles_h, T, H);
     if (next < end)
       load_tile(in_next, xb + (nxt.t0 * x_row_bytes + 2 * nxt.h0), dyb + (nxt.t0 * dy_row_bytes + 2 * nxt.h0),
-                lane_x, lane_dy, x_row_bytes, dy_row_bytes, nxt.rows, q);
+                lane_x, lane_dy, x_row_bytes, dy_row_bytes, nxt.rows, 8 * p < nxt.cols, q);
 
     // ---- elementwise: packed bf16 results and partial maxima -------------
     uint32_t Yp[kRows][4], Gp[kRows][4], Up[kRows][4];  // y, d_gate, d_up
@@ -500,28 +520,36 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
     __syncthreads();
 
     // ---- one thread per group: maximum, scale, inverse ---------------------
-    if (tid < 2 * kTile) {
-      const int g = tid;  // g < 128: d_gate of row g; else d_up of row g - 128
-      float m = 0.0f;
+    for (int id = tid; id < kRowGroups + kColGroups; id += kThreads) {
+      if (id < kRowGroups) {
+        const int row = id & (kTile - 1), hs = id >> 7, half = hs / kSub, sub = hs % kSub;
+        const int g = half * kTile + row;  // the row-partial column of this half and row
+        float m = 0.0f;
 #pragma unroll
-      for (int pp = 0; pp < 16; ++pp) m = fmaxf(m, s_rowpart[pp * kRowPartStride + g]);
-      const float scale = group_scale<F>(m);
-      const float inv = 1.0f / scale;
-      s_inv[g] = inv;
-      if (inv == __builtin_huge_valf()) s_flag[0] = 1;
-      const uint32_t off = (uint32_t)((g & (kTile - 1)) * row_groups + (g >> 7) * (H / kGroup));
-      if ((g & (kTile - 1)) < cur.rows) grad_input_s[cur.t0 * row_groups + cur.hb + off] = scale;
-    } else if (tid < 3 * kTile) {
-      const int c = tid - 2 * kTile;  // channel within the tile
-      const int idx = ((c >> 2) & 1) * 64 + (c >> 3) * 4 + (c & 3);
-      float m = 0.0f;
+        for (int pp = 0; pp < kLanesPerRowGroup; ++pp)
+          m = fmaxf(m, s_rowpart[(sub * kLanesPerRowGroup + pp) * kRowPartStride + g]);
+        const float scale = group_scale<F>(m);
+        const float inv = 1.0f / scale;
+        s_inv[id] = inv;
+        if (inv == __builtin_huge_valf()) s_flag[0] = 1;
+        // groups of channels past H (ragged H) do not exist
+        if (row < cur.rows && sub * kG < cur.cols)
+          grad_input_s[(cur.t0 + row) * row_groups + (half * H + cur.h0) / kG + sub] = scale;
+      } else {
+        const int cid = id - kRowGroups, c = cid & (kTile - 1), sub = cid >> 7;  // channel within the tile
+        const int idx = ((c >> 2) & 1) * 64 + (c >> 3) * 4 + (c & 3);
+        float m = 0.0f;
 #pragma unroll 8
-      for (int qq = 0; qq < kQ; ++qq) m = fmaxf(m, s_colpart[qq * kTile + idx]);
-      const float scale = group_scale<F>(m);
-      const float inv = 1.0f / scale;
-      s_inv[2 * kTile + c] = inv;
-      if (inv == __builtin_huge_valf()) s_flag[0] = 1;
-      y_s_t[cur.h0 * col_groups + cur.tb + (uint32_t)(c * col_groups)] = scale;
+        for (int qq = 0; qq < kPairsPerColGroup; ++qq)
+          m = fmaxf(m, s_colpart[(sub * kPairsPerColGroup + qq) * kTile + idx]);
+        const float scale = group_scale<F>(m);
+        const float inv = 1.0f / scale;
+        s_inv[id] = inv;
+        if (inv == __builtin_huge_valf()) s_flag[0] = 1;
+        // token groups past T (ragged T) and channels past H do not exist
+        if (c < cur.cols && sub * kG < cur.rows)
+          y_s_t[(cur.h0 + c) * col_groups + cur.t0 / kG + sub] = scale;
+      }
     }
     __syncthreads();
 
@@ -530,19 +558,22 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
       float idg[kRows], idu[kRows], iy[8];
 #pragma unroll
       for (int i = 0; i < kRows; ++i) {
-        idg[i] = s_inv[kRows * q + i];
-        idu[i] = s_inv[kTile + kRows * q + i];
+        idg[i] = s_inv[sub_row * kTile + kRows * q + i];
+        idu[i] = s_inv[(kSub + sub_row) * kTile + kRows * q + i];
       }
-      const float4 inv_y0 = *reinterpret_cast<const float4*>(s_inv + 2 * kTile + 8 * p);
-      const float4 inv_y1 = *reinterpret_cast<const float4*>(s_inv + 2 * kTile + 8 * p + 4);
+      const float* inv_col = s_inv + kRowGroups + sub_col * kTile + 8 * p;
+      const float4 inv_y0 = *reinterpret_cast<const float4*>(inv_col);
+      const float4 inv_y1 = *reinterpret_cast<const float4*>(inv_col + 4);
       iy[0] = inv_y0.x, iy[1] = inv_y0.y, iy[2] = inv_y0.z, iy[3] = inv_y0.w;
       iy[4] = inv_y1.x, iy[5] = inv_y1.y, iy[6] = inv_y1.z, iy[7] = inv_y1.w;
       // The record count covers the tile's existing rows only: the range check
-      // of the buffer unit drops the stores of missing rows of a ragged T.
+      // of the buffer unit drops the stores of missing rows of a ragged T; a
+      // lane whose channels are past H (ragged H) stores at an offset past it.
       const __amdgpu_buffer_rsrc_t gq_buf =
           buffer_of(grad_input_q + (cur.t0 * gq_row_bytes + cur.h0), (uint32_t)(cur.rows * gq_row_bytes));
-      quantise_rows_and_y<F, false>(Gp, Up, Yp, idg, idu, iy, gq_buf, lane_gq, (uint32_t)gq_row_bytes, (uint32_t)H,
-                                 s_yqt, p, q);
+      const uint32_t lane_gq_here = 8 * (p & ~1) < cur.cols ? lane_gq : kDropped;
+      quantise_rows_and_y<F, false>(Gp, Up, Yp, idg, idu, iy, gq_buf, lane_gq_here, (uint32_t)gq_row_bytes,
+                                    (uint32_t)H, s_yqt, p, q);
       __syncthreads();
       // Rare: some group's inverse overflowed (its maximum is below
       // 127 * 2^-128).  Recompute the tile from its inputs and rewrite every
@@ -551,18 +582,19 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
       if (s_flag[0]) {
         TileIn again;
         load_tile(again, xb + (cur.t0 * x_row_bytes + 2 * cur.h0), dyb + (cur.t0 * dy_row_bytes + 2 * cur.h0),
-                  lane_x, lane_dy, x_row_bytes, dy_row_bytes, cur.rows, q);
+                  lane_x, lane_dy, x_row_bytes, dy_row_bytes, cur.rows, 8 * p < cur.cols, q);
         float rg2[kRows], ru2[kRows], cm2[8];
         elementwise(again, s_tab, Yp, Gp, Up, rg2, ru2, cm2);
-        quantise_rows_and_y<F, true>(Gp, Up, Yp, idg, idu, iy, gq_buf, lane_gq, (uint32_t)gq_row_bytes, (uint32_t)H,
-                                  s_yqt, p, q);
+        quantise_rows_and_y<F, true>(Gp, Up, Yp, idg, idu, iy, gq_buf, lane_gq_here, (uint32_t)gq_row_bytes,
+                                     (uint32_t)H, s_yqt, p, q);
         __syncthreads();
       }
     }
 
     // ---- transposed codes out: eight neighbouring threads per 128-byte row --
     {
-      const __amdgpu_buffer_rsrc_t yq_buf = buffer_of(y_q_t + (cur.h0 * T + cur.t0), (uint32_t)(kTile * T));
+      // rows past H (ragged H) lie past the record count
+      const __amdgpu_buffer_rsrc_t yq_buf = buffer_of(y_q_t + (cur.h0 * T + cur.t0), (uint32_t)(cur.cols * T));
 #pragma unroll
       for (int step = 0; step < kOutSteps; ++step) {
         const int id = tid + step * kThreads;
@@ -786,14 +818,15 @@ namespace {
 template <Fmt F>
 int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float* grad_input_s, void* y_q_t,
                     float* y_s_t, int64_t T, int64_t H, int64_t group, void* stream) {
-  if (group != kGroup) return SILUQUANT_ERR_BAD_GROUP;
-  if (T < 0 || H < 0 || H % kTile != 0) return SILUQUANT_ERR_BAD_SHAPE;
+  if (group != 32 && group != 64 && group != 128) return SILUQUANT_ERR_BAD_GROUP;
+  if (T < 0 || H < 0 || H % group != 0) return SILUQUANT_ERR_BAD_SHAPE;
   if (T == 0 || H == 0) return SILUQUANT_OK;
   // Tile indices are int; a lane's byte offset inside a tile (< 512 * H for x)
   // must fit in 32 bits, and a tile's output span (128 rows of 2H bytes of
   // grad_input_q, 128 rows of T bytes of y_q_t) in a buffer resource's
   // 31-bit record count.
-  if (T > (int64_t(1) << 23) || H > (int64_t(1) << 22) || ((T + kTile - 1) / kTile) * (H / kTile) > 0x7fffffff)
+  const int64_t tiles_t = (T + kTile - 1) / kTile, tiles_h64 = (H + kTile - 1) / kTile;
+  if (T > (int64_t(1) << 23) || H > (int64_t(1) << 22) || tiles_t * tiles_h64 > 0x7fffffff)
     return SILUQUANT_ERR_BAD_SHAPE;
   if (!x || !grad_y || !grad_input_q || !grad_input_s || !y_q_t || !y_s_t) return SILUQUANT_ERR_NULL_PTR;
   auto mis16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; };
@@ -801,9 +834,9 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
   if (mis16(x) || mis16(grad_y) || mis16(grad_input_q) || mis16(y_q_t) || mis4(grad_input_s) || mis4(y_s_t))
     return SILUQUANT_ERR_MISALIGNED;
   const int64_t pairs = T * H;
-  const int64_t col_groups = (T + kGroup - 1) / kGroup;
+  const int64_t col_groups = (T + group - 1) / group;
   const void* bufs[6] = {x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t};
-  const int64_t sizes[6] = {4 * pairs, 2 * pairs, 2 * pairs, 4 * (2 * pairs / kGroup), pairs, 4 * H * col_groups};
+  const int64_t sizes[6] = {4 * pairs, 2 * pairs, 2 * pairs, 4 * (2 * pairs / group), pairs, 4 * H * col_groups};
   for (int i = 0; i < 6; ++i)
     for (int j = i + 1; j < 6; ++j)
       if (overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
@@ -812,14 +845,17 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
   int rc = ensure_table(&dev);
   if (rc != SILUQUANT_OK) return rc;
 
-  const int tiles_h = (int)(H / kTile);
-  const int tiles = (int)col_groups * tiles_h;
+  const int tiles_h = (int)tiles_h64;
+  const int tiles = (int)(tiles_t * tiles_h64);
   // Persistent grid: as many workgroups as fit on the device at once (a
   // multiple of 8, one share per XCD), or one per tile if there are fewer.
   int grid = g_cu_count[dev] * kWorkgroupsPerCU;
   grid = grid >= 8 ? grid - grid % 8 : grid;
   if (tiles < grid) grid = tiles;
-  hipLaunchKernelGGL(silu_quant_bwd_kernel<F>, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+  auto kernel = group == 128 ? silu_quant_bwd_kernel<F, 128>
+                : group == 64 ? silu_quant_bwd_kernel<F, 64>
+                              : silu_quant_bwd_kernel<F, 32>;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(grad_y),
                      static_cast<int8_t*>(grad_input_q), grad_input_s, static_cast<int8_t*>(y_q_t), y_s_t, T, H,
                      tiles_h, tiles);
@@ -832,21 +868,21 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
 extern "C" {
 
 __attribute__((visibility("default"))) int64_t siluquant_algorithmic_bytes(int64_t T, int64_t H, int64_t group) {
-  if (T < 0 || H < 0 || group != kGroup) return -1;
+  if (T < 0 || H < 0 || (group != 32 && group != 64 && group != 128)) return -1;
   const int64_t pairs = T * H;
   // x (4) + grad_y (2) in; grad_input_q (2) + y_q_t (1) out, per pair; plus
-  // one fp32 scale per group on each axis (128 channels of a 2H row; 128
-  // tokens, or the shorter last group, of a row of y^T).
-  return 9 * pairs + 4 * T * ((2 * H + kGroup - 1) / kGroup) + 4 * H * ((T + kGroup - 1) / kGroup);
+  // one fp32 scale per group on each axis (`group` channels of a 2H row;
+  // `group` tokens, or the shorter last group, of a row of y^T).
+  return 9 * pairs + 4 * T * ((2 * H + group - 1) / group) + 4 * H * ((T + group - 1) / group);
 }
 
 __attribute__((visibility("default"))) const char* siluquant_strerror(int status) {
   switch (status) {
     case SILUQUANT_OK: return "ok";
     case SILUQUANT_ERR_NULL_PTR: return "a buffer pointer is NULL";
-    case SILUQUANT_ERR_BAD_SHAPE: return "T and H must be non-negative multiples of 128";
-    case SILUQUANT_ERR_BAD_GROUP: return "group must be 128";
-    case SILUQUANT_ERR_MISALIGNED: return "x, grad_y, grad_input_q, y_q_t need 16-byte and scales 4-byte alignment";
+    case SILUQUANT_ERR_BAD_SHAPE: return "sizes must be non-negative, H (or K) a multiple of the group, and within the limits";
+    case SILUQUANT_ERR_BAD_GROUP: return "unsupported group size (the passes take 128, 64 or 32; the forward pass and the GEMM 128)";
+    case SILUQUANT_ERR_MISALIGNED: return "a buffer is not aligned (code and input tensors 16 bytes, scales 4 bytes)";
     case SILUQUANT_ERR_OVERLAP: return "buffers overlap";
     case SILUQUANT_ERR_DEVICE: return "HIP runtime error (device query or sigmoid table build)";
     case SILUQUANT_ERR_LAUNCH_FAILED: return "kernel launch failed";

@@ -68,8 +68,9 @@ def _ptrs(T, H, misalign=None, null=None, overlap=False):
 
 
 @pytest.mark.parametrize("T,H,group,code", [
-    (256, 256, 64, 3), (256, 256, 0, 3), (256, 256, 256, 3),
+    (256, 256, 48, 3), (256, 256, 0, 3), (256, 256, 256, 3), (256, 256, 16, 3),
     (-128, 256, 128, 2), (256, -128, 128, 2), (256, 200, 128, 2), (256, 136, 128, 2), (100, 64, 128, 2),
+    (256, 96, 64, 2), (256, 200, 64, 2), (256, 80, 32, 2),
 ])
 @pytest.mark.parametrize("fp8", [False, True])
 def test_bad_shape_and_group(lib, T, H, group, code, fp8):
@@ -145,7 +146,15 @@ def test_algorithmic_bytes(lib, shape):
 
 def test_algorithmic_bytes_rejects(lib):
     assert sq.algorithmic_bytes(-1, 128) == -1
-    assert sq.algorithmic_bytes(128, 128, 64) == -1
+    assert sq.algorithmic_bytes(128, 128, 48) == -1
+    assert sq.algorithmic_bytes(128, 128, 256) == -1
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_algorithmic_bytes_smaller_groups(lib, group):
+    # T = 200, H = 96: 2H/group row groups per token, ceil(200/group) token groups per channel
+    T, H = 200, 96
+    assert sq.algorithmic_bytes(T, H, group) == 9 * T * H + 4 * T * (2 * H // group) + 4 * H * -(-T // group)
 
 
 def test_forward_rejects_bad_arguments(lib):

@@ -236,3 +236,62 @@ def test_empty_inputs_are_no_ops():
         dy = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
         sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *sq.empty_outputs(T, H, DEV))
     torch.cuda.synchronize()
+
+
+def check_group(x, grad_y, group, label, fp8=False):
+    """Parity for a group size other than 128: every code and scale bit-equal."""
+    T, H = grad_y.shape
+    outs = sq.empty_outputs(T, H, x.device, group=group, fp8=fp8)
+    for o in outs:  # poison: every element must be written
+        o.fill_(0x7F if o.dtype == torch.uint8 else -7 if o.dtype == torch.int8 else float("nan"))
+    fn = sq.silu_dot_fwd_bwd_quant_fuse_fp8 if fp8 else sq.silu_dot_fwd_bwd_quant_fuse
+    fn(x, grad_y, *outs, group_size=group)
+    torch.cuda.synchronize()
+    got = [o.cpu().numpy() for o in outs]
+    ofn = oracle.silu_dot_fwd_bwd_quant_fuse_fp8 if fp8 else oracle.silu_dot_fwd_bwd_quant_fuse
+    want = ofn(_bits(x), _bits(grad_y), group_size=group)
+    for name, g, w in zip(("grad_input_q", "grad_input_s", "y_q_t", "y_s_t"), got, want):
+        assert g.shape == w.shape, (label, name, g.shape, w.shape)
+        gb, wb = g.view(np.uint8 if g.dtype.itemsize == 1 else np.uint32), w.view(np.uint8 if w.dtype.itemsize == 1 else np.uint32)
+        bad = int((gb != wb).sum())
+        assert bad == 0, "%s %s: %d of %d differ" % (label, name, bad, g.size)
+    print("%s: bit-exact" % label, flush=True)
+
+
+# Group sizes 64 and 32 divide the 128 x 128 tile; H need only be a multiple of
+# the group, so the last channel block may hold 32, 64 or 96 channels.
+@pytest.mark.parametrize("T,H,group", [(256, 256, 64), (256, 256, 32), (300, 192, 64), (1000, 160, 32),
+                                       (129, 96, 32), (4096, 1408, 64), (2048, 1376, 32), (77, 64, 64),
+                                       (1, 32, 32), (4100, 448, 64)])
+def test_smaller_groups_and_ragged_h(T, H, group):
+    print("case groups", T, H, group, flush=True)
+    x, dy = random_inputs(T, H, device=DEV, seed=T + 3 * H + group)
+    check_group(x, dy, group, "T=%d H=%d group=%d" % (T, H, group))
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_smaller_groups_workloads(group):
+    for name in ("t8192_h4096", "t32768_h2048_outliers"):
+        print("case groups", name, group, flush=True)
+        x, dy = make_inputs(name, device=DEV)
+        check_group(x, dy, group, "%s group=%d" % (name, group))
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_smaller_groups_fp8_and_overflowed_inverse(group):
+    x, dy = random_inputs(640, 320, device=DEV, seed=group)
+    check_group(x, dy, group, "fp8 T=640 H=320 group=%d" % group, fp8=True)
+    # a group whose maximum is below 127 * 2^-128 (gate 20: d_gate == up)
+    T, H = 128, 192
+    x, dy = _const(T, H, 20.0, 0.0, 1.0)
+    x[:, H:H + 4] = torch.tensor([2.0**-130, -(2.0**-131), 0.0, 2.0**-133], dtype=torch.float32).to(torch.bfloat16).to(DEV)
+    check_group(x, dy, group, "tiny groups group=%d" % group)
+    check_group(x, dy, group, "tiny groups fp8 group=%d" % group, fp8=True)
+
+
+def test_group_size_errors():
+    x, dy = random_inputs(128, 96, device=DEV)
+    with pytest.raises(ValueError):  # 96 is not a multiple of 64
+        sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *sq.empty_outputs(128, 96, DEV, group=64), group_size=64)
+    with pytest.raises(ValueError):
+        sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *sq.empty_outputs(128, 96, DEV, group=32), group_size=48)
