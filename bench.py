@@ -30,12 +30,15 @@ KERNEL_SRC = os.path.join(ROOT, "swiglu_backward_int8_amd", "csrc", "siluquant.h
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+GEMM_SRC = os.path.join(ROOT, "swiglu_backward_int8_amd", "csrc", "i8gemm.hip")
+
+
+def kernel_source_digest(path: str = KERNEL_SRC) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, src: str = KERNEL_SRC):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
     try:
@@ -44,7 +47,7 @@ def measured_traffic(workload: str):
     except (OSError, ValueError):
         return None
     entry = rec.get(workload)
-    if not entry or entry.get("kernel_source_sha") != kernel_source_digest():
+    if not entry or entry.get("kernel_source_sha") != kernel_source_digest(src):
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -204,12 +207,14 @@ def run_gemm(args):
             "peak": PEAK_INT8_TOPS,
             "unit": "TOP/s",
             "frac": round(achieved / PEAK_INT8_TOPS, 4),
-            "traffic": measured_traffic(args.op + ":t16384_h11008"),
+            "traffic": measured_traffic(args.op + ":t16384_h11008", GEMM_SRC),
             "kernel": "i8_gemm_kernel",
             "avg_launch_us": round(per_launch_s * 1e6, 3),
         },
         "cpu_baseline": None,
     }
+    if args.probes:
+        out["probes"] = stream_probes(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = gemm_cpu_baseline(A, sA, B, sB, b_rows)
     print(json.dumps(out), flush=True)
