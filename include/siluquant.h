@@ -109,8 +109,8 @@ int silu_dot_fwd_bwd_quant_fuse_fp8(const void* x, const void* grad_y, void* gra
  *
  * The fused launch shape of kquant_swiglu_q8_1_rows on the page "kquant_mmq.rs"
  * (docs.atlascybernetics.ai): y = bf16((silu(gate) * up) * w[t]) rounded once to
- * bf16 (nearest, ties to even), then quantised per row in groups of 128
- * contiguous channels exactly as above (scale = amax/127, 1.0 for an all-zero
+ * bf16 (nearest, ties to even), then quantised per row in groups of `group`
+ * (128, 64 or 32) contiguous channels exactly as above (scale = amax/127, 1.0 for an all-zero
  * group; q = clamp(rne(v * inv)), v == 0 -> 0).  With no row weight, y is the
  * same bf16 value the backward pass recomputes.  The page's `limit` argument
  * has no stated meaning and is not provided.
@@ -118,9 +118,10 @@ int silu_dot_fwd_bwd_quant_fuse_fp8(const void* x, const void* grad_y, void* gra
  *   x           bf16 [T, 2H] as above (read only; 16-byte aligned)
  *   row_weight  fp32 [T], or NULL for weight 1 (4-byte aligned)
  *   y_q         int8 [T, H]       codes (16-byte aligned)
- *   y_s         fp32 [T, H/128]   one scale per group (4-byte aligned)
+ *   y_s         fp32 [T, H/group] one scale per group (4-byte aligned)
  *   y_bf16      bf16 [T, H] the rounded y, or NULL (16-byte aligned)
- * Sizes: any T >= 0 (T <= 2^31), H a multiple of 128 (H <= 2^22), group 128.
+ *   (y_s is [T, H/group] for group 128, 64 or 32.)
+ * Sizes: any T >= 0 (T <= 2^31), H a multiple of the group (H <= 2^22).
  * Same ownership, asynchrony and error conventions as above.
  */
 int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q, float* y_s, void* y_bf16, int64_t T,
@@ -134,8 +135,8 @@ int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q, float* y
  * contraction axis of the GEMM that reads each product.  This is that GEMM, on
  * the matrix cores (v_mfma_i32_32x32x32_i8):
  *   C[m, n] = sum_g sA[m, g] * sB[n / Bb, g] * sum_{k in group g} A[m, k] * B[n, k]
- *   A  int8 [M, K] row-major (16-byte aligned), sA fp32 [M, K/128];
- *   B  int8 [N, K] row-major (16-byte aligned), sB fp32 [ceil(N/Bb), K/128];
+ *   A  int8 [M, K] row-major (16-byte aligned), sA fp32 [M, K/group];
+ *   B  int8 [N, K] row-major (16-byte aligned), sB fp32 [ceil(N/Bb), K/group];
  *   Bb = b_rows_per_scale: 1 (a scale per row of B and group, as y_s_t) or 128
  *        (one per 128 x 128 block of B, a pre-quantised weight);
  *   C  [M, N] row-major, fp32 (c_dtype SILUQUANT_GEMM_OUT_F32, 4-byte aligned)
@@ -146,9 +147,11 @@ int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q, float* y
  * Arithmetic: each group's integer dot is exact (int32); the groups are
  *   accumulated in ascending order as acc = fma(float(dot), sA * sB, acc) in
  *   fp32; bf16 output rounds that once (nearest, ties to even).
+ * Group: `group` is 128, 64 or 32 (the pass's group sizes); sA is then
+ *   [M, K/group] and sB [ceil(N/Bb), K/group].
  * Sizes: any M, N >= 0 (M == 0 or N == 0 is a no-op), K >= 0 a multiple of 128
- *   (K == 0 writes zeros), group must be 128.  Same ownership, asynchrony and
- *   status conventions as above; C must not overlap an input.
+ *   (K == 0 writes zeros).  Same ownership, asynchrony and status conventions
+ *   as above; C must not overlap an input.
  */
 enum siluquant_gemm_out { SILUQUANT_GEMM_OUT_F32 = 0, SILUQUANT_GEMM_OUT_BF16 = 1 };
 int i8_gemm_group_scaled(const int8_t* A, const float* sA, const int8_t* B, const float* sB, void* C, int64_t M,

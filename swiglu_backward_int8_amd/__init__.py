@@ -154,20 +154,23 @@ def _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size: i
 def silu_fwd_quant(x, y_q, y_s, row_weight=None, y_bf16=None, group_size: int = GROUP):
     """Forward SwiGLU with row-wise int8 quantisation: y = bf16((silu(gate) * up)
     * row_weight[t]) from x = [gate | up] [T, 2H]; writes y_q int8 [T, H] and
-    y_s fp32 [T, H/128], and y_bf16 [T, H] if given.  Enqueued on the current
-    stream of x's device; returns None."""
+    y_s fp32 [T, H/group_size] (group_size 128, 64 or 32; H a multiple of it),
+    and y_bf16 [T, H] if given.  Enqueued on the current stream of x's device;
+    returns None."""
     import torch
 
     if x.dim() != 2 or x.shape[1] % 2:
         raise ValueError("x must be [T, 2H]")
     T, H = int(x.shape[0]), int(x.shape[1]) // 2
-    if group_size != GROUP:
-        raise ValueError("group_size must be 128")
+    if group_size not in GROUPS:
+        raise ValueError("group_size must be one of %s" % (GROUPS,))
+    if H % group_size:
+        raise ValueError("H must be a multiple of group_size")
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU; got %s" % dev)
     checks = [("x", x, torch.bfloat16, (T, 2 * H)), ("y_q", y_q, torch.int8, (T, H)),
-              ("y_s", y_s, torch.float32, (T, H // GROUP))]
+              ("y_s", y_s, torch.float32, (T, H // group_size))]
     if row_weight is not None:
         checks.append(("row_weight", row_weight, torch.float32, (T,)))
     if y_bf16 is not None:
@@ -188,24 +191,26 @@ GEMM_OUT_F32, GEMM_OUT_BF16 = 0, 1
 
 def i8_gemm_group_scaled(A, sA, B, sB, C, b_rows_per_scale: int = 1, group_size: int = GROUP):
     """C = A . B^T of group-scaled int8 operands on the matrix cores:
-    C[m, n] = sum_g sA[m, g] * sB[n // b_rows_per_scale, g] * (A[m, g-th 128] . B[n, g-th 128]).
-    A int8 [M, K], sA fp32 [M, K/128], B int8 [N, K], sB fp32
-    [ceil(N / b_rows_per_scale), K/128] (b_rows_per_scale 1 or 128); C fp32 or
-    bf16 [M, N] is overwritten.  Enqueued on the current stream of A's device."""
+    C[m, n] = sum_g sA[m, g] * sB[n // b_rows_per_scale, g] * (A[m, group g] . B[n, group g]).
+    Groups are group_size (128, 64 or 32) wide along K; K is a multiple of 128.
+    A int8 [M, K], sA fp32 [M, K/group_size], B int8 [N, K], sB fp32
+    [ceil(N / b_rows_per_scale), K/group_size] (b_rows_per_scale 1 or 128); C
+    fp32 or bf16 [M, N] is overwritten.  Enqueued on the current stream of A's
+    device."""
     import torch
 
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1]:
         raise ValueError("A must be [M, K] and B [N, K]")
     M, K = int(A.shape[0]), int(A.shape[1])
     N = int(B.shape[0])
-    if group_size != GROUP or K % GROUP:
-        raise ValueError("K must be a multiple of 128 and group_size 128")
+    if group_size not in GROUPS or K % GROUP:
+        raise ValueError("K must be a multiple of 128 and group_size one of %s" % (GROUPS,))
     if b_rows_per_scale not in (1, 128):
         raise ValueError("b_rows_per_scale must be 1 or 128")
     dev = A.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU; got %s" % dev)
-    groups = K // GROUP
+    groups = K // group_size
     if C.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("C must be float32 or bfloat16")
     checks = [("A", A, torch.int8, (M, K)), ("sA", sA, torch.float32, (M, groups)),
@@ -222,10 +227,10 @@ def i8_gemm_group_scaled(A, sA, B, sB, C, b_rows_per_scale: int = 1, group_size:
     _check(code, "i8_gemm_group_scaled")
 
 
-def forward_bytes(T: int, H: int, with_bf16: bool = False, with_weight: bool = False) -> int:
+def forward_bytes(T: int, H: int, with_bf16: bool = False, with_weight: bool = False, group: int = GROUP) -> int:
     """Bytes the forward quantiser must move: x (4 per pair) in, codes (1) and
-    one fp32 scale per 128 codes out, plus bf16 y (2) and the row weights."""
-    return 5 * T * H + 4 * (T * H // GROUP) + (2 * T * H if with_bf16 else 0) + (4 * T if with_weight else 0)
+    one fp32 scale per `group` codes out, plus bf16 y (2) and the row weights."""
+    return 5 * T * H + 4 * (T * H // group) + (2 * T * H if with_bf16 else 0) + (4 * T if with_weight else 0)
 
 
 def empty_outputs(T: int, H: int, device, group: int = GROUP, fp8: bool = False):

@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "siluquant.h"
 
 namespace {
@@ -66,14 +68,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// One group's operands in flight: kChunksPerThread 16-byte chunks and one scale.
+// One stage (128 of K) in flight: kChunksPerThread 16-byte chunks and the
+// thread's scale of each of the stage's kSub groups.
+template <int kSub>
 struct Stage {
   i32x4 v[kChunksPerThread];
-  float sc, sb;
+  float sc[kSub], sb[kSub];
 };
 
-// kBlockScale: B's scale rows cover 128 rows (constant over a wave's 64 columns).
-template <bool kBf16Out, bool kBlockScale>
+// kBlockScale: B's scale rows cover 128 rows (constant over a wave's 64
+// columns).  kG: the group size along K (128, 64 or 32); a stage of 128 of K
+// holds kSub = 128 / kG groups, each promoted on its own.
+template <bool kBf16Out, bool kBlockScale, int kG>
 __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* __restrict__ A,
                                                                   const float* __restrict__ sA,
                                                                   const int8_t* __restrict__ B,
@@ -81,7 +87,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
                                                                   int64_t M, int64_t N, int64_t K, int b_rows,
                                                                   int tiles_m, int tiles_n, int per_xcd) {
   __shared__ __attribute__((aligned(16))) char s_tile[2][kStageBytes];
-  __shared__ __attribute__((aligned(16))) float s_scale[2][kBM + kBN];
+  constexpr int kSub = kBK / kG, kStepsPerGroup = 4 / kSub;  // MFMA k-steps (32 of K) per group
+  __shared__ __attribute__((aligned(16))) float s_scale[2][kSub][kBM + kBN];
 
   const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (tile >= tiles_m * tiles_n) return;
@@ -95,7 +102,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = (wave / kWavesN) * 64, wn = (wave % kWavesN) * 64;  // the wave's 64 x 64 corner
-  const int groups = (int)(K / kBK);
+  const int stages = (int)(K / kBK), groups = (int)(K / kG);
 
   // Rows past M or N read as zeros: the buffer's record count ends at the last row.
   const int a_rows = M - m0 < kBM ? (int)(M - m0) : kBM;
@@ -119,7 +126,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
   constexpr int kAPer = kAChunks / kGemmThreads;  // A chunks per thread
   const int g_off = (tid >> 3) * (int)K + 16 * (tid & 7);
   const int l_off = lds_at(tid >> 3, tid & 7);
-  auto load_stage = [&](int g, Stage& st) {
+  auto load_stage = [&](int g, Stage<kSub>& st) {
     const int k0 = g * kBK;
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
@@ -127,19 +134,25 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
       st.v[i] = __builtin_bit_cast(
           i32x4, __builtin_amdgcn_raw_buffer_load_b128(i < kAPer ? ra : rb, g_off, k0 + row_step * (int)K, 0));
     }
-    st.sc = sc_live ? sc_ptr[g] : 0.0f;
-    if constexpr (kBlockScale) st.sb = sb_blk[g];
+#pragma unroll
+    for (int j = 0; j < kSub; ++j) {
+      st.sc[j] = sc_live ? sc_ptr[g * kSub + j] : 0.0f;
+      if constexpr (kBlockScale) st.sb[j] = sb_blk[g * kSub + j];
+    }
   };
-  auto store_stage = [&](int buf, const Stage& st) {
+  auto store_stage = [&](int buf, const Stage<kSub>& st) {
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
       const int row_step = (i < kAPer ? i : i - kAPer) * (kGemmThreads / 8);
       *reinterpret_cast<i32x4*>(&s_tile[buf][(i < kAPer ? 0 : kBM * kBK) + row_step * kBK +
                                             (l_off ^ (16 * ((row_step >> 3) & 7)))]) = st.v[i];
     }
-    float sc = st.sc;
-    if constexpr (kBlockScale) sc = sc_is_a ? sc * st.sb : 0.0f;
-    if (tid < kBM + kBN) s_scale[buf][tid] = sc;
+#pragma unroll
+    for (int j = 0; j < kSub; ++j) {
+      float sc = st.sc[j];
+      if constexpr (kBlockScale) sc = sc_is_a ? sc * st.sb[j] : 0.0f;
+      if (tid < kBM + kBN) s_scale[buf][j][tid] = sc;
+    }
   };
 
   float acc[2][2][16];
@@ -167,38 +180,46 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
   // already holds the product.
   auto compute = [&](int buf) {
     const char* t = s_tile[buf];
-    i32x16 I[2][2];
+    // With several groups per stage the loop over them stays rolled, so that
+    // one group's int32 sums are promoted before the next group's MFMAs start
+    // (unrolled, the scheduler overlaps them and runs out of registers).
+#pragma unroll 1
+    for (int j = 0; j < kSub; ++j) {
+      i32x16 I[2][2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      i32x4 fa[2], fb[2];
+      for (int s = j * kStepsPerGroup; s < (j + 1) * kStepsPerGroup; ++s) {
+        i32x4 fa[2], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const i32x4*>(t + off(a_base, i, s));
+        for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const i32x4*>(t + off(a_base, i, s));
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const i32x4*>(t + off(b_base, j, s));
+        for (int jj = 0; jj < 2; ++jj) fb[jj] = *reinterpret_cast<const i32x4*>(t + off(b_base, jj, s));
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          I[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], s == 0 ? (i32x16){} : I[i][j], 0, 0, 0);
-    }
-    float sb[2];
-    if constexpr (!kBlockScale) {
+          for (int jj = 0; jj < 2; ++jj)
+            I[i][jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[jj],
+                                                             s == j * kStepsPerGroup ? (i32x16){} : I[i][jj], 0, 0, 0);
+      }
+      const float* scl = s_scale[buf][j];
+      float sb[2];
+      if constexpr (!kBlockScale) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) sb[j] = s_scale[buf][kBM + wn + 32 * j + lrow];
-    }
+        for (int jj = 0; jj < 2; ++jj) sb[jj] = scl[kBM + wn + 32 * jj + lrow];
+      }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < 2; ++i) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 sa = *reinterpret_cast<const float4*>(&s_scale[buf][wm + 32 * i + 8 * q + 4 * lhalf]);
-        const float sav[4] = {sa.x, sa.y, sa.z, sa.w};
+        for (int q = 0; q < 4; ++q) {
+          const float4 sa = *reinterpret_cast<const float4*>(&scl[wm + 32 * i + 8 * q + 4 * lhalf]);
+          const float sav[4] = {sa.x, sa.y, sa.z, sa.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q + e;
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q + e;
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const float sc = kBlockScale ? sav[e] : sav[e] * sb[j];
-            acc[i][j][r] = __builtin_fmaf((float)I[i][j][r], sc, acc[i][j][r]);
+            for (int jj = 0; jj < 2; ++jj) {
+              const float sc = kBlockScale ? sav[e] : sav[e] * sb[jj];
+              acc[i][jj][r] = __builtin_fmaf((float)I[i][jj][r], sc, acc[i][jj][r]);
+            }
           }
         }
       }
@@ -207,8 +228,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
 
   // The next group's operands are loaded into registers while this group is
   // computed from LDS, then written to the other LDS buffer.
-  Stage st;
-  if (groups > 0) {
+  Stage<kSub> st;
+  if (stages > 0) {
     load_stage(0, st);
     store_stage(0, st);
   }
@@ -216,13 +237,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
   // The fence keeps the LDS writes (which wait for the loads) after the whole
   // group's compute, so that the loads have that long to arrive.
   auto group_step = [&](int g, int buf) {
-    if (g + 1 < groups) load_stage(g + 1, st);
+    if (g + 1 < stages) load_stage(g + 1, st);
     compute(buf);
     __builtin_amdgcn_sched_barrier(0);
-    if (g + 1 < groups) store_stage(buf ^ 1, st);
+    if (g + 1 < stages) store_stage(buf ^ 1, st);
     __syncthreads();
   };
-  for (int g = 0; g < groups; ++g) group_step(g, g & 1);
+  for (int g = 0; g < stages; ++g) group_step(g, g & 1);
 
   // epilogue: row m0 + wm + 32 i + 8 q + 4 lhalf + e, column n0 + wn + 32 j + lrow
 #pragma unroll
@@ -257,7 +278,7 @@ __attribute__((visibility("default"))) int i8_gemm_group_scaled(const int8_t* A,
                                                                 const float* sB, void* C, int64_t M, int64_t N,
                                                                 int64_t K, int64_t group, int64_t b_rows_per_scale,
                                                                 int c_dtype, void* stream) {
-  if (group != kBK) return SILUQUANT_ERR_BAD_GROUP;
+  if (group != 32 && group != 64 && group != 128) return SILUQUANT_ERR_BAD_GROUP;
   if (M < 0 || N < 0 || K < 0 || K % kBK != 0 || (b_rows_per_scale != 1 && b_rows_per_scale != kBN) ||
       (c_dtype != SILUQUANT_GEMM_OUT_F32 && c_dtype != SILUQUANT_GEMM_OUT_BF16))
     return SILUQUANT_ERR_BAD_SHAPE;
@@ -270,7 +291,7 @@ __attribute__((visibility("default"))) int i8_gemm_group_scaled(const int8_t* A,
   auto mis = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
   if (mis(A, 16) || mis(B, 16) || mis(sA, 4) || mis(sB, 4) || mis(C, c_dtype == SILUQUANT_GEMM_OUT_F32 ? 4 : 2))
     return SILUQUANT_ERR_MISALIGNED;
-  const int64_t groups = K / kBK;
+  const int64_t groups = K / group;
   const int64_t c_bytes = M * N * (c_dtype == SILUQUANT_GEMM_OUT_F32 ? 4 : 2);
   const void* in[4] = {A, sA, B, sB};
   const int64_t in_bytes[4] = {M * K, 4 * M * groups, N * K, 4 * ((N + b_rows_per_scale - 1) / b_rows_per_scale) * groups};
@@ -282,8 +303,16 @@ __attribute__((visibility("default"))) int i8_gemm_group_scaled(const int8_t* A,
   const dim3 grid(8 * per_xcd), block(kGemmThreads);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = c_dtype == SILUQUANT_GEMM_OUT_BF16, blk = b_rows_per_scale == kBN;
-  auto kernel = bf16 ? (blk ? i8_gemm_kernel<true, true> : i8_gemm_kernel<true, false>)
-                     : (blk ? i8_gemm_kernel<false, true> : i8_gemm_kernel<false, false>);
+  using KernelFn = void (*)(const int8_t*, const float*, const int8_t*, const float*, void*, int64_t, int64_t, int64_t,
+                            int, int, int, int);
+  auto pick = [&](auto g_tag) -> KernelFn {
+    constexpr int kG = decltype(g_tag)::value;
+    return bf16 ? (blk ? i8_gemm_kernel<true, true, kG> : i8_gemm_kernel<true, false, kG>)
+                : (blk ? i8_gemm_kernel<false, true, kG> : i8_gemm_kernel<false, false, kG>);
+  };
+  const KernelFn kernel = group == 128 ? pick(std::integral_constant<int, 128>{})
+                          : group == 64 ? pick(std::integral_constant<int, 64>{})
+                                        : pick(std::integral_constant<int, 32>{});
   hipLaunchKernelGGL(kernel, grid, block, 0, s, A, sA, B, sB, C, M, N, K, (int)b_rows_per_scale, (int)tiles_m,
                      (int)tiles_n, per_xcd);
   if (hipGetLastError() != hipSuccess) return SILUQUANT_ERR_LAUNCH_FAILED;

@@ -37,7 +37,6 @@
 
 namespace {
 
-constexpr int kGroup = 128;
 constexpr int kTile = 128;
 // Lane (q, p) of a workgroup owns tokens kRows*q .. kRows*q + kRows - 1 and
 // channels 8p .. 8p+7 of the tile: 16 lanes span the tile's 128 channels and
@@ -617,14 +616,15 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
 
 // ---------------------------------------------------------------------------
 // Forward quantiser: y = bf16((silu(gate) * up) * w[t]), quantised per row in
-// groups of 128 channels (y_q [T, H], y_s [T, H/128]), optionally also the
-// bf16 y itself.  The fused launch shape follows the page "kquant_mmq.rs"
-// (kquant_swiglu_q8_1_rows: swiglu times an optional row weight, rounded to
-// bf16, then group-quantised), with this library's 128-channel groups.
+// groups of kG = 128, 64 or 32 channels (y_q [T, H], y_s [T, H/kG]),
+// optionally also the bf16 y itself.  The fused launch shape follows the page
+// "kquant_mmq.rs" (kquant_swiglu_q8_1_rows: swiglu times an optional row
+// weight, rounded to bf16, then group-quantised), with this library's groups.
 //
 // A wave owns 4 rows x 128 channels per unit (16 lanes per row, 8 channels
-// per lane, 16-byte loads); the group maximum is a 4-step DPP butterfly inside
-// the 16-lane row, so no LDS and no barrier is needed beyond the sigmoid table.
+// per lane, 16-byte loads); the group maximum is a DPP butterfly over the
+// group's lanes inside the 16-lane row, so no LDS and no barrier is needed
+// beyond the sigmoid table.
 // Workgroups are persistent and each wave walks units w, w + waves, ... with
 // the next unit's inputs in flight.
 constexpr int kFwdThreads = 512;
@@ -636,12 +636,14 @@ __device__ __forceinline__ float dpp_max(float v) {
   return fmaxf(v, __int_as_float(o));
 }
 
-// Maximum over the 16 lanes of a DPP row: lane pairs, quads, half rows, row.
-__device__ __forceinline__ float row16_max(float v) {
-  v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
-  v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
-  v = dpp_max<0x141>(v);  // row_half_mirror
-  v = dpp_max<0x140>(v);  // row_mirror
+// Maximum over the kG / 8 lanes of a group inside a 16-lane DPP row (lane p
+// holds channels 8p..8p+7): lane pairs, quads, half rows, the whole row.
+template <int kG>
+__device__ __forceinline__ float group_lanes_max(float v) {
+  v = dpp_max<0xB1>(v);                     // quad_perm [1,0,3,2]
+  v = dpp_max<0x4E>(v);                     // quad_perm [2,3,0,1]: 4 lanes, 32 channels
+  if constexpr (kG >= 64) v = dpp_max<0x141>(v);   // row_half_mirror: 8 lanes
+  if constexpr (kG >= 128) v = dpp_max<0x140>(v);  // row_mirror: 16 lanes
   return v;
 }
 
@@ -649,6 +651,7 @@ struct FwdIn {
   uint4 g, u;
 };
 
+template <int kG>
 __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ row_weight, int8_t* __restrict__ y_q,
     float* __restrict__ y_s, uint16_t* __restrict__ y_bf16, int64_t T, int64_t H, int tiles_h, int64_t units) {
@@ -666,7 +669,7 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
   const bool odd = p & 1;
   const int64_t waves = (int64_t)gridDim.x * (kFwdThreads / 64);
   int64_t u = (int64_t)blockIdx.x * (kFwdThreads / 64) + (tid >> 6);
-  const int64_t groups = H / kGroup;
+  const int64_t groups = H / kG;
 
   auto coords = [&](int64_t unit, int64_t& t, int64_t& h0, int64_t& hb) {
     const int64_t rb = unit / tiles_h;
@@ -674,8 +677,12 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
     t = 4 * rb + r;
     h0 = hb * kTile;
   };
+  // In the last channel block of an H that is not a multiple of 128 only the
+  // lanes with 8 p < H - h0 hold channels (H is a multiple of the group, so a
+  // group's lanes are all in or all out).
+  auto live = [&](int64_t h0) { return h0 + 8 * p < H; };
   auto load = [&](FwdIn& in, int64_t t, int64_t h0) {
-    if (t < T) {
+    if (t < T && live(h0)) {
       const uint16_t* xr = x + t * 2 * H + h0 + 8 * p;
       in.g = load_stream(xr);
       in.u = load_stream(xr + H);
@@ -717,7 +724,7 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
       Yp[k] = pack_bf16(y0, y1);
       m = amax3(m, y0, y1);
     }
-    m = row16_max(m);
+    m = group_lanes_max<kG>(m);
     const float scale = group_scale(m);
     const float inv = 1.0f / scale;
     uint2 c;
@@ -727,7 +734,7 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
       c = codes8<false>(Yp, inv);
     // The even lane of each pair stores the pair's 16 codes.
     const uint2 other = make_uint2(swap_neighbour(c.x), swap_neighbour(c.y));
-    if (t < T) {
+    if (t < T && live(h0)) {
       // Plain non-temporal stores: for this write-light pass they measured
       // faster than the system-scope policy the backward pass uses.
       if (!odd)
@@ -736,7 +743,7 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
       if (y_bf16 != nullptr)
         __builtin_nontemporal_store((u32x4){Yp[0], Yp[1], Yp[2], Yp[3]},
                                     reinterpret_cast<u32x4*>(y_bf16 + t * H + h0 + 8 * p));
-      if (p == 0) y_s[t * groups + hb] = scale;
+      if (p % (kG / 8) == 0) y_s[t * groups + (h0 + 8 * p) / kG] = scale;
     }
     in = in_next;
     u = un;
@@ -912,8 +919,8 @@ __attribute__((visibility("default"))) int silu_dot_fwd_bwd_quant_fuse_fp8(const
 __attribute__((visibility("default"))) int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q,
                                                           float* y_s, void* y_bf16, int64_t T, int64_t H,
                                                           int64_t group, void* stream) {
-  if (group != kGroup) return SILUQUANT_ERR_BAD_GROUP;
-  if (T < 0 || H < 0 || H % kTile != 0) return SILUQUANT_ERR_BAD_SHAPE;
+  if (group != 32 && group != 64 && group != 128) return SILUQUANT_ERR_BAD_GROUP;
+  if (T < 0 || H < 0 || H % group != 0) return SILUQUANT_ERR_BAD_SHAPE;
   if (T == 0 || H == 0) return SILUQUANT_OK;
   if (T > (int64_t(1) << 31) || H > (int64_t(1) << 22) || T > (int64_t(1) << 40) / H) return SILUQUANT_ERR_BAD_SHAPE;
   if (!x || !y_q || !y_s) return SILUQUANT_ERR_NULL_PTR;
@@ -923,20 +930,22 @@ __attribute__((visibility("default"))) int silu_fwd_quant(const void* x, const f
     return SILUQUANT_ERR_MISALIGNED;
   const int64_t pairs = T * H;
   const void* bufs[5] = {x, row_weight, y_q, y_s, y_bf16};
-  const int64_t sizes[5] = {4 * pairs, 4 * T, pairs, 4 * (pairs / kGroup), 2 * pairs};
+  const int64_t sizes[5] = {4 * pairs, 4 * T, pairs, 4 * (pairs / group), 2 * pairs};
   for (int i = 0; i < 5; ++i)
     for (int j = i + 1; j < 5; ++j)
       if (bufs[i] && bufs[j] && overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
   int dev = 0;
   int rc = ensure_table(&dev);
   if (rc != SILUQUANT_OK) return rc;
-  const int tiles_h = (int)(H / kTile);
+  const int tiles_h = (int)((H + kTile - 1) / kTile);
   const int64_t units = ((T + 3) / 4) * tiles_h;
   const int64_t waves_needed = units;
   int64_t grid = (int64_t)g_cu_count[dev] * kFwdWorkgroupsPerCU;
   const int64_t wg_needed = (waves_needed + kFwdThreads / 64 - 1) / (kFwdThreads / 64);
   if (wg_needed < grid) grid = wg_needed;
-  hipLaunchKernelGGL(silu_fwd_quant_kernel, dim3((unsigned)grid), dim3(kFwdThreads), 0,
+  auto kernel = group == 128 ? silu_fwd_quant_kernel<128> : group == 64 ? silu_fwd_quant_kernel<64>
+                                                                      : silu_fwd_quant_kernel<32>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kFwdThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(x), row_weight, y_q, y_s,
                      static_cast<uint16_t*>(y_bf16), T, H, tiles_h, units);
   return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;

@@ -159,7 +159,8 @@ def test_algorithmic_bytes_smaller_groups(lib, group):
 
 def test_forward_rejects_bad_arguments(lib):
     f = lib.silu_fwd_quant
-    assert f(BASE, None, BASE + 2**24, BASE + 2**25, None, 8, 256, 64, None) == 3
+    assert f(BASE, None, BASE + 2**24, BASE + 2**25, None, 8, 256, 48, None) == 3
+    assert f(BASE, None, BASE + 2**24, BASE + 2**25, None, 8, 96, 64, None) == 2
     assert f(BASE, None, BASE + 2**24, BASE + 2**25, None, 8, 200, 128, None) == 2
     assert f(BASE, None, BASE + 2**24, BASE + 2**25, None, -1, 256, 128, None) == 2
     assert f(None, None, BASE + 2**24, BASE + 2**25, None, 8, 256, 128, None) == 1
@@ -180,7 +181,7 @@ def test_gemm_rejects_bad_arguments(lib):
             args[["A", "sA", "B", "sB", "C", "M", "N", "K", "group", "bb", "out", "stream"].index(k)] = v
         return f(*args)
 
-    assert call(group=64) == 3
+    assert call(group=48) == 3 and call(group=256) == 3
     assert call(K=200) == 2 and call(M=-1) == 2 and call(N=-5) == 2 and call(K=-128) == 2
     assert call(bb=64) == 2 and call(out=2) == 2
     assert call(A=None) == 1 and call(sB=None) == 1 and call(C=None) == 1

@@ -20,12 +20,12 @@ def _bits(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run(x, w=None, want_bf16=False):
+def run(x, w=None, want_bf16=False, group=128):
     T, H = x.shape[0], x.shape[1] // 2
     yq = torch.full((T, H), -7, dtype=torch.int8, device=DEV)
-    ys = torch.full((T, H // 128), float("nan"), dtype=torch.float32, device=DEV)
-    yb = torch.empty((T, H), dtype=torch.bfloat16, device=DEV) if want_bf16 else None
-    sq.silu_fwd_quant(x, yq, ys, row_weight=w, y_bf16=yb)
+    ys = torch.full((T, H // group), float("nan"), dtype=torch.float32, device=DEV)
+    yb = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device=DEV) if want_bf16 else None
+    sq.silu_fwd_quant(x, yq, ys, row_weight=w, y_bf16=yb, group_size=group)
     torch.cuda.synchronize()
     out = [yq.cpu().numpy(), ys.cpu().numpy()]
     if want_bf16:
@@ -33,9 +33,10 @@ def run(x, w=None, want_bf16=False):
     return out
 
 
-def check(x, w=None, want_bf16=False, label=""):
-    got = run(x, w, want_bf16)
-    want = oracle.silu_fwd_quant(_bits(x), None if w is None else w.cpu().numpy(), want_bf16=want_bf16)
+def check(x, w=None, want_bf16=False, label="", group=128):
+    got = run(x, w, want_bf16, group)
+    want = oracle.silu_fwd_quant(_bits(x), None if w is None else w.cpu().numpy(), group_size=group,
+                                 want_bf16=want_bf16)
     assert np.array_equal(got[1].view(np.uint32), want[1].view(np.uint32)), "%s: scales differ" % label
     d = np.abs(got[0].astype(np.int16) - want[0].astype(np.int16))
     assert int(d.max(initial=0)) == 0, "%s: %d codes differ" % (label, int((d > 0).sum()))
@@ -106,3 +107,20 @@ def test_forward_y_equals_backward_recompute():
     yb = run(x, want_bf16=True)[2]
     y, _ = sq.eval_intermediates(x, dy)
     assert np.array_equal(yb, _bits(y))
+
+
+# Groups of 64 and 32 channels, and H any multiple of the group (the last
+# 128-channel block then holds 32, 64 or 96 channels).
+@pytest.mark.parametrize("T,H,group", [(256, 256, 64), (256, 256, 32), (301, 192, 64), (1000, 160, 32),
+                                       (5, 96, 32), (4096, 1376, 32), (4099, 448, 64), (1, 64, 64)])
+def test_forward_groups_and_ragged_h(T, H, group):
+    x, _ = random_inputs(T, H, device=DEV, seed=7 * T + H + group)
+    w = torch.rand(T, device=DEV, generator=torch.Generator(device=DEV).manual_seed(T)) * 4 - 2
+    check(x, label="T=%d H=%d group=%d" % (T, H, group), group=group)
+    check(x, w=w, want_bf16=True, label="T=%d H=%d group=%d weighted" % (T, H, group), group=group)
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_forward_groups_workload(group):
+    x, _ = make_inputs("t32768_h2048_outliers", device=DEV)
+    check(x, label="outliers group=%d" % group, group=group)

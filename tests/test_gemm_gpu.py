@@ -162,3 +162,51 @@ def test_gemm_binding_rejects_bad_tensors():
         sq.i8_gemm_group_scaled(A, s, A, s, C, b_rows_per_scale=64)
     with pytest.raises(ValueError):
         sq.i8_gemm_group_scaled(A[:, :200], s, A[:, :200], s, C)
+
+
+# K groups of 64 and 32 (the pass's smaller group sizes): a stage of 128 of K
+# holds two or four groups, each promoted on its own.
+@pytest.mark.parametrize("group", [64, 32])
+@pytest.mark.parametrize("M,N,K,b_rows", [(256, 256, 512, 1), (200, 136, 384, 128), (77, 300, 256, 1)])
+def test_gemm_smaller_groups(group, M, N, K, b_rows):
+    rng = np.random.default_rng(M + N + K + group)
+    A = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    B = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    sA = (rng.random((M, K // group)) * 10.0 ** rng.uniform(-6, 0, (M, K // group))).astype(np.float32)
+    nb = -(-N // b_rows)
+    sB = (rng.random((nb, K // group)) + 0.01).astype(np.float32)
+    t = [torch.from_numpy(a).to(DEV) for a in (A, sA, B, sB)]
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    sq.i8_gemm_group_scaled(*t, C, b_rows_per_scale=b_rows, group_size=group)
+    torch.cuda.synchronize()
+    want, want_abs = oracle.i8_gemm_group_scaled(A, sA, B, sB, group_size=group, b_rows_per_scale=b_rows)
+    check(C.cpu().numpy().astype(np.float64), want, want_abs, K * 128 // group,
+          label="M=%d N=%d K=%d Bb=%d group=%d" % (M, N, K, b_rows, group))
+
+
+@pytest.mark.parametrize("group", [64, 32])
+def test_gemm_consumes_smaller_group_outputs(group):
+    # the pass with group 64 or 32, then dgrad and wgrad with the same K groups
+    x, dy = make_inputs("t4096_h1408", device=DEV, T=1024)
+    T, H = dy.shape
+    gq, gs, yq, ys = sq.empty_outputs(T, H, DEV, group=group)
+    sq.silu_dot_fwd_bwd_quant_fuse(x, dy, gq, gs, yq, ys, group_size=group)
+    D = 256
+    gen = torch.Generator(device=DEV).manual_seed(23)
+    W = torch.randint(-127, 128, (D, 2 * H), dtype=torch.int8, device=DEV, generator=gen)
+    sW = torch.rand((D, 2 * H // group), device=DEV, generator=gen)
+    C = torch.empty((T, D), dtype=torch.float32, device=DEV)
+    sq.i8_gemm_group_scaled(gq, gs, W, sW, C, b_rows_per_scale=1, group_size=group)
+    go = torch.randint(-127, 128, (D, T), dtype=torch.int8, device=DEV, generator=gen)
+    sgo = torch.rand((D, T // group), device=DEV, generator=gen)
+    C2 = torch.empty((D, H), dtype=torch.float32, device=DEV)
+    sq.i8_gemm_group_scaled(go, sgo, yq, ys, C2, b_rows_per_scale=1, group_size=group)
+    torch.cuda.synchronize()
+    want, want_abs = oracle.i8_gemm_group_scaled(gq.cpu().numpy(), gs.cpu().numpy(), W.cpu().numpy(),
+                                                 sW.cpu().numpy(), group_size=group)
+    check(C.cpu().numpy().astype(np.float64), want, want_abs, 2 * H * 128 // group,
+          label="dgrad of the pass, group %d" % group)
+    want, want_abs = oracle.i8_gemm_group_scaled(go.cpu().numpy(), sgo.cpu().numpy(), yq.cpu().numpy(),
+                                                 ys.cpu().numpy(), group_size=group)
+    check(C2.cpu().numpy().astype(np.float64), want, want_abs, T * 128 // group,
+          label="wgrad of the pass, group %d" % group)
