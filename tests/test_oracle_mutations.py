@@ -68,17 +68,45 @@ MUTANTS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_pins_catch_mutant(name, tmp_path):
+# The pin file most likely to catch a family of mutants runs first, so that the
+# child run (which stops at the first failure) ends early.
+FIRST = {"gemm_": "tests/test_oracle_gemm.py", "fp8_": "tests/test_oracle_fp8.py",
+         "forward_": "tests/test_oracle_forward.py"}
+
+
+def _run_mutant(name, workdir):
+    """Build the mutant and run the pins against it; returns (caught, output)."""
     old, new = MUTANTS[name]
     src = open(SRC).read()
-    assert src.count(old) == 1, "mutation anchor not found once: %r" % old
-    mutant = tmp_path / "mutant.c"
-    mutant.write_text(src.replace(old, new))
-    lib = tmp_path / "libmutant.so"
+    if src.count(old) != 1:
+        return None, "mutation anchor not found once: %r" % old
+    mutant = os.path.join(workdir, "mutant_%s.c" % name)
+    with open(mutant, "w") as f:
+        f.write(src.replace(old, new))
+    lib = os.path.join(workdir, "libmutant_%s.so" % name)
     subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fPIC", "-shared",
-                    "-fvisibility=hidden", str(mutant), "-o", str(lib), "-lm"], check=True)
-    env = dict(os.environ, SILUQUANT_ORACLE_LIB=str(lib))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] + PINS,
+                    "-fvisibility=hidden", mutant, "-o", lib, "-lm"], check=True)
+    first = [f for pre, f in FIRST.items() if name.startswith(pre)]
+    pins = first + [f for f in PINS if f not in first]
+    env = dict(os.environ, SILUQUANT_ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] + pins,
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
-    assert r.returncode != 0, "mutant %s passed every pin:\n%s" % (name, r.stdout[-2000:])
+    return r.returncode != 0, r.stdout[-2000:]
+
+
+@pytest.fixture(scope="module")
+def mutant_results(tmp_path_factory):
+    """Every mutant built and run against the pins, six at a time."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    workdir = str(tmp_path_factory.mktemp("mutants"))
+    with ThreadPoolExecutor(max_workers=6) as pool:
+        futures = {name: pool.submit(_run_mutant, name, workdir) for name in MUTANTS}
+        return {name: f.result() for name, f in futures.items()}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, mutant_results):
+    caught, out = mutant_results[name]
+    assert caught is not None, out
+    assert caught, "mutant %s passed every pin:\n%s" % (name, out)
