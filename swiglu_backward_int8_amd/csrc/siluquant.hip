@@ -108,6 +108,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(void* base, uint32_t
 __device__ __forceinline__ void store_stream(__amdgpu_buffer_rsrc_t buf, uint32_t offset, uint4 v) {
   __builtin_amdgcn_raw_buffer_store_b128((u32x4){v.x, v.y, v.z, v.w}, buf, offset, 0, kStreamStorePolicy);
 }
+// The transposed y_q_t codes are stored without the non-temporal bit (sc1
+// only): each tile writes 128-byte pieces of 128 different rows, and letting
+// them be cached, so that neighbouring tiles' pieces of a row meet before they
+// reach DRAM, measured 10% faster for the whole pass than streaming them
+// (287 us against 318 us at T = 16384, H = 11008).
+constexpr int kYqStorePolicy = 16;
+__device__ __forceinline__ void store_yq(__amdgpu_buffer_rsrc_t buf, uint32_t offset, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128((u32x4){v.x, v.y, v.z, v.w}, buf, offset, 0, kYqStorePolicy);
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -291,20 +300,20 @@ __device__ __forceinline__ Tile tile_at(int tile, int tiles_h, int64_t T, int64_
 __device__ __forceinline__ void store_yq_piece(__amdgpu_buffer_rsrc_t buf, uint32_t off, uint4 v, int bytes,
                                                int align) {
   if (bytes == 16 && align == 16) {
-    store_stream(buf, off, v);
+    store_yq(buf, off, v);
     return;
   }
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if (4 * j + 4 <= bytes && align >= 4) {
-      __builtin_amdgcn_raw_buffer_store_b32(w[j], buf, off + 4 * j, 0, kStreamStorePolicy);
+      __builtin_amdgcn_raw_buffer_store_b32(w[j], buf, off + 4 * j, 0, kYqStorePolicy);
     } else {
 #pragma unroll
       for (int b = 0; b < 4; ++b)
         if (4 * j + b < bytes)
           __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(w[j] >> (8 * b)), buf, off + 4 * j + b, 0,
-                                               kStreamStorePolicy);
+                                               kYqStorePolicy);
     }
   }
 }
@@ -601,7 +610,7 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
         const int phys = (id & 7) ^ ((h >> 3) & 7);
         const uint4 v = *reinterpret_cast<const uint4*>(s_yqt + h * kTile + phys * 16);
         if (cur.rows == kTile && yq_align == 16)
-          store_stream(yq_buf, lane_yq[step], v);
+          store_yq(yq_buf, lane_yq[step], v);
         else
           store_yq_piece(yq_buf, lane_yq[step], v, min(16, max(0, cur.rows - 16 * (id & 7))), yq_align);
       }
