@@ -1,0 +1,123 @@
+"""The largest shapes the entry points accept (GPU).
+
+The byte offsets inside a tile, the buffer record counts and the tile indices
+are 32-bit: these cases run each entry point at (or next to) the limit its
+header states and compare slices of the outputs with the oracle run on the
+same slices of the inputs.  Token rows, 128-token groups and 128-channel
+groups are independent of each other, so a slice of 256 tokens (or channels)
+aligned to 128 has exactly the oracle's outputs for those tokens (channels).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import swiglu_backward_int8_amd as sq
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available()
+    sq.prepare()
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _inputs(T, H, seed):
+    gen = torch.Generator(device=DEV).manual_seed(seed)
+    x = torch.randn((T, 2 * H), generator=gen, device=DEV).to(torch.bfloat16)
+    dy = (torch.randn((T, H), generator=gen, device=DEV) * 0.01).to(torch.bfloat16)
+    return x, dy
+
+
+def _equal(label, got, want):
+    for name, g, w in zip(("grad_input_q", "grad_input_s", "y_q_t", "y_s_t"), got, want):
+        gb = g.view(np.uint8 if g.dtype.itemsize == 1 else np.uint32)
+        wb = w.view(np.uint8 if w.dtype.itemsize == 1 else np.uint32)
+        assert g.shape == w.shape and np.array_equal(gb, wb), "%s %s: %d differ" % (label, name, int((gb != wb).sum()))
+
+
+def test_backward_at_the_token_limit():
+    # T = 2^23 (the largest T), H = 128: y_q_t rows are 8 MiB long
+    T, H = 1 << 23, 128
+    print("case T=2^23 H=128", flush=True)
+    x, dy = _inputs(T, H, 1)
+    gq, gs, yq, ys = sq.empty_outputs(T, H, DEV)
+    sq.silu_dot_fwd_bwd_quant_fuse(x, dy, gq, gs, yq, ys)
+    torch.cuda.synchronize()
+    for t0 in (0, T // 2 + 128, T - 256):
+        want = oracle.silu_dot_fwd_bwd_quant_fuse(_bits(x[t0:t0 + 256]), _bits(dy[t0:t0 + 256]))
+        got = (gq[t0:t0 + 256].cpu().numpy(), gs[t0:t0 + 256].cpu().numpy(),
+               yq[:, t0:t0 + 256].cpu().numpy(), ys[:, t0 // 128:t0 // 128 + 2].cpu().numpy())
+        _equal("T=2^23 tokens %d.." % t0, got, want)
+    del x, dy, gq, gs, yq, ys
+    torch.cuda.empty_cache()
+
+
+def test_backward_at_the_channel_limit():
+    # H = 2^22 (the largest H), T = 128: a lane's offset in x reaches 2^31 - 16
+    T, H = 128, 1 << 22
+    print("case T=128 H=2^22", flush=True)
+    x, dy = _inputs(T, H, 2)
+    gq, gs, yq, ys = sq.empty_outputs(T, H, DEV)
+    sq.silu_dot_fwd_bwd_quant_fuse(x, dy, gq, gs, yq, ys)
+    torch.cuda.synchronize()
+    for h0 in (0, H // 2 + 128, H - 256):
+        xs = torch.cat([x[:, h0:h0 + 256], x[:, H + h0:H + h0 + 256]], dim=1)
+        want = oracle.silu_dot_fwd_bwd_quant_fuse(_bits(xs), _bits(dy[:, h0:h0 + 256]))
+        g0, g1 = h0 // 128, (H + h0) // 128
+        got = (torch.cat([gq[:, h0:h0 + 256], gq[:, H + h0:H + h0 + 256]], dim=1).cpu().numpy(),
+               torch.cat([gs[:, g0:g0 + 2], gs[:, g1:g1 + 2]], dim=1).cpu().numpy(),
+               yq[h0:h0 + 256].cpu().numpy(), ys[h0:h0 + 256].cpu().numpy())
+        _equal("H=2^22 channels %d.." % h0, got, want)
+    del x, dy, gq, gs, yq, ys
+    torch.cuda.empty_cache()
+
+
+def test_backward_past_the_limits_is_rejected():
+    # shapes past the limits are refused before any device work
+    for T, H in (((1 << 23) + 1, 128), (128, (1 << 22) + 128)):
+        assert sq.raw_call(1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40, 6 << 40, T, H, 128, 0) == 2
+
+
+def test_forward_at_the_channel_limit():
+    T, H = 128, 1 << 22
+    print("case forward T=128 H=2^22", flush=True)
+    x, _ = _inputs(T, H, 3)
+    yq = torch.empty((T, H), dtype=torch.int8, device=DEV)
+    ys = torch.empty((T, H // 128), dtype=torch.float32, device=DEV)
+    sq.silu_fwd_quant(x, yq, ys)
+    torch.cuda.synchronize()
+    for h0 in (0, H - 256):
+        xs = torch.cat([x[:, h0:h0 + 256], x[:, H + h0:H + h0 + 256]], dim=1)
+        wq, ws = oracle.silu_fwd_quant(_bits(xs))
+        assert np.array_equal(yq[:, h0:h0 + 256].cpu().numpy(), wq)
+        assert np.array_equal(ys[:, h0 // 128:h0 // 128 + 2].cpu().numpy().view(np.uint32), ws.view(np.uint32))
+    del x, yq, ys
+    torch.cuda.empty_cache()
+
+
+def test_gemm_at_the_k_limit():
+    # K = 2^22 (the largest K): a tile's rows of A span 2^29 bytes of one buffer
+    M, N, K = 256, 256, 1 << 22
+    print("case GEMM K=2^22", flush=True)
+    gen = torch.Generator(device=DEV).manual_seed(4)
+    A = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=DEV, generator=gen)
+    B = torch.randint(-127, 128, (N, K), dtype=torch.int8, device=DEV, generator=gen)
+    sA = torch.rand((M, K // 128), device=DEV, generator=gen) * 1e-4
+    sB = torch.rand((N, K // 128), device=DEV, generator=gen) * 1e-4
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    sq.i8_gemm_group_scaled(A, sA, B, sB, C)
+    torch.cuda.synchronize()
+    rows, cols = [0, 129, 255], [1, 200, 255]
+    want, want_abs = oracle.i8_gemm_group_scaled(A[rows].cpu().numpy(), sA[rows].cpu().numpy(),
+                                                 B[cols].cpu().numpy(), sB[cols].cpu().numpy())
+    got = C[rows][:, cols].cpu().numpy().astype(np.float64)
+    bound = (K // 128 + 2) * 2.0**-24 * want_abs
+    assert np.all(np.abs(got - want) <= bound), (got, want)
