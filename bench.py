@@ -52,10 +52,12 @@ def measured_traffic(workload: str, src: str = KERNEL_SRC):
     return entry.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x, dy, w, min_seconds: float = 10.0, max_calls: int = 5, fp8: bool = False):
+def cpu_baseline(x, dy, w, min_seconds: float = 10.0, max_calls: int = 5, fp8: bool = False,
+                 forward: bool = False):
     """The oracle, single-threaded, on the whole workload: calls are repeated
     until at least min_seconds of CPU work (at most max_calls); the rate is the
-    algorithmic bytes of all calls over their total time."""
+    algorithmic bytes of all calls over their total time (the op's own bytes:
+    the backward pass, its E4M3 variant, or the forward quantiser)."""
     import numpy as np
     import torch
 
@@ -63,16 +65,20 @@ def cpu_baseline(x, dy, w, min_seconds: float = 10.0, max_calls: int = 5, fp8: b
     import swiglu_backward_int8_amd as sq
 
     xb = x.view(torch.int16).cpu().numpy().view(np.uint16)
-    db = dy.view(torch.int16).cpu().numpy().view(np.uint16)
+    db = None if forward else dy.view(torch.int16).cpu().numpy().view(np.uint16)
     oracle.build(force=False)
     calls, total = 0, 0.0
     while calls < max_calls and (calls == 0 or total < min_seconds):
         t = time.perf_counter()
-        (oracle.silu_dot_fwd_bwd_quant_fuse_fp8 if fp8 else oracle.silu_dot_fwd_bwd_quant_fuse)(xb, db)
+        if forward:
+            oracle.silu_fwd_quant(xb)
+        else:
+            (oracle.silu_dot_fwd_bwd_quant_fuse_fp8 if fp8 else oracle.silu_dot_fwd_bwd_quant_fuse)(xb, db)
         total += time.perf_counter() - t
         calls += 1
+    nbytes = sq.forward_bytes(w.T, w.H) if forward else sq.algorithmic_bytes(w.T, w.H)
     return {
-        "value": round(calls * sq.algorithmic_bytes(w.T, w.H) / total / 1e9, 4),
+        "value": round(calls * nbytes / total / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
@@ -339,9 +345,9 @@ def main():
     }
     if args.probes:
         out["probes"] = stream_probes(dev)
-    if not args.no_cpu_baseline and not forward:
+    if not args.no_cpu_baseline:
         x, dy, _ = bufs[0]
-        out["cpu_baseline"] = cpu_baseline(x, dy, w, fp8=fp8)
+        out["cpu_baseline"] = cpu_baseline(x, dy, w, fp8=fp8, forward=forward)
     print(json.dumps(out), flush=True)
 
 
