@@ -27,7 +27,7 @@ extern "C" {
 enum siluquant_status {
   SILUQUANT_OK = 0,
   SILUQUANT_ERR_NULL_PTR = 1,      /* a buffer pointer is NULL while T*H > 0 */
-  SILUQUANT_ERR_BAD_SHAPE = 2,     /* T < 0, H < 0, H not a multiple of the group, or too large */
+  SILUQUANT_ERR_BAD_SHAPE = 2,     /* T < 0, H < 0, H not a multiple of 8 (K of 128), or too large */
   SILUQUANT_ERR_BAD_GROUP = 3,     /* a group size the entry point does not take */
   SILUQUANT_ERR_MISALIGNED = 4,    /* x, grad_y, grad_input_q, y_q_t not 16-byte aligned,
                                       or a scale buffer not 4-byte aligned */
@@ -45,8 +45,10 @@ enum siluquant_status {
  *   grad_y  bf16 [T, H]  row-major; the gradient of y = silu(gate) * up.
  * Outputs (fully overwritten; every element written):
  *   grad_input_q  int8 [T, 2H]       [d_gate | d_up] quantised per row, in groups of
- *                                    128 contiguous channels (d_gate groups first);
- *   grad_input_s  fp32 [T, 2H/128]   one scale per such group;
+ *                                    128 consecutive positions of the 2H-long row
+ *                                    (the last group of a row has the 2H % 128
+ *                                    positions that remain);
+ *   grad_input_s  fp32 [T, ceil(2H/128)]  one scale per such group;
  *   y_q_t         int8 [H, T]        y transposed, quantised in groups of 128
  *                                    consecutive tokens along each row (the last
  *                                    group of a T that is not a multiple of 128
@@ -62,12 +64,16 @@ enum siluquant_status {
  *   -128 is never produced.  Inputs must be finite and keep y, d_gate and d_up
  *   finite.
  * Group size: `group` is 128 (the page's default), 64 or 32; the scale tensors
- *   are then grad_input_s fp32 [T, 2H/group] and y_s_t fp32 [H, ceil(T/group)].
- *   Groups of 2H-row channels never straddle d_gate and d_up because H must be
- *   a multiple of `group`.  Any other group returns SILUQUANT_ERR_BAD_GROUP.
- * Sizes: any T >= 0, H >= 0 a multiple of `group` (T == 0 or H == 0 is a
- *   no-op that returns SILUQUANT_OK), T <= 2^23, H <= 2^22.  y_q_t is written
- *   with 16-byte stores when T % 16 == 0; other T work, with narrower stores.
+ *   are then grad_input_s fp32 [T, ceil(2H/group)] and y_s_t fp32
+ *   [H, ceil(T/group)].  When H is not a multiple of `group`, the group at
+ *   row position group * floor(H/group) holds the last H % group channels of
+ *   d_gate and the first channels of d_up.  Any other group returns
+ *   SILUQUANT_ERR_BAD_GROUP.
+ * Sizes: any T >= 0, H >= 0 a multiple of 8 (every row then starts on 16
+ *   bytes; T == 0 or H == 0 is a no-op that returns SILUQUANT_OK), T <= 2^23,
+ *   H <= 2^22.  y_q_t is written with 16-byte stores when T % 16 == 0; other T
+ *   work, with narrower stores.  H a multiple of `group` takes the aligned
+ *   kernel; other H a second kernel with two work items per tile.
  * Ownership: the caller allocates and owns every buffer; the library keeps no
  *   pointer after the call returns.  Buffers must not overlap.
  * Asynchrony: the work is enqueued on `stream` and the call returns without
@@ -118,10 +124,11 @@ int silu_dot_fwd_bwd_quant_fuse_fp8(const void* x, const void* grad_y, void* gra
  *   x           bf16 [T, 2H] as above (read only; 16-byte aligned)
  *   row_weight  fp32 [T], or NULL for weight 1 (4-byte aligned)
  *   y_q         int8 [T, H]       codes (16-byte aligned)
- *   y_s         fp32 [T, H/group] one scale per group (4-byte aligned)
+ *   y_s         fp32 [T, ceil(H/group)] one scale per group (4-byte aligned)
  *   y_bf16      bf16 [T, H] the rounded y, or NULL (16-byte aligned)
- *   (y_s is [T, H/group] for group 128, 64 or 32.)
- * Sizes: any T >= 0 (T <= 2^31), H a multiple of the group (H <= 2^22).
+ * Sizes: any T >= 0 (T <= 2^31), H a multiple of 8 (H <= 2^22); the last group
+ *   of a row has the H % group channels that remain when H is not a multiple
+ *   of the group.
  * Same ownership, asynchrony and error conventions as above.
  */
 int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q, float* y_s, void* y_bf16, int64_t T,

@@ -103,7 +103,8 @@ def silu_dot_fwd_bwd_quant_fuse(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_
     """Recompute y = silu(gate) * up from x = [gate | up] and write the int8 codes
     and fp32 scales of [d_gate, d_up] (per row, groups of group_size channels)
     and of y^T (groups of group_size tokens) into the given output tensors.
-    group_size is 128 (the default), 64 or 32, and H must be a multiple of it.
+    group_size is 128 (the default), 64 or 32; H must be a multiple of 8, and
+    when it is not a multiple of group_size one group straddles d_gate and d_up.
     Enqueued on the current stream of x's device; returns None."""
     _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size, fp8=False)
 
@@ -123,7 +124,7 @@ def _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size: i
         raise ValueError("x must be [T, 2H] and grad_y [T, H]; got %s and %s" % (tuple(x.shape), tuple(grad_y.shape)))
     if group_size not in GROUPS:
         raise ValueError("group_size must be one of %s" % (GROUPS,))
-    want = output_shapes(T, H, group_size) if H % group_size == 0 else None
+    want = output_shapes(T, H, group_size)
     checks = [
         ("x", x, torch.bfloat16, (T, 2 * H)),
         ("grad_y", grad_y, torch.bfloat16, (T, H)),
@@ -154,7 +155,8 @@ def _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size: i
 def silu_fwd_quant(x, y_q, y_s, row_weight=None, y_bf16=None, group_size: int = GROUP):
     """Forward SwiGLU with row-wise int8 quantisation: y = bf16((silu(gate) * up)
     * row_weight[t]) from x = [gate | up] [T, 2H]; writes y_q int8 [T, H] and
-    y_s fp32 [T, H/group_size] (group_size 128, 64 or 32; H a multiple of it),
+    y_s fp32 [T, ceil(H/group_size)] (group_size 128, 64 or 32; H a multiple of
+    8, the last group of a row partial when H is not a multiple of group_size),
     and y_bf16 [T, H] if given.  Enqueued on the current stream of x's device;
     returns None."""
     import torch
@@ -164,13 +166,11 @@ def silu_fwd_quant(x, y_q, y_s, row_weight=None, y_bf16=None, group_size: int = 
     T, H = int(x.shape[0]), int(x.shape[1]) // 2
     if group_size not in GROUPS:
         raise ValueError("group_size must be one of %s" % (GROUPS,))
-    if H % group_size:
-        raise ValueError("H must be a multiple of group_size")
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU; got %s" % dev)
     checks = [("x", x, torch.bfloat16, (T, 2 * H)), ("y_q", y_q, torch.int8, (T, H)),
-              ("y_s", y_s, torch.float32, (T, H // group_size))]
+              ("y_s", y_s, torch.float32, (T, -(-H // group_size)))]
     if row_weight is not None:
         checks.append(("row_weight", row_weight, torch.float32, (T,)))
     if y_bf16 is not None:
@@ -230,7 +230,7 @@ def i8_gemm_group_scaled(A, sA, B, sB, C, b_rows_per_scale: int = 1, group_size:
 def forward_bytes(T: int, H: int, with_bf16: bool = False, with_weight: bool = False, group: int = GROUP) -> int:
     """Bytes the forward quantiser must move: x (4 per pair) in, codes (1) and
     one fp32 scale per `group` codes out, plus bf16 y (2) and the row weights."""
-    return 5 * T * H + 4 * (T * H // group) + (2 * T * H if with_bf16 else 0) + (4 * T if with_weight else 0)
+    return 5 * T * H + 4 * T * (-(-H // group)) + (2 * T * H if with_bf16 else 0) + (4 * T if with_weight else 0)
 
 
 def empty_outputs(T: int, H: int, device, group: int = GROUP, fp8: bool = False):

@@ -8,11 +8,13 @@
 // arithmetic contract is spelled out in include/siluquant.h.
 //
 // Design (one kernel, one pass over HBM):
-//   * one 512-thread workgroup per 128-token x 128-channel tile; every group of
-//     both quantisation axes lies inside one tile, so no workgroup ever waits on
-//     another;
-//   * lane (q, p) = (tid / 16, tid % 16) owns tokens 4q..4q+3 and channels
-//     8p..8p+7: each of its 12 loads is 16 bytes and a wave's load covers four
+//   * persistent 1024-thread workgroups, one per CU, walk 128-token x
+//     128-channel tiles; every group of both quantisation axes lies inside one
+//     tile, so no workgroup ever waits on another (when H is not a multiple of
+//     the group, silu_quant_bwd_shift_kernel keeps this with shifted windows
+//     for the d_up half);
+//   * lane (q, p) = (tid / 16, tid % 16) owns tokens 2q, 2q+1 and channels
+//     8p..8p+7: each of its loads is 16 bytes and a wave's load covers four
 //     whole 256-byte row segments;
 //   * sigmoid comes from a 31 KB table in LDS indexed by the bf16 bits of the
 //     gate.  Gates are bf16, so only 7,223 inputs give a sigmoid outside
@@ -88,6 +90,7 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // Every input byte is read once and every output byte written once, so all
 // global traffic is marked non-temporal (streaming): it does not displace the
@@ -249,36 +252,51 @@ __device__ __forceinline__ uint2 codes8(const uint32_t (&w)[4], float inv) {
                     codes4<F, kSafe>(bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3]), inv));
 }
 
-struct TileIn {
-  uint4 g[kRows], u[kRows], d[kRows];
+template <int R>
+struct TileInR {
+  uint4 g[R], u[R], d[R];
 };
+using TileIn = TileInR<kRows>;
 
 // The tile base is uniform (scalar registers) and the lane's byte offset is a
 // fixed 32-bit value.  In the last token block of a ragged T only `rows` of
 // the 128 rows exist, and in the last channel block of an H that is not a
 // multiple of 128 only `cols` channels (lane_live: 8 p < cols); the missing
 // values read as zeros, whose y, d_gate and d_up are zero and so never raise
-// a maximum.
-__device__ __forceinline__ void load_tile(TileIn& in, const char* xt, const char* dyt, uint32_t lane_x,
+// a maximum.  The loads are non-temporal unless kNt is false (inputs that a
+// neighbouring workgroup reads again soon).
+__device__ __forceinline__ uint4 load_plain(const void* ptr) { return *reinterpret_cast<const uint4*>(ptr); }
+template <bool kNt = true, int R>
+__device__ __forceinline__ void load_tile(TileInR<R>& in, const char* xt, const char* dyt, uint32_t lane_x,
                                           uint32_t lane_dy, int64_t x_row_bytes, int64_t dy_row_bytes, int rows,
                                           bool lane_live, int q) {
   const bool full = rows == kTile;
 #pragma unroll
-  for (int i = 0; i < kRows; ++i) {
-    if (lane_live && (full || kRows * q + i < rows)) {
-      in.g[i] = load_stream(xt + i * x_row_bytes + lane_x);
-      in.u[i] = load_stream(xt + i * x_row_bytes + (x_row_bytes >> 1) + lane_x);
-      in.d[i] = load_stream(dyt + i * dy_row_bytes + lane_dy);
+  for (int i = 0; i < R; ++i) {
+    if (lane_live && (full || R * q + i < rows)) {
+      in.g[i] = kNt ? load_stream(xt + i * x_row_bytes + lane_x) : load_plain(xt + i * x_row_bytes + lane_x);
+      in.u[i] = kNt ? load_stream(xt + i * x_row_bytes + (x_row_bytes >> 1) + lane_x)
+                    : load_plain(xt + i * x_row_bytes + (x_row_bytes >> 1) + lane_x);
+      in.d[i] = kNt ? load_stream(dyt + i * dy_row_bytes + lane_dy) : load_plain(dyt + i * dy_row_bytes + lane_dy);
     } else {
       in.g[i] = in.u[i] = in.d[i] = make_uint4(0, 0, 0, 0);
     }
   }
 }
 
+// Raw buffer loads: 32-bit offsets from a uniform base, and an offset past the
+// record count reads zeros without touching memory.
+constexpr int kStreamLoadPolicy = 2;  // nt
+__device__ __forceinline__ uint4 load_buf(__amdgpu_buffer_rsrc_t buf, uint32_t offset) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(buf, offset, 0, kStreamLoadPolicy);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 struct Tile {
   int tb, hb;
   int rows;  // tokens of this tile that exist: 128 except in the last block of a ragged T
   int cols;  // channels that exist: 128 except in the last block of a ragged H
+             // (zero or less in a block that holds only a shifted window)
   int64_t t0, h0;
 };
 
@@ -321,12 +339,13 @@ __device__ __forceinline__ void store_yq_piece(__amdgpu_buffer_rsrc_t buf, uint3
 // The elementwise part of one tile for one lane: packed bf16 y, d_gate and
 // d_up ([row][word], channel pairs per word), plus the lane's partial maxima of
 // unrounded magnitudes per row of d_gate and d_up (rg, ru) and per channel of
-// y (cm).
-__device__ __forceinline__ void elementwise(const TileIn& in, const float* s_tab, uint32_t (&Yp)[kRows][4],
-                                            uint32_t (&Gp)[kRows][4], uint32_t (&Up)[kRows][4],
-                                            float (&rg)[kRows], float (&ru)[kRows], float (&cm)[8]) {
+// y (cm).  Without kUp, d_up and ru are left alone.
+template <bool kUp = true, int R>
+__device__ __forceinline__ void elementwise(const TileInR<R>& in, const float* s_tab, uint32_t (&Yp)[R][4],
+                                            uint32_t (&Gp)[R][4], uint32_t (&Up)[R][4], float (&rg)[R],
+                                            float (&ru)[R], float (&cm)[8]) {
 #pragma unroll
-  for (int i = 0; i < kRows; i += 2) {
+  for (int i = 0; i < R; i += 2) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       float yv[2][2];
@@ -341,13 +360,13 @@ __device__ __forceinline__ void elementwise(const TileIn& in, const float* s_tab
         pair_f32(s1, bf16_hi(gw), bf16_hi(uw), bf16_hi(dw), y1, dg1, du1);
         Yp[i + r][k] = pack_bf16(y0, y1);
         Gp[i + r][k] = pack_bf16(dg0, dg1);
-        Up[i + r][k] = pack_bf16(du0, du1);
+        if (kUp) Up[i + r][k] = pack_bf16(du0, du1);
         if (k == 0) {
           rg[i + r] = fmaxf(fabsf(dg0), fabsf(dg1));
-          ru[i + r] = fmaxf(fabsf(du0), fabsf(du1));
+          if (kUp) ru[i + r] = fmaxf(fabsf(du0), fabsf(du1));
         } else {
           rg[i + r] = amax3(rg[i + r], dg0, dg1);
-          ru[i + r] = amax3(ru[i + r], du0, du1);
+          if (kUp) ru[i + r] = amax3(ru[i + r], du0, du1);
         }
         yv[r][0] = y0;
         yv[r][1] = y1;
@@ -363,12 +382,54 @@ __device__ __forceinline__ void elementwise(const TileIn& in, const float* s_tab
   }
 }
 
-// Position of the kRows-byte piece q of transposed row h (128 bytes) in the
+// A shifted window of the second half (silu_quant_bwd_shift_kernel): d_up =
+// grad_y * silu(gate), the same operations as pair_f32, from in.g and in.d.
+// With kTail (window 0), lanes with tail set hold the last channels of d_gate
+// instead, from in.u as well: one chain serves both, d_gate = ((d u) s) m and
+// d_up = d (g s), with the operands picked per lane, in pair_f32's order.
+__device__ __forceinline__ float window_value(float s, float g, float u, float d, bool tail) {
+  const float a = tail ? d * u : g * s;  // d_gate's d u, or silu
+  const float b = tail ? a * s : d * a;  // d_gate's (d u) s, or d_up
+  const float c = 1.0f - s;
+  const float k = g * c;
+  const float m = 1.0f + k;
+  return tail ? b * m : b;
+}
+
+template <bool kTail, int R>
+__device__ __forceinline__ void elementwise_window(const TileInR<R>& in, bool tail, const float* s_tab,
+                                                   uint32_t (&Vp)[R][4], float (&rv)[R]) {
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t gw = (&in.g[i].x)[k], dw = (&in.d[i].x)[k];
+      uint32_t olo, ohi;
+      sigma_offsets2(gw, olo, ohi);
+      const float s0 = lds_f32(s_tab, olo), s1 = lds_f32(s_tab, ohi);
+      float v0, v1;
+      if constexpr (kTail) {
+        const uint32_t uw = (&in.u[i].x)[k];
+        v0 = window_value(s0, bf16_lo(gw), bf16_lo(uw), bf16_lo(dw), tail);
+        v1 = window_value(s1, bf16_hi(gw), bf16_hi(uw), bf16_hi(dw), tail);
+      } else {
+        const float silu0 = bf16_lo(gw) * s0, silu1 = bf16_hi(gw) * s1;
+        v0 = bf16_lo(dw) * silu0;
+        v1 = bf16_hi(dw) * silu1;
+      }
+      Vp[i][k] = pack_bf16(v0, v1);
+      rv[i] = k == 0 ? fmaxf(fabsf(v0), fabsf(v1)) : amax3(rv[i], v0, v1);
+    }
+  }
+}
+
+// Position of the R-byte piece q of transposed row h (128 bytes) in the
 // LDS transpose buffer.  16-byte chunks are swapped by (h >> 3) & 7: a wave's
 // writes (16 rows 8 apart) spread over the banks, and every chunk stays
 // contiguous for the 16-byte read-back.
+template <int R>
 __device__ __forceinline__ int yqt_byte(int h, int q) {
-  const int b = kRows * q;
+  const int b = R * q;
   return h * kTile + ((((b >> 4) ^ ((h >> 3) & 7)) << 4) | (b & 15));
 }
 
@@ -386,36 +447,50 @@ __device__ __forceinline__ uint4 pair_rows16(uint2 r0, uint2 r1, bool odd) {
   return odd ? make_uint4(recv.x, recv.y, r1.x, r1.y) : make_uint4(r0.x, r0.y, recv.x, recv.y);
 }
 
-// gq_buf covers the tile's 128 rows of grad_input_q (its base is the tile's
-// first code); lane_gq addresses row kRows*q + (p & 1), channel 8 * (p & ~1).
+// Codes of one half of the row groups for the lane's rows, as whole 16-byte
+// pieces per lane pair: gq_buf covers the tile's rows of grad_input_q, lane
+// addresses row R*q + (p & 1) at the pair's 16 codes, or lies past the
+// records (the stores drop).
+template <Fmt F, bool kSafe, int R>
+__device__ __forceinline__ void store_half_codes(const uint32_t (&Vp)[R][4], const float (&inv)[R],
+                                                 __amdgpu_buffer_rsrc_t gq_buf, uint32_t lane, uint32_t gq_row_bytes,
+                                                 int p) {
+  const bool odd = p & 1;
+#pragma unroll
+  for (int i = 0; i < R; i += 2)
+    store_stream(gq_buf, i * gq_row_bytes + lane,
+                 pair_rows16(codes8<kSafe, F>(Vp[i], inv[i]), codes8<kSafe, F>(Vp[i + 1], inv[i + 1]), odd));
+}
+
+// y codes, transposed, into the LDS transpose buffer: channel 8p + j gets the
+// lane's R tokens.
+template <Fmt F, bool kSafe, int R>
+__device__ __forceinline__ void stage_y_codes(const uint32_t (&Yp)[R][4], const float (&iy)[8], char* s_yqt, int p,
+                                              int q) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float v[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) v[i] = (j & 1) ? bf16_hi(Yp[i][j >> 1]) : bf16_lo(Yp[i][j >> 1]);
+    char* dst = s_yqt + yqt_byte<R>(8 * p + j, q);
+    if constexpr (R == 4)
+      *reinterpret_cast<uint32_t*>(dst) = codes4<F, kSafe>(v[0], v[1], v[2], v[3], iy[j]);
+    else
+      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)codes2<F, kSafe>(v[0], v[1], iy[j]);
+  }
+}
+
+// Both halves' codes and the staged y codes of a tile.  lane_gq addresses the
+// lane pair's d_gate codes (d_up's lie H further), or lies past the records.
 template <Fmt F, bool kSafe>
 __device__ __forceinline__ void quantise_rows_and_y(const uint32_t (&Gp)[kRows][4], const uint32_t (&Up)[kRows][4],
                                                     const uint32_t (&Yp)[kRows][4], const float (&idg)[kRows],
                                                     const float (&idu)[kRows], const float (&iy)[8],
                                                     __amdgpu_buffer_rsrc_t gq_buf, uint32_t lane_gq,
                                                     uint32_t gq_row_bytes, uint32_t H, char* s_yqt, int p, int q) {
-  const bool odd = p & 1;
-#pragma unroll
-  for (int i = 0; i < kRows; i += 2) {
-    // lane_gq is past the buffer's records for channels past H: those stores drop
-    const uint32_t row = i * gq_row_bytes + lane_gq;
-    store_stream(gq_buf, row,
-                 pair_rows16(codes8<kSafe, F>(Gp[i], idg[i]), codes8<kSafe, F>(Gp[i + 1], idg[i + 1]), odd));
-    store_stream(gq_buf, row + H,
-                 pair_rows16(codes8<kSafe, F>(Up[i], idu[i]), codes8<kSafe, F>(Up[i + 1], idu[i + 1]), odd));
-  }
-  // y codes, transposed: channel 8p + j gets the lane's kRows tokens.
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float v[kRows];
-#pragma unroll
-    for (int i = 0; i < kRows; ++i) v[i] = (j & 1) ? bf16_hi(Yp[i][j >> 1]) : bf16_lo(Yp[i][j >> 1]);
-    char* dst = s_yqt + yqt_byte(8 * p + j, q);
-    if constexpr (kRows == 4)
-      *reinterpret_cast<uint32_t*>(dst) = codes4<F, kSafe>(v[0], v[1], v[2], v[3], iy[j]);
-    else
-      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)codes2<F, kSafe>(v[0], v[1], iy[j]);
-  }
+  store_half_codes<F, kSafe>(Gp, idg, gq_buf, lane_gq, gq_row_bytes, p);
+  store_half_codes<F, kSafe>(Up, idu, gq_buf, lane_gq + H, gq_row_bytes, p);
+  stage_y_codes<F, kSafe>(Yp, iy, s_yqt, p, q);
 }
 
 // Persistent kernel: workgroup b walks tiles first, first + stride, ... < end.
@@ -624,8 +699,281 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
 }
 
 // ---------------------------------------------------------------------------
+// H not a multiple of the group: r = H mod kG > 0, with H a multiple of 8 so
+// that every row starts on 16 bytes.  The row groups run over the 2H-long row
+// [d_gate | d_up]: d_gate's whole groups (channels below H - r) still line up
+// with the 128-channel blocks, but d_up's groups are shifted by r against them
+// and one group straddles the two halves.  The second half is therefore taken
+// over windows of its own: window hb holds positions (H - r) + h0 + [0, 128)
+// of the row, i.e. d_up at channels h0 - r + [0, 128), except that in window 0
+// the first r positions are the last r channels of d_gate.  The window's
+// groups line up with it again, and the straddling group lies in window 0.
+//
+// The workgroups of each XCD split into two teams that walk the XCD's tiles
+// in order: the first does y, d_gate and the y^T codes from the tile's gate,
+// up and grad_y, like silu_quant_bwd_kernel; the second does the windows
+// from gate and grad_y (and up where a window holds d_gate).  The teams are
+// sized to the work of their tiles, so that they move through the tiles at
+// about the same pace and the windows' loads mostly hit L2 lines the first
+// team has just read (its loads are plain, not non-temporal, for that: 546 us
+// against 680 us at T = 16384, H = 11000).  Each workgroup runs one kind of
+// work in its own loop, so neither needs more registers than the aligned
+// kernel; one workgroup taking both halves of a tile needs more than the 128
+// a lane has at 16 waves per CU, and spilled versions measured slower still.
+// The blocks run to ceil((H + r) / 128), so the last may hold a window only.
+template <Fmt F, int kG>
+__global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void silu_quant_bwd_shift_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ grad_y, int8_t* __restrict__ grad_input_q,
+    float* __restrict__ grad_input_s, int8_t* __restrict__ y_q_t, float* __restrict__ y_s_t, int64_t T, int64_t H,
+    int tiles_h, int tiles, int r, int first_team) {
+  // kG-wide groups: kSub of them per 128 channels of a row and per 128 tokens
+  // of a channel.  The inverses of row group (sub, row) sit at
+  // s_inv[sub * 128 + row] and, for the first kind of work, those of column
+  // group (sub, channel) at s_inv[kHalfGroups + sub * 128 + channel].
+  static_assert(kG == 32 || kG == 64 || kG == 128, "group sizes that divide the tile");
+  constexpr int kSub = kTile / kG;
+  constexpr int kHalfGroups = kTile * kSub, kColGroups = kTile * kSub;
+  constexpr int kLanesPerRowGroup = kG / 8;
+  constexpr int kPairsPerColGroup = kG / kRows;
+  static_assert(kHalfGroups + kColGroups <= kInvFloats, "inverse slots");
+
+  __shared__ __align__(16) float lds[kLdsFloats];
+  float* s_tab = lds;
+  float* s_rowpart = lds + kSigEntries;
+  float* s_colpart = s_rowpart + kRowPartFloats;
+  float* s_inv = s_colpart + kColPartFloats;
+  char* s_yqt = reinterpret_cast<char*>(s_rowpart);
+  int* s_flag = reinterpret_cast<int*>(s_inv + kInvFloats);
+
+  const int tid = threadIdx.x;
+  const int p = tid & 15;
+  const int q = tid >> 4;
+
+  const int64_t x_row_bytes = 4 * H, dy_row_bytes = 2 * H, gq_row_bytes = 2 * H;
+  const int64_t row_groups = (2 * H + kG - 1) / kG, col_groups = (T + kG - 1) / kG;
+  const int64_t lim_a = H - r, lim_b = H + r;  // channel ends of d_gate's whole groups and of the windows
+  const int yq_align = (T & 15) == 0 ? 16 : (T & 3) == 0 ? 4 : 1;
+  const uint32_t lane_x = (uint32_t)(kRows * q * x_row_bytes + 16 * p);
+  const uint32_t lane_dy = (uint32_t)(kRows * q * dy_row_bytes + 16 * p);
+  const uint32_t lane_gq = (uint32_t)((kRows * q + (p & 1)) * gq_row_bytes + 8 * (p & ~1));
+  constexpr uint32_t kDropped = 0x80000000u;  // past any record count
+  constexpr int kOutSteps = kTile * kTile / 16 / kThreads;
+  const int sub_row = p / kLanesPerRowGroup, sub_col = q / kPairsPerColGroup;
+  float* rp = s_rowpart + p * kRowPartStride + kRows * q;
+
+  // With first_team > 0 (the grid a multiple of 8), the workgroups of one XCD
+  // (every 8th) take one contiguous eighth of the tiles; the first first_team
+  // of them form the first team, the rest the second.  With first_team == 0
+  // (an even grid) consecutive pairs of workgroups walk all tiles, one of each
+  // team.
+  int tile, end, stride, role;
+  if (first_team > 0) {
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
+    role = local >= first_team;
+    tile = (int)(((int64_t)tiles * xcd) >> 3) + (role ? local - first_team : local);
+    end = (int)(((int64_t)tiles * (xcd + 1)) >> 3);
+    stride = role ? per_xcd - first_team : first_team;
+  } else {
+    tile = blockIdx.x >> 1;
+    end = tiles;
+    stride = gridDim.x >> 1;
+    role = blockIdx.x & 1;
+  }
+
+  const char* xb = reinterpret_cast<const char*>(x);
+  const char* dyb = reinterpret_cast<const char*>(grad_y);
+  auto load_first = [&](TileIn& in, const Tile& c) {
+    load_tile<false>(in, xb + (c.t0 * x_row_bytes + 2 * c.h0), dyb + (c.t0 * dy_row_bytes + 2 * c.h0), lane_x, lane_dy,
+              x_row_bytes, dy_row_bytes, c.rows, 8 * p < c.cols, q);
+  };
+  // A window's inputs, through buffer resources over the tile's existing rows
+  // (rows past a ragged T and lanes past the window read zeros).  Outside
+  // window 0 the window starts r channels before the block; in window 0, lanes
+  // 8p < r read d_gate's last channels (and their up values) and the others
+  // start at channel 8p - r.  Offsets stay non-negative: a lane with 8p >= r
+  // has lane_x >= 16p >= 2r.
+  auto load_window = [&](TileIn& in, const Tile& c) {
+    const bool first = c.hb == 0, tail = first && 8 * p < r;
+    const int64_t back = first ? 0 : 2 * r;
+    const uint32_t adj = !first ? 0u : tail ? (uint32_t)(2 * (H - r)) : (uint32_t)(-2 * r);
+    const bool live = c.h0 + 8 * p < lim_b;
+    const uint32_t off_x = live ? lane_x + adj : kDropped, off_dy = live ? lane_dy + adj : kDropped;
+    const uint32_t off_u = tail ? off_x + (uint32_t)(x_row_bytes >> 1) : kDropped;
+    const __amdgpu_buffer_rsrc_t xbuf =
+        buffer_of(const_cast<char*>(xb) + (c.t0 * x_row_bytes + 2 * c.h0 - back), (uint32_t)(c.rows * x_row_bytes));
+    const __amdgpu_buffer_rsrc_t dybuf = buffer_of(const_cast<char*>(dyb) + (c.t0 * dy_row_bytes + 2 * c.h0 - back),
+                                                   (uint32_t)(c.rows * dy_row_bytes));
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      in.g[i] = load_buf(xbuf, off_x + (uint32_t)(i * x_row_bytes));
+      in.d[i] = load_buf(dybuf, off_dy + (uint32_t)(i * dy_row_bytes));
+      in.u[i] = first ? load_buf(xbuf, off_u + (uint32_t)(i * x_row_bytes)) : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  {
+    const float4* src = reinterpret_cast<const float4*>(g_sigma_tab);
+    float4* dst = reinterpret_cast<float4*>(s_tab);
+    for (int i = tid; i < kSigEntries / 4; i += kThreads) dst[i] = src[i];
+  }
+  __syncthreads();
+
+  TileIn in, in_next;
+  Tile cur = tile_at(tile < end ? tile : 0, tiles_h, T, H);
+
+  if (role == 0) {
+    // ---- y, d_gate and y^T: like silu_quant_bwd_kernel without d_up ---------
+    if (tile < end) load_first(in, cur);
+    while (tile < end) {
+      const int next = tile + stride;
+      const Tile nxt = tile_at(next < end ? next : tile, tiles_h, T, H);
+      if (next < end) load_first(in_next, nxt);
+      uint32_t Yp[kRows][4], Gp[kRows][4], Up[kRows][4];
+      float rg[kRows], ru[kRows], cm[8];
+      elementwise<false>(in, s_tab, Yp, Gp, Up, rg, ru, cm);
+      if (tid == 0) s_flag[0] = 0;
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) rp[i] = rg[i];
+      float4* cp = reinterpret_cast<float4*>(s_colpart + q * kTile + 4 * p);
+      cp[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
+      cp[16] = make_float4(cm[4], cm[5], cm[6], cm[7]);
+      __syncthreads();
+      for (int id = tid; id < kHalfGroups + kColGroups; id += kThreads) {
+        if (id < kHalfGroups) {
+          const int row = id & (kTile - 1), sub = id >> 7;
+          float m = 0.0f;
+#pragma unroll
+          for (int pp = 0; pp < kLanesPerRowGroup; ++pp)
+            m = fmaxf(m, s_rowpart[(sub * kLanesPerRowGroup + pp) * kRowPartStride + row]);
+          const float scale = group_scale<F>(m);
+          const float inv = 1.0f / scale;
+          s_inv[id] = inv;
+          if (inv == __builtin_huge_valf()) s_flag[0] = 1;
+          // d_gate's last r channels belong to the straddling group (window 0)
+          if (row < cur.rows && cur.h0 + sub * kG < lim_a)
+            grad_input_s[(cur.t0 + row) * row_groups + cur.h0 / kG + sub] = scale;
+        } else {
+          const int cid = id - kHalfGroups, c = cid & (kTile - 1), sub = cid >> 7;
+          const int idx = ((c >> 2) & 1) * 64 + (c >> 3) * 4 + (c & 3);
+          float m = 0.0f;
+#pragma unroll 8
+          for (int qq = 0; qq < kPairsPerColGroup; ++qq)
+            m = fmaxf(m, s_colpart[(sub * kPairsPerColGroup + qq) * kTile + idx]);
+          const float scale = group_scale<F>(m);
+          const float inv = 1.0f / scale;
+          s_inv[id] = inv;
+          if (inv == __builtin_huge_valf()) s_flag[0] = 1;
+          if (c < cur.cols && sub * kG < cur.rows)
+            y_s_t[(cur.h0 + c) * col_groups + cur.t0 / kG + sub] = scale;
+        }
+      }
+      __syncthreads();
+      float idg[kRows], iy[8];
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) idg[i] = s_inv[sub_row * kTile + kRows * q + i];
+      const float* inv_col = s_inv + kHalfGroups + sub_col * kTile + 8 * p;
+      const float4 inv_y0 = *reinterpret_cast<const float4*>(inv_col);
+      const float4 inv_y1 = *reinterpret_cast<const float4*>(inv_col + 4);
+      iy[0] = inv_y0.x, iy[1] = inv_y0.y, iy[2] = inv_y0.z, iy[3] = inv_y0.w;
+      iy[4] = inv_y1.x, iy[5] = inv_y1.y, iy[6] = inv_y1.z, iy[7] = inv_y1.w;
+      const __amdgpu_buffer_rsrc_t gq_buf =
+          buffer_of(grad_input_q + (cur.t0 * gq_row_bytes + cur.h0), (uint32_t)(cur.rows * gq_row_bytes));
+      // the pair's first channel and lim_a are multiples of 16: a pair is wholly in or out
+      const uint32_t lane_a = cur.h0 + 8 * (p & ~1) < lim_a ? lane_gq : kDropped;
+      store_half_codes<F, false>(Gp, idg, gq_buf, lane_a, (uint32_t)gq_row_bytes, p);
+      stage_y_codes<F, false>(Yp, iy, s_yqt, p, q);
+      __syncthreads();
+      if (s_flag[0]) {  // rare: as in silu_quant_bwd_kernel
+        TileIn again;
+        load_first(again, cur);
+        float rg2[kRows], ru2[kRows], cm2[8];
+        elementwise<false>(again, s_tab, Yp, Gp, Up, rg2, ru2, cm2);
+        store_half_codes<F, true>(Gp, idg, gq_buf, lane_a, (uint32_t)gq_row_bytes, p);
+        stage_y_codes<F, true>(Yp, iy, s_yqt, p, q);
+        __syncthreads();
+      }
+      if (cur.cols > 0) {  // a block past H holds a window only
+        const __amdgpu_buffer_rsrc_t yq_buf = buffer_of(y_q_t + (cur.h0 * T + cur.t0), (uint32_t)(cur.cols * T));
+#pragma unroll
+        for (int step = 0; step < kOutSteps; ++step) {
+          const int id = tid + step * kThreads;
+          const int h = id >> 3;
+          const int phys = (id & 7) ^ ((h >> 3) & 7);
+          const uint32_t lane_yq = (uint32_t)((id >> 3) * T + 16 * (id & 7));
+          const uint4 v = *reinterpret_cast<const uint4*>(s_yqt + h * kTile + phys * 16);
+          if (cur.rows == kTile && yq_align == 16)
+            store_yq(yq_buf, lane_yq, v);
+          else
+            store_yq_piece(yq_buf, lane_yq, v, min(16, max(0, cur.rows - 16 * (id & 7))), yq_align);
+        }
+      }
+      in = in_next;
+      tile = next;
+      cur = nxt;
+      if (tile < end) __syncthreads();  // the transpose buffer is read before it is rewritten
+    }
+  } else {
+    // ---- the second half over window hb ---------------------------------------
+    if (tile < end) load_window(in, cur);
+    while (tile < end) {
+      const int next = tile + stride;
+      const Tile nxt = tile_at(next < end ? next : tile, tiles_h, T, H);
+      if (next < end) load_window(in_next, nxt);
+      const bool tail = cur.hb == 0 && 8 * p < r;
+      uint32_t Vp[kRows][4];
+      float rv[kRows];
+      if (cur.hb == 0)
+        elementwise_window<true>(in, tail, s_tab, Vp, rv);
+      else
+        elementwise_window<false>(in, false, s_tab, Vp, rv);
+      if (tid == 0) s_flag[0] = 0;
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) rp[i] = rv[i];
+      __syncthreads();
+      for (int id = tid; id < kHalfGroups; id += kThreads) {
+        const int row = id & (kTile - 1), sub = id >> 7;
+        float m = 0.0f;
+#pragma unroll
+        for (int pp = 0; pp < kLanesPerRowGroup; ++pp)
+          m = fmaxf(m, s_rowpart[(sub * kLanesPerRowGroup + pp) * kRowPartStride + row]);
+        const float scale = group_scale<F>(m);
+        const float inv = 1.0f / scale;
+        s_inv[id] = inv;
+        if (inv == __builtin_huge_valf()) s_flag[0] = 1;
+        if (row < cur.rows && cur.h0 + sub * kG < lim_b)
+          grad_input_s[(cur.t0 + row) * row_groups + (lim_a + cur.h0) / kG + sub] = scale;
+      }
+      __syncthreads();
+      float iv[kRows];
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) iv[i] = s_inv[sub_row * kTile + kRows * q + i];
+      const __amdgpu_buffer_rsrc_t gq_buf =
+          buffer_of(grad_input_q + (cur.t0 * gq_row_bytes + cur.h0), (uint32_t)(cur.rows * gq_row_bytes));
+      // position (H - r) + h0 + 8 (p & ~1) of the row; the pair's first
+      // channel and lim_b are multiples of 16
+      const uint32_t lane_b = cur.h0 + 8 * (p & ~1) < lim_b ? lane_gq + (uint32_t)lim_a : kDropped;
+      store_half_codes<F, false>(Vp, iv, gq_buf, lane_b, (uint32_t)gq_row_bytes, p);
+      if (s_flag[0]) {
+        TileIn again;
+        load_window(again, cur);
+        float rv2[kRows];
+        if (cur.hb == 0)
+          elementwise_window<true>(again, tail, s_tab, Vp, rv2);
+        else
+          elementwise_window<false>(again, false, s_tab, Vp, rv2);
+        store_half_codes<F, true>(Vp, iv, gq_buf, lane_b, (uint32_t)gq_row_bytes, p);
+      }
+      in = in_next;
+      tile = next;
+      cur = nxt;
+      if (tile < end) __syncthreads();  // partials, inverses and the flag are rewritten
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Forward quantiser: y = bf16((silu(gate) * up) * w[t]), quantised per row in
-// groups of kG = 128, 64 or 32 channels (y_q [T, H], y_s [T, H/kG]),
+// groups of kG = 128, 64 or 32 channels (y_q [T, H], y_s [T, ceil(H/kG)]),
 // optionally also the bf16 y itself.  The fused launch shape follows the page
 // "kquant_mmq.rs" (kquant_swiglu_q8_1_rows: swiglu times an optional row
 // weight, rounded to bf16, then group-quantised), with this library's groups.
@@ -678,7 +1026,10 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
   const bool odd = p & 1;
   const int64_t waves = (int64_t)gridDim.x * (kFwdThreads / 64);
   int64_t u = (int64_t)blockIdx.x * (kFwdThreads / 64) + (tid >> 6);
-  const int64_t groups = H / kG;
+  const int64_t groups = (H + kG - 1) / kG;
+  // Rows of y_q start on 16 bytes when H % 16 == 0: then the even lane of
+  // each pair stores the pair's 16 codes; else each lane stores its own 8.
+  const bool pair_stores = (H & 15) == 0;
 
   auto coords = [&](int64_t unit, int64_t& t, int64_t& h0, int64_t& hb) {
     const int64_t rb = unit / tiles_h;
@@ -687,8 +1038,9 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
     h0 = hb * kTile;
   };
   // In the last channel block of an H that is not a multiple of 128 only the
-  // lanes with 8 p < H - h0 hold channels (H is a multiple of the group, so a
-  // group's lanes are all in or all out).
+  // lanes with 8 p < H - h0 hold channels (H is a multiple of 8); the others
+  // read zeros, which never raise a group's maximum, so the last group of a
+  // row may be partial.
   auto live = [&](int64_t h0) { return h0 + 8 * p < H; };
   auto load = [&](FwdIn& in, int64_t t, int64_t h0) {
     if (t < T && live(h0)) {
@@ -741,14 +1093,18 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
       c = codes8<true>(Yp, inv);
     else
       c = codes8<false>(Yp, inv);
-    // The even lane of each pair stores the pair's 16 codes.
     const uint2 other = make_uint2(swap_neighbour(c.x), swap_neighbour(c.y));
     if (t < T && live(h0)) {
       // Plain non-temporal stores: for this write-light pass they measured
-      // faster than the system-scope policy the backward pass uses.
-      if (!odd)
-        __builtin_nontemporal_store((u32x4){c.x, c.y, other.x, other.y},
-                                    reinterpret_cast<u32x4*>(y_q + t * H + h0 + 8 * p));
+      // faster than the system-scope policy the backward pass uses.  With
+      // H % 16 == 0 the odd lane of a live even lane is live too.
+      if (pair_stores) {
+        if (!odd)
+          __builtin_nontemporal_store((u32x4){c.x, c.y, other.x, other.y},
+                                      reinterpret_cast<u32x4*>(y_q + t * H + h0 + 8 * p));
+      } else {
+        __builtin_nontemporal_store((u32x2){c.x, c.y}, reinterpret_cast<u32x2*>(y_q + t * H + h0 + 8 * p));
+      }
       if (y_bf16 != nullptr)
         __builtin_nontemporal_store((u32x4){Yp[0], Yp[1], Yp[2], Yp[3]},
                                     reinterpret_cast<u32x4*>(y_bf16 + t * H + h0 + 8 * p));
@@ -831,18 +1187,26 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 
 namespace {
 
+// Share of the first team among an XCD's workgroups in the kernel for H not a
+// multiple of the group, in eighths (the measured best of 3..7 at T = 16384,
+// H = 11000).
+constexpr int kFirstTeamEighths = 5;
+
 template <Fmt F>
 int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float* grad_input_s, void* y_q_t,
                     float* y_s_t, int64_t T, int64_t H, int64_t group, void* stream) {
   if (group != 32 && group != 64 && group != 128) return SILUQUANT_ERR_BAD_GROUP;
-  if (T < 0 || H < 0 || H % group != 0) return SILUQUANT_ERR_BAD_SHAPE;
+  // Rows of every tensor start on 16 bytes: H a multiple of 8.
+  if (T < 0 || H < 0 || H % 8 != 0) return SILUQUANT_ERR_BAD_SHAPE;
   if (T == 0 || H == 0) return SILUQUANT_OK;
   // Tile indices are int; a lane's byte offset inside a tile (< 512 * H for x)
-  // must fit in 32 bits, and a tile's output span (128 rows of 2H bytes of
-  // grad_input_q, 128 rows of T bytes of y_q_t) in a buffer resource's
-  // 31-bit record count.
-  const int64_t tiles_t = (T + kTile - 1) / kTile, tiles_h64 = (H + kTile - 1) / kTile;
-  if (T > (int64_t(1) << 23) || H > (int64_t(1) << 22) || tiles_t * tiles_h64 > 0x7fffffff)
+  // must fit in 32 bits, and a tile's span (128 rows of 4H bytes of x, of 2H
+  // bytes of grad_input_q, of T bytes of y_q_t) in a buffer resource's 32-bit
+  // record count.  With H not a multiple of the group, the blocks cover the
+  // shifted windows, up to H + H % group.
+  const int64_t r = H % group;
+  const int64_t tiles_t = (T + kTile - 1) / kTile, tiles_h64 = (H + r + kTile - 1) / kTile;
+  if (T > (int64_t(1) << 23) || H > (int64_t(1) << 22) || 2 * tiles_t * tiles_h64 > 0x7fffffff)
     return SILUQUANT_ERR_BAD_SHAPE;
   if (!x || !grad_y || !grad_input_q || !grad_input_s || !y_q_t || !y_s_t) return SILUQUANT_ERR_NULL_PTR;
   auto mis16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; };
@@ -852,7 +1216,8 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
   const int64_t pairs = T * H;
   const int64_t col_groups = (T + group - 1) / group;
   const void* bufs[6] = {x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t};
-  const int64_t sizes[6] = {4 * pairs, 2 * pairs, 2 * pairs, 4 * (2 * pairs / group), pairs, 4 * H * col_groups};
+  const int64_t sizes[6] = {4 * pairs, 2 * pairs, 2 * pairs, 4 * T * ((2 * H + group - 1) / group), pairs,
+                            4 * H * col_groups};
   for (int i = 0; i < 6; ++i)
     for (int j = i + 1; j < 6; ++j)
       if (overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
@@ -868,13 +1233,39 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
   int grid = g_cu_count[dev] * kWorkgroupsPerCU;
   grid = grid >= 8 ? grid - grid % 8 : grid;
   if (tiles < grid) grid = tiles;
-  auto kernel = group == 128 ? silu_quant_bwd_kernel<F, 128>
-                : group == 64 ? silu_quant_bwd_kernel<F, 64>
-                              : silu_quant_bwd_kernel<F, 32>;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(grad_y),
-                     static_cast<int8_t*>(grad_input_q), grad_input_s, static_cast<int8_t*>(y_q_t), y_s_t, T, H,
-                     tiles_h, tiles);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+  const uint16_t* dys = static_cast<const uint16_t*>(grad_y);
+  int8_t* gq = static_cast<int8_t*>(grad_input_q);
+  int8_t* yq = static_cast<int8_t*>(y_q_t);
+  if (r == 0) {
+    auto kernel = group == 128 ? silu_quant_bwd_kernel<F, 128>
+                  : group == 64 ? silu_quant_bwd_kernel<F, 64>
+                                : silu_quant_bwd_kernel<F, 32>;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, xs, dys, gq, grad_input_s, yq, y_s_t, T, H, tiles_h,
+                       tiles);
+  } else {
+    // Two teams per XCD, sized to their work: per tile the first team moves
+    // about 8 bytes per (t, h) to and from HBM and the second about 5 (its
+    // reads mostly from L2), and the first computes more; it takes 5/8 of the
+    // workgroups.  Without enough workgroups per XCD, pairs of workgroups
+    // share each tile.
+    int first_team = 0;
+    grid = g_cu_count[dev] * kWorkgroupsPerCU;
+    grid = grid - grid % 8;
+    if (grid >= 16 && 2 * tiles >= grid) {
+      const int per_xcd = grid / 8;
+      first_team = (per_xcd * kFirstTeamEighths + 4) / 8;
+      first_team = first_team < 1 ? 1 : first_team > per_xcd - 1 ? per_xcd - 1 : first_team;
+    } else {
+      grid = 2 * tiles;
+    }
+    auto kernel = group == 128 ? silu_quant_bwd_shift_kernel<F, 128>
+                  : group == 64 ? silu_quant_bwd_shift_kernel<F, 64>
+                                : silu_quant_bwd_shift_kernel<F, 32>;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, xs, dys, gq, grad_input_s, yq, y_s_t, T, H, tiles_h,
+                       tiles, (int)r, first_team);
+  }
   if (hipGetLastError() != hipSuccess) return SILUQUANT_ERR_LAUNCH_FAILED;
   return SILUQUANT_OK;
 }
@@ -896,7 +1287,7 @@ __attribute__((visibility("default"))) const char* siluquant_strerror(int status
   switch (status) {
     case SILUQUANT_OK: return "ok";
     case SILUQUANT_ERR_NULL_PTR: return "a buffer pointer is NULL";
-    case SILUQUANT_ERR_BAD_SHAPE: return "sizes must be non-negative, H (or K) a multiple of the group, and within the limits";
+    case SILUQUANT_ERR_BAD_SHAPE: return "sizes must be non-negative and within the limits, H a multiple of 8 and K of 128";
     case SILUQUANT_ERR_BAD_GROUP: return "unsupported group size (the passes take 128, 64 or 32; the forward pass and the GEMM 128)";
     case SILUQUANT_ERR_MISALIGNED: return "a buffer is not aligned (code and input tensors 16 bytes, scales 4 bytes)";
     case SILUQUANT_ERR_OVERLAP: return "buffers overlap";
@@ -929,7 +1320,8 @@ __attribute__((visibility("default"))) int silu_fwd_quant(const void* x, const f
                                                           float* y_s, void* y_bf16, int64_t T, int64_t H,
                                                           int64_t group, void* stream) {
   if (group != 32 && group != 64 && group != 128) return SILUQUANT_ERR_BAD_GROUP;
-  if (T < 0 || H < 0 || H % group != 0) return SILUQUANT_ERR_BAD_SHAPE;
+  // Rows start on 16 bytes (x, y_bf16) and 8 bytes (y_q): H a multiple of 8.
+  if (T < 0 || H < 0 || H % 8 != 0) return SILUQUANT_ERR_BAD_SHAPE;
   if (T == 0 || H == 0) return SILUQUANT_OK;
   if (T > (int64_t(1) << 31) || H > (int64_t(1) << 22) || T > (int64_t(1) << 40) / H) return SILUQUANT_ERR_BAD_SHAPE;
   if (!x || !y_q || !y_s) return SILUQUANT_ERR_NULL_PTR;
@@ -939,7 +1331,7 @@ __attribute__((visibility("default"))) int silu_fwd_quant(const void* x, const f
     return SILUQUANT_ERR_MISALIGNED;
   const int64_t pairs = T * H;
   const void* bufs[5] = {x, row_weight, y_q, y_s, y_bf16};
-  const int64_t sizes[5] = {4 * pairs, 4 * T, pairs, 4 * (pairs / group), 2 * pairs};
+  const int64_t sizes[5] = {4 * pairs, 4 * T, pairs, 4 * T * ((H + group - 1) / group), 2 * pairs};
   for (int i = 0; i < 5; ++i)
     for (int j = i + 1; j < 5; ++j)
       if (bufs[i] && bufs[j] && overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;

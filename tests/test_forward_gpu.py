@@ -23,7 +23,7 @@ def _bits(t):
 def run(x, w=None, want_bf16=False, group=128):
     T, H = x.shape[0], x.shape[1] // 2
     yq = torch.full((T, H), -7, dtype=torch.int8, device=DEV)
-    ys = torch.full((T, H // group), float("nan"), dtype=torch.float32, device=DEV)
+    ys = torch.full((T, -(-H // group)), float("nan"), dtype=torch.float32, device=DEV)
     yb = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device=DEV) if want_bf16 else None
     sq.silu_fwd_quant(x, yq, ys, row_weight=w, y_bf16=yb, group_size=group)
     torch.cuda.synchronize()
@@ -96,8 +96,12 @@ def test_empty_and_errors():
     sq.silu_fwd_quant(x, torch.empty((0, 128), dtype=torch.int8, device=DEV),
                       torch.empty((0, 1), dtype=torch.float32, device=DEV))
     x, _ = random_inputs(8, 200, device=DEV)
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError):  # y_s must be [8, ceil(200 / 128)]
         sq.silu_fwd_quant(x, torch.empty((8, 200), dtype=torch.int8, device=DEV),
+                          torch.empty((8, 1), dtype=torch.float32, device=DEV))
+    x, _ = random_inputs(8, 100, device=DEV)
+    with pytest.raises(ValueError):  # H not a multiple of 8
+        sq.silu_fwd_quant(x, torch.empty((8, 100), dtype=torch.int8, device=DEV),
                           torch.empty((8, 1), dtype=torch.float32, device=DEV))
 
 
@@ -115,6 +119,17 @@ def test_forward_y_equals_backward_recompute():
                                        (5, 96, 32), (4096, 1376, 32), (4099, 448, 64), (1, 64, 64)])
 def test_forward_groups_and_ragged_h(T, H, group):
     x, _ = random_inputs(T, H, device=DEV, seed=7 * T + H + group)
+    w = torch.rand(T, device=DEV, generator=torch.Generator(device=DEV).manual_seed(T)) * 4 - 2
+    check(x, label="T=%d H=%d group=%d" % (T, H, group), group=group)
+    check(x, w=w, want_bf16=True, label="T=%d H=%d group=%d weighted" % (T, H, group), group=group)
+
+
+# H any multiple of 8: the last group of a row is partial, and with
+# H % 16 == 8 each lane stores its own 8 codes.
+@pytest.mark.parametrize("T,H,group", [(100, 200, 128), (64, 40, 32), (300, 1000, 64), (17, 8, 128),
+                                       (1000, 1064, 128), (129, 2056, 32), (5, 24, 64)])
+def test_forward_partial_groups(T, H, group):
+    x, _ = random_inputs(T, H, device=DEV, seed=3 * T + H + group)
     w = torch.rand(T, device=DEV, generator=torch.Generator(device=DEV).manual_seed(T)) * 4 - 2
     check(x, label="T=%d H=%d group=%d" % (T, H, group), group=group)
     check(x, w=w, want_bf16=True, label="T=%d H=%d group=%d weighted" % (T, H, group), group=group)

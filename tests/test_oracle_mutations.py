@@ -64,6 +64,9 @@ MUTANTS = {
     "gemm_b_scale_row_zero": ("sB[(n / b_rows_per_scale) * groups + g]", "sB[g]"),
     "gemm_b_not_transposed": ("(int64_t)B[n * K + k]", "(int64_t)B[k * N + n]"),
     "gemm_group_offset": ("for (int64_t k = g * group; k < (g + 1) * group; ++k)", "for (int64_t k = 0; k < group; ++k)"),
+    "row_groups_split_at_halves": ("      int64_t n = (2 * H - c0 < group) ? 2 * H - c0 : group;\n      grad_input_s",
+                                   "      int64_t n = (2 * H - c0 < group) ? 2 * H - c0 : group;\n"
+                                   "      if (c0 < H && c0 + n > H) n = H - c0;\n      grad_input_s"),
     "fp8_nan_beyond_range": ("if (a >= 448.0) return sign | 0x7E;", "if (a >= 464.0) return sign | 0x7F;"),
 }
 

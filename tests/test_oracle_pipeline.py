@@ -16,6 +16,10 @@
   codes and the per-channel rows of y_s_t, and leaves the row-group scales
   alone; any sub-grid of 128 x 128 blocks, run on
   its own, reproduces the matching slices of the full result.
+* Row groups are consecutive positions of the 2H-long row [d_gate | d_up]:
+  with H not a multiple of the group, one group holds d_gate's last channels
+  and d_up's first ones (closed form with a saturated gate), and every group,
+  straddling or partial, equals the pinned one-group quantiser on that slice.
 """
 
 from fractions import Fraction
@@ -247,6 +251,38 @@ def test_trailing_partial_token_group():
     want = np.array([float(rn32(Fraction(float(a)) / 127)) if a > 0 else 1.0 for a in tail], np.float32)
     assert np.array_equal(ys[:, 1], want)
     assert np.all(np.abs(yq[:, 128:]).max(axis=1)[tail > 0] == 127)
+
+
+def test_straddling_group_closed_form():
+    # H = 40, group 32: the 80-long row has groups [0, 32), [32, 64) and the
+    # partial [64, 80).  A saturated gate (s == 1) with u = d = 1 gives
+    # d_gate = 1 and d_up = 20 exactly, so the middle group (d_gate 32..39,
+    # d_up 0..23) has maximum 20: scale rn(20/127), d_gate codes
+    # rne(127/20 * (1 + tiny)) = 6 and d_up codes 127.  Groups split at the
+    # halves would give the d_gate tail its own scale 1/127 and codes 127.
+    T, H, group = 8, 40, 32
+    xb, dyb = _const_inputs(T, H, 20.0, 1.0, 1.0)
+    gq, gs, yq, ys = oracle.silu_dot_fwd_bwd_quant_fuse(xb, dyb, group_size=group)
+    assert gs.shape == (T, 3) and gq.shape == (T, 80)
+    s1 = float(rn32(Fraction(1) / 127))
+    s20 = float(rn32(Fraction(20) / 127))
+    assert np.all(gs[:, 0] == np.float32(s1)) and np.all(gq[:, :32] == 127)
+    assert np.all(gs[:, 1] == np.float32(s20)) and np.all(gs[:, 2] == np.float32(s20))
+    assert np.all(gq[:, 32:40] == 6) and np.all(gq[:, 40:] == 127)
+
+
+@pytest.mark.parametrize("T,H,group", [(64, 200, 128), (40, 40, 32), (16, 8, 128), (32, 104, 64), (20, 72, 32)])
+def test_row_groups_over_the_whole_row(T, H, group):
+    xt, dyt = random_inputs(T, H, seed=T + H + group)
+    xb, dyb = _np_bits(xt), _np_bits(dyt)
+    gq, gs, yq, ys = oracle.silu_dot_fwd_bwd_quant_fuse(xb, dyb, group_size=group)
+    _, D = oracle.intermediates(xb, dyb)
+    n = -(-2 * H // group)
+    assert gs.shape == (T, n) and gq.shape == (T, 2 * H)
+    for t in range(T):
+        for j in range(n):
+            q, s = oracle.quant_group(D[t, j * group:(j + 1) * group])
+            assert s == gs[t, j] and np.array_equal(q, gq[t, j * group:(j + 1) * group]), (t, j)
 
 
 def test_empty_inputs():

@@ -223,9 +223,9 @@ def test_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):
         x2, dy2 = random_inputs(200, 128, device=DEV)
         sq.silu_dot_fwd_bwd_quant_fuse(x2, dy2, *sq.empty_outputs(128, 128, DEV))
-    with pytest.raises(ValueError):  # H not a multiple of 128
-        x3, dy3 = random_inputs(128, 200, device=DEV)
-        sq.silu_dot_fwd_bwd_quant_fuse(x3, dy3, *sq.empty_outputs(128, 200, DEV))
+    with pytest.raises(ValueError):  # H not a multiple of 8
+        x3, dy3 = random_inputs(128, 100, device=DEV)
+        sq.silu_dot_fwd_bwd_quant_fuse(x3, dy3, *sq.empty_outputs(128, 100, DEV))
     with pytest.raises(ValueError):
         sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *outs, group_size=64)
 
@@ -290,8 +290,50 @@ def test_smaller_groups_fp8_and_overflowed_inverse(group):
 
 
 def test_group_size_errors():
+    x, dy = random_inputs(128, 100, device=DEV)
+    with pytest.raises(ValueError):  # 100 is not a multiple of 8
+        sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *sq.empty_outputs(128, 100, DEV, group=64), group_size=64)
     x, dy = random_inputs(128, 96, device=DEV)
-    with pytest.raises(ValueError):  # 96 is not a multiple of 64
-        sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *sq.empty_outputs(128, 96, DEV, group=64), group_size=64)
     with pytest.raises(ValueError):
         sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *sq.empty_outputs(128, 96, DEV, group=32), group_size=48)
+
+
+# H not a multiple of the group (any multiple of 8): one row group holds the
+# last H % group channels of d_gate and the first of d_up, the d_up groups sit
+# shifted against the 128-channel blocks, and the row's last group may be
+# partial.  Shapes cover r = H % group from 8 to 120, H below the group, and
+# windows that need one block more than the channels (r > 128 - H % 128).
+@pytest.mark.parametrize("T,H,group", [(256, 200, 128), (129, 40, 32), (64, 8, 128), (300, 1000, 128),
+                                       (1000, 1064, 64), (128, 136, 128), (4096, 1400, 128), (333, 520, 32),
+                                       (77, 2056, 64), (1, 24, 32), (130, 248, 128), (640, 11000, 128)])
+def test_straddling_groups(T, H, group):
+    print("case straddle", T, H, group, flush=True)
+    x, dy = random_inputs(T, H, device=DEV, seed=5 * T + H + group)
+    check_group(x, dy, group, "straddle T=%d H=%d group=%d" % (T, H, group))
+
+
+@pytest.mark.parametrize("T,H,group", [(256, 200, 128), (300, 1000, 64), (129, 40, 32)])
+def test_straddling_groups_fp8(T, H, group):
+    print("case straddle fp8", T, H, group, flush=True)
+    x, dy = random_inputs(T, H, device=DEV, seed=T + H + group)
+    check_group(x, dy, group, "straddle fp8 T=%d H=%d group=%d" % (T, H, group), fp8=True)
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_straddling_groups_edge_values(group):
+    # saturated gate, u = d = 1: d_gate = 1 and d_up = 20, so the straddling
+    # group's maximum comes from the d_up side; then a straddling group of
+    # tiny values whose inverse overflows, and zero rows
+    T, H = 256, 40 if group == 32 else 200
+    x, dy = _const(T, H, 20.0, 1.0, 1.0)
+    check_group(x, dy, group, "straddle const group=%d" % group)
+    check_group(x, dy, group, "straddle const fp8 group=%d" % group, fp8=True)
+    r = H % group
+    x, dy = _const(T, H, 20.0, 0.0, 1.0)  # d_gate = d u = 0, d_up = 20 d
+    tiny = torch.tensor([2.0**-130, -(2.0**-131), 0.0, 2.0**-133], dtype=torch.float32).to(torch.bfloat16).to(DEV)
+    x[:, 2 * H - 4:] = tiny  # up at d_gate's last channels: d_gate (and y) tiny there
+    dy[:, :group - r] = 0.0  # d_up's share of the straddling group is zero
+    x[7] = 0.0
+    dy[9] = 0.0
+    check_group(x, dy, group, "straddle tiny group=%d" % group)
+    check_group(x, dy, group, "straddle tiny fp8 group=%d" % group, fp8=True)
