@@ -27,7 +27,7 @@ extern "C" {
 enum siluquant_status {
   SILUQUANT_OK = 0,
   SILUQUANT_ERR_NULL_PTR = 1,      /* a buffer pointer is NULL while T*H > 0 */
-  SILUQUANT_ERR_BAD_SHAPE = 2,     /* T < 0, H < 0, H not a multiple of 8 (K of 128), or too large */
+  SILUQUANT_ERR_BAD_SHAPE = 2,     /* T < 0, H < 0, H not a multiple of 8 (K of the group), or too large */
   SILUQUANT_ERR_BAD_GROUP = 3,     /* a group size the entry point does not take */
   SILUQUANT_ERR_MISALIGNED = 4,    /* x, grad_y, grad_input_q, y_q_t not 16-byte aligned,
                                       or a scale buffer not 4-byte aligned */
@@ -156,8 +156,8 @@ int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q, float* y
  *   fp32; bf16 output rounds that once (nearest, ties to even).
  * Group: `group` is 128, 64 or 32 (the pass's group sizes); sA is then
  *   [M, K/group] and sB [ceil(N/Bb), K/group].
- * Sizes: any M, N >= 0 (M == 0 or N == 0 is a no-op), K >= 0 a multiple of 128
- *   (K == 0 writes zeros).  Same ownership, asynchrony and status conventions
+ * Sizes: any M, N >= 0 (M == 0 or N == 0 is a no-op), K >= 0 a multiple of
+ *   the group (K == 0 writes zeros), K <= 2^22.  Same ownership, asynchrony and status conventions
  *   as above; C must not overlap an input.
  */
 enum siluquant_gemm_out { SILUQUANT_GEMM_OUT_F32 = 0, SILUQUANT_GEMM_OUT_BF16 = 1 };

@@ -192,7 +192,7 @@ GEMM_OUT_F32, GEMM_OUT_BF16 = 0, 1
 def i8_gemm_group_scaled(A, sA, B, sB, C, b_rows_per_scale: int = 1, group_size: int = GROUP):
     """C = A . B^T of group-scaled int8 operands on the matrix cores:
     C[m, n] = sum_g sA[m, g] * sB[n // b_rows_per_scale, g] * (A[m, group g] . B[n, group g]).
-    Groups are group_size (128, 64 or 32) wide along K; K is a multiple of 128.
+    Groups are group_size (128, 64 or 32) wide along K; K is a multiple of it.
     A int8 [M, K], sA fp32 [M, K/group_size], B int8 [N, K], sB fp32
     [ceil(N / b_rows_per_scale), K/group_size] (b_rows_per_scale 1 or 128); C
     fp32 or bf16 [M, N] is overwritten.  Enqueued on the current stream of A's
@@ -203,8 +203,8 @@ def i8_gemm_group_scaled(A, sA, B, sB, C, b_rows_per_scale: int = 1, group_size:
         raise ValueError("A must be [M, K] and B [N, K]")
     M, K = int(A.shape[0]), int(A.shape[1])
     N = int(B.shape[0])
-    if group_size not in GROUPS or K % GROUP:
-        raise ValueError("K must be a multiple of 128 and group_size one of %s" % (GROUPS,))
+    if group_size not in GROUPS or K % group_size:
+        raise ValueError("group_size must be one of %s and K a multiple of it" % (GROUPS,))
     if b_rows_per_scale not in (1, 128):
         raise ValueError("b_rows_per_scale must be 1 or 128")
     dev = A.device

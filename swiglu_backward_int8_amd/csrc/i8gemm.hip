@@ -3,12 +3,13 @@
 //
 //   C[m, n] = sum_g sA[m, g] * sB[n / Bb, g] * sum_{k in group g} A[m, k] * B[n, k]
 //
-// A [M, K] and B [N, K] are int8 row-major (C = A . B^T), groups are 128 wide
-// along K, sA is fp32 [M, K/128], sB fp32 [ceil(N/Bb), K/128] with Bb = 1 (one
-// scale per row, as y_s_t) or 128 (one per 128-row block, a weight's layout).
+// A [M, K] and B [N, K] are int8 row-major (C = A . B^T), groups are G = 128,
+// 64 or 32 wide along K (K a multiple of G), sA is fp32 [M, K/G], sB fp32
+// [ceil(N/Bb), K/G] with Bb = 1 (one scale per row, as y_s_t) or 128 (one per
+// 128-row block, a weight's layout).
 // The fusion bullet of the page "kernelgen-challenge-9-task3-silu-quant"
 // names the two quantisations (K-group for [d_gate, d_up] along channels,
-// M-group for y^T along tokens); each is a group-128 split of the contraction
+// M-group for y^T along tokens); each is a group split of the contraction
 // axis of the GEMM that reads it:
 //   dgrad:  dX[T, D]  = grad_input_q[T, 2H] . Wt[D, 2H]^T      (K = 2H)
 //   wgrad:  dW[D, H]  = go_q_t[D, T] . y_q_t[H, T]^T           (K = T)
@@ -102,7 +103,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = (wave / kWavesN) * 64, wn = (wave % kWavesN) * 64;  // the wave's 64 x 64 corner
-  const int stages = (int)(K / kBK), groups = (int)(K / kG);
+  // K is a multiple of kG; with kG < 128 the last stage may hold fewer than
+  // kSub groups, and its chunks past K read as zeros (see load_stage).
+  const int stages = (int)((K + kBK - 1) / kBK), groups = (int)(K / kG);
 
   // Rows past M or N read as zeros: the buffer's record count ends at the last row.
   const int a_rows = M - m0 < kBM ? (int)(M - m0) : kBM;
@@ -125,19 +128,26 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
   // thread's offset XOR a constant plus a constant.
   constexpr int kAPer = kAChunks / kGemmThreads;  // A chunks per thread
   const int g_off = (tid >> 3) * (int)K + 16 * (tid & 7);
+  // In a last stage that K ends inside (a multiple of 32 bytes), the chunks
+  // past K take an offset past the record count and read as zeros; so do
+  // their groups' scales, which do not exist.
+  const int k_last = (stages - 1) * kBK;
+  const int g_off_last = 16 * (tid & 7) < K - k_last ? g_off : (int)0x80000000;
   const int l_off = lds_at(tid >> 3, tid & 7);
   auto load_stage = [&](int g, Stage<kSub>& st) {
     const int k0 = g * kBK;
+    const int off = g == stages - 1 ? g_off_last : g_off;
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
       const int row_step = (i < kAPer ? i : i - kAPer) * (kGemmThreads / 8);
       st.v[i] = __builtin_bit_cast(
-          i32x4, __builtin_amdgcn_raw_buffer_load_b128(i < kAPer ? ra : rb, g_off, k0 + row_step * (int)K, 0));
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(i < kAPer ? ra : rb, off, k0 + row_step * (int)K, 0));
     }
 #pragma unroll
     for (int j = 0; j < kSub; ++j) {
-      st.sc[j] = sc_live ? sc_ptr[g * kSub + j] : 0.0f;
-      if constexpr (kBlockScale) st.sb[j] = sb_blk[g * kSub + j];
+      const bool live = g * kSub + j < groups;
+      st.sc[j] = sc_live && live ? sc_ptr[g * kSub + j] : 0.0f;
+      if constexpr (kBlockScale) st.sb[j] = live ? sb_blk[g * kSub + j] : 0.0f;
     }
   };
   auto store_stage = [&](int buf, const Stage<kSub>& st) {
@@ -279,7 +289,7 @@ __attribute__((visibility("default"))) int i8_gemm_group_scaled(const int8_t* A,
                                                                 int64_t K, int64_t group, int64_t b_rows_per_scale,
                                                                 int c_dtype, void* stream) {
   if (group != 32 && group != 64 && group != 128) return SILUQUANT_ERR_BAD_GROUP;
-  if (M < 0 || N < 0 || K < 0 || K % kBK != 0 || (b_rows_per_scale != 1 && b_rows_per_scale != kBN) ||
+  if (M < 0 || N < 0 || K < 0 || K % group != 0 || (b_rows_per_scale != 1 && b_rows_per_scale != kBN) ||
       (c_dtype != SILUQUANT_GEMM_OUT_F32 && c_dtype != SILUQUANT_GEMM_OUT_BF16))
     return SILUQUANT_ERR_BAD_SHAPE;
   if (M == 0 || N == 0) return SILUQUANT_OK;

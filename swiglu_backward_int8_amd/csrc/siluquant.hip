@@ -1287,7 +1287,7 @@ __attribute__((visibility("default"))) const char* siluquant_strerror(int status
   switch (status) {
     case SILUQUANT_OK: return "ok";
     case SILUQUANT_ERR_NULL_PTR: return "a buffer pointer is NULL";
-    case SILUQUANT_ERR_BAD_SHAPE: return "sizes must be non-negative and within the limits, H a multiple of 8 and K of 128";
+    case SILUQUANT_ERR_BAD_SHAPE: return "sizes must be non-negative and within the limits, H a multiple of 8 and K of the group";
     case SILUQUANT_ERR_BAD_GROUP: return "unsupported group size (the passes take 128, 64 or 32; the forward pass and the GEMM 128)";
     case SILUQUANT_ERR_MISALIGNED: return "a buffer is not aligned (code and input tensors 16 bytes, scales 4 bytes)";
     case SILUQUANT_ERR_OVERLAP: return "buffers overlap";

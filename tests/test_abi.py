@@ -184,6 +184,8 @@ def test_gemm_rejects_bad_arguments(lib):
 
     assert call(group=48) == 3 and call(group=256) == 3
     assert call(K=200) == 2 and call(M=-1) == 2 and call(N=-5) == 2 and call(K=-128) == 2
+    # K must be a multiple of the group (of 128 only for group 128)
+    assert call(K=96, group=64) == 2 and call(K=48, group=32) == 2 and call(K=192) == 2
     assert call(bb=64) == 2 and call(out=2) == 2
     assert call(A=None) == 1 and call(sB=None) == 1 and call(C=None) == 1
     assert call(A=A + 8) == 4 and call(B=B + 4) == 4 and call(sA=sA + 2) == 4 and call(C=C + 2) == 4
