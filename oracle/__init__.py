@@ -97,6 +97,10 @@ def _load():
         lib.oracle_silu_dot_fwd_bwd_quant_fuse_fp8.argtypes = [u16p, u16p, u8p, f32p, u8p, f32p, i64, i64, i64]
         lib.oracle_silu_dot_fwd_bwd_quant_fuse_fp8.restype = ctypes.c_int
         i8p, f64p = ctypes.POINTER(ctypes.c_int8), ctypes.POINTER(ctypes.c_double)
+        lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+        lib.oracle_silu_fwd_quant_q8_1.argtypes = [u16p, f32p, u8p, i64, i64]
+        lib.oracle_silu_fwd_quant_q8_1.restype = ctypes.c_int
         lib.oracle_i8_gemm_group_scaled.argtypes = [i8p, f32p, i8p, f32p, f64p, f64p, i64, i64, i64, i64, i64]
         lib.oracle_i8_gemm_group_scaled.restype = ctypes.c_int
         _lib = lib
@@ -254,6 +258,39 @@ def silu_fwd_quant(x, w=None, group_size: int = GROUP, want_bf16: bool = False):
     if rc != 0:
         raise RuntimeError("oracle_silu_fwd_quant failed with code %d" % rc)
     return (yq, ys, yb) if want_bf16 else (yq, ys)
+
+
+def f32_to_f16(x: float) -> int:
+    """Nearest IEEE binary16 bit pattern of an fp32 value (ties to even)."""
+    return int(_load().oracle_f32_to_f16(float(np.float32(x))))
+
+
+def silu_fwd_quant_q8_1(x, w=None):
+    """The forward quantiser in the q8_1 block layout: uint8 [T, (H/32) * 36],
+    each 36-byte block the binary16 d and sum, then 32 int8 codes (H a
+    multiple of 32)."""
+    x = _as_bits(x)
+    T, H2 = x.shape
+    H = H2 // 2
+    out = np.zeros((T, (H // 32) * 36), dtype=np.uint8)
+    wp = None
+    if w is not None:
+        w = np.ascontiguousarray(np.asarray(w, dtype=np.float32))
+        assert w.shape == (T,)
+        wp = _ptr(w, ctypes.c_float)
+    rc = _load().oracle_silu_fwd_quant_q8_1(_ptr(x, ctypes.c_uint16), wp, _ptr(out, ctypes.c_uint8), T, H)
+    if rc != 0:
+        raise RuntimeError("oracle_silu_fwd_quant_q8_1 failed with code %d" % rc)
+    return out
+
+
+def split_q8_1(blocks):
+    """(d, sum, codes) of a q8_1 array [T, nb * 36]: float16 [T, nb] twice and
+    int8 [T, nb, 32]."""
+    b = np.ascontiguousarray(blocks).reshape(blocks.shape[0], -1, 36)
+    d = np.ascontiguousarray(b[:, :, 0:2]).view(np.float16)[:, :, 0]
+    s = np.ascontiguousarray(b[:, :, 2:4]).view(np.float16)[:, :, 0]
+    return d, s, np.ascontiguousarray(b[:, :, 4:]).view(np.int8)
 
 
 def f32_to_e4m3(x: float) -> int:

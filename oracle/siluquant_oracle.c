@@ -334,6 +334,72 @@ ORACLE_API int oracle_silu_dot_fwd_bwd_quant_fuse_fp8(const uint16_t* x, const u
   return rc;
 }
 
+/* ---- IEEE binary16 and the q8_1 block layout -------------------------------- */
+
+/* Nearest binary16 bit pattern of x (ties to even), subnormals (k * 2^-24)
+ * kept, infinity from 65520 up (the midpoint between 65504 and 2^16); NaN is
+ * outside the domain.  Works in double, where every step below is exact. */
+ORACLE_API uint16_t oracle_f32_to_f16(float x) {
+  uint16_t sign = signbit(x) ? 0x8000 : 0x0000;
+  double a = fabs((double)x);
+  if (isinf(a)) return sign | 0x7C00;
+  if (a < ldexp(1.0, -14)) {                  /* below 2^-14: subnormals k * 2^-24, k = 0..1024 */
+    double k = nearbyint(a * ldexp(1.0, 24)); /* k == 1024 is the smallest normal, 2^-14 */
+    return sign | (uint16_t)k;                /* and encodes as exponent field 1, mantissa 0 */
+  }
+  int e;
+  double m = frexp(a, &e);             /* a = m * 2^e, m in [0.5, 1) */
+  double mant = nearbyint(m * 2048.0); /* 1024 .. 2048: the leading one plus 10 fraction bits */
+  if (mant == 2048.0) {
+    mant = 1024.0;
+    e += 1;
+  }
+  int efield = e - 1 + 15;
+  if (efield >= 31) return sign | 0x7C00; /* past 65504: infinity */
+  return sign | (uint16_t)(efield << 10) | (uint16_t)((int)mant - 1024);
+}
+
+/* The forward quantiser's output in the block_q8_1 layout of the page
+ * "kquant_mmq.rs": per row, H/32 blocks of 32 channels, 36 bytes each.  The
+ * page gives a block's content (32 int8 codes and a half2 (d, sum)) and size,
+ * not the byte order or what the sum adds up; the readings here: bytes 0-1
+ * hold d, the group-32 scale above rounded to binary16; bytes 2-3 the sum,
+ * fl32(scale * sum(q)) rounded to binary16, i.e. the block's values as its
+ * codes give them; bytes 4-35 the codes, both halves little-endian.  H must be
+ * a multiple of 32 (the page's k % 32 == 0). */
+ORACLE_API int oracle_silu_fwd_quant_q8_1(const uint16_t* x, const float* w, uint8_t* blocks, int64_t T, int64_t H) {
+  if (T < 0 || H < 0 || H % 32 != 0) return ORACLE_BAD_ARG;
+  if (T == 0 || H == 0) return ORACLE_OK;
+  int64_t nb = H / 32;
+  int8_t* q = (int8_t*)malloc((size_t)(T * H));
+  float* sc = (float*)malloc((size_t)(T * nb) * sizeof(float));
+  if (!q || !sc) {
+    free(q);
+    free(sc);
+    return ORACLE_NO_MEMORY;
+  }
+  int rc = oracle_silu_fwd_quant(x, w, q, sc, NULL, T, H, 32);
+  for (int64_t t = 0; rc == ORACLE_OK && t < T; ++t) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const int8_t* qb = q + t * H + 32 * b;
+      uint8_t* blk = blocks + (t * nb + b) * 36;
+      int sum = 0;
+      for (int i = 0; i < 32; ++i) sum += qb[i];
+      float scale = sc[t * nb + b];
+      float dequant_sum = scale * (float)sum;
+      uint16_t d16 = oracle_f32_to_f16(scale), s16 = oracle_f32_to_f16(dequant_sum);
+      blk[0] = (uint8_t)(d16 & 0xFF);
+      blk[1] = (uint8_t)(d16 >> 8);
+      blk[2] = (uint8_t)(s16 & 0xFF);
+      blk[3] = (uint8_t)(s16 >> 8);
+      memcpy(blk + 4, qb, 32);
+    }
+  }
+  free(q);
+  free(sc);
+  return rc;
+}
+
 /* ---- the group-scaled int8 product ------------------------------------------ */
 
 ORACLE_API int oracle_i8_gemm_group_scaled(const int8_t* A, const float* sA, const int8_t* B, const float* sB,

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "siluquant_oracle.c")
 PINS = ["tests/test_oracle_pipeline.py", "tests/test_oracle_quant.py",
         "tests/test_oracle_elementwise.py", "tests/test_oracle_sigmoid.py", "tests/test_oracle_forward.py",
-        "tests/test_oracle_fp8.py", "tests/test_oracle_gemm.py"]
+        "tests/test_oracle_fp8.py", "tests/test_oracle_gemm.py", "tests/test_oracle_q8_1.py"]
 
 MUTANTS = {
     "sigmoid_sign": ("exp(-(double)g)", "exp((double)g)"),
@@ -67,6 +67,13 @@ MUTANTS = {
     "row_groups_split_at_halves": ("      int64_t n = (2 * H - c0 < group) ? 2 * H - c0 : group;\n      grad_input_s",
                                    "      int64_t n = (2 * H - c0 < group) ? 2 * H - c0 : group;\n"
                                    "      if (c0 < H && c0 + n > H) n = H - c0;\n      grad_input_s"),
+    "f16_truncates": ("double mant = nearbyint(m * 2048.0);", "double mant = floor(m * 2048.0);"),
+    "f16_subnormal_step": ("double k = nearbyint(a * ldexp(1.0, 24));", "double k = nearbyint(a * ldexp(1.0, 23));"),
+    "f16_exponent_bias": ("int efield = e - 1 + 15;", "int efield = e - 1 + 16;"),
+    "q8_1_header_swapped": ("uint16_t d16 = oracle_f32_to_f16(scale), s16 = oracle_f32_to_f16(dequant_sum);",
+                            "uint16_t s16 = oracle_f32_to_f16(scale), d16 = oracle_f32_to_f16(dequant_sum);"),
+    "q8_1_sum_of_codes": ("float dequant_sum = scale * (float)sum;", "float dequant_sum = (float)sum;"),
+    "q8_1_codes_after_header_shift": ("memcpy(blk + 4, qb, 32);", "memcpy(blk + 4, qb + 1, 31);"),
     "fp8_nan_beyond_range": ("if (a >= 448.0) return sign | 0x7E;", "if (a >= 464.0) return sign | 0x7F;"),
 }
 
@@ -74,7 +81,8 @@ MUTANTS = {
 # The pin file most likely to catch a family of mutants runs first, so that the
 # child run (which stops at the first failure) ends early.
 FIRST = {"gemm_": "tests/test_oracle_gemm.py", "fp8_": "tests/test_oracle_fp8.py",
-         "forward_": "tests/test_oracle_forward.py"}
+         "forward_": "tests/test_oracle_forward.py", "f16_": "tests/test_oracle_q8_1.py",
+         "q8_1_": "tests/test_oracle_q8_1.py"}
 
 
 def _run_mutant(name, workdir):
