@@ -8,7 +8,7 @@ code tensors and both scale tensors) divided by the time per call.
 
 Prints one JSON line.  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--op backward|forward|fp8|gemm_dgrad|gemm_wgrad]
+                    [--op backward|forward|forward_q8_1|fp8|gemm_dgrad|gemm_wgrad]
                     [--no-cpu-baseline] [--probes]
 """
 
@@ -53,11 +53,12 @@ def measured_traffic(workload: str, src: str = KERNEL_SRC):
 
 
 def cpu_baseline(x, dy, w, min_seconds: float = 10.0, max_calls: int = 5, fp8: bool = False,
-                 forward: bool = False):
+                 forward: bool = False, q8_1: bool = False):
     """The oracle, single-threaded, on the whole workload: calls are repeated
     until at least min_seconds of CPU work (at most max_calls); the rate is the
     algorithmic bytes of all calls over their total time (the op's own bytes:
-    the backward pass, its E4M3 variant, or the forward quantiser)."""
+    the backward pass, its E4M3 variant, or the forward quantiser in either
+    layout)."""
     import numpy as np
     import torch
 
@@ -70,13 +71,16 @@ def cpu_baseline(x, dy, w, min_seconds: float = 10.0, max_calls: int = 5, fp8: b
     calls, total = 0, 0.0
     while calls < max_calls and (calls == 0 or total < min_seconds):
         t = time.perf_counter()
-        if forward:
+        if forward and q8_1:
+            oracle.silu_fwd_quant_q8_1(xb)
+        elif forward:
             oracle.silu_fwd_quant(xb)
         else:
             (oracle.silu_dot_fwd_bwd_quant_fuse_fp8 if fp8 else oracle.silu_dot_fwd_bwd_quant_fuse)(xb, db)
         total += time.perf_counter() - t
         calls += 1
-    nbytes = sq.forward_bytes(w.T, w.H) if forward else sq.algorithmic_bytes(w.T, w.H)
+    nbytes = (sq.forward_q8_1_bytes(w.T, w.H) if q8_1 else sq.forward_bytes(w.T, w.H)) if forward \
+        else sq.algorithmic_bytes(w.T, w.H)
     return {
         "value": round(calls * nbytes / total / 1e9, 4),
         "unit": "GB/s",
@@ -233,9 +237,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="t16384_h11008")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=["backward", "forward", "fp8"] + sorted(GEMMS), default="backward",
+    ap.add_argument("--op", choices=["backward", "forward", "forward_q8_1", "fp8"] + sorted(GEMMS),
+                    default="backward",
                     help="backward: the fused SwiGLU backward + two-axis int8 pass (the headline); "
                          "forward: SwiGLU forward + row-wise int8 quantisation; "
+                         "forward_q8_1: the same in 32-channel q8_1 blocks; "
                          "fp8: the backward pass with OCP FP8 E4M3 codes; "
                          "gemm_dgrad / gemm_wgrad: the group-scaled int8 GEMMs that consume its outputs")
     ap.add_argument("--probes", action="store_true",
@@ -258,16 +264,21 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    forward = args.op == "forward"
+    q8_1 = args.op == "forward_q8_1"
+    forward = args.op == "forward" or q8_1
     fp8 = args.op == "fp8"
-    nbytes = sq.forward_bytes(w.T, w.H) if forward else sq.algorithmic_bytes(w.T, w.H)
+    nbytes = (sq.forward_q8_1_bytes(w.T, w.H) if q8_1 else sq.forward_bytes(w.T, w.H)) if forward \
+        else sq.algorithmic_bytes(w.T, w.H)
     # Rotate buffer sets so that one pass over them exceeds twice the 256 MB
     # last-level cache: every step then reads its inputs from HBM.
     sets = max(1, -(-512 * 2**20 // nbytes))
     bufs = []
     for r in range(sets):
         x, dy = make_inputs(w, device=dev, seed=w.seed + 1000 * r)
-        if forward:
+        if q8_1:
+            del dy
+            bufs.append((x, None, (torch.empty((w.T, (w.H // 32) * sq.Q8_1_BLOCK), dtype=torch.uint8, device=dev),)))
+        elif forward:
             del dy
             outs = (torch.empty((w.T, w.H), dtype=torch.int8, device=dev),
                     torch.empty((w.T, w.H // 128), dtype=torch.float32, device=dev))
@@ -279,7 +290,9 @@ def main():
 
     def step(i):
         x, dy, outs = bufs[i % sets]
-        if forward:
+        if q8_1:
+            sq.silu_fwd_quant_q8_1(x, *outs)
+        elif forward:
             sq.silu_fwd_quant(x, *outs)
         elif fp8:
             sq.silu_dot_fwd_bwd_quant_fuse_fp8(x, dy, *outs)
@@ -307,7 +320,9 @@ def main():
     achieved = nbytes / per_launch_s / 1e9
     value = nbytes * args.steps / wall / 1e9
     metric = "achieved HBM GB/s (+% of MI355X peak) for fused silu fwd/bwd+int8 quant"
-    if forward:
+    if q8_1:
+        metric = "achieved HBM GB/s (+% of MI355X peak) for fused silu forward + q8_1 block quant"
+    elif forward:
         metric = "achieved HBM GB/s (+% of MI355X peak) for fused silu forward + row-wise int8 quant"
     elif fp8:
         metric = "achieved HBM GB/s (+% of MI355X peak) for fused silu fwd/bwd+fp8 e4m3 quant"
@@ -326,7 +341,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": w.name, "T": w.T, "H": w.H, "group": 128,
+            "workload": w.name, "T": w.T, "H": w.H, "group": 32 if q8_1 else 128,
             "bytes_per_step": nbytes, "pairs_per_s": round(w.T * w.H * args.steps / wall, 1),
             "buffer_sets": sets,
         },
@@ -336,9 +351,10 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic({"forward": "forward:", "fp8": "fp8:"}.get(args.op, "") + w.name),
-            "kernel": {"forward": "silu_fwd_quant_kernel", "fp8": "silu_quant_bwd_kernel<Fmt::kFp8>"}.get(
-                args.op, "silu_quant_bwd_kernel<Fmt::kInt8>"),
+            "traffic": measured_traffic({"forward": "forward:", "forward_q8_1": "forward_q8_1:", "fp8": "fp8:"}.get(
+                args.op, "") + w.name),
+            "kernel": {"forward": "silu_fwd_quant_kernel", "forward_q8_1": "silu_fwd_quant_kernel<32, q8_1>",
+                       "fp8": "silu_quant_bwd_kernel<Fmt::kFp8>"}.get(args.op, "silu_quant_bwd_kernel<Fmt::kInt8>"),
             "avg_launch_us": round(per_launch_s * 1e6, 3),
         },
         "cpu_baseline": None,
@@ -347,7 +363,7 @@ def main():
         out["probes"] = stream_probes(dev)
     if not args.no_cpu_baseline:
         x, dy, _ = bufs[0]
-        out["cpu_baseline"] = cpu_baseline(x, dy, w, fp8=fp8, forward=forward)
+        out["cpu_baseline"] = cpu_baseline(x, dy, w, fp8=fp8, forward=forward, q8_1=q8_1)
     print(json.dumps(out), flush=True)
 
 

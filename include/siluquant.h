@@ -135,6 +135,30 @@ int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q, float* y
                    int64_t H, int64_t group, void* stream);
 
 /*
+ * silu_fwd_quant_q8_1 -- the forward quantiser in the page's q8_1 block layout.
+ *
+ * The page "kquant_mmq.rs" (docs.atlascybernetics.ai) writes the fused
+ * swiglu rows as block_q8_1: per 32 channels, 32 int8 codes and a half2
+ * (d, sum), 36 bytes.  y is computed and quantised exactly as silu_fwd_quant
+ * with group 32; the block holds, in this order (the page gives the content
+ * and size, not the order):
+ *   bytes 0-1   d    the group's fp32 scale (amax/127, 1.0 for an all-zero
+ *                    group) rounded to IEEE binary16 (nearest, ties to even)
+ *   bytes 2-3   sum  fl32(scale * sum of the 32 codes) rounded to binary16:
+ *                    the block's values as its codes give them
+ *   bytes 4-35  the 32 codes, channel order
+ * both halves little-endian.  d overflows to infinity for scales past 65504
+ * (|y| above about 8.3e6) and is 0 below 2^-25: the format's range.
+ *
+ *   x           bf16 [T, 2H] as above (read only; 16-byte aligned)
+ *   row_weight  fp32 [T], or NULL for weight 1 (4-byte aligned)
+ *   y_q8        uint8 [T, (H/32) * 36] the blocks (4-byte aligned)
+ * Sizes: any T >= 0 (T <= 2^31), H a multiple of 32 (H <= 2^22).
+ * Same ownership, asynchrony and error conventions as above.
+ */
+int silu_fwd_quant_q8_1(const void* x, const float* row_weight, void* y_q8, int64_t T, int64_t H, void* stream);
+
+/*
  * i8_gemm_group_scaled -- the consumer of the two quantised layouts.
  *
  * The fusion bullet of the page "kernelgen-challenge-9-task3-silu-quant"

@@ -28,8 +28,9 @@ _ERRORS = {
     7: (RuntimeError, "LAUNCH_FAILED"),
 }
 
-EXPORTED = ("silu_dot_fwd_bwd_quant_fuse", "silu_dot_fwd_bwd_quant_fuse_fp8", "silu_fwd_quant", "i8_gemm_group_scaled", "siluquant_prepare", "siluquant_strerror",
-            "siluquant_algorithmic_bytes", "siluquant_eval_sigmoid", "siluquant_eval_intermediates")
+EXPORTED = ("silu_dot_fwd_bwd_quant_fuse", "silu_dot_fwd_bwd_quant_fuse_fp8", "silu_fwd_quant", "silu_fwd_quant_q8_1",
+            "i8_gemm_group_scaled", "siluquant_prepare", "siluquant_strerror", "siluquant_algorithmic_bytes",
+            "siluquant_eval_sigmoid", "siluquant_eval_intermediates")
 
 _lib = None
 
@@ -55,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.siluquant_algorithmic_bytes.restype = i64
         L.silu_fwd_quant.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
         L.silu_fwd_quant.restype = ctypes.c_int
+        L.silu_fwd_quant_q8_1.argtypes = [vp, vp, vp, i64, i64, vp]
+        L.silu_fwd_quant_q8_1.restype = ctypes.c_int
         L.i8_gemm_group_scaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, vp]
         L.i8_gemm_group_scaled.restype = ctypes.c_int
         L.siluquant_eval_sigmoid.argtypes = [vp, vp, i64, vp]
@@ -184,6 +187,41 @@ def silu_fwd_quant(x, y_q, y_s, row_weight=None, y_bf16=None, group_size: int = 
                                         y_bf16.data_ptr() if y_bf16 is not None else None, T, H, group_size,
                                         torch.cuda.current_stream(dev).cuda_stream))
     _check(code, "silu_fwd_quant")
+
+
+Q8_1_BLOCK = 36  # bytes per 32 channels: binary16 d and sum, then 32 int8 codes
+
+
+def silu_fwd_quant_q8_1(x, y_q8, row_weight=None):
+    """Forward SwiGLU quantised in the q8_1 block layout: y = bf16((silu(gate)
+    * up) * row_weight[t]) from x = [gate | up] [T, 2H] (H a multiple of 32)
+    into y_q8 uint8 [T, (H/32) * 36]: per 32 channels the binary16 d (the
+    group scale, amax / 127) and sum (fl32(d * sum of the codes)), then the
+    32 int8 codes.  Enqueued on the current stream of x's device; returns None."""
+    import torch
+
+    if x.dim() != 2 or x.shape[1] % 2:
+        raise ValueError("x must be [T, 2H]")
+    T, H = int(x.shape[0]), int(x.shape[1]) // 2
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU; got %s" % dev)
+    checks = [("x", x, torch.bfloat16, (T, 2 * H)), ("y_q8", y_q8, torch.uint8, (T, (H // 32) * Q8_1_BLOCK))]
+    if row_weight is not None:
+        checks.append(("row_weight", row_weight, torch.float32, (T,)))
+    for name, t, dt, shape in checks:
+        if t.dtype != dt or t.device != dev or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+            raise ValueError("%s must be a contiguous %s tensor of shape %s on %s" % (name, dt, shape, dev))
+    with torch.cuda.device(dev):
+        code = int(lib().silu_fwd_quant_q8_1(x.data_ptr(), row_weight.data_ptr() if row_weight is not None else None,
+                                             y_q8.data_ptr(), T, H, torch.cuda.current_stream(dev).cuda_stream))
+    _check(code, "silu_fwd_quant_q8_1")
+
+
+def forward_q8_1_bytes(T: int, H: int, with_weight: bool = False) -> int:
+    """Bytes the q8_1 forward quantiser must move: x (4 per pair) in, 36 per
+    32 channels out, plus the row weights."""
+    return 4 * T * H + T * (H // 32) * Q8_1_BLOCK + (4 * T if with_weight else 0)
 
 
 GEMM_OUT_F32, GEMM_OUT_BF16 = 0, 1

@@ -1008,7 +1008,28 @@ struct FwdIn {
   uint4 g, u;
 };
 
-template <int kG>
+// Sum of the four signed bytes of a word.
+__device__ __forceinline__ int byte_sum(uint32_t w) {
+  return (int)(int8_t)(w & 0xffu) + (int)(int8_t)((w >> 8) & 0xffu) + (int)(int8_t)((w >> 16) & 0xffu) +
+         ((int)w >> 24);
+}
+
+// Sum over the four lanes of a DPP quad.
+__device__ __forceinline__ int quad_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
+  return v;
+}
+
+// IEEE binary16 bits of an fp32 value (v_cvt_f16_f32: nearest, ties to even;
+// subnormals kept).
+__device__ __forceinline__ uint32_t f16_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+
+// kQ81: the output is the q8_1 block layout of the page "kquant_mmq.rs" (kG
+// is 32): per row H/32 blocks of 36 bytes, the binary16 d (the group scale)
+// and sum (fl32(scale * sum of the codes)), then the 32 codes.  y_q then
+// points at the blocks (4-byte aligned) and y_s and y_bf16 are unused.
+template <int kG, bool kQ81 = false>
 __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ row_weight, int8_t* __restrict__ y_q,
     float* __restrict__ y_s, uint16_t* __restrict__ y_bf16, int64_t T, int64_t H, int tiles_h, int64_t units) {
@@ -1093,6 +1114,28 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
       c = codes8<true>(Yp, inv);
     else
       c = codes8<false>(Yp, inv);
+    if constexpr (kQ81) {
+      // A block is 4 lanes (a DPP quad); lane k of it stores its 8 codes at
+      // bytes 4 + 8k of the block (two 4-byte stores: blocks are 36 bytes
+      // apart), lane 0 the half2 (d, sum).  Assembling a unit's 144 bytes in
+      // LDS for 16-byte stores measured slower (235 us against 225 us at
+      // T = 16384, H = 11008).
+      static_assert(kG == 32, "q8_1 blocks are 32 channels");
+      const int qsum = quad_sum(byte_sum(c.x) + byte_sum(c.y));
+      if (t < T && live(h0)) {
+        uint32_t* blk = reinterpret_cast<uint32_t*>(y_q + t * (H / 32) * 36 + ((h0 + 8 * p) >> 5) * 36);
+        const int k = p & 3;
+        __builtin_nontemporal_store(c.x, blk + 1 + 2 * k);
+        __builtin_nontemporal_store(c.y, blk + 2 + 2 * k);
+        if (k == 0) __builtin_nontemporal_store(f16_bits(scale) | (f16_bits(scale * (float)qsum) << 16), blk);
+      }
+      in = in_next;
+      u = un;
+      t = tn;
+      h0 = h0n;
+      hb = hbn;
+      continue;
+    }
     const uint2 other = make_uint2(swap_neighbour(c.x), swap_neighbour(c.y));
     if (t < T && live(h0)) {
       // Plain non-temporal stores: for this write-light pass they measured
@@ -1270,6 +1313,27 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
   return SILUQUANT_OK;
 }
 
+using ForwardKernel = void (*)(const uint16_t*, const float*, int8_t*, float*, uint16_t*, int64_t, int64_t, int,
+                               int64_t);
+
+// Persistent grid for the forward quantiser: units of 4 rows x 128 channels,
+// one per wave, as many workgroups as fit on the device or as the units need.
+int launch_forward(ForwardKernel kernel, const void* x, const float* row_weight, int8_t* y_q, float* y_s,
+                   void* y_bf16, int64_t T, int64_t H, void* stream) {
+  int dev = 0;
+  int rc = ensure_table(&dev);
+  if (rc != SILUQUANT_OK) return rc;
+  const int tiles_h = (int)((H + kTile - 1) / kTile);
+  const int64_t units = ((T + 3) / 4) * tiles_h;
+  int64_t grid = (int64_t)g_cu_count[dev] * kFwdWorkgroupsPerCU;
+  const int64_t wg_needed = (units + kFwdThreads / 64 - 1) / (kFwdThreads / 64);
+  if (wg_needed < grid) grid = wg_needed;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kFwdThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(x), row_weight, y_q, y_s, static_cast<uint16_t*>(y_bf16), T, H,
+                     tiles_h, units);
+  return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1335,21 +1399,27 @@ __attribute__((visibility("default"))) int silu_fwd_quant(const void* x, const f
   for (int i = 0; i < 5; ++i)
     for (int j = i + 1; j < 5; ++j)
       if (bufs[i] && bufs[j] && overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
-  int dev = 0;
-  int rc = ensure_table(&dev);
-  if (rc != SILUQUANT_OK) return rc;
-  const int tiles_h = (int)((H + kTile - 1) / kTile);
-  const int64_t units = ((T + 3) / 4) * tiles_h;
-  const int64_t waves_needed = units;
-  int64_t grid = (int64_t)g_cu_count[dev] * kFwdWorkgroupsPerCU;
-  const int64_t wg_needed = (waves_needed + kFwdThreads / 64 - 1) / (kFwdThreads / 64);
-  if (wg_needed < grid) grid = wg_needed;
   auto kernel = group == 128 ? silu_fwd_quant_kernel<128> : group == 64 ? silu_fwd_quant_kernel<64>
                                                                       : silu_fwd_quant_kernel<32>;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kFwdThreads), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(x), row_weight, y_q, y_s,
-                     static_cast<uint16_t*>(y_bf16), T, H, tiles_h, units);
-  return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;
+  return launch_forward(kernel, x, row_weight, y_q, y_s, y_bf16, T, H, stream);
+}
+
+__attribute__((visibility("default"))) int silu_fwd_quant_q8_1(const void* x, const float* row_weight, void* y_q8,
+                                                               int64_t T, int64_t H, void* stream) {
+  // blocks of 32 channels (the page's k % 32 == 0)
+  if (T < 0 || H < 0 || H % 32 != 0) return SILUQUANT_ERR_BAD_SHAPE;
+  if (T == 0 || H == 0) return SILUQUANT_OK;
+  if (T > (int64_t(1) << 31) || H > (int64_t(1) << 22) || T > (int64_t(1) << 40) / H) return SILUQUANT_ERR_BAD_SHAPE;
+  if (!x || !y_q8) return SILUQUANT_ERR_NULL_PTR;
+  auto mis = [](const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; };
+  if (mis(x, 16) || mis(y_q8, 4) || (row_weight && mis(row_weight, 4))) return SILUQUANT_ERR_MISALIGNED;
+  const void* bufs[3] = {x, row_weight, y_q8};
+  const int64_t sizes[3] = {4 * T * H, 4 * T, T * (H / 32) * 36};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (bufs[i] && bufs[j] && overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
+  return launch_forward(silu_fwd_quant_kernel<32, true>, x, row_weight, static_cast<int8_t*>(y_q8), nullptr,
+                        nullptr, T, H, stream);
 }
 
 __attribute__((visibility("default"))) int siluquant_eval_sigmoid(const void* gate, float* s, int64_t n,

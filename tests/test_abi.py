@@ -171,6 +171,19 @@ def test_forward_rejects_bad_arguments(lib):
     assert f(None, None, None, None, None, 0, 256, 128, None) == 0
 
 
+def test_forward_q8_1_rejects_bad_arguments(lib):
+    f = lib.silu_fwd_quant_q8_1
+    assert f(BASE, None, BASE + 2**24, 8, 48, None) == 2      # H not a multiple of 32
+    assert f(BASE, None, BASE + 2**24, -1, 64, None) == 2
+    assert f(None, None, BASE + 2**24, 8, 64, None) == 1
+    assert f(BASE, None, None, 8, 64, None) == 1
+    assert f(BASE + 8, None, BASE + 2**24, 8, 64, None) == 4  # x off 16 bytes
+    assert f(BASE, None, BASE + 2**24 + 2, 8, 64, None) == 4  # blocks off 4 bytes
+    assert f(BASE, BASE + 2**26 + 2, BASE + 2**24, 8, 64, None) == 4
+    assert f(BASE, None, BASE + 256, 8, 64, None) == 5        # blocks inside x
+    assert f(None, None, None, 0, 64, None) == 0
+
+
 def test_gemm_rejects_bad_arguments(lib):
     f = lib.i8_gemm_group_scaled
     A, sA, B, sB, C = BASE, BASE + 2**26, BASE + 2**27, BASE + 2**28, BASE + 2**29
