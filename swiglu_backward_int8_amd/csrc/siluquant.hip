@@ -1117,17 +1117,19 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
     if constexpr (kQ81) {
       // A block is 4 lanes (a DPP quad); lane k of it stores its 8 codes at
       // bytes 4 + 8k of the block (two 4-byte stores: blocks are 36 bytes
-      // apart), lane 0 the half2 (d, sum).  Assembling a unit's 144 bytes in
-      // LDS for 16-byte stores measured slower (235 us against 225 us at
-      // T = 16384, H = 11008).
+      // apart), lane 0 the half2 (d, sum).  The stores are plain, so that the
+      // 4-byte pieces of a line merge in L2: non-temporal ones reached DRAM
+      // as 1.27x the bytes and took 228 us against 178 us at T = 16384,
+      // H = 11008.  Assembling a unit's 144 bytes in LDS for 16-byte stores
+      // was slower too.
       static_assert(kG == 32, "q8_1 blocks are 32 channels");
       const int qsum = quad_sum(byte_sum(c.x) + byte_sum(c.y));
       if (t < T && live(h0)) {
         uint32_t* blk = reinterpret_cast<uint32_t*>(y_q + t * (H / 32) * 36 + ((h0 + 8 * p) >> 5) * 36);
         const int k = p & 3;
-        __builtin_nontemporal_store(c.x, blk + 1 + 2 * k);
-        __builtin_nontemporal_store(c.y, blk + 2 + 2 * k);
-        if (k == 0) __builtin_nontemporal_store(f16_bits(scale) | (f16_bits(scale * (float)qsum) << 16), blk);
+        blk[1 + 2 * k] = c.x;
+        blk[2 + 2 * k] = c.y;
+        if (k == 0) blk[0] = f16_bits(scale) | (f16_bits(scale * (float)qsum) << 16);
       }
       in = in_next;
       u = un;
