@@ -121,3 +121,51 @@ def test_gemm_at_the_k_limit():
     got = C[rows][:, cols].cpu().numpy().astype(np.float64)
     bound = (K // 128 + 2) * 2.0**-24 * want_abs
     assert np.all(np.abs(got - want) <= bound), (got, want)
+
+
+def test_straddling_kernel_at_the_channel_limit():
+    # H = 2^22 - 8 with group 128: r = 120, so the windows run one block past
+    # H (H + r > 2^22) and a window lane's offset in x comes close to 2^31.
+    # The first 256 and the last 256 channels of the row are checked: the
+    # straddling group holds d_gate's last 120 channels and d_up's first 8.
+    T, H, G = 128, (1 << 22) - 8, 128
+    print("case straddle T=128 H=2^22-8", flush=True)
+    x, dy = _inputs(T, H, 5)
+    gq, gs, yq, ys = sq.empty_outputs(T, H, DEV, group=G)
+    sq.silu_dot_fwd_bwd_quant_fuse(x, dy, gq, gs, yq, ys, group_size=G)
+    torch.cuda.synchronize()
+    _, D = oracle.intermediates(_bits(torch.cat([x[:, H - 256:H], x[:, 2 * H - 256:]], dim=1)),
+                                _bits(dy[:, H - 256:]))
+    _, D0 = oracle.intermediates(_bits(torch.cat([x[:, :256], x[:, H:H + 256]], dim=1)), _bits(dy[:, :256]))
+    # concatenated row positions H - 120 .. H + 7: d_gate's last 120, d_up's first 8
+    j = (H - 120) // G
+    gq_np, gs_np = gq.cpu().numpy(), gs.cpu().numpy()
+    for t in range(T):
+        seg = np.concatenate([D[t, 256 - 120:256], D0[t, 256:256 + 8]])
+        q, s = oracle.quant_group(seg)
+        assert s == gs_np[t, j] and np.array_equal(q, gq_np[t, H - 120:H + 8]), t
+        # the last group of the row: d_up's last 2H - (H + 8) = H - 8 ... its
+        # final (2H) % 128 = 112 positions
+        n = (2 * H) % G
+        q, s = oracle.quant_group(D[t, 512 - n:512])
+        assert s == gs_np[t, -1] and np.array_equal(q, gq_np[t, 2 * H - n:]), t
+    del x, dy, gq, gs, yq, ys
+    torch.cuda.empty_cache()
+
+
+def test_straddling_kernel_at_the_token_limit():
+    # T = 2^23, H = 8, group 32: every row is a single partial group of 16
+    # (8 of d_gate, 8 of d_up), in one block; y_q_t rows are 8 MiB long
+    T, H, G = 1 << 23, 8, 32
+    print("case straddle T=2^23 H=8", flush=True)
+    x, dy = _inputs(T, H, 6)
+    gq, gs, yq, ys = sq.empty_outputs(T, H, DEV, group=G)
+    sq.silu_dot_fwd_bwd_quant_fuse(x, dy, gq, gs, yq, ys, group_size=G)
+    torch.cuda.synchronize()
+    for t0 in (0, T // 2 + 96, T - 256):
+        want = oracle.silu_dot_fwd_bwd_quant_fuse(_bits(x[t0:t0 + 256]), _bits(dy[t0:t0 + 256]), group_size=G)
+        got = (gq[t0:t0 + 256].cpu().numpy(), gs[t0:t0 + 256].cpu().numpy(),
+               yq[:, t0:t0 + 256].cpu().numpy(), ys[:, t0 // G:t0 // G + 256 // G].cpu().numpy())
+        _equal("straddle T=2^23 tokens %d.." % t0, got, want)
+    del x, dy, gq, gs, yq, ys
+    torch.cuda.empty_cache()
