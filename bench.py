@@ -91,6 +91,32 @@ def cpu_baseline(x, dy, w, min_seconds: float = 10.0, max_calls: int = 5, fp8: b
     }
 
 
+def launch_distribution(step, stream, n: int, dev):
+    """After the timed region: per-launch durations of n more calls (an event
+    between every two), as median, 10th and 90th percentile, and one cold
+    call after 1 GiB of writes has flushed the caches, all in microseconds."""
+    import torch
+
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    evs[0].record(stream)
+    for i in range(n):
+        step(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    d = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n))
+    pick = lambda f: round(d[min(n - 1, int(f * n))], 2)
+    flush = torch.empty(2**30, dtype=torch.uint8, device=dev)
+    flush.fill_(1)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    step(0)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    del flush
+    return {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9), "calls": n,
+            "cold": round(c0.elapsed_time(c1) * 1e3, 2)}
+
+
 def stream_probes(dev, reps: int = 20):
     """Plain streaming kernels of known size, for the attainable bandwidth and for
     scaling hardware byte counters: a 1 GiB copy (1 GiB read + 1 GiB written) and
@@ -319,6 +345,7 @@ def main():
     per_launch_s = gpu_ms / 1e3 / args.steps
     achieved = nbytes / per_launch_s / 1e9
     value = nbytes * args.steps / wall / 1e9
+    timing = launch_distribution(step, stream, min(args.steps, 50), dev)
     metric = "achieved HBM GB/s (+% of MI355X peak) for fused silu fwd/bwd+int8 quant"
     if q8_1:
         metric = "achieved HBM GB/s (+% of MI355X peak) for fused silu forward + q8_1 block quant"
@@ -357,6 +384,7 @@ def main():
                        "fp8": "silu_quant_bwd_kernel<Fmt::kFp8>"}.get(args.op, "silu_quant_bwd_kernel<Fmt::kInt8>"),
             "avg_launch_us": round(per_launch_s * 1e6, 3),
         },
+        "launch_us": timing,
         "cpu_baseline": None,
     }
     if args.probes:
