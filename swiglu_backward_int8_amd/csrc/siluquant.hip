@@ -23,11 +23,18 @@
 //     table is built once per device with fp64 exp rounded to fp32, which makes
 //     the sigmoid bit-exact rather than within an ulp;
 //   * group maxima: each lane reduces inside its registers, writes partial
-//     maxima to LDS, and one thread per group (384 groups per tile) finishes
-//     the reduction and computes scale and inverse with IEEE division;
+//     maxima to LDS, and one thread per group (384 groups per tile at group
+//     128) finishes the reduction and computes scale and inverse with IEEE
+//     division;
 //   * grad_input_q is stored straight from registers (a wave writes four whole
 //     128-byte row segments); y_q_t goes through an XOR-swizzled LDS transpose
 //     so that it, too, leaves in whole 128-byte rows.
+//
+// The same kernel, templated on the code format, writes OCP FP8 E4M3 codes
+// (silu_dot_fwd_bwd_quant_fuse_fp8).  The file also holds the forward
+// quantiser of the page "kquant_mmq.rs" (silu_fwd_quant_kernel: fp32 scales,
+// or the page's q8_1 blocks) and small diagnostic kernels that run the
+// sigmoid and elementwise helpers on their own for the tests.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
