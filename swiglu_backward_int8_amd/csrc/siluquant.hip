@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -1181,6 +1182,191 @@ __device__ __forceinline__ float sigma_of(uint32_t gb, int64_t i) {
   return g_sigma_tab[((i & 1) ? hi : lo) >> 2];
 }
 
+// ---------------------------------------------------------------------------
+// H not a multiple of 8: rows start off 16 bytes, so the tiled kernels' wide
+// loads do not apply.  A plain path with the same arithmetic: 2-byte loads,
+// byte stores, the sigmoid from the device table, a wave per 128 positions of
+// a row and a lane per channel for the token groups.  Grid-stride loops cover
+// any size.
+
+// One code of a value with inverse scale inv (the low byte).
+template <Fmt F, bool kSafe>
+__device__ __forceinline__ uint32_t code1(float v, float inv) {
+  if constexpr (F == Fmt::kInt8)
+    return code_word<kSafe>(v, inv) & 0xffu;
+  else
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fp8_input<kSafe>(v, inv), 0.0f, 0, false) & 0xffu;
+}
+
+// Maximum over the lanes of a group: all 64, or each 32-lane half for
+// groups of 32.
+template <int kWidth>
+__device__ __forceinline__ float lanes_max(float m) {
+#pragma unroll
+  for (int off = kWidth / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  return m;
+}
+
+// A wave takes 128 consecutive positions of a row (128 / kG groups): lane l
+// the positions l and l + 64, whose groups are reduced over the lanes that
+// share them.  Returns the scale of the lane's group for each of its two
+// positions; a group's first lane stores it at scale_row[group].
+template <Fmt F, int kG>
+__device__ __forceinline__ void narrow_groups(const float (&a)[2], float (&scale)[2], float* scale_row, int64_t c0,
+                                              int64_t n_row, int lane) {
+  float m[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) m[k] = kG == 32 ? lanes_max<32>(a[k]) : lanes_max<64>(a[k]);
+  if (kG == 128) m[0] = m[1] = fmaxf(m[0], m[1]);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    scale[k] = group_scale<F>(m[k]);
+    const int64_t c = c0 + lane + 64 * k;
+    if ((kG < 128 || k == 0) && lane % (kG < 64 ? kG : 64) == 0 && c < n_row) scale_row[c / kG] = scale[k];
+  }
+}
+
+// Row groups of the 2H-long row [d_gate | d_up].
+template <Fmt F, int kG>
+__global__ __launch_bounds__(256) void silu_quant_rows_narrow_kernel(const uint16_t* __restrict__ x,
+                                                                     const uint16_t* __restrict__ grad_y,
+                                                                     uint8_t* __restrict__ grad_input_q,
+                                                                     float* __restrict__ grad_input_s, int64_t T,
+                                                                     int64_t H) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row_groups = (2 * H + kG - 1) / kG, units = (2 * H + 127) / 128;
+  const int64_t waves = (int64_t)gridDim.x * 4;
+  for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < T * units; w += waves) {
+    const int64_t t = w / units, c0 = (w - t * units) * 128;
+    float v[2], a[2], scale[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t c = c0 + lane + 64 * k, h = c < H ? c : c - H;
+      v[k] = a[k] = 0.0f;
+      if (c < 2 * H) {
+        const uint32_t gb = x[t * 2 * H + h];
+        float y, dg, du;
+        pair_f32(sigma_of(gb, 0), bf16_lo(gb), bf16_lo(x[t * 2 * H + H + h]), bf16_lo(grad_y[t * H + h]), y, dg,
+                 du);
+        const float val = c < H ? dg : du;
+        a[k] = fabsf(val);
+        v[k] = bf16_lo(pack_bf16(val, 0.0f));
+      }
+    }
+    narrow_groups<F, kG>(a, scale, grad_input_s + t * row_groups, c0, 2 * H, lane);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t c = c0 + lane + 64 * k;
+      const float inv = 1.0f / scale[k];
+      if (c < 2 * H)
+        grad_input_q[t * 2 * H + c] =
+            (uint8_t)(inv == __builtin_huge_valf() ? code1<F, true>(v[k], inv) : code1<F, false>(v[k], inv));
+    }
+  }
+}
+
+// Token groups of y^T: lane l of a 64-thread workgroup takes channel
+// 64 b + l of group g for work item (b, g); the group's kG values of y stay
+// in registers between the maximum and the codes.
+template <Fmt F, int kG>
+__global__ __launch_bounds__(64) void silu_quant_cols_narrow_kernel(const uint16_t* __restrict__ x,
+                                                                    uint8_t* __restrict__ y_q_t,
+                                                                    float* __restrict__ y_s_t, int64_t T,
+                                                                    int64_t H) {
+  const int64_t col_groups = (T + kG - 1) / kG, hblocks = (H + 63) / 64;
+  for (int64_t item = blockIdx.x; item < col_groups * hblocks; item += gridDim.x) {
+    const int64_t g = item / hblocks, h = (item - g * hblocks) * 64 + threadIdx.x, t0 = g * kG;
+    if (h >= H) continue;
+    const int n = T - t0 < kG ? (int)(T - t0) : kG;
+    uint32_t yb[kG / 2];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kG; ++i) {
+      float yv = 0.0f;
+      if (i < n) {
+        const uint32_t gb = x[(t0 + i) * 2 * H + h];
+        const float silu = bf16_lo(gb) * sigma_of(gb, 0);
+        yv = silu * bf16_lo(x[(t0 + i) * 2 * H + H + h]);
+        m = fmaxf(m, fabsf(yv));
+      }
+      const uint32_t b = pack_bf16(yv, 0.0f) & 0xffffu;
+      yb[i / 2] = (i & 1) ? (yb[i / 2] | (b << 16)) : b;
+    }
+    const float scale = group_scale<F>(m);
+    const float inv = 1.0f / scale;
+    const bool safe = inv == __builtin_huge_valf();
+    uint8_t* row = y_q_t + h * T + t0;
+    if ((T & 15) == 0 && n == kG) {
+      // rows of y^T start on 16 bytes: the lane's kG codes as 16-byte pieces
+#pragma unroll
+      for (int q = 0; q < kG / 16; ++q) {
+        uint32_t wd[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wd[e] = 0;
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const int i = 16 * q + 4 * e + bb;
+            const float yv = (i & 1) ? bf16_hi(yb[i / 2]) : bf16_lo(yb[i / 2]);
+            wd[e] |= (safe ? code1<F, true>(yv, inv) : code1<F, false>(yv, inv)) << (8 * bb);
+          }
+        }
+        *reinterpret_cast<uint4*>(row + 16 * q) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kG; ++i) {
+        if (i < n) {
+          const float yv = (i & 1) ? bf16_hi(yb[i / 2]) : bf16_lo(yb[i / 2]);
+          row[i] = (uint8_t)(safe ? code1<F, true>(yv, inv) : code1<F, false>(yv, inv));
+        }
+      }
+    }
+    y_s_t[h * col_groups + g] = scale;
+  }
+}
+
+// The forward quantiser's rows (H-long), 128 positions per wave as above.
+template <int kG>
+__global__ __launch_bounds__(256) void silu_fwd_quant_narrow_kernel(const uint16_t* __restrict__ x,
+                                                                    const float* __restrict__ row_weight,
+                                                                    int8_t* __restrict__ y_q, float* __restrict__ y_s,
+                                                                    uint16_t* __restrict__ y_bf16, int64_t T,
+                                                                    int64_t H) {
+  const int lane = threadIdx.x & 63;
+  const int64_t groups = (H + kG - 1) / kG, units = (H + 127) / 128;
+  const int64_t waves = (int64_t)gridDim.x * 4;
+  for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < T * units; w += waves) {
+    const int64_t t = w / units, c0 = (w - t * units) * 128;
+    const float wt = row_weight != nullptr ? row_weight[t] : 1.0f;
+    uint32_t b[2];
+    float a[2], scale[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t h = c0 + lane + 64 * k;
+      float yv = 0.0f;
+      if (h < H) {
+        const uint32_t gb = x[t * 2 * H + h];
+        yv = (bf16_lo(gb) * sigma_of(gb, 0)) * bf16_lo(x[t * 2 * H + H + h]);
+        if (row_weight != nullptr) yv = yv * wt;
+      }
+      a[k] = fabsf(yv);
+      b[k] = pack_bf16(yv, 0.0f) & 0xffffu;
+    }
+    narrow_groups<Fmt::kInt8, kG>(a, scale, y_s + t * groups, c0, H, lane);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t h = c0 + lane + 64 * k;
+      const float inv = 1.0f / scale[k], yv = bf16_lo(b[k]);
+      if (h < H) {
+        y_q[t * H + h] = (int8_t)(inv == __builtin_huge_valf() ? code1<Fmt::kInt8, true>(yv, inv)
+                                                               : code1<Fmt::kInt8, false>(yv, inv));
+        if (y_bf16 != nullptr) y_bf16[t * H + h] = (uint16_t)b[k];
+      }
+    }
+  }
+}
+
 __global__ void eval_sigmoid_kernel(const uint16_t* __restrict__ gate, float* __restrict__ s, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
@@ -1249,8 +1435,7 @@ template <Fmt F>
 int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float* grad_input_s, void* y_q_t,
                     float* y_s_t, int64_t T, int64_t H, int64_t group, void* stream) {
   if (group != 32 && group != 64 && group != 128) return SILUQUANT_ERR_BAD_GROUP;
-  // Rows of every tensor start on 16 bytes: H a multiple of 8.
-  if (T < 0 || H < 0 || H % 8 != 0) return SILUQUANT_ERR_BAD_SHAPE;
+  if (T < 0 || H < 0) return SILUQUANT_ERR_BAD_SHAPE;
   if (T == 0 || H == 0) return SILUQUANT_OK;
   // Tile indices are int; a lane's byte offset inside a tile (< 512 * H for x)
   // must fit in 32 bits, and a tile's span (128 rows of 4H bytes of x, of 2H
@@ -1279,6 +1464,27 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
   int rc = ensure_table(&dev);
   if (rc != SILUQUANT_OK) return rc;
 
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+  const uint16_t* dys = static_cast<const uint16_t*>(grad_y);
+  if (H % 8 != 0) {
+    // rows off 16 bytes: the plain path, a kernel per quantisation axis
+    const int64_t row_waves = T * ((2 * H + 127) / 128);
+    const int64_t col_items = ((T + group - 1) / group) * ((H + 63) / 64);
+    const int64_t rows_grid = std::min<int64_t>((row_waves + 3) / 4, (int64_t)g_cu_count[dev] * 16);
+    const int64_t cols_grid = std::min<int64_t>(col_items, (int64_t)g_cu_count[dev] * 64);
+    auto rows = group == 128 ? silu_quant_rows_narrow_kernel<F, 128>
+                : group == 64 ? silu_quant_rows_narrow_kernel<F, 64>
+                              : silu_quant_rows_narrow_kernel<F, 32>;
+    hipLaunchKernelGGL(rows, dim3((unsigned)rows_grid), dim3(256), 0, s, xs, dys,
+                       static_cast<uint8_t*>(grad_input_q), grad_input_s, T, H);
+    auto cols = group == 128 ? silu_quant_cols_narrow_kernel<F, 128>
+                : group == 64 ? silu_quant_cols_narrow_kernel<F, 64>
+                              : silu_quant_cols_narrow_kernel<F, 32>;
+    hipLaunchKernelGGL(cols, dim3((unsigned)cols_grid), dim3(64), 0, s, xs, static_cast<uint8_t*>(y_q_t), y_s_t, T,
+                       H);
+    return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;
+  }
   const int tiles_h = (int)tiles_h64;
   const int tiles = (int)(tiles_t * tiles_h64);
   // Persistent grid: as many workgroups as fit on the device at once (a
@@ -1286,9 +1492,6 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
   int grid = g_cu_count[dev] * kWorkgroupsPerCU;
   grid = grid >= 8 ? grid - grid % 8 : grid;
   if (tiles < grid) grid = tiles;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const uint16_t* xs = static_cast<const uint16_t*>(x);
-  const uint16_t* dys = static_cast<const uint16_t*>(grad_y);
   int8_t* gq = static_cast<int8_t*>(grad_input_q);
   int8_t* yq = static_cast<int8_t*>(y_q_t);
   if (r == 0) {
@@ -1361,7 +1564,7 @@ __attribute__((visibility("default"))) const char* siluquant_strerror(int status
   switch (status) {
     case SILUQUANT_OK: return "ok";
     case SILUQUANT_ERR_NULL_PTR: return "a buffer pointer is NULL";
-    case SILUQUANT_ERR_BAD_SHAPE: return "sizes must be non-negative and within the limits, H a multiple of 8 and K of the group";
+    case SILUQUANT_ERR_BAD_SHAPE: return "sizes must be non-negative and within the limits, K a multiple of the group, H of 32 for q8_1 blocks";
     case SILUQUANT_ERR_BAD_GROUP: return "unsupported group size (the passes take 128, 64 or 32; the forward pass and the GEMM 128)";
     case SILUQUANT_ERR_MISALIGNED: return "a buffer is not aligned (code and input tensors 16 bytes, scales 4 bytes)";
     case SILUQUANT_ERR_OVERLAP: return "buffers overlap";
@@ -1394,8 +1597,7 @@ __attribute__((visibility("default"))) int silu_fwd_quant(const void* x, const f
                                                           float* y_s, void* y_bf16, int64_t T, int64_t H,
                                                           int64_t group, void* stream) {
   if (group != 32 && group != 64 && group != 128) return SILUQUANT_ERR_BAD_GROUP;
-  // Rows start on 16 bytes (x, y_bf16) and 8 bytes (y_q): H a multiple of 8.
-  if (T < 0 || H < 0 || H % 8 != 0) return SILUQUANT_ERR_BAD_SHAPE;
+  if (T < 0 || H < 0) return SILUQUANT_ERR_BAD_SHAPE;
   if (T == 0 || H == 0) return SILUQUANT_OK;
   if (T > (int64_t(1) << 31) || H > (int64_t(1) << 22) || T > (int64_t(1) << 40) / H) return SILUQUANT_ERR_BAD_SHAPE;
   if (!x || !y_q || !y_s) return SILUQUANT_ERR_NULL_PTR;
@@ -1409,6 +1611,20 @@ __attribute__((visibility("default"))) int silu_fwd_quant(const void* x, const f
   for (int i = 0; i < 5; ++i)
     for (int j = i + 1; j < 5; ++j)
       if (bufs[i] && bufs[j] && overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
+  if (H % 8 != 0) {
+    // rows off 16 bytes (x, y_bf16) and 8 bytes (y_q): the plain path
+    int dev = 0;
+    int rc = ensure_table(&dev);
+    if (rc != SILUQUANT_OK) return rc;
+    const int64_t waves = T * ((H + 127) / 128);
+    const int64_t grid = std::min<int64_t>((waves + 3) / 4, (int64_t)g_cu_count[dev] * 16);
+    auto kernel = group == 128 ? silu_fwd_quant_narrow_kernel<128>
+                  : group == 64 ? silu_fwd_quant_narrow_kernel<64>
+                                : silu_fwd_quant_narrow_kernel<32>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint16_t*>(x), row_weight, y_q, y_s, static_cast<uint16_t*>(y_bf16), T, H);
+    return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;
+  }
   auto kernel = group == 128 ? silu_fwd_quant_kernel<128> : group == 64 ? silu_fwd_quant_kernel<64>
                                                                       : silu_fwd_quant_kernel<32>;
   return launch_forward(kernel, x, row_weight, y_q, y_s, y_bf16, T, H, stream);

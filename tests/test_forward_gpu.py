@@ -100,8 +100,8 @@ def test_empty_and_errors():
         sq.silu_fwd_quant(x, torch.empty((8, 200), dtype=torch.int8, device=DEV),
                           torch.empty((8, 1), dtype=torch.float32, device=DEV))
     x, _ = random_inputs(8, 100, device=DEV)
-    with pytest.raises(ValueError):  # H not a multiple of 8
-        sq.silu_fwd_quant(x, torch.empty((8, 100), dtype=torch.int8, device=DEV),
+    with pytest.raises(ValueError):  # y_q must be [8, 100]
+        sq.silu_fwd_quant(x, torch.empty((8, 104), dtype=torch.int8, device=DEV),
                           torch.empty((8, 1), dtype=torch.float32, device=DEV))
 
 
@@ -139,3 +139,12 @@ def test_forward_partial_groups(T, H, group):
 def test_forward_groups_workload(group):
     x, _ = make_inputs("t32768_h2048_outliers", device=DEV)
     check(x, label="outliers group=%d" % group, group=group)
+
+
+# H not a multiple of 8: the plain path (2-byte loads, byte stores).
+@pytest.mark.parametrize("T,H,group", [(100, 100, 128), (64, 5, 32), (300, 1001, 64), (17, 1, 128), (129, 2050, 32)])
+def test_forward_h_not_a_multiple_of_8(T, H, group):
+    x, _ = random_inputs(T, H, device=DEV, seed=5 * T + H + group)
+    w = torch.rand(T, device=DEV, generator=torch.Generator(device=DEV).manual_seed(T)) * 4 - 2
+    check(x, label="narrow T=%d H=%d group=%d" % (T, H, group), group=group)
+    check(x, w=w, want_bf16=True, label="narrow T=%d H=%d group=%d weighted" % (T, H, group), group=group)

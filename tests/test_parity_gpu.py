@@ -223,9 +223,9 @@ def test_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):
         x2, dy2 = random_inputs(200, 128, device=DEV)
         sq.silu_dot_fwd_bwd_quant_fuse(x2, dy2, *sq.empty_outputs(128, 128, DEV))
-    with pytest.raises(ValueError):  # H not a multiple of 8
+    with pytest.raises(ValueError):  # outputs for another H
         x3, dy3 = random_inputs(128, 100, device=DEV)
-        sq.silu_dot_fwd_bwd_quant_fuse(x3, dy3, *sq.empty_outputs(128, 100, DEV))
+        sq.silu_dot_fwd_bwd_quant_fuse(x3, dy3, *sq.empty_outputs(128, 104, DEV))
     with pytest.raises(ValueError):
         sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *outs, group_size=64)
 
@@ -291,8 +291,8 @@ def test_smaller_groups_fp8_and_overflowed_inverse(group):
 
 def test_group_size_errors():
     x, dy = random_inputs(128, 100, device=DEV)
-    with pytest.raises(ValueError):  # 100 is not a multiple of 8
-        sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *sq.empty_outputs(128, 100, DEV, group=64), group_size=64)
+    with pytest.raises(ValueError):  # scales shaped for group 128
+        sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *sq.empty_outputs(128, 100, DEV), group_size=64)
     x, dy = random_inputs(128, 96, device=DEV)
     with pytest.raises(ValueError):
         sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *sq.empty_outputs(128, 96, DEV, group=32), group_size=48)
@@ -385,3 +385,28 @@ def test_hip_graph_capture_and_replay():
         want, want_abs = oracle.i8_gemm_group_scaled(outs[0].cpu().numpy(), outs[1].cpu().numpy(), W.cpu().numpy(),
                                                      sW.cpu().numpy(), b_rows_per_scale=128)
         assert np.all(np.abs(C.cpu().numpy() - want) <= (2 * H // 128 + 2) * 2.0**-24 * want_abs)
+
+
+# H not a multiple of 8: rows start off 16 bytes and a plain path with 2-byte
+# loads and byte stores runs; groups still straddle d_gate and d_up.
+@pytest.mark.parametrize("T,H,group", [(256, 100, 128), (129, 1, 32), (64, 3, 128), (300, 1001, 64),
+                                       (1000, 2050, 128), (77, 13, 32), (4096, 1410, 128), (1, 250, 64)])
+def test_h_not_a_multiple_of_8(T, H, group):
+    print("case narrow", T, H, group, flush=True)
+    x, dy = random_inputs(T, H, device=DEV, seed=7 * T + H + group)
+    check_group(x, dy, group, "narrow T=%d H=%d group=%d" % (T, H, group))
+
+
+@pytest.mark.parametrize("T,H,group", [(256, 100, 128), (300, 1001, 32)])
+def test_h_not_a_multiple_of_8_fp8_and_edges(T, H, group):
+    x, dy = random_inputs(T, H, device=DEV, seed=T + H)
+    check_group(x, dy, group, "narrow fp8 T=%d H=%d group=%d" % (T, H, group), fp8=True)
+    # a saturated gate, a group of tiny values whose inverse overflows, zero rows
+    x, dy = _const(T, H, 20.0, 0.0, 1.0)
+    tiny = torch.tensor([2.0**-130, -(2.0**-131), 0.0, 2.0**-133], dtype=torch.float32).to(torch.bfloat16).to(DEV)
+    x[:, 2 * H - 4:] = tiny
+    dy[:, :group] = 0.0
+    x[7] = 0.0
+    dy[9] = 0.0
+    check_group(x, dy, group, "narrow tiny T=%d H=%d group=%d" % (T, H, group))
+    check_group(x, dy, group, "narrow tiny fp8 T=%d H=%d group=%d" % (T, H, group), fp8=True)
