@@ -27,7 +27,8 @@ extern "C" {
 enum siluquant_status {
   SILUQUANT_OK = 0,
   SILUQUANT_ERR_NULL_PTR = 1,      /* a buffer pointer is NULL while T*H > 0 */
-  SILUQUANT_ERR_BAD_SHAPE = 2,     /* T < 0, H < 0, H not a multiple of 8 (K of the group), or too large */
+  SILUQUANT_ERR_BAD_SHAPE = 2,     /* T < 0, H < 0, too large, H not a multiple of 32 (q8_1 blocks)
+                                      or K not a multiple of the group (GEMM) */
   SILUQUANT_ERR_BAD_GROUP = 3,     /* a group size the entry point does not take */
   SILUQUANT_ERR_MISALIGNED = 4,    /* x, grad_y, grad_input_q, y_q_t not 16-byte aligned,
                                       or a scale buffer not 4-byte aligned */
@@ -69,11 +70,13 @@ enum siluquant_status {
  *   row position group * floor(H/group) holds the last H % group channels of
  *   d_gate and the first channels of d_up.  Any other group returns
  *   SILUQUANT_ERR_BAD_GROUP.
- * Sizes: any T >= 0, H >= 0 a multiple of 8 (every row then starts on 16
- *   bytes; T == 0 or H == 0 is a no-op that returns SILUQUANT_OK), T <= 2^23,
- *   H <= 2^22.  y_q_t is written with 16-byte stores when T % 16 == 0; other T
- *   work, with narrower stores.  H a multiple of `group` takes the aligned
- *   kernel; other H a second kernel with two work items per tile.
+ * Sizes: any T >= 0 and H >= 0 (T == 0 or H == 0 is a no-op that returns
+ *   SILUQUANT_OK), T <= 2^23, H <= 2^22.  y_q_t is written with 16-byte
+ *   stores when T % 16 == 0; other T work, with narrower stores.  The results
+ *   do not depend on the kernel that runs: H a multiple of `group` takes the
+ *   tiled kernel; other multiples of 8 a second tiled kernel with two work
+ *   items per tile; H not a multiple of 8 (rows then start off 16 bytes) a
+ *   slower path with 2-byte loads.
  * Ownership: the caller allocates and owns every buffer; the library keeps no
  *   pointer after the call returns.  Buffers must not overlap.
  * Asynchrony: the work is enqueued on `stream` and the call returns without
@@ -126,9 +129,9 @@ int silu_dot_fwd_bwd_quant_fuse_fp8(const void* x, const void* grad_y, void* gra
  *   y_q         int8 [T, H]       codes (16-byte aligned)
  *   y_s         fp32 [T, ceil(H/group)] one scale per group (4-byte aligned)
  *   y_bf16      bf16 [T, H] the rounded y, or NULL (16-byte aligned)
- * Sizes: any T >= 0 (T <= 2^31), H a multiple of 8 (H <= 2^22); the last group
- *   of a row has the H % group channels that remain when H is not a multiple
- *   of the group.
+ * Sizes: any T >= 0 (T <= 2^31), any H >= 0 (H <= 2^22); the last group of a
+ *   row has the H % group channels that remain when H is not a multiple of
+ *   the group.  H not a multiple of 8 takes a slower path with 2-byte loads.
  * Same ownership, asynchrony and error conventions as above.
  */
 int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q, float* y_s, void* y_bf16, int64_t T,

@@ -106,8 +106,9 @@ def silu_dot_fwd_bwd_quant_fuse(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_
     """Recompute y = silu(gate) * up from x = [gate | up] and write the int8 codes
     and fp32 scales of [d_gate, d_up] (per row, groups of group_size channels)
     and of y^T (groups of group_size tokens) into the given output tensors.
-    group_size is 128 (the default), 64 or 32; H must be a multiple of 8, and
-    when it is not a multiple of group_size one group straddles d_gate and d_up.
+    group_size is 128 (the default), 64 or 32; any H: when it is not a multiple
+    of group_size one group straddles d_gate and d_up, and when it is not a
+    multiple of 8 a slower path with 2-byte loads runs.
     Enqueued on the current stream of x's device; returns None."""
     _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size, fp8=False)
 
@@ -158,8 +159,8 @@ def _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size: i
 def silu_fwd_quant(x, y_q, y_s, row_weight=None, y_bf16=None, group_size: int = GROUP):
     """Forward SwiGLU with row-wise int8 quantisation: y = bf16((silu(gate) * up)
     * row_weight[t]) from x = [gate | up] [T, 2H]; writes y_q int8 [T, H] and
-    y_s fp32 [T, ceil(H/group_size)] (group_size 128, 64 or 32; H a multiple of
-    8, the last group of a row partial when H is not a multiple of group_size),
+    y_s fp32 [T, ceil(H/group_size)] (group_size 128, 64 or 32; any H, the last
+    group of a row partial when H is not a multiple of group_size),
     and y_bf16 [T, H] if given.  Enqueued on the current stream of x's device;
     returns None."""
     import torch
