@@ -552,23 +552,34 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
   // this lane's row and column groups: channels 8p.. and tokens kRows q..
   const int sub_row = p / kLanesPerRowGroup, sub_col = q / kPairsPerColGroup;
 
-  int tile, end, stride;
+  // Each XCD takes a contiguous range of tiles (row-major over (tb, hb)).
+  // When an XCD's resident workgroups cover less than a row of tiles, the
+  // XCDs start their ranges at different column phases (rotated by 1/8 of a
+  // row per XCD), so that the tiles in flight together do not all sit at the
+  // same offsets of rows whose pitch has many factors of two.
+  int tile, end, stride, range_begin = 0, range_len = 1, phase = 0;
   if ((gridDim.x & 7) == 0) {
     const int xcd = blockIdx.x & 7, per_xcd = gridDim.x >> 3;
     const int begin = (int)(((int64_t)tiles * xcd) >> 3);
     end = (int)(((int64_t)tiles * (xcd + 1)) >> 3);
     tile = begin + (int)(blockIdx.x >> 3);
     stride = per_xcd;
+    range_begin = begin;
+    range_len = end > begin ? end - begin : 1;
+    phase = tiles_h > per_xcd ? (xcd * tiles_h) / 8 % range_len : 0;
   } else {
     tile = blockIdx.x;
     end = tiles;
     stride = gridDim.x;
+    range_len = tiles > 0 ? tiles : 1;
   }
+  // the tile that the range's i-th slot holds (a rotation of the range)
+  auto placed = [&](int t) { return range_begin + (t - range_begin + phase) % range_len; };
 
   const char* xb = reinterpret_cast<const char*>(x);
   const char* dyb = reinterpret_cast<const char*>(grad_y);
   TileIn in, in_next;
-  Tile cur = tile_at(tile < end ? tile : 0, tiles_h, T, H);
+  Tile cur = tile_at(tile < end ? placed(tile) : 0, tiles_h, T, H);
   if (tile < end)
     load_tile(in, xb + (cur.t0 * x_row_bytes + 2 * cur.h0), dyb + (cur.t0 * dy_row_bytes + 2 * cur.h0), lane_x,
               lane_dy, x_row_bytes, dy_row_bytes, cur.rows, 8 * p < cur.cols, q);
@@ -582,7 +593,7 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
   while (tile < end) {
     // ---- the next tile's inputs stay in flight through this whole iteration --
     const int next = tile + stride;
-    const Tile nxt = tile_at(next < end ? next : tile, tiles_h, T, H);
+    const Tile nxt = tile_at(placed(next < end ? next : tile), tiles_h, T, H);
     if (next < end)
       load_tile(in_next, xb + (nxt.t0 * x_row_bytes + 2 * nxt.h0), dyb + (nxt.t0 * dy_row_bytes + 2 * nxt.h0),
                 lane_x, lane_dy, x_row_bytes, dy_row_bytes, nxt.rows, 8 * p < nxt.cols, q);
