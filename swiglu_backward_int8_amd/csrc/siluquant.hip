@@ -501,9 +501,9 @@ __device__ __forceinline__ void quantise_rows_and_y(const uint32_t (&Gp)[kRows][
 
 // Persistent kernel: workgroup b walks tiles first, first + stride, ... < end.
 // Workgroups are dealt to the 8 XCDs round-robin by index, so with a grid that
-// is a multiple of 8, the workgroups of one XCD take one contiguous eighth of
-// the tiles (row-major over 128 x 128 tiles) and walk it together: neighbouring
-// tiles, whose scale writes share cache lines, then meet in the same L2.
+// is a multiple of 8, the workgroups of one XCD take one eighth of the tiles
+// (row-major over 128 x 128 tiles) and walk it together: neighbouring tiles
+// of a row, whose scale writes share cache lines, then meet in the same L2.
 // One workgroup per CU; the next tile's inputs are requested at the top of each
 // iteration and stay in flight while the current tile is processed.
 template <Fmt F, int kG>
@@ -552,29 +552,44 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
   // this lane's row and column groups: channels 8p.. and tokens kRows q..
   const int sub_row = p / kLanesPerRowGroup, sub_col = q / kPairsPerColGroup;
 
-  // Each XCD takes a contiguous range of tiles (row-major over (tb, hb)).
-  // When an XCD's resident workgroups cover less than a row of tiles, the
-  // XCDs start their ranges at different column phases (rotated by 1/8 of a
-  // row per XCD), so that the tiles in flight together do not all sit at the
-  // same offsets of rows whose pitch has many factors of two.
-  int tile, end, stride, range_begin = 0, range_len = 1, phase = 0;
+  // Each XCD walks an eighth of the tiles (row-major over (tb, hb)), so that
+  // the tiles it has in flight together are neighbours.  Which eighth, so
+  // that the tiles in flight on all XCDs together do not sit at the same
+  // offsets of rows whose pitch has many factors of two:
+  //   * a row of tiles longer than an XCD's share of the grid: contiguous
+  //     ranges, each XCD starting at its own column phase (the range rotated
+  //     by 1/8 of a row per XCD);
+  //   * shorter rows (an XCD covers whole rows at a time), with a multiple
+  //     of 8 rows: XCD x takes the tile rows x, x + 8, x + 16, ..., so that
+  //     the rows in flight form one band instead of eight far-apart ones.
+  int tile, end, stride, xcd = 0, range_begin = 0, range_len = 1, phase = 0;
+  bool interleave = false;
   if ((gridDim.x & 7) == 0) {
-    const int xcd = blockIdx.x & 7, per_xcd = gridDim.x >> 3;
+    const int per_xcd = gridDim.x >> 3;
+    xcd = blockIdx.x & 7;
     const int begin = (int)(((int64_t)tiles * xcd) >> 3);
     end = (int)(((int64_t)tiles * (xcd + 1)) >> 3);
     tile = begin + (int)(blockIdx.x >> 3);
     stride = per_xcd;
     range_begin = begin;
     range_len = end > begin ? end - begin : 1;
-    phase = tiles_h > per_xcd ? (xcd * tiles_h) / 8 % range_len : 0;
+    if (tiles_h > per_xcd)
+      phase = (xcd * tiles_h) / 8 % range_len;
+    else
+      interleave = tiles % (8 * tiles_h) == 0;
   } else {
     tile = blockIdx.x;
     end = tiles;
     stride = gridDim.x;
     range_len = tiles > 0 ? tiles : 1;
   }
-  // the tile that the range's i-th slot holds (a rotation of the range)
-  auto placed = [&](int t) { return range_begin + (t - range_begin + phase) % range_len; };
+  // the tile that slot t of the XCD's range holds
+  auto placed = [&](int t) {
+    const int s = range_begin + (t - range_begin + phase) % range_len;
+    if (!interleave) return s;
+    const int l = s - range_begin;
+    return (8 * (l / tiles_h) + xcd) * tiles_h + l % tiles_h;
+  };
 
   const char* xb = reinterpret_cast<const char*>(x);
   const char* dyb = reinterpret_cast<const char*>(grad_y);
