@@ -370,6 +370,7 @@ def main():
         "config": {
             "workload": w.name, "T": w.T, "H": w.H, "group": 32 if q8_1 else 128,
             "bytes_per_step": nbytes, "pairs_per_s": round(w.T * w.H * args.steps / wall, 1),
+            "input_elements_per_s": round((2 if args.op.startswith("forward") else 3) * w.T * w.H * args.steps / wall, 1),
             "buffer_sets": sets,
         },
         "roofline": {
