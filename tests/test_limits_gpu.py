@@ -169,3 +169,56 @@ def test_straddling_kernel_at_the_token_limit():
         _equal("straddle T=2^23 tokens %d.." % t0, got, want)
     del x, dy, gq, gs, yq, ys
     torch.cuda.empty_cache()
+
+
+def test_narrow_kernels_at_the_token_limit():
+    # T = 2^23, H = 3 (not a multiple of 8: the 2-byte-load kernels), group
+    # 32: every row is one partial group of 6; y_q_t rows are 8 MiB long
+    T, H, G = 1 << 23, 3, 32
+    print("case narrow T=2^23 H=3", flush=True)
+    x, dy = _inputs(T, H, 7)
+    gq, gs, yq, ys = sq.empty_outputs(T, H, DEV, group=G)
+    sq.silu_dot_fwd_bwd_quant_fuse(x, dy, gq, gs, yq, ys, group_size=G)
+    torch.cuda.synchronize()
+    for t0 in (0, T // 2 + 64, T - 256):
+        want = oracle.silu_dot_fwd_bwd_quant_fuse(_bits(x[t0:t0 + 256]), _bits(dy[t0:t0 + 256]), group_size=G)
+        got = (gq[t0:t0 + 256].cpu().numpy(), gs[t0:t0 + 256].cpu().numpy(),
+               yq[:, t0:t0 + 256].cpu().numpy(), ys[:, t0 // G:t0 // G + 256 // G].cpu().numpy())
+        _equal("narrow T=2^23 tokens %d.." % t0, got, want)
+    del x, dy, gq, gs, yq, ys
+    torch.cuda.empty_cache()
+
+
+def test_narrow_kernels_at_the_channel_limit():
+    # H = 2^22 - 1 with group 128: r = 127, so the straddling group holds
+    # d_gate's last 127 channels and d_up's first one, and the row's last
+    # group is d_up's final 126 channels.  T = 64 is one partial token group.
+    T, H, G = 64, (1 << 22) - 1, 128
+    print("case narrow T=64 H=2^22-1", flush=True)
+    x, dy = _inputs(T, H, 8)
+    gq, gs, yq, ys = sq.empty_outputs(T, H, DEV, group=G)
+    sq.silu_dot_fwd_bwd_quant_fuse(x, dy, gq, gs, yq, ys, group_size=G)
+    torch.cuda.synchronize()
+    Y1, D1 = oracle.intermediates(_bits(torch.cat([x[:, H - 256:H], x[:, 2 * H - 256:]], dim=1)),
+                                  _bits(dy[:, H - 256:]))
+    Y0, D0 = oracle.intermediates(_bits(torch.cat([x[:, :256], x[:, H:H + 256]], dim=1)), _bits(dy[:, :256]))
+    r, n = H % G, (2 * H) % G
+    j = (H - r) // G
+    head_q, head_s = gq[:, :256].cpu().numpy(), gs[:, :2].cpu().numpy()
+    mid_q, mid_s = gq[:, H - r:H - r + G].cpu().numpy(), gs[:, j].cpu().numpy()
+    tail_q, tail_s = gq[:, 2 * H - n:].cpu().numpy(), gs[:, -1].cpu().numpy()
+    for t in range(T):
+        for k in range(2):
+            q, s = oracle.quant_group(D0[t, 128 * k:128 * k + 128])
+            assert s == head_s[t, k] and np.array_equal(q, head_q[t, 128 * k:128 * k + 128]), (t, k)
+        q, s = oracle.quant_group(np.concatenate([D1[t, 256 - r:256], D0[t, 256:256 + G - r]]))
+        assert s == mid_s[t] and np.array_equal(q, mid_q[t]), t
+        q, s = oracle.quant_group(D1[t, 512 - n:512])
+        assert s == tail_s[t] and np.array_equal(q, tail_q[t]), t
+    for Y, c0 in ((Y0, 0), (Y1, H - 256)):
+        yq_np, ys_np = yq[c0:c0 + 256].cpu().numpy(), ys[c0:c0 + 256, 0].cpu().numpy()
+        for c in range(256):
+            q, s = oracle.quant_group(Y[:, c])
+            assert s == ys_np[c] and np.array_equal(q, yq_np[c]), c0 + c
+    del x, dy, gq, gs, yq, ys
+    torch.cuda.empty_cache()
