@@ -1080,49 +1080,61 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
   const int lane = tid & 63;
   const int r = lane >> 4, p = lane & 15;
   const bool odd = p & 1;
+  // A unit is the same for the whole wave, so its coordinates and base
+  // addresses live in scalar registers; a lane only adds its fixed offset
+  // (row r of the unit, channels 8p..8p+7).  Rows past T and channels past H
+  // take offsets past their buffer's record count: loads read zeros and
+  // stores are dropped.
   const int64_t waves = (int64_t)gridDim.x * (kFwdThreads / 64);
-  int64_t u = (int64_t)blockIdx.x * (kFwdThreads / 64) + (tid >> 6);
+  const int64_t first = (int64_t)blockIdx.x * (kFwdThreads / 64) + __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t step_rb = waves / tiles_h, step_hb = waves - step_rb * tiles_h;
   const int64_t groups = (H + kG - 1) / kG;
   // Rows of y_q start on 16 bytes when H % 16 == 0: then the even lane of
   // each pair stores the pair's 16 codes; else each lane stores its own 8.
   const bool pair_stores = (H & 15) == 0;
+  constexpr uint32_t kOut = 0x80000000u;  // past any record count
+  const uint32_t x_row = (uint32_t)(4 * H);
+  const uint32_t q_row = kQ81 ? (uint32_t)(H / 32 * 36) : (uint32_t)H;
+  const uint32_t lane_x = r * x_row + 16 * p, lane_xu = lane_x + 2 * (uint32_t)H;
+  const uint32_t lane_q = kQ81 ? r * q_row + (uint32_t)(8 * p / 32) * 36 + 4 * (1 + 2 * (p & 3)) : r * q_row + 8 * p;
+  const uint32_t lane_s = 4 * (r * (uint32_t)groups + (uint32_t)(8 * p / kG));
 
-  auto coords = [&](int64_t unit, int64_t& t, int64_t& h0, int64_t& hb) {
-    const int64_t rb = unit / tiles_h;
-    hb = unit - rb * tiles_h;
-    t = 4 * rb + r;
-    h0 = hb * kTile;
+  struct Unit {
+    int64_t rb, hb;  // unit row block (4 tokens) and channel block (128)
   };
-  // In the last channel block of an H that is not a multiple of 128 only the
-  // lanes with 8 p < H - h0 hold channels (H is a multiple of 8); the others
-  // read zeros, which never raise a group's maximum, so the last group of a
-  // row may be partial.
-  auto live = [&](int64_t h0) { return h0 + 8 * p < H; };
-  auto load = [&](FwdIn& in, int64_t t, int64_t h0) {
-    if (t < T && live(h0)) {
-      const uint16_t* xr = x + t * 2 * H + h0 + 8 * p;
-      in.g = load_stream(xr);
-      in.u = load_stream(xr + H);
-    } else {
-      in.g = make_uint4(0, 0, 0, 0);
-      in.u = in.g;
+  auto advance = [&](Unit& c) {
+    c.rb += step_rb;
+    c.hb += step_hb;
+    if (c.hb >= tiles_h) {
+      c.hb -= tiles_h;
+      ++c.rb;
     }
   };
+  auto rows_of = [&](const Unit& c) { return T - 4 * c.rb < 4 ? (uint32_t)(T - 4 * c.rb) : 4u; };
+  auto load = [&](FwdIn& in, const Unit& c) {
+    const int64_t t0 = 4 * c.rb, h0 = c.hb * kTile;
+    const __amdgpu_buffer_rsrc_t xb =
+        buffer_of(const_cast<uint16_t*>(x) + (t0 * 2 * H + h0), rows_of(c) * x_row - 2 * (uint32_t)h0);
+    const bool live = h0 + 8 * p < H;
+    in.g = load_buf(xb, live ? lane_x : kOut);
+    in.u = load_buf(xb, live ? lane_xu : kOut);
+  };
 
+  const int64_t u0 = first;
+  Unit cur = {u0 / tiles_h, u0 - (u0 / tiles_h) * tiles_h};
   FwdIn in, in_next;
-  int64_t t = 0, h0 = 0, hb = 0;
-  if (u < units) {
-    coords(u, t, h0, hb);
-    load(in, t, h0);
-  }
-  while (u < units) {
-    const int64_t un = u + waves;
-    int64_t tn = 0, h0n = 0, hbn = 0;
-    if (un < units) {
-      coords(un, tn, h0n, hbn);
-      load(in_next, tn, h0n);
-    }
-    const float wt = (row_weight != nullptr && t < T) ? row_weight[t] : 1.0f;
+  if (u0 < units) load(in, cur);
+  for (int64_t u = u0; u < units; u += waves) {
+    Unit nxt = cur;
+    advance(nxt);
+    if (u + waves < units) load(in_next, nxt);
+    const int64_t t0 = 4 * cur.rb, h0 = cur.hb * kTile;
+    const uint32_t rows = rows_of(cur);
+    const bool live = h0 + 8 * p < H;
+    float wt = 1.0f;
+    if (row_weight != nullptr)
+      wt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                         buffer_of(const_cast<float*>(row_weight) + t0, 4 * rows), 4 * r, 0, 0));
     uint32_t Yp[4];
     float m = 0.0f;
     const uint32_t gw[4] = {in.g.x, in.g.y, in.g.z, in.g.w};
@@ -1159,42 +1171,37 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
       // was slower too.
       static_assert(kG == 32, "q8_1 blocks are 32 channels");
       const int qsum = quad_sum(byte_sum(c.x) + byte_sum(c.y));
-      if (t < T && live(h0)) {
-        uint32_t* blk = reinterpret_cast<uint32_t*>(y_q + t * (H / 32) * 36 + ((h0 + 8 * p) >> 5) * 36);
-        const int k = p & 3;
-        blk[1 + 2 * k] = c.x;
-        blk[2 + 2 * k] = c.y;
-        if (k == 0) blk[0] = f16_bits(scale) | (f16_bits(scale * (float)qsum) << 16);
-      }
-      in = in_next;
-      u = un;
-      t = tn;
-      h0 = h0n;
-      hb = hbn;
-      continue;
-    }
-    const uint2 other = make_uint2(swap_neighbour(c.x), swap_neighbour(c.y));
-    if (t < T && live(h0)) {
-      // Plain non-temporal stores: for this write-light pass they measured
-      // faster than the system-scope policy the backward pass uses.  With
-      // H % 16 == 0 the odd lane of a live even lane is live too.
+      const __amdgpu_buffer_rsrc_t qb =
+          buffer_of(y_q + (t0 * q_row + (h0 >> 5) * 36), rows * q_row - (uint32_t)(h0 >> 5) * 36);
+      const uint32_t off = live ? lane_q : kOut;
+      __builtin_amdgcn_raw_buffer_store_b32(c.x, qb, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(c.y, qb, off + 4, 0, 0);
+      if ((p & 3) == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(f16_bits(scale) | (f16_bits(scale * (float)qsum) << 16), qb,
+                                              off - 4, 0, 0);
+    } else {
+      // Non-temporal code stores: for this write-light pass they measured
+      // faster than the system-scope policy the backward pass uses.
+      const uint2 other = make_uint2(swap_neighbour(c.x), swap_neighbour(c.y));
+      const __amdgpu_buffer_rsrc_t qb = buffer_of(y_q + (t0 * H + h0), rows * q_row - (uint32_t)h0);
+      const uint32_t off = live ? lane_q : kOut;
       if (pair_stores) {
-        if (!odd)
-          __builtin_nontemporal_store((u32x4){c.x, c.y, other.x, other.y},
-                                      reinterpret_cast<u32x4*>(y_q + t * H + h0 + 8 * p));
+        if (!odd) __builtin_amdgcn_raw_buffer_store_b128((u32x4){c.x, c.y, other.x, other.y}, qb, off, 0, 2);
       } else {
-        __builtin_nontemporal_store((u32x2){c.x, c.y}, reinterpret_cast<u32x2*>(y_q + t * H + h0 + 8 * p));
+        __builtin_amdgcn_raw_buffer_store_b64((u32x2){c.x, c.y}, qb, off, 0, 2);
       }
       if (y_bf16 != nullptr)
-        __builtin_nontemporal_store((u32x4){Yp[0], Yp[1], Yp[2], Yp[3]},
-                                    reinterpret_cast<u32x4*>(y_bf16 + t * H + h0 + 8 * p));
-      if (p % (kG / 8) == 0) y_s[t * groups + (h0 + 8 * p) / kG] = scale;
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){Yp[0], Yp[1], Yp[2], Yp[3]},
+                                               buffer_of(y_bf16 + (t0 * H + h0), 2 * (rows * q_row - (uint32_t)h0)),
+                                               live ? 2 * lane_q : kOut, 0, 2);
+      if (p % (kG / 8) == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __float_as_uint(scale),
+            buffer_of(y_s + (t0 * groups + h0 / kG), 4 * (rows * (uint32_t)groups - (uint32_t)(h0 / kG))),
+            live ? lane_s : kOut, 0, 0);
     }
     in = in_next;
-    u = un;
-    t = tn;
-    h0 = h0n;
-    hb = hbn;
+    cur = nxt;
   }
 }
 
