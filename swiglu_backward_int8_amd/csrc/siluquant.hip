@@ -214,6 +214,35 @@ __device__ __forceinline__ float group_scale(float amax_unrounded) {
   return amax == 0.0f ? 1.0f : amax / kQmax<F>;
 }
 
+// The int8 scale and its inverse without a division per group.  The rounded
+// amax is a bf16 number, (1 + i/128) * 2^(e-127) with 7 mantissa bits i.
+// For e >= 8 (amax >= 2^-119) amax/127 and 1/(amax/127) are normal numbers,
+// and rounding commutes with scaling by a power of two, so
+//   scale = RN(amax / 127)   = RN((1 + i/128) / 127) * 2^(e-127),
+//   inv   = RN(1 / scale)    = RN(1 / RN((1 + i/128) / 127)) * 2^(127-e):
+// table entry i scaled by the exponent (exact).  Smaller amax, and 0, take
+// the divisions.  qtab[i] = {RN((1 + i/128) / 127), RN(1 / that)}.
+__device__ __forceinline__ void scale_and_inverse(float amax_unrounded, const float2* qtab, float& scale,
+                                                  float& inv) {
+  const float amax = bf16_lo(pack_bf16(amax_unrounded, 0.0f));
+  const uint32_t bits = __float_as_uint(amax);
+  const int e = (int)(bits >> 23);
+  if (e >= 8) {
+    const float2 t = qtab[(bits >> 16) & 127u];
+    scale = __builtin_amdgcn_ldexpf(t.x, e - 127);
+    inv = __builtin_amdgcn_ldexpf(t.y, 127 - e);
+  } else {
+    scale = amax == 0.0f ? 1.0f : amax / 127.0f;
+    inv = 1.0f / scale;
+  }
+}
+__device__ __forceinline__ void fill_scale_table(float2* qtab, int tid) {
+  if (tid < 128) {
+    const float sc = (1.0f + (float)tid / 128.0f) / 127.0f;
+    qtab[tid] = make_float2(sc, 1.0f / sc);
+  }
+}
+
 // E4M3 codes: the fp32 product v * inv converted by v_cvt_pk_fp8_f32 (nearest,
 // ties to even; a zero keeps its sign).  With a finite inverse |v * inv| stays
 // within 448 * (1 + 2^-22), which converts to +-448; kSafe serves groups whose
@@ -1069,11 +1098,13 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ row_weight, int8_t* __restrict__ y_q,
     float* __restrict__ y_s, uint16_t* __restrict__ y_bf16, int64_t T, int64_t H, int tiles_h, int64_t units) {
   __shared__ __align__(16) float s_tab[kSigEntries];
+  __shared__ __align__(16) float2 s_qtab[128];
   const int tid = threadIdx.x;
   {
     const float4* src = reinterpret_cast<const float4*>(g_sigma_tab);
     float4* dst = reinterpret_cast<float4*>(s_tab);
     for (int i = tid; i < kSigEntries / 4; i += kFwdThreads) dst[i] = src[i];
+    fill_scale_table(s_qtab, tid);
   }
   __syncthreads();
 
@@ -1154,8 +1185,8 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
       m = amax3(m, y0, y1);
     }
     m = group_lanes_max<kG>(m);
-    const float scale = group_scale(m);
-    const float inv = 1.0f / scale;
+    float scale, inv;
+    scale_and_inverse(m, s_qtab, scale, inv);
     uint2 c;
     if (__builtin_expect(inv == __builtin_huge_valf(), 0))
       c = codes8<true>(Yp, inv);
