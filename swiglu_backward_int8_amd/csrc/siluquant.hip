@@ -1051,10 +1051,14 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
 constexpr int kFwdThreads = 512;
 constexpr int kFwdWorkgroupsPerCU = 3;  // 24 waves per CU; the measured best of 16..32
 
+// The values are magnitudes (non-negative, no NaN), whose bit patterns order
+// like unsigned integers: an integer maximum needs no canonicalisation and
+// folds the DPP move into the v_max_u32.
 template <int kCtrl>
 __device__ __forceinline__ float dpp_max(float v) {
-  const int o = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), kCtrl, 0xf, 0xf, false);
-  return fmaxf(v, __int_as_float(o));
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)b, kCtrl, 0xf, 0xf, true);
+  return __uint_as_float(b > o ? b : o);
 }
 
 // Maximum over the kG / 8 lanes of a group inside a 16-lane DPP row (lane p
@@ -1093,7 +1097,7 @@ __device__ __forceinline__ uint32_t f16_bits(float v) { return __builtin_bit_cas
 // is 32): per row H/32 blocks of 36 bytes, the binary16 d (the group scale)
 // and sum (fl32(scale * sum of the codes)), then the 32 codes.  y_q then
 // points at the blocks (4-byte aligned) and y_s and y_bf16 are unused.
-template <int kG, bool kQ81 = false>
+template <int kG, bool kQ81 = false, bool kWeighted = false>
 __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ row_weight, int8_t* __restrict__ y_q,
     float* __restrict__ y_s, uint16_t* __restrict__ y_bf16, int64_t T, int64_t H, int tiles_h, int64_t units) {
@@ -1163,7 +1167,7 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
     const uint32_t rows = rows_of(cur);
     const bool live = h0 + 8 * p < H;
     float wt = 1.0f;
-    if (row_weight != nullptr)
+    if constexpr (kWeighted)
       wt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                          buffer_of(const_cast<float*>(row_weight) + t0, 4 * rows), 4 * r, 0, 0));
     uint32_t Yp[4];
@@ -1177,7 +1181,7 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
       const float s0 = lds_f32(s_tab, olo), s1 = lds_f32(s_tab, ohi);
       float y0 = (bf16_lo(gw[k]) * s0) * bf16_lo(uw[k]);
       float y1 = (bf16_hi(gw[k]) * s1) * bf16_hi(uw[k]);
-      if (row_weight != nullptr) {
+      if constexpr (kWeighted) {
         y0 = y0 * wt;
         y1 = y1 * wt;
       }
@@ -1689,8 +1693,10 @@ __attribute__((visibility("default"))) int silu_fwd_quant(const void* x, const f
                        static_cast<const uint16_t*>(x), row_weight, y_q, y_s, static_cast<uint16_t*>(y_bf16), T, H);
     return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;
   }
-  auto kernel = group == 128 ? silu_fwd_quant_kernel<128> : group == 64 ? silu_fwd_quant_kernel<64>
-                                                                      : silu_fwd_quant_kernel<32>;
+  const bool w = row_weight != nullptr;
+  auto kernel = group == 128 ? (w ? silu_fwd_quant_kernel<128, false, true> : silu_fwd_quant_kernel<128>)
+                : group == 64 ? (w ? silu_fwd_quant_kernel<64, false, true> : silu_fwd_quant_kernel<64>)
+                              : (w ? silu_fwd_quant_kernel<32, false, true> : silu_fwd_quant_kernel<32>);
   return launch_forward(kernel, x, row_weight, y_q, y_s, y_bf16, T, H, stream);
 }
 
@@ -1708,8 +1714,8 @@ __attribute__((visibility("default"))) int silu_fwd_quant_q8_1(const void* x, co
   for (int i = 0; i < 3; ++i)
     for (int j = i + 1; j < 3; ++j)
       if (bufs[i] && bufs[j] && overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
-  return launch_forward(silu_fwd_quant_kernel<32, true>, x, row_weight, static_cast<int8_t*>(y_q8), nullptr,
-                        nullptr, T, H, stream);
+  return launch_forward(row_weight ? silu_fwd_quant_kernel<32, true, true> : silu_fwd_quant_kernel<32, true>, x,
+                        row_weight, static_cast<int8_t*>(y_q8), nullptr, nullptr, T, H, stream);
 }
 
 __attribute__((visibility("default"))) int siluquant_eval_sigmoid(const void* gate, float* s, int64_t n,
