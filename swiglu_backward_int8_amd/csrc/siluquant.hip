@@ -1076,16 +1076,15 @@ struct FwdIn {
   uint4 g, u;
 };
 
-// Sum of the four signed bytes of a word.
-__device__ __forceinline__ int byte_sum(uint32_t w) {
-  return (int)(int8_t)(w & 0xffu) + (int)(int8_t)((w >> 8) & 0xffu) + (int)(int8_t)((w >> 16) & 0xffu) +
-         ((int)w >> 24);
+// Sum of the eight signed bytes of two words: a dot product with bytes of 1.
+__device__ __forceinline__ int byte_sum8(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_sdot4((int)a, 0x01010101, __builtin_amdgcn_sdot4((int)b, 0x01010101, 0, false), false);
 }
 
-// Sum over the four lanes of a DPP quad.
+// Sum over the four lanes of a DPP quad (each source lane is inside the quad).
 __device__ __forceinline__ int quad_sum(int v) {
-  v += __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
-  v += __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xf, 0xf, true);  // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xf, 0xf, true);  // quad_perm [2,3,0,1]
   return v;
 }
 
@@ -1205,7 +1204,7 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
       // H = 11008.  Assembling a unit's 144 bytes in LDS for 16-byte stores
       // was slower too.
       static_assert(kG == 32, "q8_1 blocks are 32 channels");
-      const int qsum = quad_sum(byte_sum(c.x) + byte_sum(c.y));
+      const int qsum = quad_sum(byte_sum8(c.x, c.y));
       const __amdgpu_buffer_rsrc_t qb =
           buffer_of(y_q + (t0 * q_row + (h0 >> 5) * 36), rows * q_row - (uint32_t)(h0 >> 5) * 36);
       const uint32_t off = live ? lane_q : kOut;
