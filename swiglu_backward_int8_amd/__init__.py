@@ -123,19 +123,19 @@ def _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size: i
     import torch
 
     code_types = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)) if fp8 else (torch.int8,)
-    T, H = int(grad_y.shape[0]) if grad_y.dim() == 2 else -1, int(grad_y.shape[-1])
-    if x.dim() != 2 or grad_y.dim() != 2 or tuple(x.shape) != (T, 2 * H):
+    if x.dim() != 2 or grad_y.dim() != 2 or tuple(x.shape) != (grad_y.shape[0], 2 * grad_y.shape[1]):
         raise ValueError("x must be [T, 2H] and grad_y [T, H]; got %s and %s" % (tuple(x.shape), tuple(grad_y.shape)))
+    T, H = int(grad_y.shape[0]), int(grad_y.shape[1])
     if group_size not in GROUPS:
         raise ValueError("group_size must be one of %s" % (GROUPS,))
     want = output_shapes(T, H, group_size)
     checks = [
         ("x", x, torch.bfloat16, (T, 2 * H)),
         ("grad_y", grad_y, torch.bfloat16, (T, H)),
-        ("grad_input_q", grad_input_q, code_types, want and want["grad_input_q"]),
-        ("grad_input_s", grad_input_s, torch.float32, want and want["grad_input_s"]),
-        ("y_q_t", y_q_t, code_types, want and want["y_q_t"]),
-        ("y_s_t", y_s_t, torch.float32, want and want["y_s_t"]),
+        ("grad_input_q", grad_input_q, code_types, want["grad_input_q"]),
+        ("grad_input_s", grad_input_s, torch.float32, want["grad_input_s"]),
+        ("y_q_t", y_q_t, code_types, want["y_q_t"]),
+        ("y_s_t", y_s_t, torch.float32, want["y_s_t"]),
     ]
     dev = x.device
     if dev.type != "cuda":
@@ -147,7 +147,7 @@ def _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size: i
             raise ValueError("%s is on %s, x on %s" % (name, t.device, dev))
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % name)
-        if shape is not None and tuple(t.shape) != tuple(shape):
+        if tuple(t.shape) != tuple(shape):
             raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream

@@ -205,3 +205,27 @@ def test_gemm_rejects_bad_arguments(lib):
     # nothing to do: success without looking at any pointer
     assert call(M=0, A=None, sA=None, B=None, sB=None, C=None) == 0
     assert call(N=0, A=None, sA=None, B=None, sB=None, C=None) == 0
+
+
+def test_binding_rejects_bad_tensors_before_any_call():
+    # shape, rank and device checks raise ValueError on the host, before the
+    # library is called (CPU tensors here, so nothing can reach a GPU)
+    import torch
+
+    x = torch.zeros((4, 16), dtype=torch.bfloat16)
+    dy = torch.zeros((4, 8), dtype=torch.bfloat16)
+    outs = sq.empty_outputs(4, 8, "cpu")
+    with pytest.raises(ValueError):  # grad_y of rank 1
+        sq.silu_dot_fwd_bwd_quant_fuse(x, dy[0], *outs)
+    with pytest.raises(ValueError):  # grad_y of rank 0
+        sq.silu_dot_fwd_bwd_quant_fuse(x, dy[0, 0], *outs)
+    with pytest.raises(ValueError):  # x not [T, 2H]
+        sq.silu_dot_fwd_bwd_quant_fuse(x[:, :15], dy, *outs)
+    with pytest.raises(ValueError):  # a group the pass does not take
+        sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *outs, group_size=16)
+    with pytest.raises(ValueError):  # tensors on the host
+        sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *outs)
+    with pytest.raises(ValueError):
+        sq.silu_fwd_quant(x, outs[0][:, :8], outs[1])
+    with pytest.raises(ValueError):
+        sq.i8_gemm_group_scaled(outs[0], outs[1], outs[0], outs[1], torch.zeros((4, 4)))
