@@ -148,3 +148,24 @@ def test_forward_h_not_a_multiple_of_8(T, H, group):
     w = torch.rand(T, device=DEV, generator=torch.Generator(device=DEV).manual_seed(T)) * 4 - 2
     check(x, label="narrow T=%d H=%d group=%d" % (T, H, group), group=group)
     check(x, w=w, want_bf16=True, label="narrow T=%d H=%d group=%d weighted" % (T, H, group), group=group)
+
+
+@pytest.mark.parametrize("group", [128, 64, 32])
+def test_forward_tiny_group_maxima(group):
+    # gate 20 (sigmoid exactly 1) and up = (1 + j/64) * 2^(-110 - t): row t's
+    # group maxima run from 2^-106 down through 2^-119 (below which the kernel
+    # leaves its scale table for the divisions), the overflowing inverses
+    # (amax < 127 * 2^-128) and subnormal y, to zero rows
+    T, H = 40, 256
+    t = torch.arange(T, dtype=torch.float64).unsqueeze(1)
+    j = torch.arange(H, dtype=torch.float64).unsqueeze(0)
+    up = ((1 + (j % 64) / 64) * torch.pow(2.0, -110 - t)).to(torch.float32)
+    x = torch.cat([torch.full((T, H), 20.0), up], dim=1).to(torch.bfloat16).to(DEV)
+    check(x, label="tiny maxima group=%d" % group, group=group)
+    w = torch.full((T,), 0.75, dtype=torch.float32, device=DEV)
+    check(x, w=w, want_bf16=True, label="tiny maxima weighted group=%d" % group, group=group)
+    q8 = torch.empty((T, H // 32 * sq.Q8_1_BLOCK), dtype=torch.uint8, device=DEV)
+    if group == 32:
+        sq.silu_fwd_quant_q8_1(x, q8)
+        torch.cuda.synchronize()
+        assert np.array_equal(q8.cpu().numpy(), oracle.silu_fwd_quant_q8_1(_bits(x)))
