@@ -588,9 +588,11 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
   //   * a row of tiles longer than an XCD's share of the grid: contiguous
   //     ranges, each XCD starting at its own column phase (the range rotated
   //     by 1/8 of a row per XCD);
-  //   * shorter rows (an XCD covers whole rows at a time), with a multiple
-  //     of 8 rows: XCD x takes the tile rows x, x + 8, x + 16, ..., so that
-  //     the rows in flight form one band instead of eight far-apart ones.
+  //   * shorter rows (an XCD covers whole rows at a time), and long rows
+  //     once an XCD's eighth spans 32 or more tile rows, with a multiple of
+  //     8 rows: XCD x takes the tile rows x, x + 8, x + 16, ..., so that the
+  //     rows in flight form one band instead of eight far-apart ones (for
+  //     long rows on top of the column phase).
   int tile, end, stride, xcd = 0, range_begin = 0, range_len = 1, phase = 0;
   bool interleave = false;
   if ((gridDim.x & 7) == 0) {
@@ -602,10 +604,8 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
     stride = per_xcd;
     range_begin = begin;
     range_len = end > begin ? end - begin : 1;
-    if (tiles_h > per_xcd)
-      phase = (xcd * tiles_h) / 8 % range_len;
-    else
-      interleave = tiles % (8 * tiles_h) == 0;
+    if (tiles_h > per_xcd) phase = (xcd * tiles_h) / 8 % range_len;
+    interleave = tiles % (8 * tiles_h) == 0 && (tiles_h <= per_xcd || tiles / (8 * tiles_h) >= 32);
   } else {
     tile = blockIdx.x;
     end = tiles;

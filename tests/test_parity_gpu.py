@@ -205,6 +205,16 @@ def test_ragged_token_counts(T, H):
     assert sum(rep.values()) == 0
 
 
+@pytest.mark.parametrize("T,H", [(32768, 4224), (8192 + 128, 4224)])
+def test_tile_walk_orders(T, H):
+    # rows of 33 tiles (longer than an XCD's share of 256 workgroups) over
+    # 256 tile rows: the XCDs take interleaved tile rows with their own column
+    # phase; over 65 tile rows (not a multiple of 8) only the phase applies
+    print("case walk T=%d H=%d" % (T, H), flush=True)
+    x, dy = random_inputs(T, H, device=DEV, seed=T + H)
+    assert sum(check(x, dy, "walk T=%d H=%d" % (T, H)).values()) == 0
+
+
 def test_ragged_tokens_outlier_workload():
     x, dy = make_inputs("t32768_h2048_outliers", device=DEV, T=3001)
     rep = check(x, dy, "outliers T=3001")
