@@ -25,7 +25,7 @@
 // MFMAs.  Each wave owns 64 x 64 = 2 x 2 MFMA blocks of 32 x 32.  Per group,
 // the A and B tiles (128 x 128 bytes each) and their scales are staged in LDS,
 // double buffered: the next group is loaded into registers while the matrix
-// cores work on this one.  Tiles are handed out in groups of 8 tile-rows, and
+// cores work on this one.  Tiles are handed out in groups of 4 tile-rows, and
 // each XCD takes a contiguous range of that order, so that the workgroups
 // resident on one XCD share A and B tiles in its L2.
 #include <hip/hip_runtime.h>
@@ -41,7 +41,7 @@ constexpr int kBK = 128;                  // the K step: one group
 constexpr int kWavesM = 2, kWavesN = 2;   // wave grid of a workgroup
 constexpr int kBM = 64 * kWavesM, kBN = 64 * kWavesN;  // tile of C: 128 x 128
 constexpr int kGemmThreads = 64 * kWavesM * kWavesN;   // 256
-constexpr int kGroupM = 8;                // tile-rows per raster group
+constexpr int kGroupM = 4;                // tile-rows per raster group (2, 6, 8, 16, 32 measured slower)
 constexpr int kStageBytes = (kBM + kBN) * kBK;         // A and B tiles of one group
 constexpr int kChunksPerThread = kStageBytes / 16 / kGemmThreads;  // 16-byte chunks staged per thread
 constexpr int kAChunks = kBM * kBK / 16;  // chunk ids below this are A's, the rest B's
