@@ -8,7 +8,8 @@ q = clamp(rne(v * inv), -127, 127)) is pinned by:
   neighbours in exact arithmetic, including a group where rounding the fp32
   product first would give a different code;
 * hand-derived worked examples whose exact results are known without running
-  any float code (derivations in the comments);
+  any float code (the fixture tests/golden/quant_worked_examples.txt, with the
+  derivations and the rules they follow);
 * brute-force rounding: with amax = 127 the scale and its inverse are exactly 1,
   so every code must be the integer nearest to v (ties to even), found here by
   comparing the two integer neighbours in exact arithmetic, for every bf16
@@ -19,6 +20,7 @@ q = clamp(rne(v * inv), -127, 127)) is pinned by:
   step plus the rounding slack of inv and v * inv.
 """
 
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -28,27 +30,28 @@ import oracle
 from exact import all_finite_bf16, bf16_bits_to_fraction, f32_bits, rn32, rne_int
 
 
-def test_worked_example_amax_one():
-    # 1/127 = 0.0078740157...: fp32 exponent -7, significand 2^30/127 =
-    # 8454660.03 -> 8454660 = 0x810204 -> bits 0x3C010204.  1 / that value is
-    # 2^30 / 8454660 = 126.99999955, which is within half an ulp (2^-18) of 127,
-    # so inv == 127 exactly and q = rne(127 * v) for bf16 v (exact products).
-    v = [1.0, -0.5, 0.25, 0.00390625, 0.5, -1.0, 0.75, 0.0]
-    q, s = oracle.quant_group(v)
-    assert f32_bits(s) == 0x3C010204
-    # 127, -63.5 -> -64 (tie, even), 31.75 -> 32, 0.496 -> 0, 63.5 -> 64 (tie),
-    # -127, 95.25 -> 95, 0
-    assert q.tolist() == [127, -64, 32, 0, 64, -127, 95, 0]
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "quant_worked_examples.txt")
 
 
-def test_worked_example_amax_127_ties_to_even():
-    # amax = 127 (a bf16 value): scale = 127/127 = 1 and inv = 1 exactly, so the
-    # codes are the values rounded half-to-even.  Half-away-from-zero would give
-    # 3, 1, -3, 127, 4 for the first five.
-    v = [2.5, 0.5, -2.5, 126.5, 3.5, 127.0, -0.5, 1.5, -126.5, 0.25]
-    q, s = oracle.quant_group(v)
-    assert s == 1.0
-    assert q.tolist() == [2, 0, -2, 126, 4, 127, 0, 2, -126, 0]
+def _worked_examples():
+    rows = []
+    for line in open(GOLDEN):
+        if line.strip() and not line.startswith("#"):
+            name, values, bits, codes = (f.strip() for f in line.split("|"))
+            rows.append((name, [float(v) for v in values.split()], int(bits, 16), [int(c) for c in codes.split()]))
+    return rows
+
+
+@pytest.mark.parametrize("name,values,bits,codes", _worked_examples(), ids=lambda v: v if isinstance(v, str) else "")
+def test_worked_examples(name, values, bits, codes):
+    # derivations in tests/golden/quant_worked_examples.txt
+    q, s = oracle.quant_group(values)
+    assert f32_bits(s) == bits, name
+    assert q.tolist() == codes, name
+
+
+def test_worked_examples_are_all_there():
+    assert [r[0] for r in _worked_examples()] == ["amax_one", "amax_127_ties"]
 
 
 def test_zero_group():
