@@ -1047,9 +1047,9 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
 // group's lanes inside the 16-lane row, so no LDS and no barrier is needed
 // beyond the sigmoid table.
 // Workgroups are persistent and each wave walks units w, w + waves, ... with
-// the next unit's inputs in flight.
+// the next two units' inputs in flight.
 constexpr int kFwdThreads = 512;
-constexpr int kFwdWorkgroupsPerCU = 3;  // 24 waves per CU; the measured best of 16..32
+constexpr int kFwdWorkgroupsPerCU = 2;  // 16 waves per CU, two units in flight each
 
 // The values are magnitudes (non-negative, no NaN), whose bit patterns order
 // like unsigned integers: an integer maximum needs no canonicalisation and
@@ -1156,12 +1156,15 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
 
   const int64_t u0 = first;
   Unit cur = {u0 / tiles_h, u0 - (u0 / tiles_h) * tiles_h};
-  FwdIn in, in_next;
+  FwdIn in, in_next, in_next2;
+  Unit nxt = cur;
+  advance(nxt);
   if (u0 < units) load(in, cur);
+  if (u0 + waves < units) load(in_next, nxt);
   for (int64_t u = u0; u < units; u += waves) {
-    Unit nxt = cur;
-    advance(nxt);
-    if (u + waves < units) load(in_next, nxt);
+    Unit nxt2 = nxt;
+    advance(nxt2);
+    if (u + 2 * waves < units) load(in_next2, nxt2);
     const int64_t t0 = 4 * cur.rb, h0 = cur.hb * kTile;
     const uint32_t rows = rows_of(cur);
     const bool live = h0 + 8 * p < H;
@@ -1235,7 +1238,9 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
             live ? lane_s : kOut, 0, 0);
     }
     in = in_next;
+    in_next = in_next2;
     cur = nxt;
+    nxt = nxt2;
   }
 }
 
