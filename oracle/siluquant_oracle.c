@@ -30,12 +30,14 @@
  *   - bf16 rounding is round-to-nearest-even on the fp32 bit pattern, with
  *     subnormals kept;
  *   - the group maximum is taken over the bf16-rounded values;
- *   - scale = amax / 127 (1.0 when amax == 0), inv = 1 / scale (both fp32),
- *     q = clamp(rne(v * inv), -127, 127) where v * inv is the exact product of
- *     the bf16 value and the fp32 inverse (the page says to multiply by the
- *     inverse and leaves the precision of that product open; the exact
- *     product is what the formula states), and q = 0 whenever v == 0 (this
- *     avoids 0 * inf when a group's scale is so small that 1/scale overflows);
+ *   - scale = amax / 127 (1.0 when amax == 0), inv = 1 / scale and the
+ *     product p = v * inv are each one fp32 operation, and
+ *     q = clamp(rne(p), -127, 127): the page asks for a multiplication by a
+ *     precomputed fp32 inverse in place of a division, and in fp32 arithmetic
+ *     that multiplication rounds its result to fp32 like every other step
+ *     here; rne then rounds that fp32 value to the nearest integer, ties to
+ *     even.  q = 0 whenever v == 0 (this avoids 0 * inf when a group's scale
+ *     is so small that 1/scale overflows);
  *   - a trailing group shorter than `group` (T or 2H not a multiple of it) is
  *     quantised over the elements it has.
  *
@@ -54,10 +56,11 @@
  * scale = amax / 448 (1.0 when amax == 0), inv = 1 / scale, and the code is
  * the e4m3 value nearest the fp32 product v * inv (ties to even), saturated to
  * +-448; a zero v gives the zero code of its own sign (E4M3 has -0 = 0x80, and
- * this also avoids 0 * inf).  Readings: the product is rounded to fp32 first,
- * because the conversion takes an fp32 input; saturation only matters for
- * groups whose inverse overflowed, since with a finite inverse |v * inv| stays
- * within 448 * (1 + 2^-22).
+ * this also avoids 0 * inf).  Readings: the product v * inv is one fp32
+ * multiplication, exactly as in the int8 quantiser above, and the code is the
+ * E4M3 value nearest that fp32 product; saturation only matters for groups
+ * whose inverse overflowed, since with a finite inverse |v * inv| stays within
+ * 448 * (1 + 2^-22).
  *
  * The group-scaled int8 product (oracle_i8_gemm_group_scaled) is the consumer
  * of the two quantised layouts: the same page's fusion bullet names the
@@ -157,11 +160,10 @@ ORACLE_API float oracle_quant_group(const float* v, int64_t n, int64_t stride, i
     float x = v[i * stride];
     int8_t out = 0;
     if (x != 0.0f) {
-      /* x has 8 significant bits and inv 24, so the double product is exact */
-      double t = (double)x * (double)inv;
-      double r = nearbyint(t); /* default rounding mode: to nearest, ties to even */
-      if (r > 127.0) r = 127.0;
-      if (r < -127.0) r = -127.0;
+      float p = x * inv;       /* one fp32 rounding (no contraction: -ffp-contract=off) */
+      float r = nearbyintf(p); /* default rounding mode: to nearest, ties to even */
+      if (r > 127.0f) r = 127.0f;
+      if (r < -127.0f) r = -127.0f;
       out = (int8_t)r;
     }
     q[i * qstride] = out;

@@ -27,8 +27,11 @@ MUTANTS = {
     "y_missing_up": ("*y = silu * u;", "*y = silu;"),
     "bf16_truncates": ("u += 0x7FFFu + lsb;", "u += 0u * lsb;"),
     "no_bf16_round_trip": ("Y[t * H + h] = bf16_round(y);", "Y[t * H + h] = y;"),
-    "ties_away_from_zero": ("nearbyint(t)", "round(t)"),
-    "fp32_product_before_rounding": ("double t = (double)x * (double)inv;", "double t = (double)(x * inv);"),
+    "ties_away_from_zero": ("float r = nearbyintf(p);", "float r = roundf(p);"),
+    "exact_product_rounded": ("float p = x * inv;       /* one fp32 rounding (no contraction: -ffp-contract=off) */\n"
+                              "      float r = nearbyintf(p);",
+                              "double p = (double)x * (double)inv;\n      float r = (float)nearbyint(p);"),
+    "quotient_not_inverse": ("float p = x * inv;", "float p = x / scale;"),
     "scale_over_128": ("amax / 127.0f", "amax / 128.0f"),
     "amax_without_abs": ("float a = fabsf(v[i * stride]);", "float a = v[i * stride];"),
     "zero_group_scale_zero": ("(amax == 0.0f) ? 1.0f : amax / 127.0f", "(amax == 0.0f) ? 0.0f : amax / 127.0f"),

@@ -3,10 +3,11 @@
 The quantiser (scale = amax / 127, 1.0 for an all-zero group; inv = 1 / scale;
 q = clamp(rne(v * inv), -127, 127)) is pinned by:
 
-* the rounding rule itself: each code is the integer nearest to the exact
-  rational product v * inv (ties to even), found by comparing the two integer
-  neighbours in exact arithmetic, including a group where rounding the fp32
-  product first would give a different code;
+* the rounding rule itself: each code is the integer nearest (ties to even)
+  to the fp32 product RN(v * inv), both roundings done here in exact rational
+  arithmetic, including a hand-derived group where rounding the exact product
+  instead would give a different code (tests/golden/quant_worked_examples.txt,
+  ``fp32_product_tie``) and a search that finds such groups;
 * hand-derived worked examples whose exact results are known without running
   any float code (the fixture tests/golden/quant_worked_examples.txt, with the
   derivations and the rules they follow);
@@ -51,7 +52,7 @@ def test_worked_examples(name, values, bits, codes):
 
 
 def test_worked_examples_are_all_there():
-    assert [r[0] for r in _worked_examples()] == ["amax_one", "amax_127_ties"]
+    assert [r[0] for r in _worked_examples()] == ["amax_one", "amax_127_ties", "fp32_product_tie"]
 
 
 def test_zero_group():
@@ -123,7 +124,7 @@ def _inv_of(scale) -> Fraction:
     return rn32(1 / Fraction(float(scale)))
 
 
-def test_codes_round_the_exact_product():
+def test_codes_round_the_fp32_product():
     rng = np.random.default_rng(11)
     for v in _random_groups(rng, n_groups=150):
         q, s = oracle.quant_group(v)
@@ -131,13 +132,15 @@ def test_codes_round_the_exact_product():
             continue
         inv = _inv_of(s)
         for x, code in zip(v, q):
-            want = max(-127, min(127, rne_int(Fraction(float(x)) * inv)))
+            want = max(-127, min(127, rne_int(rn32(Fraction(float(x)) * inv))))
             assert int(code) == want, (float(x), float(s), int(code), want)
 
 
-def _first_double_rounding_case():
-    """A group (amax, v) where rounding v * inv to fp32 first lands on a tie that
-    the exact product is not on, so the two rules give different codes."""
+def _double_rounding_cases(limit=None):
+    """Groups (amax, v) where the fp32 product RN(v * inv) is a tie k + 1/2
+    that the exact product v * inv is not on, so rounding the product to fp32
+    first gives a different code than rounding the exact product."""
+    cases = []
     for num in range(129, 256):
         amax = Fraction(num, 2)  # bf16-exact values in (64, 128)
         inv = rn32(1 / rn32(amax / 127))
@@ -148,13 +151,16 @@ def _first_double_rounding_case():
             exact = v * inv
             via_f32 = rn32(exact)
             if rne_int(exact) != rne_int(via_f32):
-                return amax, v, rne_int(exact), rne_int(via_f32)
-    return None
+                cases.append((amax, v, rne_int(via_f32), rne_int(exact)))
+                if limit and len(cases) >= limit:
+                    return cases
+    return cases
 
 
-def test_exact_product_differs_from_fp32_product_somewhere():
-    case = _first_double_rounding_case()
-    assert case is not None
-    amax, v, want, other = case
-    q, s = oracle.quant_group([float(amax), float(v)])
-    assert int(q[1]) == want != other
+def test_fp32_product_not_the_exact_product():
+    cases = _double_rounding_cases(limit=20)
+    assert len(cases) == 20
+    for amax, v, want, other in cases:
+        q, s = oracle.quant_group([float(amax), float(v)])
+        assert int(q[0]) == 127
+        assert int(q[1]) == want != other, (amax, v)
