@@ -9,8 +9,12 @@
  * quantising and the multiplication by a precomputed inverse scale.
  *
  * Plain C ABI: pointers and sizes only.  Device pointers are HIP device (or
- * managed) memory on the current HIP device; the stream is a hipStream_t
- * passed as void* (NULL = the null stream).
+ * managed) memory on the current HIP device; `stream` is a hipStream_t (NULL =
+ * the null stream).  The library allocates nothing, keeps no state between
+ * calls and never waits on a stream: every call checks its arguments, asks
+ * the runtime for the current device's compute-unit count, enqueues its
+ * kernels and returns, so a call may be captured into a HIP graph, the first
+ * call of a process included.
  */
 #ifndef SILUQUANT_H
 #define SILUQUANT_H
@@ -20,6 +24,10 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* The HIP runtime's stream handle, declared as the runtime declares it so
+ * that this header needs no HIP header (repeating the typedef is allowed). */
+typedef struct ihipStream_t* hipStream_t;
 
 /* Status codes.  Every argument check runs on the host before any HIP call,
  * so a call that returns one of the first five codes has touched neither the
@@ -33,8 +41,8 @@ enum siluquant_status {
   SILUQUANT_ERR_MISALIGNED = 4,    /* x, grad_y, grad_input_q, y_q_t not 16-byte aligned,
                                       or a scale buffer not 4-byte aligned */
   SILUQUANT_ERR_OVERLAP = 5,       /* two buffers share bytes */
-  SILUQUANT_ERR_DEVICE = 6,        /* a HIP runtime call failed (device query, the one-time
-                                      sigmoid table build) */
+  SILUQUANT_ERR_DEVICE = 6,        /* a HIP runtime call failed (no current device, or the
+                                      device query failed) */
   SILUQUANT_ERR_LAUNCH_FAILED = 7, /* the kernel launch reported an error */
 };
 
@@ -60,8 +68,8 @@ enum siluquant_status {
  * d_gate = ((d*u)*s) * (1 + g*(1 - s)); d_up = d*(g*s); each rounded to bf16
  * (nearest, ties to even) before quantising.  Per group: amax over the bf16
  * values, scale = amax/127 (1.0 when amax == 0), inv = 1/scale (fp32),
- * q = clamp(rne(v*inv), -127, 127) rounding the exact product of the bf16 value
- * and the fp32 inverse (one rounding, ties to even), with q = 0 for v == 0.
+ * p = v*inv (one fp32 multiplication), q = clamp(rne(p), -127, 127) (nearest
+ * integer, ties to even), with q = 0 for v == 0.
  *   -128 is never produced.  Inputs must be finite and keep y, d_gate and d_up
  *   finite.
  * Group size: `group` is 128 (the page's default), 64 or 32; the scale tensors
@@ -80,14 +88,14 @@ enum siluquant_status {
  * Ownership: the caller allocates and owns every buffer; the library keeps no
  *   pointer after the call returns.  Buffers must not overlap.
  * Asynchrony: the work is enqueued on `stream` and the call returns without
- *   waiting; outputs are valid once the stream reaches this point.  The first
- *   call on each device also builds a 31 KB sigmoid table in device memory and
- *   waits for that build (once per device, per process).
+ *   waiting; outputs are valid once the stream reaches this point.  The
+ *   kernels' 31 KB sigmoid table is constant data of the library's code
+ *   object, so no call builds, allocates or waits for anything.
  * Returns a siluquant_status code.
  */
 int silu_dot_fwd_bwd_quant_fuse(const void* x, const void* grad_y, int8_t* grad_input_q, float* grad_input_s,
                                 int8_t* y_q_t, float* y_s_t, int64_t T, int64_t H, int64_t group,
-                                void* stream);
+                                hipStream_t stream);
 
 /*
  * silu_dot_fwd_bwd_quant_fuse_fp8 -- the same pass with FP8 codes.
@@ -111,7 +119,7 @@ int silu_dot_fwd_bwd_quant_fuse(const void* x, const void* grad_y, int8_t* grad_
  *   NaN codes (0x7F, 0xFF) are never produced.
  */
 int silu_dot_fwd_bwd_quant_fuse_fp8(const void* x, const void* grad_y, void* grad_input_q, float* grad_input_s,
-                                    void* y_q_t, float* y_s_t, int64_t T, int64_t H, int64_t group, void* stream);
+                                    void* y_q_t, float* y_s_t, int64_t T, int64_t H, int64_t group, hipStream_t stream);
 
 /*
  * silu_fwd_quant -- forward SwiGLU with row-wise int8 group quantisation.
@@ -135,7 +143,7 @@ int silu_dot_fwd_bwd_quant_fuse_fp8(const void* x, const void* grad_y, void* gra
  * Same ownership, asynchrony and error conventions as above.
  */
 int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q, float* y_s, void* y_bf16, int64_t T,
-                   int64_t H, int64_t group, void* stream);
+                   int64_t H, int64_t group, hipStream_t stream);
 
 /*
  * silu_fwd_quant_q8_1 -- the forward quantiser in the page's q8_1 block layout.
@@ -159,7 +167,7 @@ int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q, float* y
  * Sizes: any T >= 0 (T <= 2^31), H a multiple of 32 (H <= 2^22).
  * Same ownership, asynchrony and error conventions as above.
  */
-int silu_fwd_quant_q8_1(const void* x, const float* row_weight, void* y_q8, int64_t T, int64_t H, void* stream);
+int silu_fwd_quant_q8_1(const void* x, const float* row_weight, void* y_q8, int64_t T, int64_t H, hipStream_t stream);
 
 /*
  * i8_gemm_group_scaled -- the consumer of the two quantised layouts.
@@ -189,11 +197,13 @@ int silu_fwd_quant_q8_1(const void* x, const float* row_weight, void* y_q8, int6
  */
 enum siluquant_gemm_out { SILUQUANT_GEMM_OUT_F32 = 0, SILUQUANT_GEMM_OUT_BF16 = 1 };
 int i8_gemm_group_scaled(const int8_t* A, const float* sA, const int8_t* B, const float* sB, void* C, int64_t M,
-                         int64_t N, int64_t K, int64_t group, int64_t b_rows_per_scale, int c_dtype, void* stream);
+                         int64_t N, int64_t K, int64_t group, int64_t b_rows_per_scale, int c_dtype, hipStream_t stream);
 
-/* Builds the sigmoid table on the current device now (otherwise the first
- * silu_dot_fwd_bwd_quant_fuse call on the device does it).  Blocks until the
- * table is in place.  Safe to call repeatedly and from several threads. */
+/* Optional: makes the HIP runtime load the library's kernels on the current
+ * device now, which it otherwise does at the first launch.  No entry point
+ * needs it first.  Enqueues nothing, allocates nothing itself; safe to call
+ * repeatedly and from several threads.  SILUQUANT_ERR_DEVICE if there is no
+ * usable current device. */
 int siluquant_prepare(void);
 
 /* Static text for a status code (never NULL). */
@@ -217,9 +227,9 @@ int64_t siluquant_algorithmic_bytes(int64_t T, int64_t H, int64_t group);
  *   from x [T, 2H] and grad_y [T, H] as above; any T, H >= 0; 2-byte aligned
  *   device buffers that must not overlap.  Enqueued on `stream`.
  * Both return siluquant_status codes with the same meanings as above. */
-int siluquant_eval_sigmoid(const void* gate, float* s, int64_t n, void* stream);
+int siluquant_eval_sigmoid(const void* gate, float* s, int64_t n, hipStream_t stream);
 int siluquant_eval_intermediates(const void* x, const void* grad_y, void* y_bf16, void* dgdu_bf16, int64_t T,
-                                 int64_t H, void* stream);
+                                 int64_t H, hipStream_t stream);
 
 #ifdef __cplusplus
 }

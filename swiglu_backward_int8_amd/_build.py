@@ -1,7 +1,8 @@
 """Build step for libsiluquant.so (in-tree, for gfx950).
 
-hipcc compiles the HIP sources (the fused SwiGLU passes and the group-scaled
-int8 GEMM) into one shared library next to this file.
+sigmoid_table.py writes the kernels' sigmoid table into _build/, then hipcc
+compiles the HIP sources (the fused SwiGLU passes and the group-scaled int8
+GEMM) into one shared library next to this file.
 Flags that matter for the numbers the library produces:
   -ffp-contract=off                  no fused multiply-add: the arithmetic order
                                      is the one written in the source;
@@ -17,6 +18,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
+GEN = os.path.join(PKG, "_build")  # generated sources (not tracked)
 SRCS = [os.path.join(PKG, "csrc", "siluquant.hip"), os.path.join(PKG, "csrc", "i8gemm.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsiluquant.so")
@@ -37,9 +39,13 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile libsiluquant.so for gfx950 and return its path."""
+    """Generate the sigmoid table, compile libsiluquant.so for gfx950 and
+    return its path."""
+    from swiglu_backward_int8_amd import sigmoid_table
+
+    sigmoid_table.write(os.path.join(GEN, "sigmoid_table.inc"))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I" + INCLUDE] + SRCS + ["-o", tmp]
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-I" + INCLUDE, "-I" + GEN] + SRCS + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature and says so; harmless
     noise = "is not a recognized feature for this target"

@@ -287,7 +287,7 @@ extern "C" {
 __attribute__((visibility("default"))) int i8_gemm_group_scaled(const int8_t* A, const float* sA, const int8_t* B,
                                                                 const float* sB, void* C, int64_t M, int64_t N,
                                                                 int64_t K, int64_t group, int64_t b_rows_per_scale,
-                                                                int c_dtype, void* stream) {
+                                                                int c_dtype, hipStream_t stream) {
   if (group != 32 && group != 64 && group != 128) return SILUQUANT_ERR_BAD_GROUP;
   if (M < 0 || N < 0 || K < 0 || K % group != 0 || (b_rows_per_scale != 1 && b_rows_per_scale != kBN) ||
       (c_dtype != SILUQUANT_GEMM_OUT_F32 && c_dtype != SILUQUANT_GEMM_OUT_BF16))
@@ -311,7 +311,7 @@ __attribute__((visibility("default"))) int i8_gemm_group_scaled(const int8_t* A,
   const int tiles = (int)(tiles_m * tiles_n);
   const int per_xcd = (tiles + 7) / 8;
   const dim3 grid(8 * per_xcd), block(kGemmThreads);
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t s = stream;
   const bool bf16 = c_dtype == SILUQUANT_GEMM_OUT_BF16, blk = b_rows_per_scale == kBN;
   using KernelFn = void (*)(const int8_t*, const float*, const int8_t*, const float*, void*, int64_t, int64_t, int64_t,
                             int, int, int, int);

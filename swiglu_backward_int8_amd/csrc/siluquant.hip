@@ -20,8 +20,8 @@
 //     gate.  Gates are bf16, so only 7,223 inputs give a sigmoid outside
 //     {0, 1/2, 1}; the table holds every magnitude between the ranges where it
 //     saturates, and clamping the index reproduces the saturated values.  The
-//     table is built once per device with fp64 exp rounded to fp32, which makes
-//     the sigmoid bit-exact rather than within an ulp;
+//     table is constant data written at build time (exp correctly rounded to
+//     fp32), which makes the sigmoid bit-exact rather than within an ulp;
 //   * group maxima: each lane reduces inside its registers, writes partial
 //     maxima to LDS, and one thread per group (384 groups per tile at group
 //     128) finishes the reduction and computes scale and inverse with IEEE
@@ -40,8 +40,6 @@
 #include <stdint.h>
 
 #include <algorithm>
-#include <atomic>
-#include <mutex>
 
 #include "siluquant.h"
 
@@ -64,12 +62,18 @@ constexpr int kWorkgroupsPerCU = 1;
 // (sign << 15) | (kSigM0 + k).  Every magnitude at or below kSigM0 gives
 // s == 1/2 for both signs, and every magnitude at or above kSigM0 + kSigL - 1
 // gives s == 1 (g > 0) or s == 0 (g < 0), so clamping k covers all bf16 gates.
+// The entries are fp32 bit patterns written at build time by
+// swiglu_backward_int8_amd/sigmoid_table.py (exp(-g) correctly rounded to
+// fp32, then den = 1 + e and s = 1 / den in fp32); they are constant data of
+// the code object, so no call builds, allocates or waits for anything.
 constexpr uint32_t kSigM0 = 0x3380;  // 2^-24
 constexpr int kSigL = 3892;          // up to 0x42B3 (-89.5 .. past the s == 0 edge at -89)
 constexpr int kSigEntries = 2 * kSigL;
 static_assert(kSigEntries % 4 == 0, "table copied in 16-byte pieces");
 
-__device__ float g_sigma_tab[kSigEntries];
+__device__ __align__(16) const uint32_t g_sigma_tab[kSigEntries] = {
+#include "sigmoid_table.inc"
+};
 
 // LDS layout (floats).  The table stays live for the workgroup's lifetime;
 // then come the partial maxima, the inverse scales and a flag.  The transposed
@@ -82,17 +86,6 @@ constexpr int kInvFloats = 3 * kTile * (kTile / kMinGroup);  // row and column i
 constexpr int kYqtBytes = kTile * kTile;
 static_assert(kYqtBytes <= kRowPartFloats * 4, "transpose buffer reuses the row partials");
 constexpr int kLdsFloats = kSigEntries + kRowPartFloats + kColPartFloats + kInvFloats + 4;
-
-__global__ void build_sigma_table_kernel() {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= kSigEntries) return;
-  uint32_t sign = i >= kSigL ? 1u : 0u;
-  uint32_t mag = kSigM0 + (uint32_t)(i - (int)sign * kSigL);
-  float g = __uint_as_float(((sign << 15) | mag) << 16);
-  float e = (float)exp(-(double)g);
-  float den = 1.0f + e;
-  g_sigma_tab[i] = 1.0f / den;
-}
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -168,18 +161,23 @@ __device__ __forceinline__ void pair_f32(float s, float g, float u, float d, flo
 __device__ __forceinline__ float amax3(float m, float a, float b) { return fmaxf(m, fmaxf(fabsf(a), fabsf(b))); }
 
 // Quantise one value: the low byte of the returned word is the int8 code.
-// One fused multiply-add forms v * inv + 1.5 * 2^23 with a single rounding.
-// For |v * inv| < 2^22 the sum lies where the fp32 spacing is 1, so that
-// rounding is the nearest integer to the exact product, ties to even (the
-// offset is even), and the integer sits in the low mantissa bits in two's
-// complement.  With a finite inverse scale |v * inv| <= 127 * (1 + 2^-22), so
-// the code is within [-127, 127] without a clamp.  kSafe serves groups whose
-// inverse overflowed to +inf: it clamps to +-127 and maps v == 0 to 0, and
-// gives the same word as the fast form for every finite inverse.
+// The product p = v * inv is one fp32 multiplication (the quantiser multiplies
+// by the precomputed inverse in fp32, like every other step), and adding
+// 1.5 * 2^23 rounds p to the nearest integer, ties to even: for |p| < 2^22 the
+// sum lies where the fp32 spacing is 1 and the offset is even, and the integer
+// sits in the low mantissa bits in two's complement.  The two operations stay
+// separate (the library is built with -ffp-contract=off): one fused
+// multiply-add would round the exact product instead, which gives another
+// code on about 1e-4 of the values.  With a finite inverse scale
+// |p| <= 127 * (1 + 2^-22), so the code is within [-127, 127] without a
+// clamp.  kSafe serves groups whose inverse overflowed to +inf: it clamps to
+// +-127 and maps v == 0 to 0, and gives the same word as the fast form for
+// every finite inverse.
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 template <bool kSafe>
 __device__ __forceinline__ uint32_t code_word(float v, float inv) {
-  float r = __builtin_fmaf(v, inv, kMagic);
+  const float p = v * inv;
+  float r = p + kMagic;
   if (kSafe) {
     r = __builtin_amdgcn_fmed3f(r, kMagic - 127.0f, kMagic + 127.0f);
     r = (v == 0.0f) ? kMagic : r;
@@ -1251,7 +1249,7 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
 __device__ __forceinline__ float sigma_of(uint32_t gb, int64_t i) {
   uint32_t lo, hi;
   sigma_offsets2(gb | (gb << 16), lo, hi);
-  return g_sigma_tab[((i & 1) ? hi : lo) >> 2];
+  return __uint_as_float(g_sigma_tab[((i & 1) ? hi : lo) >> 2]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1462,30 +1460,15 @@ __global__ void eval_intermediates_kernel(const uint16_t* __restrict__ x, const 
   dgdu_out[t * 2 * H + H + h] = (uint16_t)pack_bf16(du, 0.0f);
 }
 
-constexpr int kMaxDevices = 64;
-std::atomic<bool> g_table_ready[kMaxDevices];
-int g_cu_count[kMaxDevices];
-std::mutex g_table_mutex;
-
-int ensure_table(int* device_out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SILUQUANT_ERR_DEVICE;
-  *device_out = dev;
-  if (g_table_ready[dev].load(std::memory_order_acquire)) return SILUQUANT_OK;
-  std::lock_guard<std::mutex> lock(g_table_mutex);
-  if (g_table_ready[dev].load(std::memory_order_relaxed)) return SILUQUANT_OK;
-  int cus = 0;
+// The current device's compute-unit count, asked of the runtime on every
+// call (the runtime answers from its cached device properties): persistent
+// grids are sized to it.  The library keeps no per-device state.
+int device_cus(int* cus_out) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SILUQUANT_ERR_DEVICE;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return SILUQUANT_ERR_DEVICE;
-  g_cu_count[dev] = cus;
-  hipStream_t s = nullptr;
-  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return SILUQUANT_ERR_DEVICE;
-  hipLaunchKernelGGL(build_sigma_table_kernel, dim3((kSigEntries + 255) / 256), dim3(256), 0, s);
-  hipError_t e1 = hipGetLastError();
-  hipError_t e2 = hipStreamSynchronize(s);
-  hipError_t e3 = hipStreamDestroy(s);
-  if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) return SILUQUANT_ERR_DEVICE;
-  g_table_ready[dev].store(true, std::memory_order_release);
+  *cus_out = cus;
   return SILUQUANT_OK;
 }
 
@@ -1505,7 +1488,7 @@ constexpr int kFirstTeamEighths = 5;
 
 template <Fmt F>
 int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float* grad_input_s, void* y_q_t,
-                    float* y_s_t, int64_t T, int64_t H, int64_t group, void* stream) {
+                    float* y_s_t, int64_t T, int64_t H, int64_t group, hipStream_t stream) {
   if (group != 32 && group != 64 && group != 128) return SILUQUANT_ERR_BAD_GROUP;
   if (T < 0 || H < 0) return SILUQUANT_ERR_BAD_SHAPE;
   if (T == 0 || H == 0) return SILUQUANT_OK;
@@ -1532,19 +1515,19 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
     for (int j = i + 1; j < 6; ++j)
       if (overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
 
-  int dev = 0;
-  int rc = ensure_table(&dev);
+  int cus = 0;
+  int rc = device_cus(&cus);
   if (rc != SILUQUANT_OK) return rc;
 
-  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipStream_t s = stream;
   const uint16_t* xs = static_cast<const uint16_t*>(x);
   const uint16_t* dys = static_cast<const uint16_t*>(grad_y);
   if (H % 8 != 0) {
     // rows off 16 bytes: the plain path, a kernel per quantisation axis
     const int64_t row_waves = T * ((2 * H + 127) / 128);
     const int64_t col_items = ((T + group - 1) / group) * ((H + 63) / 64);
-    const int64_t rows_grid = std::min<int64_t>((row_waves + 3) / 4, (int64_t)g_cu_count[dev] * 16);
-    const int64_t cols_grid = std::min<int64_t>(col_items, (int64_t)g_cu_count[dev] * 64);
+    const int64_t rows_grid = std::min<int64_t>((row_waves + 3) / 4, (int64_t)cus * 16);
+    const int64_t cols_grid = std::min<int64_t>(col_items, (int64_t)cus * 64);
     auto rows = group == 128 ? silu_quant_rows_narrow_kernel<F, 128>
                 : group == 64 ? silu_quant_rows_narrow_kernel<F, 64>
                               : silu_quant_rows_narrow_kernel<F, 32>;
@@ -1561,7 +1544,7 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
   const int tiles = (int)(tiles_t * tiles_h64);
   // Persistent grid: as many workgroups as fit on the device at once (a
   // multiple of 8, one share per XCD), or one per tile if there are fewer.
-  int grid = g_cu_count[dev] * kWorkgroupsPerCU;
+  int grid = cus * kWorkgroupsPerCU;
   grid = grid >= 8 ? grid - grid % 8 : grid;
   if (tiles < grid) grid = tiles;
   int8_t* gq = static_cast<int8_t*>(grad_input_q);
@@ -1579,7 +1562,7 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
     // workgroups.  Without enough workgroups per XCD, pairs of workgroups
     // share each tile.
     int first_team = 0;
-    grid = g_cu_count[dev] * kWorkgroupsPerCU;
+    grid = cus * kWorkgroupsPerCU;
     grid = grid - grid % 8;
     if (grid >= 16 && 2 * tiles >= grid) {
       const int per_xcd = grid / 8;
@@ -1604,16 +1587,16 @@ using ForwardKernel = void (*)(const uint16_t*, const float*, int8_t*, float*, u
 // Persistent grid for the forward quantiser: units of 4 rows x 128 channels,
 // one per wave, as many workgroups as fit on the device or as the units need.
 int launch_forward(ForwardKernel kernel, const void* x, const float* row_weight, int8_t* y_q, float* y_s,
-                   void* y_bf16, int64_t T, int64_t H, void* stream) {
-  int dev = 0;
-  int rc = ensure_table(&dev);
+                   void* y_bf16, int64_t T, int64_t H, hipStream_t stream) {
+  int cus = 0;
+  int rc = device_cus(&cus);
   if (rc != SILUQUANT_OK) return rc;
   const int tiles_h = (int)((H + kTile - 1) / kTile);
   const int64_t units = ((T + 3) / 4) * tiles_h;
-  int64_t grid = (int64_t)g_cu_count[dev] * kFwdWorkgroupsPerCU;
+  int64_t grid = (int64_t)cus * kFwdWorkgroupsPerCU;
   const int64_t wg_needed = (units + kFwdThreads / 64 - 1) / (kFwdThreads / 64);
   if (wg_needed < grid) grid = wg_needed;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kFwdThreads), 0, static_cast<hipStream_t>(stream),
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kFwdThreads), 0, stream,
                      static_cast<const uint16_t*>(x), row_weight, y_q, y_s, static_cast<uint16_t*>(y_bf16), T, H,
                      tiles_h, units);
   return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;
@@ -1637,37 +1620,46 @@ __attribute__((visibility("default"))) const char* siluquant_strerror(int status
     case SILUQUANT_OK: return "ok";
     case SILUQUANT_ERR_NULL_PTR: return "a buffer pointer is NULL";
     case SILUQUANT_ERR_BAD_SHAPE: return "sizes must be non-negative and within the limits, K a multiple of the group, H of 32 for q8_1 blocks";
-    case SILUQUANT_ERR_BAD_GROUP: return "unsupported group size (the passes take 128, 64 or 32; the forward pass and the GEMM 128)";
+    case SILUQUANT_ERR_BAD_GROUP: return "unsupported group size (every entry point takes 128, 64 or 32; q8_1 blocks are always 32)";
     case SILUQUANT_ERR_MISALIGNED: return "a buffer is not aligned (code and input tensors 16 bytes, scales 4 bytes)";
     case SILUQUANT_ERR_OVERLAP: return "buffers overlap";
-    case SILUQUANT_ERR_DEVICE: return "HIP runtime error (device query or sigmoid table build)";
+    case SILUQUANT_ERR_DEVICE: return "HIP runtime error (no current device, or a device query failed)";
     case SILUQUANT_ERR_LAUNCH_FAILED: return "kernel launch failed";
     default: return "unknown status";
   }
 }
 
 __attribute__((visibility("default"))) int siluquant_prepare(void) {
-  int dev = 0;
-  return ensure_table(&dev);
+  // Asking for a kernel's attributes makes the runtime load the library's
+  // code object on the current device, which it would otherwise do at the
+  // first launch.
+  int cus = 0;
+  int rc = device_cus(&cus);
+  if (rc != SILUQUANT_OK) return rc;
+  hipFuncAttributes attr;
+  if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(silu_quant_bwd_kernel<Fmt::kInt8, 128>)) !=
+      hipSuccess)
+    return SILUQUANT_ERR_DEVICE;
+  return SILUQUANT_OK;
 }
 
 __attribute__((visibility("default"))) int silu_dot_fwd_bwd_quant_fuse(const void* x, const void* grad_y,
                                                                        int8_t* grad_input_q, float* grad_input_s,
                                                                        int8_t* y_q_t, float* y_s_t, int64_t T,
-                                                                       int64_t H, int64_t group, void* stream) {
+                                                                       int64_t H, int64_t group, hipStream_t stream) {
   return launch_backward<Fmt::kInt8>(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, T, H, group, stream);
 }
 
 __attribute__((visibility("default"))) int silu_dot_fwd_bwd_quant_fuse_fp8(const void* x, const void* grad_y,
                                                                            void* grad_input_q, float* grad_input_s,
                                                                            void* y_q_t, float* y_s_t, int64_t T,
-                                                                           int64_t H, int64_t group, void* stream) {
+                                                                           int64_t H, int64_t group, hipStream_t stream) {
   return launch_backward<Fmt::kFp8>(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, T, H, group, stream);
 }
 
 __attribute__((visibility("default"))) int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q,
                                                           float* y_s, void* y_bf16, int64_t T, int64_t H,
-                                                          int64_t group, void* stream) {
+                                                          int64_t group, hipStream_t stream) {
   if (group != 32 && group != 64 && group != 128) return SILUQUANT_ERR_BAD_GROUP;
   if (T < 0 || H < 0) return SILUQUANT_ERR_BAD_SHAPE;
   if (T == 0 || H == 0) return SILUQUANT_OK;
@@ -1685,15 +1677,15 @@ __attribute__((visibility("default"))) int silu_fwd_quant(const void* x, const f
       if (bufs[i] && bufs[j] && overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
   if (H % 8 != 0) {
     // rows off 16 bytes (x, y_bf16) and 8 bytes (y_q): the plain path
-    int dev = 0;
-    int rc = ensure_table(&dev);
+    int cus = 0;
+    int rc = device_cus(&cus);
     if (rc != SILUQUANT_OK) return rc;
     const int64_t waves = T * ((H + 127) / 128);
-    const int64_t grid = std::min<int64_t>((waves + 3) / 4, (int64_t)g_cu_count[dev] * 16);
+    const int64_t grid = std::min<int64_t>((waves + 3) / 4, (int64_t)cus * 16);
     auto kernel = group == 128 ? silu_fwd_quant_narrow_kernel<128>
                   : group == 64 ? silu_fwd_quant_narrow_kernel<64>
                                 : silu_fwd_quant_narrow_kernel<32>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(x), row_weight, y_q, y_s, static_cast<uint16_t*>(y_bf16), T, H);
     return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;
   }
@@ -1705,7 +1697,7 @@ __attribute__((visibility("default"))) int silu_fwd_quant(const void* x, const f
 }
 
 __attribute__((visibility("default"))) int silu_fwd_quant_q8_1(const void* x, const float* row_weight, void* y_q8,
-                                                               int64_t T, int64_t H, void* stream) {
+                                                               int64_t T, int64_t H, hipStream_t stream) {
   // blocks of 32 channels (the page's k % 32 == 0)
   if (T < 0 || H < 0 || H % 32 != 0) return SILUQUANT_ERR_BAD_SHAPE;
   if (T == 0 || H == 0) return SILUQUANT_OK;
@@ -1723,7 +1715,7 @@ __attribute__((visibility("default"))) int silu_fwd_quant_q8_1(const void* x, co
 }
 
 __attribute__((visibility("default"))) int siluquant_eval_sigmoid(const void* gate, float* s, int64_t n,
-                                                                  void* stream) {
+                                                                  hipStream_t stream) {
   if (n < 0) return SILUQUANT_ERR_BAD_SHAPE;
   if (n == 0) return SILUQUANT_OK;
   if (!gate || !s) return SILUQUANT_ERR_NULL_PTR;
@@ -1731,17 +1723,14 @@ __attribute__((visibility("default"))) int siluquant_eval_sigmoid(const void* ga
     return SILUQUANT_ERR_MISALIGNED;
   if (overlaps(gate, 2 * n, s, 4 * n)) return SILUQUANT_ERR_OVERLAP;
   if (n > (int64_t(1) << 40)) return SILUQUANT_ERR_BAD_SHAPE;
-  int dev = 0;
-  int rc = ensure_table(&dev);
-  if (rc != SILUQUANT_OK) return rc;
   hipLaunchKernelGGL(eval_sigmoid_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(gate), s, n);
+                     stream, static_cast<const uint16_t*>(gate), s, n);
   return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;
 }
 
 __attribute__((visibility("default"))) int siluquant_eval_intermediates(const void* x, const void* grad_y,
                                                                         void* y_bf16, void* dgdu_bf16, int64_t T,
-                                                                        int64_t H, void* stream) {
+                                                                        int64_t H, hipStream_t stream) {
   if (T < 0 || H < 0) return SILUQUANT_ERR_BAD_SHAPE;
   if (T == 0 || H == 0) return SILUQUANT_OK;
   if (T > (int64_t(1) << 40) / H) return SILUQUANT_ERR_BAD_SHAPE;
@@ -1754,11 +1743,8 @@ __attribute__((visibility("default"))) int siluquant_eval_intermediates(const vo
   for (int i = 0; i < 4; ++i)
     for (int j = i + 1; j < 4; ++j)
       if (overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
-  int dev = 0;
-  int rc = ensure_table(&dev);
-  if (rc != SILUQUANT_OK) return rc;
   hipLaunchKernelGGL(eval_intermediates_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(x),
+                     stream, static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(grad_y), static_cast<uint16_t*>(y_bf16),
                      static_cast<uint16_t*>(dgdu_bf16), T, H);
   return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;

@@ -47,6 +47,22 @@ def test_product_library_does_not_link_the_oracle():
     assert "liboracle" not in deps
 
 
+def test_library_allocates_nothing_and_never_waits():
+    # The boundary enqueues kernels on the caller's stream and returns: the
+    # library imports no HIP routine that allocates or frees memory, creates
+    # or destroys a stream or event, copies memory or waits for the device.
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--undefined-only", sq.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    names = [line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()]
+    hip = sorted({n for n in names if n.startswith("hip")})
+    allowed = {"hipDeviceGetAttribute", "hipFuncGetAttributes", "hipGetDevice", "hipGetLastError",
+               "hipLaunchKernel"}
+    assert hip and set(hip) <= allowed, hip
+    assert "__hipRegisterFatBinary" in out  # the kernels' code object, registered at load
+
+
 # Fake, well-aligned, non-overlapping addresses: every call below must be
 # rejected by the host-side checks, so none of them is ever dereferenced.
 BASE = 1 << 40
