@@ -101,6 +101,8 @@ def _load():
         lib.oracle_f32_to_f16.restype = ctypes.c_uint16
         lib.oracle_silu_fwd_quant_q8_1.argtypes = [u16p, f32p, u8p, i64, i64]
         lib.oracle_silu_fwd_quant_q8_1.restype = ctypes.c_int
+        lib.oracle_kquant_swiglu_q8_1_rows.argtypes = [u16p, u16p, f32p, u16p, u8p, i64, i64]
+        lib.oracle_kquant_swiglu_q8_1_rows.restype = ctypes.c_int
         lib.oracle_i8_gemm_group_scaled.argtypes = [i8p, f32p, i8p, f32p, f64p, f64p, i64, i64, i64, i64, i64]
         lib.oracle_i8_gemm_group_scaled.restype = ctypes.c_int
         _lib = lib
@@ -282,6 +284,30 @@ def silu_fwd_quant_q8_1(x, w=None):
     if rc != 0:
         raise RuntimeError("oracle_silu_fwd_quant_q8_1 failed with code %d" % rc)
     return out
+
+
+def kquant_swiglu_q8_1_rows(gate, up, w=None, want_h: bool = True):
+    """The page's fused launch shape: separate bf16 gate and up [rows, inter]
+    (inter a multiple of 32), optional fp32 row weight; returns the q8_1
+    blocks uint8 [rows, inter/32 * 36] and, if want_h, the bf16 bits of h as
+    uint16 [rows, inter]."""
+    gate = _as_bits(gate)
+    up = _as_bits(up)
+    assert gate.shape == up.shape and gate.ndim == 2
+    rows, inter = gate.shape
+    out = np.zeros((rows, (inter // 32) * 36), dtype=np.uint8)
+    h = np.zeros((rows, inter), dtype=np.uint16) if want_h else None
+    wp = None
+    if w is not None:
+        w = np.ascontiguousarray(np.asarray(w, dtype=np.float32))
+        assert w.shape == (rows,)
+        wp = _ptr(w, ctypes.c_float)
+    rc = _load().oracle_kquant_swiglu_q8_1_rows(_ptr(gate, ctypes.c_uint16), _ptr(up, ctypes.c_uint16), wp,
+                                                _ptr(h, ctypes.c_uint16) if h is not None else None,
+                                                _ptr(out, ctypes.c_uint8), rows, inter)
+    if rc != 0:
+        raise RuntimeError("oracle_kquant_swiglu_q8_1_rows failed with code %d" % rc)
+    return (out, h) if want_h else out
 
 
 def split_q8_1(blocks):

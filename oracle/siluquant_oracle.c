@@ -369,6 +369,19 @@ ORACLE_API uint16_t oracle_f32_to_f16(float x) {
  * fl32(scale * sum(q)) rounded to binary16, i.e. the block's values as its
  * codes give them; bytes 4-35 the codes, both halves little-endian.  H must be
  * a multiple of 32 (the page's k % 32 == 0). */
+/* One 36-byte block from 32 codes and their scale (the layout read above). */
+static void oracle_q8_1_block(const int8_t* qb, float scale, uint8_t* blk) {
+  int sum = 0;
+  for (int i = 0; i < 32; ++i) sum += qb[i];
+  float dequant_sum = scale * (float)sum;
+  uint16_t d16 = oracle_f32_to_f16(scale), s16 = oracle_f32_to_f16(dequant_sum);
+  blk[0] = (uint8_t)(d16 & 0xFF);
+  blk[1] = (uint8_t)(d16 >> 8);
+  blk[2] = (uint8_t)(s16 & 0xFF);
+  blk[3] = (uint8_t)(s16 >> 8);
+  memcpy(blk + 4, qb, 32);
+}
+
 ORACLE_API int oracle_silu_fwd_quant_q8_1(const uint16_t* x, const float* w, uint8_t* blocks, int64_t T, int64_t H) {
   if (T < 0 || H < 0 || H % 32 != 0) return ORACLE_BAD_ARG;
   if (T == 0 || H == 0) return ORACLE_OK;
@@ -381,25 +394,48 @@ ORACLE_API int oracle_silu_fwd_quant_q8_1(const uint16_t* x, const float* w, uin
     return ORACLE_NO_MEMORY;
   }
   int rc = oracle_silu_fwd_quant(x, w, q, sc, NULL, T, H, 32);
-  for (int64_t t = 0; rc == ORACLE_OK && t < T; ++t) {
-    for (int64_t b = 0; b < nb; ++b) {
-      const int8_t* qb = q + t * H + 32 * b;
-      uint8_t* blk = blocks + (t * nb + b) * 36;
-      int sum = 0;
-      for (int i = 0; i < 32; ++i) sum += qb[i];
-      float scale = sc[t * nb + b];
-      float dequant_sum = scale * (float)sum;
-      uint16_t d16 = oracle_f32_to_f16(scale), s16 = oracle_f32_to_f16(dequant_sum);
-      blk[0] = (uint8_t)(d16 & 0xFF);
-      blk[1] = (uint8_t)(d16 >> 8);
-      blk[2] = (uint8_t)(s16 & 0xFF);
-      blk[3] = (uint8_t)(s16 >> 8);
-      memcpy(blk + 4, qb, 32);
-    }
-  }
+  for (int64_t t = 0; rc == ORACLE_OK && t < T; ++t)
+    for (int64_t b = 0; b < nb; ++b) oracle_q8_1_block(q + t * H + 32 * b, sc[t * nb + b], blocks + (t * nb + b) * 36);
   free(q);
   free(sc);
   return rc;
+}
+
+/* The fused launch of the page "kquant_mmq.rs" in its own argument shape
+ * (kquant_swiglu_q8_1_rows): gate and up are separate bf16 [rows, inter]
+ * arrays, w an optional fp32 weight per row, and the call writes both
+ * h = bf16((silu(gate) * up) * w[row]) [rows, inter] (when h_bf16 is not
+ * NULL) and the q8_1 blocks of h [rows, inter/32 * 36].  inter must be a
+ * multiple of 32.  Row by row: h as in oracle_silu_fwd_quant, then per 32
+ * channels the group quantiser and the block above.  The page's `limit`
+ * argument has no stated meaning and is not modelled. */
+ORACLE_API int oracle_kquant_swiglu_q8_1_rows(const uint16_t* gate, const uint16_t* up, const float* w,
+                                              uint16_t* h_bf16, uint8_t* blocks, int64_t rows, int64_t inter) {
+  if (rows < 0 || inter < 0 || inter % 32 != 0) return ORACLE_BAD_ARG;
+  if (rows == 0 || inter == 0) return ORACLE_OK;
+  int64_t nb = inter / 32;
+  float* Y = (float*)malloc((size_t)inter * sizeof(float));
+  if (!Y) return ORACLE_NO_MEMORY;
+  for (int64_t t = 0; t < rows; ++t) {
+    for (int64_t h = 0; h < inter; ++h) {
+      float g = oracle_bf16_to_f32(gate[t * inter + h]);
+      float u = oracle_bf16_to_f32(up[t * inter + h]);
+      float s = oracle_sigmoid(g);
+      float silu = g * s;
+      float v = silu * u;
+      if (w) v = v * w[t];
+      uint16_t b = oracle_f32_to_bf16(v);
+      Y[h] = oracle_bf16_to_f32(b);
+      if (h_bf16) h_bf16[t * inter + h] = b;
+    }
+    for (int64_t b = 0; b < nb; ++b) {
+      int8_t qb[32];
+      float scale = oracle_quant_group(&Y[32 * b], 32, 1, qb, 1);
+      oracle_q8_1_block(qb, scale, blocks + (t * nb + b) * 36);
+    }
+  }
+  free(Y);
+  return ORACLE_OK;
 }
 
 /* ---- the group-scaled int8 product ------------------------------------------ */

@@ -77,6 +77,14 @@ MUTANTS = {
                             "uint16_t s16 = oracle_f32_to_f16(scale), d16 = oracle_f32_to_f16(dequant_sum);"),
     "q8_1_sum_of_codes": ("float dequant_sum = scale * (float)sum;", "float dequant_sum = (float)sum;"),
     "q8_1_codes_after_header_shift": ("memcpy(blk + 4, qb, 32);", "memcpy(blk + 4, qb + 1, 31);"),
+    "kquant_rows_gate_from_up": ("float g = oracle_bf16_to_f32(gate[t * inter + h]);",
+                                 "float g = oracle_bf16_to_f32(up[t * inter + h]);"),
+    "kquant_rows_weight_dropped": ("      if (w) v = v * w[t];\n      uint16_t b = oracle_f32_to_bf16(v);\n"
+                                   "      Y[h] = oracle_bf16_to_f32(b);\n      if (h_bf16)",
+                                   "      uint16_t b = oracle_f32_to_bf16(v);\n"
+                                   "      Y[h] = oracle_bf16_to_f32(b);\n      if (h_bf16)"),
+    "kquant_rows_blocks_rotated": ("oracle_q8_1_block(qb, scale, blocks + (t * nb + b) * 36);",
+                                   "oracle_q8_1_block(qb, scale, blocks + (t * nb + (b + 1) % nb) * 36);"),
     "fp8_nan_beyond_range": ("if (a >= 448.0) return sign | 0x7E;", "if (a >= 464.0) return sign | 0x7F;"),
 }
 
@@ -85,7 +93,7 @@ MUTANTS = {
 # child run (which stops at the first failure) ends early.
 FIRST = {"gemm_": "tests/test_oracle_gemm.py", "fp8_": "tests/test_oracle_fp8.py",
          "forward_": "tests/test_oracle_forward.py", "f16_": "tests/test_oracle_q8_1.py",
-         "q8_1_": "tests/test_oracle_q8_1.py"}
+         "q8_1_": "tests/test_oracle_q8_1.py", "kquant_": "tests/test_oracle_q8_1.py"}
 
 
 def _run_mutant(name, workdir):

@@ -110,3 +110,45 @@ def test_q8_1_needs_h_a_multiple_of_32():
     xt, _ = random_inputs(4, 48, seed=3)
     with pytest.raises(RuntimeError):
         oracle.silu_fwd_quant_q8_1(_bits(xt))
+
+
+# The page's own argument shape (kquant_swiglu_q8_1_rows on the page
+# "kquant_mmq.rs"): separate gate and up arrays, an optional row weight, and
+# both the bf16 h and its q8_1 blocks written.  The page states the fused
+# launch is byte-identical to the swiglu launch followed by the q8_1 launch;
+# here that is the pinned forward quantiser (for h) and the pinned q8_1
+# layout (for the blocks) on x = [gate | up].
+
+@pytest.mark.parametrize("rows,inter,weighted", [(16, 256, False), (9, 96, True), (5, 32, True), (1, 64, False)])
+def test_separate_gate_up_equals_the_two_launches(rows, inter, weighted):
+    xt, _ = random_inputs(rows, inter, seed=3 * rows + inter)
+    xb = _bits(xt)
+    gate = np.ascontiguousarray(xb[:, :inter])
+    up = np.ascontiguousarray(xb[:, inter:])
+    w = (np.random.default_rng(rows).random(rows) * 4 - 2).astype(np.float32) if weighted else None
+    blocks, h = oracle.kquant_swiglu_q8_1_rows(gate, up, w)
+    _, _, yb = oracle.silu_fwd_quant(xb, w, group_size=32, want_bf16=True)
+    assert np.array_equal(h, yb)
+    assert np.array_equal(blocks, oracle.silu_fwd_quant_q8_1(xb, w))
+    assert np.array_equal(oracle.kquant_swiglu_q8_1_rows(gate, up, w, want_h=False), blocks)
+
+
+def test_separate_gate_up_saturated_closed_form():
+    # gate 20 (s == 1), up 0.5, weight 3: h = bf16(10 * 3) = 30 exactly in
+    # every channel; scale rn(30/127), codes 127, sum(q) = 32 * 127
+    rows, inter = 2, 64
+    gate = np.full((rows, inter), 0x41A0, dtype=np.uint16)  # bf16 20.0
+    up = np.full((rows, inter), 0x3F00, dtype=np.uint16)    # bf16 0.5
+    blocks, h = oracle.kquant_swiglu_q8_1_rows(gate, up, np.full(rows, 3.0, dtype=np.float32))
+    assert np.all(h == 0x41F0)  # bf16 30.0
+    d, s, q = oracle.split_q8_1(blocks)
+    scale = rn32(Fraction(30) / 127)
+    assert np.all(q == 127)
+    assert np.all(d == np.float16(np.float32(float(scale))))
+    assert np.all(s == np.float16(np.float32(float(rn32(Fraction(float(scale)) * 4064)))))
+
+
+def test_separate_gate_up_needs_inter_a_multiple_of_32():
+    g = np.zeros((2, 48), dtype=np.uint16)
+    with pytest.raises(RuntimeError):
+        oracle.kquant_swiglu_q8_1_rows(g, g)
