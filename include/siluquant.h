@@ -164,10 +164,33 @@ int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q, float* y
  *   x           bf16 [T, 2H] as above (read only; 16-byte aligned)
  *   row_weight  fp32 [T], or NULL for weight 1 (4-byte aligned)
  *   y_q8        uint8 [T, (H/32) * 36] the blocks (4-byte aligned)
- * Sizes: any T >= 0 (T <= 2^31), H a multiple of 32 (H <= 2^22).
+ * Sizes: any T >= 0 (T <= 2^28), H a multiple of 32 (H <= 2^22).
  * Same ownership, asynchrony and error conventions as above.
  */
 int silu_fwd_quant_q8_1(const void* x, const float* row_weight, void* y_q8, int64_t T, int64_t H, hipStream_t stream);
+
+/*
+ * kquant_swiglu_q8_1_rows -- the same forward quantiser in the argument shape
+ * of the page's fused launch.
+ *
+ * The page "kquant_mmq.rs" (docs.atlascybernetics.ai) documents
+ * kquant_swiglu_q8_1_rows: separate gate and up inputs, an optional weight
+ * per row, and two outputs, h = bf16(swiglu(gate, up) * w[row]) and the
+ * block_q8_1 blocks of h, byte-identical to the swiglu launch followed by the
+ * q8_1 launch.  Here h and the blocks are exactly those of silu_fwd_quant_q8_1
+ * (with y_bf16) on x = [gate | up]:
+ *   gate, up  bf16 [rows, inter] row-major (read only; 16-byte aligned; they
+ *             may share memory with each other)
+ *   w         fp32 [rows], or NULL for weight 1 (4-byte aligned)
+ *   h_bf16    bf16 [rows, inter] the rounded h, or NULL (16-byte aligned)
+ *   out_q8    uint8 [rows, (inter/32) * 36] the blocks (4-byte aligned)
+ * Sizes: any rows >= 0 (rows <= 2^28), inter a multiple of 32 (the page's
+ *   check), inter <= 2^22.  The page's `limit` argument has no stated meaning
+ *   and is not provided.  Outputs must not overlap any other buffer.
+ * Same ownership, asynchrony and error conventions as above.
+ */
+int kquant_swiglu_q8_1_rows(const void* gate, const void* up, const float* w, void* h_bf16, void* out_q8,
+                            int64_t rows, int64_t inter, hipStream_t stream);
 
 /*
  * i8_gemm_group_scaled -- the consumer of the two quantised layouts.

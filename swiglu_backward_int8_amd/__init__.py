@@ -29,7 +29,7 @@ _ERRORS = {
 }
 
 EXPORTED = ("silu_dot_fwd_bwd_quant_fuse", "silu_dot_fwd_bwd_quant_fuse_fp8", "silu_fwd_quant", "silu_fwd_quant_q8_1",
-            "i8_gemm_group_scaled", "siluquant_prepare", "siluquant_strerror", "siluquant_algorithmic_bytes",
+            "kquant_swiglu_q8_1_rows", "i8_gemm_group_scaled", "siluquant_prepare", "siluquant_strerror", "siluquant_algorithmic_bytes",
             "siluquant_eval_sigmoid", "siluquant_eval_intermediates")
 
 _lib = None
@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.silu_fwd_quant.restype = ctypes.c_int
         L.silu_fwd_quant_q8_1.argtypes = [vp, vp, vp, i64, i64, vp]
         L.silu_fwd_quant_q8_1.restype = ctypes.c_int
+        L.kquant_swiglu_q8_1_rows.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp]
+        L.kquant_swiglu_q8_1_rows.restype = ctypes.c_int
         L.i8_gemm_group_scaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, vp]
         L.i8_gemm_group_scaled.restype = ctypes.c_int
         L.siluquant_eval_sigmoid.argtypes = [vp, vp, i64, vp]
@@ -217,6 +219,39 @@ def silu_fwd_quant_q8_1(x, y_q8, row_weight=None):
         code = int(lib().silu_fwd_quant_q8_1(x.data_ptr(), row_weight.data_ptr() if row_weight is not None else None,
                                              y_q8.data_ptr(), T, H, torch.cuda.current_stream(dev).cuda_stream))
     _check(code, "silu_fwd_quant_q8_1")
+
+
+def kquant_swiglu_q8_1_rows(gate, up, out_q8, w=None, h_bf16=None):
+    """The page's fused launch shape (kquant_swiglu_q8_1_rows): separate bf16
+    gate and up [rows, inter] (inter a multiple of 32), optional fp32 weight
+    per row; writes the q8_1 blocks of h = bf16((silu(gate) * up) * w[row])
+    into out_q8 uint8 [rows, (inter/32) * 36] and, if given, h into h_bf16
+    [rows, inter].  Enqueued on the current stream of gate's device; returns
+    None."""
+    import torch
+
+    if gate.dim() != 2:
+        raise ValueError("gate must be [rows, inter]")
+    rows, inter = int(gate.shape[0]), int(gate.shape[1])
+    dev = gate.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU; got %s" % dev)
+    checks = [("gate", gate, torch.bfloat16, (rows, inter)), ("up", up, torch.bfloat16, (rows, inter)),
+              ("out_q8", out_q8, torch.uint8, (rows, (inter // 32) * Q8_1_BLOCK))]
+    if w is not None:
+        checks.append(("w", w, torch.float32, (rows,)))
+    if h_bf16 is not None:
+        checks.append(("h_bf16", h_bf16, torch.bfloat16, (rows, inter)))
+    for name, t, dt, shape in checks:
+        if t.dtype != dt or t.device != dev or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+            raise ValueError("%s must be a contiguous %s tensor of shape %s on %s" % (name, dt, shape, dev))
+    with torch.cuda.device(dev):
+        code = int(lib().kquant_swiglu_q8_1_rows(gate.data_ptr(), up.data_ptr(),
+                                                 w.data_ptr() if w is not None else None,
+                                                 h_bf16.data_ptr() if h_bf16 is not None else None,
+                                                 out_q8.data_ptr(), rows, inter,
+                                                 torch.cuda.current_stream(dev).cuda_stream))
+    _check(code, "kquant_swiglu_q8_1_rows")
 
 
 def forward_q8_1_bytes(T: int, H: int, with_weight: bool = False) -> int:

@@ -49,11 +49,9 @@ constexpr int kTile = 128;
 // Lane (q, p) of a workgroup owns tokens kRows*q .. kRows*q + kRows - 1 and
 // channels 8p .. 8p+7 of the tile: 16 lanes span the tile's 128 channels and
 // 128 / kRows groups of 16 lanes span its 128 tokens.
-#ifndef SILUQUANT_ROWS_PER_LANE
-#define SILUQUANT_ROWS_PER_LANE 2
-#endif
-constexpr int kRows = SILUQUANT_ROWS_PER_LANE;
-static_assert(kRows == 2 || kRows == 4, "rows per lane");
+// Two rows per lane: 1024 threads per tile, and the 114-127 registers a lane
+// then needs fit 16 waves per CU.
+constexpr int kRows = 2;
 constexpr int kQ = kTile / kRows;        // lane groups along the tokens
 constexpr int kThreads = 16 * kQ;        // 1024 for two rows per lane
 constexpr int kWorkgroupsPerCU = 1;
@@ -505,11 +503,9 @@ __device__ __forceinline__ void stage_y_codes(const uint32_t (&Yp)[R][4], const 
     float v[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) v[i] = (j & 1) ? bf16_hi(Yp[i][j >> 1]) : bf16_lo(Yp[i][j >> 1]);
+    static_assert(R == 2, "two tokens per lane: one 2-byte piece per channel");
     char* dst = s_yqt + yqt_byte<R>(8 * p + j, q);
-    if constexpr (R == 4)
-      *reinterpret_cast<uint32_t*>(dst) = codes4<F, kSafe>(v[0], v[1], v[2], v[3], iy[j]);
-    else
-      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)codes2<F, kSafe>(v[0], v[1], iy[j]);
+    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)codes2<F, kSafe>(v[0], v[1], iy[j]);
   }
 }
 
@@ -1090,14 +1086,19 @@ __device__ __forceinline__ int quad_sum(int v) {
 // subnormals kept).
 __device__ __forceinline__ uint32_t f16_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
 
+// Row t of gate starts at gate + t * in_row and row t of up at up + t * in_row
+// (bf16 elements): x = [gate | up] gives up = gate + H and in_row = 2H, the
+// page's separate gate and up arrays in_row = H.
 // kQ81: the output is the q8_1 block layout of the page "kquant_mmq.rs" (kG
 // is 32): per row H/32 blocks of 36 bytes, the binary16 d (the group scale)
 // and sum (fl32(scale * sum of the codes)), then the 32 codes.  y_q then
-// points at the blocks (4-byte aligned) and y_s and y_bf16 are unused.
+// points at the blocks (4-byte aligned) and y_s is unused.  y_bf16, if not
+// null, receives the rounded y [T, H] in either layout.
 template <int kG, bool kQ81 = false, bool kWeighted = false>
 __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ row_weight, int8_t* __restrict__ y_q,
-    float* __restrict__ y_s, uint16_t* __restrict__ y_bf16, int64_t T, int64_t H, int tiles_h, int64_t units) {
+    const uint16_t* __restrict__ gate, const uint16_t* __restrict__ up, int64_t in_row,
+    const float* __restrict__ row_weight, int8_t* __restrict__ y_q, float* __restrict__ y_s,
+    uint16_t* __restrict__ y_bf16, int64_t T, int64_t H, int tiles_h, int64_t units) {
   __shared__ __align__(16) float s_tab[kSigEntries];
   __shared__ __align__(16) float2 s_qtab[128];
   const int tid = threadIdx.x;
@@ -1125,9 +1126,10 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
   // each pair stores the pair's 16 codes; else each lane stores its own 8.
   const bool pair_stores = (H & 15) == 0;
   constexpr uint32_t kOut = 0x80000000u;  // past any record count
-  const uint32_t x_row = (uint32_t)(4 * H);
+  const uint32_t x_row = (uint32_t)(2 * in_row);  // bytes from one input row to the next
   const uint32_t q_row = kQ81 ? (uint32_t)(H / 32 * 36) : (uint32_t)H;
-  const uint32_t lane_x = r * x_row + 16 * p, lane_xu = lane_x + 2 * (uint32_t)H;
+  const uint32_t lane_x = r * x_row + 16 * p;
+  const uint32_t lane_h = 2 * (r * (uint32_t)H + 8 * p);  // the lane's y in y_bf16
   const uint32_t lane_q = kQ81 ? r * q_row + (uint32_t)(8 * p / 32) * 36 + 4 * (1 + 2 * (p & 3)) : r * q_row + 8 * p;
   const uint32_t lane_s = 4 * (r * (uint32_t)groups + (uint32_t)(8 * p / kG));
 
@@ -1145,11 +1147,13 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
   auto rows_of = [&](const Unit& c) { return T - 4 * c.rb < 4 ? (uint32_t)(T - 4 * c.rb) : 4u; };
   auto load = [&](FwdIn& in, const Unit& c) {
     const int64_t t0 = 4 * c.rb, h0 = c.hb * kTile;
-    const __amdgpu_buffer_rsrc_t xb =
-        buffer_of(const_cast<uint16_t*>(x) + (t0 * 2 * H + h0), rows_of(c) * x_row - 2 * (uint32_t)h0);
+    // records up to the last channel of the unit's last row
+    const uint32_t bytes = (rows_of(c) - 1) * x_row + 2 * (uint32_t)(H - h0);
+    const __amdgpu_buffer_rsrc_t gb = buffer_of(const_cast<uint16_t*>(gate) + (t0 * in_row + h0), bytes);
+    const __amdgpu_buffer_rsrc_t ub = buffer_of(const_cast<uint16_t*>(up) + (t0 * in_row + h0), bytes);
     const bool live = h0 + 8 * p < H;
-    in.g = load_buf(xb, live ? lane_x : kOut);
-    in.u = load_buf(xb, live ? lane_xu : kOut);
+    in.g = load_buf(gb, live ? lane_x : kOut);
+    in.u = load_buf(ub, live ? lane_x : kOut);
   };
 
   const int64_t u0 = first;
@@ -1214,6 +1218,10 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
       if ((p & 3) == 0)
         __builtin_amdgcn_raw_buffer_store_b32(f16_bits(scale) | (f16_bits(scale * (float)qsum) << 16), qb,
                                               off - 4, 0, 0);
+      if (y_bf16 != nullptr)
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){Yp[0], Yp[1], Yp[2], Yp[3]},
+                                               buffer_of(y_bf16 + (t0 * H + h0), 2 * (rows * (uint32_t)H - (uint32_t)h0)),
+                                               live ? lane_h : kOut, 0, 2);
     } else {
       // Non-temporal code stores: for this write-light pass they measured
       // faster than the system-scope policy the backward pass uses.
@@ -1228,7 +1236,7 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
       if (y_bf16 != nullptr)
         __builtin_amdgcn_raw_buffer_store_b128((u32x4){Yp[0], Yp[1], Yp[2], Yp[3]},
                                                buffer_of(y_bf16 + (t0 * H + h0), 2 * (rows * q_row - (uint32_t)h0)),
-                                               live ? 2 * lane_q : kOut, 0, 2);
+                                               live ? lane_h : kOut, 0, 2);
       if (p % (kG / 8) == 0)
         __builtin_amdgcn_raw_buffer_store_b32(
             __float_as_uint(scale),
@@ -1581,13 +1589,13 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
   return SILUQUANT_OK;
 }
 
-using ForwardKernel = void (*)(const uint16_t*, const float*, int8_t*, float*, uint16_t*, int64_t, int64_t, int,
-                               int64_t);
+using ForwardKernel = void (*)(const uint16_t*, const uint16_t*, int64_t, const float*, int8_t*, float*, uint16_t*,
+                               int64_t, int64_t, int, int64_t);
 
 // Persistent grid for the forward quantiser: units of 4 rows x 128 channels,
 // one per wave, as many workgroups as fit on the device or as the units need.
-int launch_forward(ForwardKernel kernel, const void* x, const float* row_weight, int8_t* y_q, float* y_s,
-                   void* y_bf16, int64_t T, int64_t H, hipStream_t stream) {
+int launch_forward(ForwardKernel kernel, const void* gate, const void* up, int64_t in_row, const float* row_weight,
+                   int8_t* y_q, float* y_s, void* y_bf16, int64_t T, int64_t H, hipStream_t stream) {
   int cus = 0;
   int rc = device_cus(&cus);
   if (rc != SILUQUANT_OK) return rc;
@@ -1596,9 +1604,9 @@ int launch_forward(ForwardKernel kernel, const void* x, const float* row_weight,
   int64_t grid = (int64_t)cus * kFwdWorkgroupsPerCU;
   const int64_t wg_needed = (units + kFwdThreads / 64 - 1) / (kFwdThreads / 64);
   if (wg_needed < grid) grid = wg_needed;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kFwdThreads), 0, stream,
-                     static_cast<const uint16_t*>(x), row_weight, y_q, y_s, static_cast<uint16_t*>(y_bf16), T, H,
-                     tiles_h, units);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kFwdThreads), 0, stream, static_cast<const uint16_t*>(gate),
+                     static_cast<const uint16_t*>(up), in_row, row_weight, y_q, y_s, static_cast<uint16_t*>(y_bf16), T,
+                     H, tiles_h, units);
   return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;
 }
 
@@ -1693,7 +1701,8 @@ __attribute__((visibility("default"))) int silu_fwd_quant(const void* x, const f
   auto kernel = group == 128 ? (w ? silu_fwd_quant_kernel<128, false, true> : silu_fwd_quant_kernel<128>)
                 : group == 64 ? (w ? silu_fwd_quant_kernel<64, false, true> : silu_fwd_quant_kernel<64>)
                               : (w ? silu_fwd_quant_kernel<32, false, true> : silu_fwd_quant_kernel<32>);
-  return launch_forward(kernel, x, row_weight, y_q, y_s, y_bf16, T, H, stream);
+  return launch_forward(kernel, x, static_cast<const uint16_t*>(x) + H, 2 * H, row_weight, y_q, y_s, y_bf16, T, H,
+                        stream);
 }
 
 __attribute__((visibility("default"))) int silu_fwd_quant_q8_1(const void* x, const float* row_weight, void* y_q8,
@@ -1701,7 +1710,7 @@ __attribute__((visibility("default"))) int silu_fwd_quant_q8_1(const void* x, co
   // blocks of 32 channels (the page's k % 32 == 0)
   if (T < 0 || H < 0 || H % 32 != 0) return SILUQUANT_ERR_BAD_SHAPE;
   if (T == 0 || H == 0) return SILUQUANT_OK;
-  if (T > (int64_t(1) << 31) || H > (int64_t(1) << 22) || T > (int64_t(1) << 40) / H) return SILUQUANT_ERR_BAD_SHAPE;
+  if (T > (int64_t(1) << 28) || H > (int64_t(1) << 22) || T > (int64_t(1) << 40) / H) return SILUQUANT_ERR_BAD_SHAPE;
   if (!x || !y_q8) return SILUQUANT_ERR_NULL_PTR;
   auto mis = [](const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; };
   if (mis(x, 16) || mis(y_q8, 4) || (row_weight && mis(row_weight, 4))) return SILUQUANT_ERR_MISALIGNED;
@@ -1711,7 +1720,32 @@ __attribute__((visibility("default"))) int silu_fwd_quant_q8_1(const void* x, co
     for (int j = i + 1; j < 3; ++j)
       if (bufs[i] && bufs[j] && overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
   return launch_forward(row_weight ? silu_fwd_quant_kernel<32, true, true> : silu_fwd_quant_kernel<32, true>, x,
-                        row_weight, static_cast<int8_t*>(y_q8), nullptr, nullptr, T, H, stream);
+                        static_cast<const uint16_t*>(x) + H, 2 * H, row_weight, static_cast<int8_t*>(y_q8), nullptr,
+                        nullptr, T, H, stream);
+}
+
+__attribute__((visibility("default"))) int kquant_swiglu_q8_1_rows(const void* gate, const void* up, const float* w,
+                                                                   void* h_bf16, void* out_q8, int64_t rows,
+                                                                   int64_t inter, hipStream_t stream) {
+  // blocks of 32 channels (the page's inter % 32 == 0)
+  if (rows < 0 || inter < 0 || inter % 32 != 0) return SILUQUANT_ERR_BAD_SHAPE;
+  if (rows == 0 || inter == 0) return SILUQUANT_OK;
+  if (rows > (int64_t(1) << 28) || inter > (int64_t(1) << 22) || rows > (int64_t(1) << 40) / inter)
+    return SILUQUANT_ERR_BAD_SHAPE;
+  if (!gate || !up || !out_q8) return SILUQUANT_ERR_NULL_PTR;
+  auto mis = [](const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; };
+  if (mis(gate, 16) || mis(up, 16) || mis(out_q8, 4) || (h_bf16 && mis(h_bf16, 16)) || (w && mis(w, 4)))
+    return SILUQUANT_ERR_MISALIGNED;
+  // the outputs may overlap nothing; the two inputs are read only and may
+  // share memory with each other
+  const void* bufs[5] = {gate, up, w, h_bf16, out_q8};
+  const int64_t sizes[5] = {2 * rows * inter, 2 * rows * inter, 4 * rows, 2 * rows * inter, rows * (inter / 32) * 36};
+  for (int i = 0; i < 5; ++i)
+    for (int j = i + 1; j < 5; ++j)
+      if (j >= 3 && bufs[i] && bufs[j] && overlaps(bufs[i], sizes[i], bufs[j], sizes[j]))
+        return SILUQUANT_ERR_OVERLAP;
+  return launch_forward(w ? silu_fwd_quant_kernel<32, true, true> : silu_fwd_quant_kernel<32, true>, gate, up, inter,
+                        w, static_cast<int8_t*>(out_q8), nullptr, h_bf16, rows, inter, stream);
 }
 
 __attribute__((visibility("default"))) int siluquant_eval_sigmoid(const void* gate, float* s, int64_t n,

@@ -178,6 +178,7 @@ def test_forward_rejects_bad_arguments(lib):
     assert f(BASE, None, BASE + 2**24, BASE + 2**25, None, 8, 256, 48, None) == 3
     assert f(BASE, None, BASE + 2**24, BASE + 2**25, None, 8, (1 << 22) + 5, 64, None) == 2
     assert f(BASE, None, BASE + 2**24, BASE + 2**25, None, -1, 256, 128, None) == 2
+    assert f(BASE, None, BASE + 2**24, BASE + 2**25, None, 2**31 + 1, 8, 128, None) == 2  # past the token limit
     assert f(None, None, BASE + 2**24, BASE + 2**25, None, 8, 256, 128, None) == 1
     assert f(BASE + 8, None, BASE + 2**24, BASE + 2**25, None, 8, 256, 128, None) == 4
     assert f(BASE, BASE + 2**26 + 2, BASE + 2**24, BASE + 2**25, None, 8, 256, 128, None) == 4
@@ -189,6 +190,7 @@ def test_forward_q8_1_rejects_bad_arguments(lib):
     f = lib.silu_fwd_quant_q8_1
     assert f(BASE, None, BASE + 2**24, 8, 48, None) == 2      # H not a multiple of 32
     assert f(BASE, None, BASE + 2**24, -1, 64, None) == 2
+    assert f(BASE, None, BASE + 2**24, 2**28 + 1, 32, None) == 2  # past the token limit
     assert f(None, None, BASE + 2**24, 8, 64, None) == 1
     assert f(BASE, None, None, 8, 64, None) == 1
     assert f(BASE + 8, None, BASE + 2**24, 8, 64, None) == 4  # x off 16 bytes
@@ -196,6 +198,28 @@ def test_forward_q8_1_rejects_bad_arguments(lib):
     assert f(BASE, BASE + 2**26 + 2, BASE + 2**24, 8, 64, None) == 4
     assert f(BASE, None, BASE + 256, 8, 64, None) == 5        # blocks inside x
     assert f(None, None, None, 0, 64, None) == 0
+
+
+def test_kquant_swiglu_q8_1_rows_rejects_bad_arguments(lib):
+    f = lib.kquant_swiglu_q8_1_rows
+    g, u, w, h, q = BASE, BASE + 2**24, BASE + 2**25, BASE + 2**26, BASE + 2**27
+    assert f(g, u, None, None, q, 8, 48, None) == 2            # inter not a multiple of 32
+    assert f(g, u, None, None, q, -1, 64, None) == 2
+    assert f(g, u, None, None, q, 8, (1 << 22) + 32, None) == 2
+    assert f(g, u, None, None, q, 2**28 + 1, 32, None) == 2
+    assert f(None, u, None, None, q, 8, 64, None) == 1
+    assert f(g, None, None, None, q, 8, 64, None) == 1
+    assert f(g, u, None, None, None, 8, 64, None) == 1
+    assert f(g + 8, u, None, None, q, 8, 64, None) == 4        # gate off 16 bytes
+    assert f(g, u + 8, None, None, q, 8, 64, None) == 4
+    assert f(g, u, w + 2, None, q, 8, 64, None) == 4
+    assert f(g, u, None, h + 8, q, 8, 64, None) == 4
+    assert f(g, u, None, None, q + 2, 8, 64, None) == 4
+    assert f(g, u, None, None, g + 512, 8, 64, None) == 5      # blocks inside gate
+    assert f(g, u, None, u + 64, q, 8, 64, None) == 5          # h inside up
+    assert f(g, u, w, h, w + 16, 8, 64, None) == 5             # blocks over the weights
+    assert f(g, g, w, h, q, 0, 64, None) == 0                  # nothing to do
+    assert f(None, None, None, None, None, 0, 64, None) == 0
 
 
 def test_gemm_rejects_bad_arguments(lib):

@@ -1,6 +1,8 @@
 """Parity of the forward quantiser's q8_1 block layout (silu_fwd_quant_q8_1)
 with the CPU oracle (GPU): every block byte equal (codes, binary16 d and sum).
-It is also checked against the library's own group-32 forward quantiser.
+It is also checked against the library's own group-32 forward quantiser, and
+the page's own launch shape (kquant_swiglu_q8_1_rows: separate gate and up,
+the bf16 h written too) against the oracle.
 """
 
 import numpy as np
@@ -44,8 +46,9 @@ def check(x, w=None, label=""):
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_workloads(name):
-    T = min(WORKLOADS[name].T, 4096)
-    x, _ = make_inputs(name, device=DEV, T=T)
+    # every workload at its full token count
+    print("case q8_1", name, flush=True)
+    x, _ = make_inputs(name, device=DEV)
     check(x, label=name)
 
 
@@ -111,3 +114,63 @@ def test_block_base_only_4_byte_aligned():
     assert np.array_equal(out.cpu().numpy(), oracle.silu_fwd_quant_q8_1(_bits(x)))
     r = raw.cpu().numpy()
     assert np.all(r[:4] == 0xA5) and np.all(r[4 + T * (H // 32) * 36:] == 0xA5)
+
+
+def run_rows(gate, up, w=None, want_h=True):
+    rows, inter = gate.shape
+    out = torch.full((rows, (inter // 32) * sq.Q8_1_BLOCK), 0xA5, dtype=torch.uint8, device=DEV)
+    h = torch.full((rows, inter), float("nan"), dtype=torch.bfloat16, device=DEV) if want_h else None
+    sq.kquant_swiglu_q8_1_rows(gate, up, out, w=w, h_bf16=h)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (_bits(h) if want_h else None)
+
+
+def check_rows(gate, up, w=None, want_h=True, label=""):
+    got, h = run_rows(gate, up, w, want_h)
+    want, want_h_bits = oracle.kquant_swiglu_q8_1_rows(_bits(gate), _bits(up), None if w is None else w.cpu().numpy())
+    bad = int((got != want).sum())
+    assert bad == 0, "%s: %d of %d block bytes differ" % (label, bad, got.size)
+    if want_h:
+        assert np.array_equal(h, want_h_bits), "%s: h differs" % label
+    print("%s exact" % label, flush=True)
+
+
+@pytest.mark.parametrize("name", ["t4096_h1408", "t32768_h2048_outliers"])
+def test_page_launch_shape_workloads(name):
+    # gate and up as separate arrays (copies of the workload's halves)
+    x, _ = make_inputs(name, device=DEV)
+    H = x.shape[1] // 2
+    gate, up = x[:, :H].contiguous(), x[:, H:].contiguous()
+    check_rows(gate, up, label=name + " separate gate/up")
+    # byte-identical to the concatenated form, as the page says of the fused launch
+    assert np.array_equal(run_rows(gate, up, want_h=False)[0], run(x))
+
+
+@pytest.mark.parametrize("rows,inter", [(1, 32), (5, 96), (1000, 160), (129, 4096), (77, 2080)])
+def test_page_launch_shape_with_and_without_weights(rows, inter):
+    x, _ = random_inputs(rows, inter, device=DEV, seed=3 * rows + inter)
+    gate, up = x[:, :inter].contiguous(), x[:, inter:].contiguous()
+    w = torch.rand(rows, device=DEV, generator=torch.Generator(device=DEV).manual_seed(rows)) * 4 - 2
+    check_rows(gate, up, label="rows=%d inter=%d" % (rows, inter))
+    check_rows(gate, up, w=w, label="rows=%d inter=%d weighted" % (rows, inter))
+    check_rows(gate, up, w=w, want_h=False, label="rows=%d inter=%d weighted, no h" % (rows, inter))
+
+
+def test_page_launch_shape_same_array_for_gate_and_up():
+    # the inputs are read only and may be one array: h = silu(g) * g
+    x, _ = random_inputs(64, 256, device=DEV, seed=23)
+    g = x[:, :256].contiguous()
+    check_rows(g, g, label="gate == up")
+
+
+def test_page_launch_shape_edges():
+    rows, inter = 16, 128
+    gate = torch.full((rows, inter), 20.0, dtype=torch.bfloat16, device=DEV)
+    up = torch.ones((rows, inter), dtype=torch.bfloat16, device=DEV)
+    gate[3] = 0.0
+    up[5, :32] = torch.tensor([2.0**-130] * 31 + [0.0]).to(torch.bfloat16)
+    up[7, 64:96] = 3.0e9
+    check_rows(gate, up, label="edges")
+    with pytest.raises(ValueError):
+        sq.kquant_swiglu_q8_1_rows(gate[:, :48].contiguous(), up[:, :48].contiguous(),
+                                   torch.empty((rows, 54), dtype=torch.uint8, device=DEV))
