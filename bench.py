@@ -6,10 +6,18 @@ workload), inputs already resident in HBM.  The metric is achieved HBM
 bandwidth: algorithmic bytes per call (reads of x and grad_y, writes of both
 code tensors and both scale tensors) divided by the time per call.
 
+Order of a run: inputs drawn on the device; the reference streams (a 1 GiB
+copy and a 2-read/1-write bf16 add, for the attainable bandwidth); a settle
+phase of about 100 ms running the op on an independent batch of the same
+shape, because the device needs some 25-30 ms of this load before its
+per-call time stops falling; W warm-up steps on the timed batch; K timed
+steps (an event between every two, reported as "steps_us"); 50 more calls for
+the per-launch distribution and a cold call; the oracle on the host.
+
 Prints one JSON line.  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--op backward|forward|forward_q8_1|fp8|gemm_dgrad|gemm_wgrad]
-                    [--no-cpu-baseline] [--probes]
+                    [--no-cpu-baseline] [--probes before|after|none] [--settle-ms MS]
 """
 
 from __future__ import annotations
@@ -117,10 +125,64 @@ def launch_distribution(step, stream, n: int, dev):
             "cold": round(c0.elapsed_time(c1) * 1e3, 2)}
 
 
-def stream_probes(dev, reps: int = 20):
+def host_description() -> dict:
+    """The host the CPU baseline ran on: CPU model, logical CPUs, and the CPUs
+    this process may use."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
+def step_series(ms):
+    """Per-step durations of the timed region (HIP events between the steps),
+    summarised: the first five steps against the rest, and all of them."""
+    us = [round(m * 1e3, 1) for m in ms]
+    head, tail = us[:5], us[5:]
+    return {"first5_mean": round(sum(head) / len(head), 2) if head else None,
+            "rest_mean": round(sum(tail) / len(tail), 2) if tail else None,
+            "min": min(us) if us else None, "all": us}
+
+
+def settle(call, ms: float) -> dict:
+    """Run the measured op on an independent batch of the same shape (not the
+    timed batch) until ms milliseconds have passed.  On MI355X the pass takes
+    about 100 calls (25-30 ms) of its own sustained load before its per-call
+    time settles (from about 320 us on the first calls to 290 us at
+    T = 16384, H = 11008); neither plain copy streams, a bf16 matmul, nor the
+    pass at a smaller shape bring the device there, while the pass on another
+    batch of the same shape does.  The W warm-up steps then run on the timed
+    batch as usual."""
+    import torch
+
+    if ms <= 0:
+        return {"ms": 0.0, "calls": 0}
+    calls = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(10):
+            call()
+        calls += 10
+        torch.cuda.synchronize()
+    return {"ms": round((time.perf_counter() - t0) * 1e3, 1), "calls": calls,
+            "batch": "an independent batch of the same shape (seed + 500), before the warm-up"}
+
+
+def stream_probes(dev, reps: int = 50):
     """Plain streaming kernels of known size, for the attainable bandwidth and for
     scaling hardware byte counters: a 1 GiB copy (1 GiB read + 1 GiB written) and
-    c = a + b on bf16 (2 reads : 1 write, close to this pass's 1.94 : 1)."""
+    c = a + b on bf16 (2 reads : 1 write, close to this pass's 1.94 : 1), each
+    repeated reps times (about 50 ms of sustained HBM traffic in all)."""
     import torch
 
     n = 2**30
@@ -204,6 +266,10 @@ def run_gemm(args):
     def step():
         sq.i8_gemm_group_scaled(A, sA, B, sB, C, b_rows_per_scale=b_rows)
 
+    C2 = torch.empty_like(C)
+    settle_info = settle(lambda: sq.i8_gemm_group_scaled(A, sA, B, sB, C2, b_rows_per_scale=b_rows), args.settle_ms)
+    settle_info["batch"] = "the same operands into a second output, before the warm-up"
+    del C2
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -247,12 +313,14 @@ def run_gemm(args):
             "kernel": "i8_gemm_kernel",
             "avg_launch_us": round(per_launch_s * 1e6, 3),
         },
+        "settle": settle_info,
         "cpu_baseline": None,
     }
-    if args.probes:
+    if args.probes != "none":
         out["probes"] = stream_probes(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = gemm_cpu_baseline(A, sA, B, sB, b_rows)
+        out["cpu_baseline"]["host"] = host_description()
     print(json.dumps(out), flush=True)
 
 
@@ -270,8 +338,13 @@ def main():
                          "forward_q8_1: the same in 32-channel q8_1 blocks; "
                          "fp8: the backward pass with OCP FP8 E4M3 codes; "
                          "gemm_dgrad / gemm_wgrad: the group-scaled int8 GEMMs that consume its outputs")
-    ap.add_argument("--probes", action="store_true",
-                    help="also time a plain 1 GiB copy and a 2-read/1-write bf16 add (reference streams)")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="before the warm-up, run the op on an independent batch of the same shape for this "
+                         "long, so that the device reaches its steady state under this load (0: skip)")
+    ap.add_argument("--probes", choices=["before", "after", "none"], default="before",
+                    help="when to time a plain 1 GiB copy and a 2-read/1-write bf16 add (reference streams "
+                         "for the attainable bandwidth): before the warm-up (default), after the timed "
+                         "region, or not at all")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this pass runs on one GPU; --gpus %d is not supported (the tensors of a "
@@ -299,7 +372,8 @@ def main():
     # last-level cache: every step then reads its inputs from HBM.
     sets = max(1, -(-512 * 2**20 // nbytes))
     bufs = []
-    for r in range(sets):
+    # one more, independent batch of the same shape for the settle phase
+    for r in list(range(sets)) + [500]:
         x, dy = make_inputs(w, device=dev, seed=w.seed + 1000 * r)
         if q8_1:
             del dy
@@ -311,11 +385,12 @@ def main():
             bufs.append((x, None, outs))
         else:
             bufs.append((x, dy, sq.empty_outputs(w.T, w.H, dev, fp8=fp8)))
+    settle_batch = bufs.pop()
     sq.prepare()
     torch.cuda.synchronize()
 
-    def step(i):
-        x, dy, outs = bufs[i % sets]
+    def step(i, batch=None):
+        x, dy, outs = batch if batch is not None else bufs[i % sets]
         if q8_1:
             sq.silu_fwd_quant_q8_1(x, *outs)
         elif forward:
@@ -325,22 +400,26 @@ def main():
         else:
             sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *outs)
 
+    probes = None
+    if args.probes == "before":
+        probes = stream_probes(dev)
+    settle_info = settle(lambda: step(0, settle_batch), args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)  # the stream every call is launched on
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
+    evs[0].record(stream)
     for i in range(args.steps):
         step(i)
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
+    gpu_ms = evs[0].elapsed_time(evs[-1])
+    series = step_series([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
 
     per_launch_s = gpu_ms / 1e3 / args.steps
     achieved = nbytes / per_launch_s / 1e9
@@ -385,14 +464,19 @@ def main():
                        "fp8": "silu_quant_bwd_kernel<Fmt::kFp8>"}.get(args.op, "silu_quant_bwd_kernel<Fmt::kInt8>"),
             "avg_launch_us": round(per_launch_s * 1e6, 3),
         },
+        "settle": settle_info,
+        "steps_us": series,
         "launch_us": timing,
         "cpu_baseline": None,
     }
-    if args.probes:
-        out["probes"] = stream_probes(dev)
+    if args.probes == "after":
+        probes = stream_probes(dev)
+    if probes is not None:
+        out["probes"] = probes
     if not args.no_cpu_baseline:
         x, dy, _ = bufs[0]
         out["cpu_baseline"] = cpu_baseline(x, dy, w, fp8=fp8, forward=forward, q8_1=q8_1)
+        out["cpu_baseline"]["host"] = host_description()
     print(json.dumps(out), flush=True)
 
 
