@@ -48,10 +48,16 @@ MUTANTS = {
                            "oracle_quant_group(&Y[t0 * H + h], n, H, &y_q_t[t0 * H + h], H)"),
     "fp8_yqt_not_transposed": ("oracle_quant_group_fp8(&Y[t0 * H + h], n, H, &y_q_t[h * T + t0], 1)",
                                "oracle_quant_group_fp8(&Y[t0 * H + h], n, H, &y_q_t[t0 * H + h], H)"),
-    "forward_missing_up": ("float v = silu * u;", "float v = silu;"),
-    "forward_ignores_weight": ("if (w) v = v * w[t];", "if (w) v = v + 0.0f * w[t];"),
-    "forward_weight_after_rounding": ("      Y[h] = oracle_bf16_to_f32(b);",
-                                      "      Y[h] = oracle_bf16_to_f32(b) * (w ? w[t] : 1.0f);"),
+    "forward_missing_up": ("float v = silu * u;\n      if (w) v = v * w[t];\n      uint16_t b = oracle_f32_to_bf16(v);\n"
+                           "      Y[h] = oracle_bf16_to_f32(b);\n      if (y_bf16)",
+                           "float v = silu;\n      if (w) v = v * w[t];\n      uint16_t b = oracle_f32_to_bf16(v);\n"
+                           "      Y[h] = oracle_bf16_to_f32(b);\n      if (y_bf16)"),
+    "forward_ignores_weight": ("if (w) v = v * w[t];\n      uint16_t b = oracle_f32_to_bf16(v);\n"
+                               "      Y[h] = oracle_bf16_to_f32(b);\n      if (y_bf16)",
+                               "if (w) v = v + 0.0f * w[t];\n      uint16_t b = oracle_f32_to_bf16(v);\n"
+                               "      Y[h] = oracle_bf16_to_f32(b);\n      if (y_bf16)"),
+    "forward_weight_after_rounding": ("      Y[h] = oracle_bf16_to_f32(b);\n      if (y_bf16)",
+                                      "      Y[h] = oracle_bf16_to_f32(b) * (w ? w[t] : 1.0f);\n      if (y_bf16)"),
     "fp8_scale_over_127": ("(amax == 0.0f) ? 1.0f : amax / 448.0f", "(amax == 0.0f) ? 1.0f : amax / 127.0f"),
     "fp8_truncates": ("double mant = nearbyint(m * 16.0);", "double mant = floor(m * 16.0);"),
     "fp8_subnormal_step": ("double k = nearbyint(a * 512.0);", "double k = nearbyint(a * 256.0);"),

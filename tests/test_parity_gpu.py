@@ -105,8 +105,8 @@ def test_workload_parity(name):
     assert sum(rep.values()) == 0  # the kernel is expected to be exact
 
 
-@pytest.mark.parametrize("name,seed", [("t4096_h1408", 1001), ("t8192_h4096", 1002),
-                                       ("t32768_h2048_outliers", 1004)])
+@pytest.mark.parametrize("name,seed", [("t256_h256", 1000), ("t4096_h1408", 1001), ("t8192_h4096", 1002),
+                                       ("t16384_h11008", 1003), ("t32768_h2048_outliers", 1004)])
 def test_workload_parity_second_seed(name, seed):
     print("case", name, seed, flush=True)
     x, dy = make_inputs(name, device=DEV, seed=seed)
