@@ -330,6 +330,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="t16384_h11008")
+    ap.add_argument("--shape", default=None, help="T,H of a plain normal workload instead of a named one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--op", choices=["backward", "forward", "forward_q8_1", "fp8"] + sorted(GEMMS),
                     default="backward",
@@ -338,6 +339,9 @@ def main():
                          "forward_q8_1: the same in 32-channel q8_1 blocks; "
                          "fp8: the backward pass with OCP FP8 E4M3 codes; "
                          "gemm_dgrad / gemm_wgrad: the group-scaled int8 GEMMs that consume its outputs")
+    ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
+                    help="replay the K timed steps as one HIP graph (auto: for workloads under 128 MB, whose "
+                         "calls take less GPU time than their Python launch)")
     ap.add_argument("--settle-ms", type=float, default=100.0,
                     help="before the warm-up, run the op on an independent batch of the same shape for this "
                          "long, so that the device reaches its steady state under this load (0: skip)")
@@ -358,9 +362,13 @@ def main():
     import torch
 
     import swiglu_backward_int8_amd as sq
-    from swiglu_backward_int8_amd.inputs import WORKLOADS, make_inputs
+    from swiglu_backward_int8_amd.inputs import WORKLOADS, Workload, make_inputs
 
     w = WORKLOADS[args.workload]
+    if args.shape:
+        # a plain normal workload of another shape (channel shards, ragged H), for profiling
+        T_, H_ = (int(v) for v in args.shape.split(","))
+        w = Workload("t%d_h%d" % (T_, H_), T_, H_, ("normal", 1.0), ("normal", 1.0), ("normal", 0.01), seed=11)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     q8_1 = args.op == "forward_q8_1"
@@ -381,7 +389,7 @@ def main():
         elif forward:
             del dy
             outs = (torch.empty((w.T, w.H), dtype=torch.int8, device=dev),
-                    torch.empty((w.T, w.H // 128), dtype=torch.float32, device=dev))
+                    torch.empty((w.T, -(-w.H // 128)), dtype=torch.float32, device=dev))
             bufs.append((x, None, outs))
         else:
             bufs.append((x, dy, sq.empty_outputs(w.T, w.H, dev, fp8=fp8)))
@@ -409,17 +417,43 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)  # the stream every call is launched on
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    evs[0].record(stream)
-    for i in range(args.steps):
-        step(i)
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = evs[0].elapsed_time(evs[-1])
-    series = step_series([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    use_graph = args.graph == "on" or (args.graph == "auto" and nbytes < 128 * 2**20)
+    if use_graph:
+        # Small workloads: a call takes less GPU time than the Python binding
+        # takes to launch it, so the K steps are captured in one HIP graph and
+        # replayed (once untimed, then once timed); the GPU time is then the
+        # kernels' and not the host's.  Per-step times are not taken.
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for i in range(args.steps):
+                    step(i)
+        stream.wait_stream(side)
+        g.replay()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu_ms = ev0.elapsed_time(ev1)
+        series = {"graph": True, "note": "K steps replayed as one HIP graph; no per-step events"}
+    else:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        evs[0].record(stream)
+        for i in range(args.steps):
+            step(i)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu_ms = evs[0].elapsed_time(evs[-1])
+        series = step_series([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
 
     per_launch_s = gpu_ms / 1e3 / args.steps
     achieved = nbytes / per_launch_s / 1e9
