@@ -11,8 +11,8 @@
 //   * persistent 1024-thread workgroups, one per CU, walk 128-token x
 //     128-channel tiles; every group of both quantisation axes lies inside one
 //     tile, so no workgroup ever waits on another (when H is not a multiple of
-//     the group, silu_quant_bwd_shift_kernel keeps this with shifted windows
-//     for the d_up half);
+//     the group, silu_quant_bwd_straddle_kernel and silu_quant_bwd_shift_kernel
+//     keep this with shifted windows for the d_up half);
 //   * lane (q, p) = (tid / 16, tid % 16) owns tokens 2q, 2q+1 and channels
 //     8p..8p+7: each of its loads is 16 bytes and a wave's load covers four
 //     whole 256-byte row segments;
@@ -764,8 +764,9 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
 // the first r positions are the last r channels of d_gate.  The window's
 // groups line up with it again, and the straddling group lies in window 0.
 //
-// The workgroups of each XCD split into two teams that walk the XCD's tiles
-// in order: the first does y, d_gate and the y^T codes from the tile's gate,
+// With groups of 64 or 32 (group 128 takes silu_quant_bwd_straddle_kernel
+// below), the workgroups of each XCD split into two teams that walk the XCD's
+// tiles in order: the first does y, d_gate and the y^T codes from the tile's gate,
 // up and grad_y, like silu_quant_bwd_kernel; the second does the windows
 // from gate and grad_y (and up where a window holds d_gate).  The teams are
 // sized to the work of their tiles, so that they move through the tiles at
@@ -1028,6 +1029,264 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
     }
   }
 }
+
+// H not a multiple of 128 with groups of 128: one workgroup takes both kinds
+// of work of a block in turn: phase 1 does y,
+// d_gate and the y^T codes from the block's gate, up and grad_y (as the
+// aligned kernel, without d_up); phase 2 does the block's window of the
+// second half (d_up at channels h0 - r + [0, 128), or in window 0 the
+// straddling group), from gate and grad_y read again.  The window's loads are
+// issued at the top of the iteration and stay in flight through phase 1; the
+// next block's main loads are issued at the top of phase 2 and stay in flight
+// through it, so a lane holds no more loaded bytes than in the aligned
+// kernel.  The main loads are plain (cached), so that the window of the next
+// block, which the neighbouring workgroup of the same XCD takes at the same
+// time, finds the r channels it shares with this block in L2.  At group 128
+// this form holds within the 128 registers a lane has at 16 waves per CU and
+// measured 8% faster than the two teams at T = 16384, H = 1376 and 11000
+// (59.0 against 64.2 us, 484 against 526 us; equal at H = 2752); at groups 64
+// and 32 it spills a few registers and was no faster, so those keep the teams.
+template <Fmt F, int kG>
+__global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void silu_quant_bwd_straddle_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ grad_y, int8_t* __restrict__ grad_input_q,
+    float* __restrict__ grad_input_s, int8_t* __restrict__ y_q_t, float* __restrict__ y_s_t, int64_t T, int64_t H,
+    int tiles_h, int tiles, int r) {
+  static_assert(kG == 32 || kG == 64 || kG == 128, "group sizes that divide the tile");
+  constexpr int kSub = kTile / kG;
+  constexpr int kHalfGroups = kTile * kSub, kColGroups = kTile * kSub;
+  constexpr int kLanesPerRowGroup = kG / 8;
+  constexpr int kPairsPerColGroup = kG / kRows;
+  static_assert(kHalfGroups + kColGroups <= kInvFloats, "inverse slots");
+
+  __shared__ __align__(16) float lds[kLdsFloats];
+  float* s_tab = lds;
+  float* s_rowpart = lds + kSigEntries;
+  float* s_colpart = s_rowpart + kRowPartFloats;
+  float* s_inv = s_colpart + kColPartFloats;
+  char* s_yqt = reinterpret_cast<char*>(s_rowpart);
+  int* s_flag = reinterpret_cast<int*>(s_inv + kInvFloats);
+
+  const int tid = threadIdx.x;
+  const int p = tid & 15;
+  const int q = tid >> 4;
+
+  const int64_t x_row_bytes = 4 * H, dy_row_bytes = 2 * H, gq_row_bytes = 2 * H;
+  const int64_t row_groups = (2 * H + kG - 1) / kG, col_groups = (T + kG - 1) / kG;
+  const int64_t lim_a = H - r, lim_b = H + r;  // channel ends of d_gate's whole groups and of the windows
+  const int yq_align = (T & 15) == 0 ? 16 : (T & 3) == 0 ? 4 : 1;
+  const uint32_t lane_x = (uint32_t)(kRows * q * x_row_bytes + 16 * p);
+  const uint32_t lane_dy = (uint32_t)(kRows * q * dy_row_bytes + 16 * p);
+  const uint32_t lane_gq = (uint32_t)((kRows * q + (p & 1)) * gq_row_bytes + 8 * (p & ~1));
+  constexpr uint32_t kDropped = 0x80000000u;  // past any record count
+  constexpr int kOutSteps = kTile * kTile / 16 / kThreads;
+  const int sub_row = p / kLanesPerRowGroup, sub_col = q / kPairsPerColGroup;
+  float* rp = s_rowpart + p * kRowPartStride + kRows * q;
+
+  // Each XCD's workgroups (every 8th) walk one contiguous eighth of the
+  // blocks in row-major order, neighbours side by side.
+  int tile, end, stride;
+  if ((gridDim.x & 7) == 0) {
+    const int xcd = blockIdx.x & 7;
+    tile = (int)(((int64_t)tiles * xcd) >> 3) + (int)(blockIdx.x >> 3);
+    end = (int)(((int64_t)tiles * (xcd + 1)) >> 3);
+    stride = gridDim.x >> 3;
+  } else {
+    tile = blockIdx.x;
+    end = tiles;
+    stride = gridDim.x;
+  }
+
+  const char* xb = reinterpret_cast<const char*>(x);
+  const char* dyb = reinterpret_cast<const char*>(grad_y);
+  auto load_first = [&](TileIn& in, const Tile& c) {
+    load_tile<false>(in, xb + (c.t0 * x_row_bytes + 2 * c.h0), dyb + (c.t0 * dy_row_bytes + 2 * c.h0), lane_x, lane_dy,
+                     x_row_bytes, dy_row_bytes, c.rows, 8 * p < c.cols, q);
+  };
+  // A window's inputs, through buffer resources over the block's existing
+  // rows (rows past a ragged T and lanes past the window read zeros).
+  // Outside window 0 the window starts r channels before the block; in
+  // window 0, lanes 8p < r read d_gate's last channels (and their up values,
+  // with_up) and the others start at channel 8p - r.  Offsets stay
+  // non-negative: a lane with 8p >= r has lane_x >= 16p >= 2r.  Only window 0
+  // needs up, so the loads issued ahead of phase 1 take gate and grad_y, and
+  // window 0's up values are loaded when phase 2 starts.
+  auto load_window = [&](TileIn& in, const Tile& c, bool with_gd, bool with_up) {
+    const bool first = c.hb == 0, tail = first && 8 * p < r;
+    const int64_t back = first ? 0 : 2 * r;
+    const uint32_t adj = !first ? 0u : tail ? (uint32_t)(2 * (H - r)) : (uint32_t)(-2 * r);
+    const bool live = c.h0 + 8 * p < lim_b;
+    const uint32_t off_x = live ? lane_x + adj : kDropped, off_dy = live ? lane_dy + adj : kDropped;
+    const uint32_t off_u = tail ? off_x + (uint32_t)(x_row_bytes >> 1) : kDropped;
+    const __amdgpu_buffer_rsrc_t xbuf =
+        buffer_of(const_cast<char*>(xb) + (c.t0 * x_row_bytes + 2 * c.h0 - back), (uint32_t)(c.rows * x_row_bytes));
+    const __amdgpu_buffer_rsrc_t dybuf = buffer_of(const_cast<char*>(dyb) + (c.t0 * dy_row_bytes + 2 * c.h0 - back),
+                                                   (uint32_t)(c.rows * dy_row_bytes));
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      if (with_gd) {
+        in.g[i] = load_buf(xbuf, off_x + (uint32_t)(i * x_row_bytes));
+        in.d[i] = load_buf(dybuf, off_dy + (uint32_t)(i * dy_row_bytes));
+      }
+      if (with_up) in.u[i] = load_buf(xbuf, off_u + (uint32_t)(i * x_row_bytes));
+    }
+  };
+
+  TileIn in, inw;
+  Tile cur = tile_at(tile < end ? tile : 0, tiles_h, T, H);
+  if (tile < end) load_first(in, cur);
+  {
+    const float4* src = reinterpret_cast<const float4*>(g_sigma_tab);
+    float4* dst = reinterpret_cast<float4*>(s_tab);
+    for (int i = tid; i < kSigEntries / 4; i += kThreads) dst[i] = src[i];
+  }
+  __syncthreads();
+
+  while (tile < end) {
+    const int next = tile + stride;
+    const Tile nxt = tile_at(next < end ? next : tile, tiles_h, T, H);
+    load_window(inw, cur, true, false);
+
+    // ---- phase 1: y, d_gate and y^T (a block past H holds a window only) ----
+    if (cur.cols > 0) {
+      uint32_t Yp[kRows][4], Gp[kRows][4], Up[kRows][4];
+      float rg[kRows], ru[kRows], cm[8];
+      elementwise<false>(in, s_tab, Yp, Gp, Up, rg, ru, cm);
+      if (tid == 0) s_flag[0] = 0;
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) rp[i] = rg[i];
+      float4* cp = reinterpret_cast<float4*>(s_colpart + q * kTile + 4 * p);
+      cp[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
+      cp[16] = make_float4(cm[4], cm[5], cm[6], cm[7]);
+      __syncthreads();
+      for (int id = tid; id < kHalfGroups + kColGroups; id += kThreads) {
+        if (id < kHalfGroups) {
+          const int row = id & (kTile - 1), sub = id >> 7;
+          float m = 0.0f;
+#pragma unroll
+          for (int pp = 0; pp < kLanesPerRowGroup; ++pp)
+            m = fmaxf(m, s_rowpart[(sub * kLanesPerRowGroup + pp) * kRowPartStride + row]);
+          const float scale = group_scale<F>(m);
+          const float inv = 1.0f / scale;
+          s_inv[id] = inv;
+          if (inv == __builtin_huge_valf()) s_flag[0] = 1;
+          // d_gate's last r channels belong to the straddling group (window 0)
+          if (row < cur.rows && cur.h0 + sub * kG < lim_a)
+            grad_input_s[(cur.t0 + row) * row_groups + cur.h0 / kG + sub] = scale;
+        } else {
+          const int cid = id - kHalfGroups, c = cid & (kTile - 1), sub = cid >> 7;
+          const int idx = ((c >> 2) & 1) * 64 + (c >> 3) * 4 + (c & 3);
+          float m = 0.0f;
+#pragma unroll 8
+          for (int qq = 0; qq < kPairsPerColGroup; ++qq)
+            m = fmaxf(m, s_colpart[(sub * kPairsPerColGroup + qq) * kTile + idx]);
+          const float scale = group_scale<F>(m);
+          const float inv = 1.0f / scale;
+          s_inv[id] = inv;
+          if (inv == __builtin_huge_valf()) s_flag[0] = 1;
+          if (c < cur.cols && sub * kG < cur.rows)
+            y_s_t[(cur.h0 + c) * col_groups + cur.t0 / kG + sub] = scale;
+        }
+      }
+      __syncthreads();
+      float idg[kRows], iy[8];
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) idg[i] = s_inv[sub_row * kTile + kRows * q + i];
+      const float* inv_col = s_inv + kHalfGroups + sub_col * kTile + 8 * p;
+      const float4 inv_y0 = *reinterpret_cast<const float4*>(inv_col);
+      const float4 inv_y1 = *reinterpret_cast<const float4*>(inv_col + 4);
+      iy[0] = inv_y0.x, iy[1] = inv_y0.y, iy[2] = inv_y0.z, iy[3] = inv_y0.w;
+      iy[4] = inv_y1.x, iy[5] = inv_y1.y, iy[6] = inv_y1.z, iy[7] = inv_y1.w;
+      const __amdgpu_buffer_rsrc_t gq_buf =
+          buffer_of(grad_input_q + (cur.t0 * gq_row_bytes + cur.h0), (uint32_t)(cur.rows * gq_row_bytes));
+      // the pair's first channel and lim_a are multiples of 16: a pair is wholly in or out
+      const uint32_t lane_a = cur.h0 + 8 * (p & ~1) < lim_a ? lane_gq : kDropped;
+      store_half_codes<F, false>(Gp, idg, gq_buf, lane_a, (uint32_t)gq_row_bytes, p);
+      stage_y_codes<F, false>(Yp, iy, s_yqt, p, q);
+      __syncthreads();
+      if (s_flag[0]) {  // rare: as in silu_quant_bwd_kernel
+        TileIn again;
+        load_first(again, cur);
+        float rg2[kRows], ru2[kRows], cm2[8];
+        elementwise<false>(again, s_tab, Yp, Gp, Up, rg2, ru2, cm2);
+        store_half_codes<F, true>(Gp, idg, gq_buf, lane_a, (uint32_t)gq_row_bytes, p);
+        stage_y_codes<F, true>(Yp, iy, s_yqt, p, q);
+        __syncthreads();
+      }
+      const __amdgpu_buffer_rsrc_t yq_buf = buffer_of(y_q_t + (cur.h0 * T + cur.t0), (uint32_t)(cur.cols * T));
+#pragma unroll
+      for (int step = 0; step < kOutSteps; ++step) {
+        const int id = tid + step * kThreads;
+        const int h = id >> 3;
+        const int phys = (id & 7) ^ ((h >> 3) & 7);
+        const uint32_t lane_yq = (uint32_t)((id >> 3) * T + 16 * (id & 7));
+        const uint4 v = *reinterpret_cast<const uint4*>(s_yqt + h * kTile + phys * 16);
+        if (cur.rows == kTile && yq_align == 16)
+          store_yq(yq_buf, lane_yq, v);
+        else
+          store_yq_piece(yq_buf, lane_yq, v, min(16, max(0, cur.rows - 16 * (id & 7))), yq_align);
+      }
+      __syncthreads();  // the transpose buffer and the inverses are read before phase 2 rewrites them
+    }
+
+    // ---- phase 2: the block's window of the second half -----------------------
+    if (next < end) load_first(in, nxt);
+    {
+      const bool tail = cur.hb == 0 && 8 * p < r;
+      uint32_t Vp[kRows][4];
+      float rv[kRows];
+      if (cur.hb == 0) {
+        load_window(inw, cur, false, true);
+        elementwise_window<true>(inw, tail, s_tab, Vp, rv);
+      } else {
+        elementwise_window<false>(inw, false, s_tab, Vp, rv);
+      }
+      if (tid == 0) s_flag[0] = 0;
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) rp[i] = rv[i];
+      __syncthreads();
+      for (int id = tid; id < kHalfGroups; id += kThreads) {
+        const int row = id & (kTile - 1), sub = id >> 7;
+        float m = 0.0f;
+#pragma unroll
+        for (int pp = 0; pp < kLanesPerRowGroup; ++pp)
+          m = fmaxf(m, s_rowpart[(sub * kLanesPerRowGroup + pp) * kRowPartStride + row]);
+        const float scale = group_scale<F>(m);
+        const float inv = 1.0f / scale;
+        s_inv[id] = inv;
+        if (inv == __builtin_huge_valf()) s_flag[0] = 1;
+        if (row < cur.rows && cur.h0 + sub * kG < lim_b)
+          grad_input_s[(cur.t0 + row) * row_groups + (lim_a + cur.h0) / kG + sub] = scale;
+      }
+      __syncthreads();
+      float iv[kRows];
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) iv[i] = s_inv[sub_row * kTile + kRows * q + i];
+      const __amdgpu_buffer_rsrc_t gq_buf =
+          buffer_of(grad_input_q + (cur.t0 * gq_row_bytes + cur.h0), (uint32_t)(cur.rows * gq_row_bytes));
+      // position (H - r) + h0 + 8 (p & ~1) of the row; the pair's first
+      // channel and lim_b are multiples of 16
+      const uint32_t lane_b = cur.h0 + 8 * (p & ~1) < lim_b ? lane_gq + (uint32_t)lim_a : kDropped;
+      // plain stores: a window's 128 code bytes of a row start H - r into
+      // it, off the 128-byte lines, and plain stores let the two partial
+      // lines merge in L2
+      store_half_codes<F, false, 0>(Vp, iv, gq_buf, lane_b, (uint32_t)gq_row_bytes, p);
+      if (s_flag[0]) {
+        TileIn again;
+        load_window(again, cur, true, cur.hb == 0);
+        float rv2[kRows];
+        if (cur.hb == 0)
+          elementwise_window<true>(again, tail, s_tab, Vp, rv2);
+        else
+          elementwise_window<false>(again, false, s_tab, Vp, rv2);
+        store_half_codes<F, true, 0>(Vp, iv, gq_buf, lane_b, (uint32_t)gq_row_bytes, p);
+      }
+    }
+    tile = next;
+    cur = nxt;
+    if (tile < end) __syncthreads();  // partials, inverses and the flag are rewritten
+  }
+}
+
 
 // ---------------------------------------------------------------------------
 // Forward quantiser: y = bf16((silu(gate) * up) * w[t]), quantised per row in
@@ -1563,6 +1822,12 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
                                 : silu_quant_bwd_kernel<F, 32>;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, xs, dys, gq, grad_input_s, yq, y_s_t, T, H, tiles_h,
                        tiles);
+  } else if (group == 128) {
+    // One workgroup per CU walks the blocks (a window-only block may follow
+    // the last whole one), both kinds of work of a block in turn.
+    auto kernel = silu_quant_bwd_straddle_kernel<F, 128>;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, xs, dys, gq, grad_input_s, yq, y_s_t, T, H, tiles_h,
+                       tiles, (int)r);
   } else {
     // Two teams per XCD, sized to their work: per tile the first team moves
     // about 8 bytes per (t, h) to and from HBM and the second about 5 (its
@@ -1579,9 +1844,7 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
     } else {
       grid = 2 * tiles;
     }
-    auto kernel = group == 128 ? silu_quant_bwd_shift_kernel<F, 128>
-                  : group == 64 ? silu_quant_bwd_shift_kernel<F, 64>
-                                : silu_quant_bwd_shift_kernel<F, 32>;
+    auto kernel = group == 64 ? silu_quant_bwd_shift_kernel<F, 64> : silu_quant_bwd_shift_kernel<F, 32>;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, xs, dys, gq, grad_input_s, yq, y_s_t, T, H, tiles_h,
                        tiles, (int)r, first_team);
   }
