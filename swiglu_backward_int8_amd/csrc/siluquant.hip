@@ -317,8 +317,9 @@ __device__ __forceinline__ void load_tile(TileInR<R>& in, const char* xt, const 
 // Raw buffer loads: 32-bit offsets from a uniform base, and an offset past the
 // record count reads zeros without touching memory.
 constexpr int kStreamLoadPolicy = 2;  // nt
+template <int kPolicy = kStreamLoadPolicy>
 __device__ __forceinline__ uint4 load_buf(__amdgpu_buffer_rsrc_t buf, uint32_t offset) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(buf, offset, 0, kStreamLoadPolicy);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(buf, offset, 0, kPolicy);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -1289,6 +1290,353 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
 
 
 // ---------------------------------------------------------------------------
+// H not a multiple of 128 with groups of 128, H > 128: r = H mod 128, and
+// n = ceil(H / 128) blocks per token block, the last one r channels wide.
+// Window w of the second half is bytes 128 (n - 1 + w) .. + 128 of the row
+// [d_gate | d_up]: the last r channels of block w - 1's d_up followed by the
+// first 128 - r of block w's.  Window 0 takes d_gate's last r channels in
+// place of block -1 (the group that straddles the halves), and window n, the
+// last r channels of block n - 1 alone, exists when r > 64.  The windows'
+// groups line up with them, so a window is quantised like a half of a tile.
+//
+// Every d_up value is computed once.  Lane p's eight channels lie in its
+// block's head (8p < 128 - r) or tail (p >= pb = 16 - r / 8), so a window is
+// the tail lanes of one block and the head lanes of the next, each lane
+// holding one eighth of a row of it: a workgroup walks runs of consecutive
+// blocks of a token block and passes each block's d_up to the next step
+// through the lane's own slot in LDS.  Runs alternate direction along the
+// row.  A forward run [a0, a1) completes windows a0 .. a1 - 1: a first step
+// computes block a0 - 1's tail (d_up, or d_gate's last channels for a0 = 0)
+// from its inputs, then block hb's step completes window hb from the carried
+// tail and its own head.  A backward run walks from a1 - 1 down to a0:
+// block hb's step completes window hb + 1 from its own tail and the carried
+// head of hb + 1 (window n at the row's end, where the carried head is zero),
+// and a last step computes block a0 - 1's tail and completes window a0.  Each
+// run thus recomputes one tail, of a block that the neighbouring run (the
+// next workgroup of the same XCD) reads at about the same time.  Runs are at
+// most 4 blocks long: longer runs scatter the tiles in flight over too many
+// DRAM pages (8 blocks measured 6% slower on the aligned pass).
+constexpr int kCarryFloats = kRows * 4 * kThreads + 2 * kThreads;  // per lane: packed bf16 d_up rows, their maxima
+constexpr int kCarryLdsFloats = kLdsFloats + kCarryFloats;
+static_assert(kLdsFloats % 4 == 0, "the carry slots start on 16 bytes");
+
+// Lane pairs (a, a + 1 mod 16) of a window store one 16-byte piece per row
+// each: the first lane of the pair the first row, the second the second.
+// When pb is even the pairs are (2m, 2m + 1); when it is odd they are
+// (2m + 1, 2m + 2 mod 16).
+__device__ __forceinline__ uint32_t from_pair_partner(uint32_t v, bool shifted, int p) {
+  if (!shifted) return swap_neighbour(v);
+  const uint32_t prev = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x121 /* row_ror:1, from lane p - 1 */, 0xf, 0xf,
+                                                           false);
+  const uint32_t next = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x12F /* row_ror:15, from lane p + 1 */, 0xf,
+                                                           0xf, false);
+  return (p & 1) ? next : prev;
+}
+
+template <Fmt F, bool kSafe>
+__device__ __forceinline__ void store_window_codes(const uint32_t (&W)[kRows][4], const float (&iw)[kRows],
+                                                   __amdgpu_buffer_rsrc_t buf, uint32_t off, bool first,
+                                                   bool shifted, int p) {
+  static_assert(kRows == 2, "one row per lane of a pair");
+  const uint2 r0 = codes8<kSafe, F>(W[0], iw[0]), r1 = codes8<kSafe, F>(W[1], iw[1]);
+  const uint2 send = first ? r1 : r0;
+  const uint2 recv = make_uint2(from_pair_partner(send.x, shifted, p), from_pair_partner(send.y, shifted, p));
+  const uint4 v = first ? make_uint4(r0.x, r0.y, recv.x, recv.y) : make_uint4(recv.x, recv.y, r1.x, r1.y);
+  // plain stores: a window's bytes start off the 128-byte lines of the row,
+  // and the partial lines of neighbouring windows merge in L2
+  __builtin_amdgcn_raw_buffer_store_b128((u32x4){v.x, v.y, v.z, v.w}, buf, off, 0, 0);
+}
+
+template <Fmt F>
+__global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void silu_quant_bwd_carry_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ grad_y, int8_t* __restrict__ grad_input_q,
+    float* __restrict__ grad_input_s, int8_t* __restrict__ y_q_t, float* __restrict__ y_s_t, int64_t T, int64_t H,
+    int n, int r, int segs, int units) {
+  constexpr int kG = 128;
+  constexpr int kRowGroups = 2 * kTile, kColGroups = kTile;
+
+  __shared__ __align__(16) float lds[kCarryLdsFloats];
+  float* s_tab = lds;
+  float* s_rowpart = lds + kSigEntries;
+  float* s_colpart = s_rowpart + kRowPartFloats;
+  float* s_inv = s_colpart + kColPartFloats;
+  char* s_yqt = reinterpret_cast<char*>(s_rowpart);
+  int* s_flag = reinterpret_cast<int*>(s_inv + kInvFloats);
+  uint4* s_carry = reinterpret_cast<uint4*>(lds + kLdsFloats);                    // [row][thread]
+  float2* s_cmax = reinterpret_cast<float2*>(lds + kLdsFloats + kRows * 4 * kThreads);  // [thread]
+
+  const int tid = threadIdx.x;
+  const int p = tid & 15;
+  const int q = tid >> 4;
+
+  const int64_t x_row_bytes = 4 * H, dy_row_bytes = 2 * H, gq_row_bytes = 2 * H;
+  const int64_t row_groups = (2 * H + kG - 1) / kG, col_groups = (T + kG - 1) / kG;
+  const int yq_align = (T & 15) == 0 ? 16 : (T & 3) == 0 ? 4 : 1;
+  const uint32_t lane_x = (uint32_t)(kRows * q * x_row_bytes + 16 * p);
+  const uint32_t lane_dy = (uint32_t)(kRows * q * dy_row_bytes + 16 * p);
+  const uint32_t lane_gq = (uint32_t)((kRows * q + (p & 1)) * gq_row_bytes + 8 * (p & ~1));
+  constexpr uint32_t kDropped = 0x80000000u;
+  constexpr int kOutSteps = kTile * kTile / 16 / kThreads;
+  float* rp = s_rowpart + p * kRowPartStride + kRows * q;
+  // the lane's place in a window: slot (p - pb) mod 16, 8 bytes each
+  const int pb = 16 - r / 8;
+  const bool tail_lane = p >= pb;
+  const int slot = (p - pb) & 15;
+  const bool first = (slot & 1) == 0, shifted = (pb & 1) != 0;
+  const int slot_a = slot & ~1;
+  const uint32_t lane_win = (uint32_t)((kRows * q + (first ? 0 : 1)) * gq_row_bytes + 8 * slot_a);
+
+  // Each XCD's workgroups (every 8th) take one contiguous eighth of the runs,
+  // neighbours side by side.
+  int unit, end, stride;
+  if ((gridDim.x & 7) == 0) {
+    const int xcd = blockIdx.x & 7;
+    unit = (int)(((int64_t)units * xcd) >> 3) + (int)(blockIdx.x >> 3);
+    end = (int)(((int64_t)units * (xcd + 1)) >> 3);
+    stride = gridDim.x >> 3;
+  } else {
+    unit = blockIdx.x;
+    end = units;
+    stride = gridDim.x;
+  }
+
+  const char* xb = reinterpret_cast<const char*>(x);
+  const char* dyb = reinterpret_cast<const char*>(grad_y);
+  // run u: token block u / segs, blocks [a0, a1); the last run of a token
+  // block walks backward and the others alternate
+  struct Run {
+    int64_t t0;
+    int rows, a0, a1;
+    bool fwd;
+  };
+  auto run_of = [&](int u) {
+    Run c;
+    const int tb = (int)((uint32_t)u / (uint32_t)segs), s = u - tb * segs;
+    c.t0 = (int64_t)tb * kTile;
+    c.rows = T - c.t0 < kTile ? (int)(T - c.t0) : kTile;
+    c.a0 = (int)((uint32_t)(s * n) / (uint32_t)segs);  // s * n < 2^30
+    c.a1 = (int)((uint32_t)((s + 1) * n) / (uint32_t)segs);
+    c.fwd = ((segs - 1 - s) & 1) != 0;
+    return c;
+  };
+  // step k of a run: a block (the tile's gate, up and grad_y) or the tail of
+  // block a0 - 1 (gate and grad_y of the tail lanes; for a0 = 0 gate, up and
+  // grad_y of d_gate's last r channels, which the tail lanes of a block
+  // starting at channel H - 128 hold)
+  auto is_tail_step = [&](const Run& c, int k) { return c.fwd ? k == 0 : k == c.a1 - c.a0; };
+  auto block_of = [&](const Run& c, int k) { return c.fwd ? c.a0 + k - 1 : c.a1 - 1 - k; };
+  auto load_step = [&](TileIn& in, int u, int k) {
+    const Run c = run_of(u);
+    // Buffers over the rows that exist, from the step's first channel on; a
+    // lane with nothing to read takes an offset past the records (zeros).  A
+    // block step reads the lanes whose channels exist; a tail step reads the
+    // tail lanes, and up only for a0 = 0.  The loads are plain (cached): a
+    // tail step reads lines that the neighbouring run loads at about the
+    // same time, and where a row is not a whole number of 128-byte lines
+    // neighbouring blocks share lines (plain loads measured 16% faster at
+    // T = 16384, H = 11000 and 8% at H = 1376 than non-temporal ones).
+    const bool tail = is_tail_step(c, k), gate_tail = c.a0 == 0;
+    const int64_t h0 = !tail ? (int64_t)kTile * block_of(c, k) : gate_tail ? H - kTile : (int64_t)kTile * (c.a0 - 1);
+    const bool live = tail ? tail_lane : h0 + 8 * p < H;
+    const __amdgpu_buffer_rsrc_t xbuf = buffer_of(const_cast<char*>(xb) + (c.t0 * x_row_bytes + 2 * h0),
+                                                  (uint32_t)(c.rows * x_row_bytes - 2 * h0));
+    const __amdgpu_buffer_rsrc_t dybuf = buffer_of(const_cast<char*>(dyb) + (c.t0 * dy_row_bytes + 2 * h0),
+                                                   (uint32_t)(c.rows * dy_row_bytes - 2 * h0));
+    const uint32_t ox = live ? lane_x : kDropped, od = live ? lane_dy : kDropped;
+    const uint32_t ou = live && (!tail || gate_tail) ? lane_x + (uint32_t)(x_row_bytes >> 1) : kDropped;
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      in.g[i] = load_buf<0>(xbuf, ox + (uint32_t)(i * x_row_bytes));
+      in.u[i] = load_buf<0>(xbuf, ou + (uint32_t)(i * x_row_bytes));
+      in.d[i] = load_buf<0>(dybuf, od + (uint32_t)(i * dy_row_bytes));
+    }
+  };
+  auto read_carry = [&](uint32_t (&Cp)[kRows][4]) {
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      const uint4 v = s_carry[i * kThreads + tid];
+      Cp[i][0] = v.x, Cp[i][1] = v.y, Cp[i][2] = v.z, Cp[i][3] = v.w;
+    }
+  };
+  auto write_carry = [&](const uint32_t (&V)[kRows][4], const float (&m)[kRows]) {
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) s_carry[i * kThreads + tid] = make_uint4(V[i][0], V[i][1], V[i][2], V[i][3]);
+    s_cmax[tid] = make_float2(m[0], m[1]);
+  };
+  // one window group per row: maximum, scale, inverse (s_inv[kTile + row])
+  auto window_groups = [&](int id, const Run& c, int w) {
+    const int row = id & (kTile - 1);
+    float m = 0.0f;
+#pragma unroll
+    for (int pp = 0; pp < 16; ++pp) m = fmaxf(m, s_rowpart[pp * kRowPartStride + kTile + row]);
+    const float scale = group_scale<F>(m);
+    s_inv[kTile + row] = 1.0f / scale;
+    const int64_t g = (int64_t)(n - 1 + w);
+    if (row < c.rows && g < row_groups) grad_input_s[(c.t0 + row) * row_groups + g] = scale;
+  };
+  // the lane's piece of window w, or an offset past the records
+  auto window_offset = [&](bool valid, int w) {
+    const int64_t at = (int64_t)kTile * (n - 1 + w) + 8 * slot_a;
+    return valid && at + 16 <= gq_row_bytes ? lane_win + (uint32_t)(kTile * (int64_t)(n - 1 + w)) : kDropped;
+  };
+
+  TileIn in, in_next;
+  int k = 0;
+  if (unit < end) load_step(in, unit, 0);
+  {
+    const float4* src = reinterpret_cast<const float4*>(g_sigma_tab);
+    float4* dst = reinterpret_cast<float4*>(s_tab);
+    for (int i = tid; i < kSigEntries / 4; i += kThreads) dst[i] = src[i];
+  }
+  __syncthreads();
+
+  while (unit < end) {
+    const Run cur = run_of(unit);
+    const int len = cur.a1 - cur.a0;
+    int nunit = unit, nk = k + 1;
+    if (nk > len) {
+      nunit = unit + stride;
+      nk = 0;
+    }
+    if (nunit < end) load_step(in_next, nunit, nk);
+    if (!cur.fwd && k == 0) {  // the head of block n (past the row) is zero
+      const uint32_t z[kRows][4] = {};
+      const float zm[kRows] = {};
+      write_carry(z, zm);
+    }
+    const bool tail_step = is_tail_step(cur, k);
+    const __amdgpu_buffer_rsrc_t gq_buf =
+        buffer_of(grad_input_q + cur.t0 * gq_row_bytes, (uint32_t)(cur.rows * gq_row_bytes));
+    // A tail step runs the block step's code on block a0 - 1's tail lanes (or
+    // on d_gate's last channels for a0 = 0) with the block's own outputs
+    // switched off: forward it only fills the slots, backward it completes
+    // window a0.  One code path keeps the registers of the block step.
+    const int hb = tail_step ? cur.a0 - 1 : block_of(cur, k);
+    const bool gate_tail = tail_step && cur.a0 == 0;
+    const int64_t h0 = (int64_t)kTile * hb;
+    const int cols = H - h0 < kTile ? (int)(H - h0) : kTile;
+    const bool has_gate = !tail_step && hb < n - 1;  // block n - 1's d_gate lies in window 0
+    const int w = tail_step ? cur.a0 : cur.fwd ? hb : hb + 1;
+    const bool wvalid = tail_step || cur.fwd || hb + 1 < cur.a1 || (cur.a1 == n && 2 * r > kTile);
+    const bool use_carry = tail_lane == cur.fwd;
+
+    uint32_t Yp[kRows][4], Gp[kRows][4], Up[kRows][4];
+    float rg[kRows], ru[kRows], cm[8];
+    elementwise(in, s_tab, Yp, Gp, Up, rg, ru, cm);
+    if (gate_tail) {
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) {
+        ru[i] = rg[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Up[i][j] = Gp[i][j];
+      }
+    }
+    if (tail_step && cur.fwd) {
+      write_carry(Up, ru);
+    } else {
+      if (tid == 0) s_flag[0] = 0;
+      {
+        const float2 cm2 = s_cmax[tid];
+        rp[0] = rg[0];
+        rp[1] = rg[1];
+        rp[kTile] = use_carry ? cm2.x : ru[0];
+        rp[kTile + 1] = use_carry ? cm2.y : ru[1];
+        float4* cp = reinterpret_cast<float4*>(s_colpart + q * kTile + 4 * p);
+        cp[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
+        cp[16] = make_float4(cm[4], cm[5], cm[6], cm[7]);
+      }
+      __syncthreads();
+      for (int id = tid; id < kRowGroups + kColGroups; id += kThreads) {
+        if (id < kTile) {
+          const int row = id;
+          float m = 0.0f;
+#pragma unroll
+          for (int pp = 0; pp < 16; ++pp) m = fmaxf(m, s_rowpart[pp * kRowPartStride + row]);
+          const float scale = group_scale<F>(m);
+          const float inv = 1.0f / scale;
+          s_inv[id] = inv;
+          if (has_gate && inv == __builtin_huge_valf()) s_flag[0] = 1;
+          if (has_gate && row < cur.rows) grad_input_s[(cur.t0 + row) * row_groups + hb] = scale;
+        } else if (id < kRowGroups) {
+          if (wvalid) window_groups(id, cur, w);
+        } else if (!tail_step) {
+          const int c = id - kRowGroups;
+          const int idx = ((c >> 2) & 1) * 64 + (c >> 3) * 4 + (c & 3);
+          float m = 0.0f;
+#pragma unroll 8
+          for (int qq = 0; qq < kQ; ++qq) m = fmaxf(m, s_colpart[qq * kTile + idx]);
+          const float scale = group_scale<F>(m);
+          const float inv = 1.0f / scale;
+          s_inv[id] = inv;
+          if (inv == __builtin_huge_valf()) s_flag[0] = 1;
+          if (c < cols) y_s_t[(h0 + c) * col_groups + cur.t0 / kG] = scale;
+        }
+      }
+      __syncthreads();
+      float idg[kRows], iw[kRows], iy[8];
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) {
+        idg[i] = s_inv[kRows * q + i];
+        iw[i] = s_inv[kTile + kRows * q + i];
+      }
+      const float* inv_col = s_inv + kRowGroups + 8 * p;
+      const float4 inv_y0 = *reinterpret_cast<const float4*>(inv_col);
+      const float4 inv_y1 = *reinterpret_cast<const float4*>(inv_col + 4);
+      iy[0] = inv_y0.x, iy[1] = inv_y0.y, iy[2] = inv_y0.z, iy[3] = inv_y0.w;
+      iy[4] = inv_y1.x, iy[5] = inv_y1.y, iy[6] = inv_y1.z, iy[7] = inv_y1.w;
+      const uint32_t off_g = has_gate ? lane_gq + (uint32_t)h0 : kDropped;
+      store_half_codes<F, false>(Gp, idg, gq_buf, off_g, (uint32_t)gq_row_bytes, p);
+      // The window takes the clamped rule directly (it gives the same words
+      // for every finite inverse), so that the carried half is not needed
+      // again and this step's d_up replaces it at once.
+      {
+        uint32_t W[kRows][4];
+        read_carry(W);
+#pragma unroll
+        for (int i = 0; i < kRows; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) W[i][j] = use_carry ? W[i][j] : Up[i][j];
+        store_window_codes<F, true>(W, iw, gq_buf, window_offset(wvalid, w), first, shifted, p);
+        write_carry(Up, ru);
+      }
+      if (!tail_step) {
+        stage_y_codes<F, false>(Yp, iy, s_yqt, p, q);
+        __syncthreads();
+        // Rare: some d_gate or y group's inverse overflowed; rewrite their
+        // codes with the clamped rule (as in silu_quant_bwd_kernel).
+        if (s_flag[0]) {
+          TileIn again;
+          load_step(again, unit, k);
+          float rg2[kRows], ru2[kRows], cm2[8];
+          elementwise(again, s_tab, Yp, Gp, Up, rg2, ru2, cm2);
+          store_half_codes<F, true>(Gp, idg, gq_buf, off_g, (uint32_t)gq_row_bytes, p);
+          stage_y_codes<F, true>(Yp, iy, s_yqt, p, q);
+          __syncthreads();
+        }
+        const __amdgpu_buffer_rsrc_t yq_buf = buffer_of(y_q_t + (h0 * T + cur.t0), (uint32_t)(cols * T));
+#pragma unroll
+        for (int step = 0; step < kOutSteps; ++step) {
+          const int id = tid + step * kThreads;
+          const int h = id >> 3;
+          const int phys = (id & 7) ^ ((h >> 3) & 7);
+          const uint32_t lane_yq = (uint32_t)((id >> 3) * T + 16 * (id & 7));
+          const uint4 v = *reinterpret_cast<const uint4*>(s_yqt + h * kTile + phys * 16);
+          if (cur.rows == kTile && yq_align == 16)
+            store_yq(yq_buf, lane_yq, v);
+          else
+            store_yq_piece(yq_buf, lane_yq, v, min(16, max(0, cur.rows - 16 * (id & 7))), yq_align);
+        }
+      }
+    }
+    const bool barrier = !(tail_step && cur.fwd);
+    in = in_next;
+    unit = nunit;
+    k = nk;
+    if (barrier && unit < end) __syncthreads();  // partials, inverses, the flag and the transpose buffer
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Forward quantiser: y = bf16((silu(gate) * up) * w[t]), quantised per row in
 // groups of kG = 128, 64 or 32 channels (y_q [T, H], y_s [T, ceil(H/kG)]),
 // optionally also the bf16 y itself.  The fused launch shape follows the page
@@ -1813,6 +2161,7 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
   // multiple of 8, one share per XCD), or one per tile if there are fewer.
   int grid = cus * kWorkgroupsPerCU;
   grid = grid >= 8 ? grid - grid % 8 : grid;
+  const int grid_cap = grid;
   if (tiles < grid) grid = tiles;
   int8_t* gq = static_cast<int8_t*>(grad_input_q);
   int8_t* yq = static_cast<int8_t*>(y_q_t);
@@ -1822,9 +2171,33 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
                                 : silu_quant_bwd_kernel<F, 32>;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, xs, dys, gq, grad_input_s, yq, y_s_t, T, H, tiles_h,
                        tiles);
+  } else if (group == 128 && H > kTile) {
+    // Runs of at most 4 consecutive blocks per token block; among the run
+    // counts that allow, the one whose rounds of runs over the grid finish
+    // first (a run costs its blocks plus about a third of a block for the
+    // tail it recomputes).
+    const int n = (int)((H + kTile - 1) / kTile);
+    const int s_min = (n + 3) / 4, s_max = std::min(n, s_min + 255);
+    int segs = s_min;
+    double best = 0.0;
+    for (int s_try = s_min; s_try <= s_max; ++s_try) {
+      const int64_t runs = tiles_t * s_try;
+      const int64_t rounds = (runs + grid_cap - 1) / grid_cap;
+      const double cost = (double)rounds * ((double)((n + s_try - 1) / s_try) + 0.35);
+      if (s_try == s_min || cost < best) {
+        best = cost;
+        segs = s_try;
+      }
+    }
+    const int64_t runs = tiles_t * segs;
+    if (runs > INT32_MAX) return SILUQUANT_ERR_BAD_SHAPE;
+    int cgrid = grid_cap;
+    if (runs < cgrid) cgrid = (int)runs;
+    hipLaunchKernelGGL(silu_quant_bwd_carry_kernel<F>, dim3(cgrid), dim3(kThreads), 0, s, xs, dys, gq, grad_input_s,
+                       yq, y_s_t, T, H, n, (int)r, segs, (int)runs);
   } else if (group == 128) {
-    // One workgroup per CU walks the blocks (a window-only block may follow
-    // the last whole one), both kinds of work of a block in turn.
+    // H < 128: one workgroup per CU walks the blocks (a window-only block
+    // follows the one partial block), both kinds of work of a block in turn.
     auto kernel = silu_quant_bwd_straddle_kernel<F, 128>;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, xs, dys, gq, grad_input_s, yq, y_s_t, T, H, tiles_h,
                        tiles, (int)r);
