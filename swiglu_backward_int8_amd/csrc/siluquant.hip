@@ -11,8 +11,9 @@
 //   * persistent 1024-thread workgroups, one per CU, walk 128-token x
 //     128-channel tiles; every group of both quantisation axes lies inside one
 //     tile, so no workgroup ever waits on another (when H is not a multiple of
-//     the group, silu_quant_bwd_straddle_kernel and silu_quant_bwd_shift_kernel
-//     keep this with shifted windows for the d_up half);
+//     the group, silu_quant_bwd_carry_kernel, silu_quant_bwd_straddle_kernel
+//     and silu_quant_bwd_shift_kernel keep this with shifted windows for the
+//     d_up half);
 //   * lane (q, p) = (tid / 16, tid % 16) owns tokens 2q, 2q+1 and channels
 //     8p..8p+7: each of its loads is 16 bytes and a wave's load covers four
 //     whole 256-byte row segments;
@@ -765,8 +766,8 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
 // the first r positions are the last r channels of d_gate.  The window's
 // groups line up with it again, and the straddling group lies in window 0.
 //
-// With groups of 64 or 32 (group 128 takes silu_quant_bwd_straddle_kernel
-// below), the workgroups of each XCD split into two teams that walk the XCD's
+// With groups of 64 or 32 (group 128 takes silu_quant_bwd_carry_kernel or,
+// for H < 128, silu_quant_bwd_straddle_kernel below), the workgroups of each XCD split into two teams that walk the XCD's
 // tiles in order: the first does y, d_gate and the y^T codes from the tile's gate,
 // up and grad_y, like silu_quant_bwd_kernel; the second does the windows
 // from gate and grad_y (and up where a window holds d_gate).  The teams are
@@ -1031,10 +1032,10 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
   }
 }
 
-// H not a multiple of 128 with groups of 128: one workgroup takes both kinds
-// of work of a block in turn: phase 1 does y,
-// d_gate and the y^T codes from the block's gate, up and grad_y (as the
-// aligned kernel, without d_up); phase 2 does the block's window of the
+// H not a multiple of 128 with groups of 128 and H < 128 (larger H takes
+// silu_quant_bwd_carry_kernel): one workgroup takes both kinds of work of a
+// block in turn: phase 1 does y, d_gate and the y^T codes from the block's
+// gate, up and grad_y (as the aligned kernel, without d_up); phase 2 does the block's window of the
 // second half (d_up at channels h0 - r + [0, 128), or in window 0 the
 // straddling group), from gate and grad_y read again.  The window's loads are
 // issued at the top of the iteration and stay in flight through phase 1; the
