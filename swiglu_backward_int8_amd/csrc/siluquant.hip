@@ -1587,9 +1587,10 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
       iy[4] = inv_y1.x, iy[5] = inv_y1.y, iy[6] = inv_y1.z, iy[7] = inv_y1.w;
       const uint32_t off_g = has_gate ? lane_gq + (uint32_t)h0 : kDropped;
       store_half_codes<F, false>(Gp, idg, gq_buf, off_g, (uint32_t)gq_row_bytes, p);
-      // The window takes the clamped rule directly (it gives the same words
-      // for every finite inverse), so that the carried half is not needed
-      // again and this step's d_up replaces it at once.
+      // A wave whose rows hold a window group with an infinite inverse takes
+      // the clamped rule for the window (the same words for every finite
+      // inverse) at once, so that the carried half is never needed again and
+      // this step's d_up replaces it straight away.
       {
         uint32_t W[kRows][4];
         read_carry(W);
@@ -1597,7 +1598,11 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
         for (int i = 0; i < kRows; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) W[i][j] = use_carry ? W[i][j] : Up[i][j];
-        store_window_codes<F, true>(W, iw, gq_buf, window_offset(wvalid, w), first, shifted, p);
+        const uint32_t off_w = window_offset(wvalid, w);
+        if (__builtin_amdgcn_ballot_w64(iw[0] == __builtin_huge_valf() || iw[1] == __builtin_huge_valf()) != 0)
+          store_window_codes<F, true>(W, iw, gq_buf, off_w, first, shifted, p);
+        else
+          store_window_codes<F, false>(W, iw, gq_buf, off_w, first, shifted, p);
         write_carry(Up, ru);
       }
       if (!tail_step) {
