@@ -766,10 +766,12 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
 // the first r positions are the last r channels of d_gate.  The window's
 // groups line up with it again, and the straddling group lies in window 0.
 //
-// With groups of 64 or 32 (group 128 takes silu_quant_bwd_carry_kernel or,
-// for H < 128, silu_quant_bwd_straddle_kernel below), the workgroups of each XCD split into two teams that walk the XCD's
-// tiles in order: the first does y, d_gate and the y^T codes from the tile's gate,
-// up and grad_y, like silu_quant_bwd_kernel; the second does the windows
+// For H < 128 with groups of 64 or 32 (larger H takes
+// silu_quant_bwd_carry_kernel, and group 128 below 128 channels
+// silu_quant_bwd_straddle_kernel), the workgroups of each XCD split into two
+// teams that walk the XCD's tiles in order: the first does y, d_gate and the
+// y^T codes from the tile's gate, up and grad_y, like silu_quant_bwd_kernel;
+// the second does the windows
 // from gate and grad_y (and up where a window holds d_gate).  The teams are
 // sized to the work of their tiles, so that they move through the tiles at
 // about the same pace and the windows' loads mostly hit L2 lines the first
@@ -1291,14 +1293,15 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
 
 
 // ---------------------------------------------------------------------------
-// H not a multiple of 128 with groups of 128, H > 128: r = H mod 128, and
-// n = ceil(H / 128) blocks per token block, the last one r channels wide.
-// Window w of the second half is bytes 128 (n - 1 + w) .. + 128 of the row
-// [d_gate | d_up]: the last r channels of block w - 1's d_up followed by the
-// first 128 - r of block w's.  Window 0 takes d_gate's last r channels in
-// place of block -1 (the group that straddles the halves), and window n, the
-// last r channels of block n - 1 alone, exists when r > 64.  The windows'
-// groups line up with them, so a window is quantised like a half of a tile.
+// H not a multiple of the group, H > 128: r = H mod 128, and n = ceil(H / 128)
+// blocks per token block, the last one r channels wide.  Window w of the
+// second half is bytes 128 (n - 1 + w) .. + 128 of the row [d_gate | d_up]:
+// the last r channels of block w - 1's d_up followed by the first 128 - r of
+// block w's.  Window 0 takes d_gate's last r channels in place of block -1
+// (it holds the group that straddles the halves), and window n, the last r
+// channels of block n - 1 alone, exists when r > 64.  Windows start on
+// multiples of 128 positions, so each holds 128 / kG whole row groups and is
+// quantised like a half of a tile.
 //
 // Every d_up value is computed once.  Lane p's eight channels lie in its
 // block's head (8p < 128 - r) or tail (p >= pb = 16 - r / 8), so a window is
@@ -1348,13 +1351,21 @@ __device__ __forceinline__ void store_window_codes(const uint32_t (&W)[kRows][4]
   __builtin_amdgcn_raw_buffer_store_b128((u32x4){v.x, v.y, v.z, v.w}, buf, off, 0, 0);
 }
 
-template <Fmt F>
+template <Fmt F, int kG>
 __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void silu_quant_bwd_carry_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ grad_y, int8_t* __restrict__ grad_input_q,
     float* __restrict__ grad_input_s, int8_t* __restrict__ y_q_t, float* __restrict__ y_s_t, int64_t T, int64_t H,
     int n, int r, int segs, int units) {
-  constexpr int kG = 128;
-  constexpr int kRowGroups = 2 * kTile, kColGroups = kTile;
+  // kG-wide groups, kSub of them per 128 positions of a row and per 128
+  // tokens of a channel.  Windows start on multiples of 128 positions, so
+  // each holds kSub whole row groups.  Inverses: d_gate group (sub, row) at
+  // s_inv[sub * 128 + row], window group (sub, row) kHalf further, column
+  // group (sub, channel) 2 kHalf further.
+  static_assert(kG == 32 || kG == 64 || kG == 128, "group sizes that divide the tile");
+  constexpr int kSub = kTile / kG, kHalf = kTile * kSub;
+  constexpr int kLanesPerRowGroup = kG / 8;
+  constexpr int kPairsPerColGroup = kG / kRows;
+  static_assert(3 * kHalf <= kInvFloats, "inverse slots");
 
   __shared__ __align__(16) float lds[kCarryLdsFloats];
   float* s_tab = lds;
@@ -1383,6 +1394,10 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
   const int pb = 16 - r / 8;
   const bool tail_lane = p >= pb;
   const int slot = (p - pb) & 15;
+  // the lane's row groups: of its block (channels 8p..) and of its window
+  // piece (positions 8 slot..); its token group
+  const int sub_row = kSub == 1 ? 0 : p / kLanesPerRowGroup, sub_win = kSub == 1 ? 0 : slot / kLanesPerRowGroup;
+  const int sub_col = kSub == 1 ? 0 : q / kPairsPerColGroup;
   const bool first = (slot & 1) == 0, shifted = (pb & 1) != 0;
   const int slot_a = slot & ~1;
   const uint32_t lane_win = (uint32_t)((kRows * q + (first ? 0 : 1)) * gq_row_bytes + 8 * slot_a);
@@ -1464,15 +1479,24 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
     for (int i = 0; i < kRows; ++i) s_carry[i * kThreads + tid] = make_uint4(V[i][0], V[i][1], V[i][2], V[i][3]);
     s_cmax[tid] = make_float2(m[0], m[1]);
   };
-  // one window group per row: maximum, scale, inverse (s_inv[kTile + row])
+  // window group (sub, row): maximum over the lanes whose pieces it holds,
+  // scale, inverse (s_inv[kHalf + sub * 128 + row])
   auto window_groups = [&](int id, const Run& c, int w) {
-    const int row = id & (kTile - 1);
+    const int row = id & (kTile - 1), sub = kSub == 1 ? 0 : id >> 7;
     float m = 0.0f;
+    if constexpr (kSub == 1) {  // every lane's piece
 #pragma unroll
-    for (int pp = 0; pp < 16; ++pp) m = fmaxf(m, s_rowpart[pp * kRowPartStride + kTile + row]);
+      for (int lane = 0; lane < 16; ++lane) m = fmaxf(m, s_rowpart[lane * kRowPartStride + kTile + row]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kLanesPerRowGroup; ++k) {
+        const int lane = (sub * kLanesPerRowGroup + k + pb) & 15;
+        m = fmaxf(m, s_rowpart[lane * kRowPartStride + kTile + row]);
+      }
+    }
     const float scale = group_scale<F>(m);
-    s_inv[kTile + row] = 1.0f / scale;
-    const int64_t g = (int64_t)(n - 1 + w);
+    s_inv[kHalf + id] = 1.0f / scale;
+    const int64_t g = (int64_t)(n - 1 + w) * kSub + sub;  // windows start on whole groups
     if (row < c.rows && g < row_groups) grad_input_s[(c.t0 + row) * row_groups + g] = scale;
   };
   // the lane's piece of window w, or an offset past the records
@@ -1547,40 +1571,42 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
         cp[16] = make_float4(cm[4], cm[5], cm[6], cm[7]);
       }
       __syncthreads();
-      for (int id = tid; id < kRowGroups + kColGroups; id += kThreads) {
-        if (id < kTile) {
-          const int row = id;
+      for (int id = tid; id < 3 * kHalf; id += kThreads) {
+        if (id < kHalf) {
+          const int row = id & (kTile - 1), sub = kSub == 1 ? 0 : id >> 7;
           float m = 0.0f;
 #pragma unroll
-          for (int pp = 0; pp < 16; ++pp) m = fmaxf(m, s_rowpart[pp * kRowPartStride + row]);
+          for (int pp = 0; pp < kLanesPerRowGroup; ++pp)
+            m = fmaxf(m, s_rowpart[(sub * kLanesPerRowGroup + pp) * kRowPartStride + row]);
           const float scale = group_scale<F>(m);
           const float inv = 1.0f / scale;
           s_inv[id] = inv;
           if (has_gate && inv == __builtin_huge_valf()) s_flag[0] = 1;
-          if (has_gate && row < cur.rows) grad_input_s[(cur.t0 + row) * row_groups + hb] = scale;
-        } else if (id < kRowGroups) {
-          if (wvalid) window_groups(id, cur, w);
+          if (has_gate && row < cur.rows) grad_input_s[(cur.t0 + row) * row_groups + hb * kSub + sub] = scale;
+        } else if (id < 2 * kHalf) {
+          if (wvalid) window_groups(id - kHalf, cur, w);
         } else if (!tail_step) {
-          const int c = id - kRowGroups;
+          const int cid = id - 2 * kHalf, c = cid & (kTile - 1), sub = kSub == 1 ? 0 : cid >> 7;
           const int idx = ((c >> 2) & 1) * 64 + (c >> 3) * 4 + (c & 3);
           float m = 0.0f;
 #pragma unroll 8
-          for (int qq = 0; qq < kQ; ++qq) m = fmaxf(m, s_colpart[qq * kTile + idx]);
+          for (int qq = 0; qq < kPairsPerColGroup; ++qq)
+            m = fmaxf(m, s_colpart[(sub * kPairsPerColGroup + qq) * kTile + idx]);
           const float scale = group_scale<F>(m);
           const float inv = 1.0f / scale;
           s_inv[id] = inv;
           if (inv == __builtin_huge_valf()) s_flag[0] = 1;
-          if (c < cols) y_s_t[(h0 + c) * col_groups + cur.t0 / kG] = scale;
+          if (c < cols && (kSub == 1 || sub * kG < cur.rows)) y_s_t[(h0 + c) * col_groups + cur.t0 / kG + sub] = scale;
         }
       }
       __syncthreads();
       float idg[kRows], iw[kRows], iy[8];
 #pragma unroll
       for (int i = 0; i < kRows; ++i) {
-        idg[i] = s_inv[kRows * q + i];
-        iw[i] = s_inv[kTile + kRows * q + i];
+        idg[i] = s_inv[sub_row * kTile + kRows * q + i];
+        iw[i] = s_inv[kHalf + sub_win * kTile + kRows * q + i];
       }
-      const float* inv_col = s_inv + kRowGroups + 8 * p;
+      const float* inv_col = s_inv + 2 * kHalf + sub_col * kTile + 8 * p;
       const float4 inv_y0 = *reinterpret_cast<const float4*>(inv_col);
       const float4 inv_y1 = *reinterpret_cast<const float4*>(inv_col + 4);
       iy[0] = inv_y0.x, iy[1] = inv_y0.y, iy[2] = inv_y0.z, iy[3] = inv_y0.w;
@@ -2177,7 +2203,7 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
                                 : silu_quant_bwd_kernel<F, 32>;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, xs, dys, gq, grad_input_s, yq, y_s_t, T, H, tiles_h,
                        tiles);
-  } else if (group == 128 && H > kTile) {
+  } else if (H > kTile) {
     // Runs of at most 4 consecutive blocks per token block; among the run
     // counts that allow, the one whose rounds of runs over the grid finish
     // first (a run costs its blocks plus about a third of a block for the
@@ -2199,8 +2225,12 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
     if (runs > INT32_MAX) return SILUQUANT_ERR_BAD_SHAPE;
     int cgrid = grid_cap;
     if (runs < cgrid) cgrid = (int)runs;
-    hipLaunchKernelGGL(silu_quant_bwd_carry_kernel<F>, dim3(cgrid), dim3(kThreads), 0, s, xs, dys, gq, grad_input_s,
-                       yq, y_s_t, T, H, n, (int)r, segs, (int)runs);
+    // the windows sit H mod 128 positions before the blocks, whatever the group
+    auto kernel = group == 128  ? silu_quant_bwd_carry_kernel<F, 128>
+                  : group == 64 ? silu_quant_bwd_carry_kernel<F, 64>
+                                : silu_quant_bwd_carry_kernel<F, 32>;
+    hipLaunchKernelGGL(kernel, dim3(cgrid), dim3(kThreads), 0, s, xs, dys, gq, grad_input_s, yq, y_s_t, T, H, n,
+                       (int)(H % kTile), segs, (int)runs);
   } else if (group == 128) {
     // H < 128: one workgroup per CU walks the blocks (a window-only block
     // follows the one partial block), both kinds of work of a block in turn.

@@ -313,7 +313,7 @@ def test_group_size_errors():
 # shifted against the 128-channel blocks, and the row's last group may be
 # partial.  Shapes cover r = H % group from 8 to 120, H below the group, and
 # windows that need one block more than the channels (r > 128 - H % 128).
-# With group 128 and H > 128 the d_up halves are handed along runs of blocks:
+# With H > 128 the d_up halves are handed along runs of blocks (any group):
 # r = 8 .. 120 with r / 8 odd and even (the window's lane pairs differ), runs
 # of one block (small T) and of three or four (T = 8192, H = 1376 and
 # T = 4096, H = 11000), and window n present (r > 64) or not.
@@ -321,7 +321,8 @@ def test_group_size_errors():
                                        (1000, 1064, 64), (128, 136, 128), (4096, 1400, 128), (333, 520, 32),
                                        (77, 2056, 64), (1, 24, 32), (130, 248, 128), (640, 11000, 128),
                                        (256, 1376, 128), (200, 272, 128), (129, 704, 128), (300, 848, 128),
-                                       (1000, 176, 128), (8192, 1376, 128), (4096, 11000, 128), (1500, 2752, 128)])
+                                       (1000, 176, 128), (8192, 1376, 128), (4096, 11000, 128), (1500, 2752, 128),
+                                       (8192, 1376, 64), (4096, 11000, 32), (3000, 2744, 64), (640, 1064, 32)])
 def test_straddling_groups(T, H, group):
     print("case straddle", T, H, group, flush=True)
     x, dy = random_inputs(T, H, device=DEV, seed=5 * T + H + group)
