@@ -25,8 +25,8 @@
 //     fp32), which makes the sigmoid bit-exact rather than within an ulp;
 //   * group maxima: each lane reduces inside its registers, writes partial
 //     maxima to LDS, and one thread per group (384 groups per tile at group
-//     128) finishes the reduction and computes scale and inverse with IEEE
-//     division;
+//     128) finishes the reduction and takes scale and inverse from a small
+//     exact table (int8) or from IEEE divisions;
 //   * grad_input_q is stored straight from registers (a wave writes four whole
 //     128-byte row segments); y_q_t goes through an XOR-swizzled LDS transpose
 //     so that it, too, leaves in whole 128-byte rows.
@@ -548,6 +548,7 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
   static_assert(kRowGroups + kColGroups <= kInvFloats, "inverse slots");
 
   __shared__ __align__(16) float lds[kLdsFloats];
+  __shared__ __align__(16) float2 s_qtab[128];
   float* s_tab = lds;
   float* s_rowpart = lds + kSigEntries;
   float* s_colpart = s_rowpart + kRowPartFloats;
@@ -627,6 +628,7 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
     const float4* src = reinterpret_cast<const float4*>(g_sigma_tab);
     float4* dst = reinterpret_cast<float4*>(s_tab);
     for (int i = tid; i < kSigEntries / 4; i += kThreads) dst[i] = src[i];
+    fill_scale_table(s_qtab, tid);
   }
   __syncthreads();
 
@@ -668,8 +670,13 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
 #pragma unroll
         for (int pp = 0; pp < kLanesPerRowGroup; ++pp)
           m = fmaxf(m, s_rowpart[(sub * kLanesPerRowGroup + pp) * kRowPartStride + g]);
-        const float scale = group_scale<F>(m);
-        const float inv = 1.0f / scale;
+        float scale, inv;
+        if constexpr (F == Fmt::kInt8) {
+          scale_and_inverse(m, s_qtab, scale, inv);
+        } else {
+          scale = group_scale<F>(m);
+          inv = 1.0f / scale;
+        }
         s_inv[id] = inv;
         if (inv == __builtin_huge_valf()) s_flag[0] = 1;
         // groups of channels past H (ragged H) do not exist
@@ -682,8 +689,13 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
 #pragma unroll 8
         for (int qq = 0; qq < kPairsPerColGroup; ++qq)
           m = fmaxf(m, s_colpart[(sub * kPairsPerColGroup + qq) * kTile + idx]);
-        const float scale = group_scale<F>(m);
-        const float inv = 1.0f / scale;
+        float scale, inv;
+        if constexpr (F == Fmt::kInt8) {
+          scale_and_inverse(m, s_qtab, scale, inv);
+        } else {
+          scale = group_scale<F>(m);
+          inv = 1.0f / scale;
+        }
         s_inv[id] = inv;
         if (inv == __builtin_huge_valf()) s_flag[0] = 1;
         // token groups past T (ragged T) and channels past H do not exist
