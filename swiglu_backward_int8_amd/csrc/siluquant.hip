@@ -1536,7 +1536,7 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
       nk = 0;
     }
     if (nunit < end) load_step(in_next, nunit, nk);
-    if (!cur.fwd && k == 0) {  // the head of block n (past the row) is zero
+    if (!cur.fwd && k == 0 && !tail_lane) {  // the head of block n (past the row) is zero
       const uint32_t z[kRows][4] = {};
       const float zm[kRows] = {};
       write_carry(z, zm);
@@ -1568,12 +1568,14 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
         for (int j = 0; j < 4; ++j) Up[i][j] = Gp[i][j];
       }
     }
+    // Only the lanes that take the carried half (the tail lanes of a forward
+    // run, the head lanes of a backward one) read or write their slots.
     if (tail_step && cur.fwd) {
-      write_carry(Up, ru);
+      if (use_carry) write_carry(Up, ru);
     } else {
       if (tid == 0) s_flag[0] = 0;
       {
-        const float2 cm2 = s_cmax[tid];
+        const float2 cm2 = use_carry ? s_cmax[tid] : make_float2(0.0f, 0.0f);
         rp[0] = rg[0];
         rp[1] = rg[1];
         rp[kTile] = use_carry ? cm2.x : ru[0];
@@ -1631,17 +1633,20 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
       // this step's d_up replaces it straight away.
       {
         uint32_t W[kRows][4];
-        read_carry(W);
+        if (use_carry) {
+          read_carry(W);
+        } else {
 #pragma unroll
-        for (int i = 0; i < kRows; ++i)
+          for (int i = 0; i < kRows; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) W[i][j] = use_carry ? W[i][j] : Up[i][j];
+            for (int j = 0; j < 4; ++j) W[i][j] = Up[i][j];
+        }
         const uint32_t off_w = window_offset(wvalid, w);
         if (__builtin_amdgcn_ballot_w64(iw[0] == __builtin_huge_valf() || iw[1] == __builtin_huge_valf()) != 0)
           store_window_codes<F, true>(W, iw, gq_buf, off_w, first, shifted, p);
         else
           store_window_codes<F, false>(W, iw, gq_buf, off_w, first, shifted, p);
-        write_carry(Up, ru);
+        if (use_carry) write_carry(Up, ru);
       }
       if (!tail_step) {
         stage_y_codes<F, false>(Yp, iy, s_yqt, p, q);
