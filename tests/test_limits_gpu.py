@@ -124,10 +124,11 @@ def test_gemm_at_the_k_limit():
 
 
 def test_straddling_kernel_at_the_channel_limit():
-    # H = 2^22 - 8 with group 128: r = 120, so the windows run one block past
-    # H (H + r > 2^22) and a window lane's offset in x comes close to 2^31.
-    # The first 256 and the last 256 channels of the row are checked: the
-    # straddling group holds d_gate's last 120 channels and d_up's first 8.
+    # H = 2^22 - 8 with group 128: r = 120, so 32,768 blocks per token block
+    # are walked in runs of four, a last window (the final r channels of d_up,
+    # r > 64) follows the last block, and a lane's offset in x comes close to
+    # 2^31.  The first 256 and the last 256 channels of the row are checked:
+    # the straddling group holds d_gate's last 120 channels and d_up's first 8.
     T, H, G = 128, (1 << 22) - 8, 128
     print("case straddle T=128 H=2^22-8", flush=True)
     x, dy = _inputs(T, H, 5)
