@@ -82,9 +82,10 @@ enum siluquant_status {
  *   SILUQUANT_OK), T <= 2^23, H <= 2^22.  y_q_t is written with 16-byte
  *   stores when T % 16 == 0; other T work, with narrower stores.  The results
  *   do not depend on the kernel that runs: H a multiple of `group` takes the
- *   tiled kernel; other multiples of 8 a second tiled kernel with two work
- *   items per tile; H not a multiple of 8 (rows then start off 16 bytes) a
- *   slower path with 2-byte loads.
+ *   tiled kernel; other multiples of 8 above 128 a tiled kernel that walks
+ *   runs of channel blocks and hands each block's d_up to the shifted d_up
+ *   groups (below 128, two work items per tile); H not a multiple of 8 (rows
+ *   then start off 16 bytes) a slower path with 2-byte loads.
  * Ownership: the caller allocates and owns every buffer; the library keeps no
  *   pointer after the call returns.  Buffers must not overlap.
  * Asynchrony: the work is enqueued on `stream` and the call returns without
