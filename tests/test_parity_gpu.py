@@ -356,6 +356,33 @@ def test_straddling_groups_edge_values(group):
     check_group(x, dy, group, "straddle tiny fp8 group=%d" % group, fp8=True)
 
 
+# Shapes drawn at random (a fixed seed, so the list is the same every run):
+# T and H anywhere up to 2500, every group size, both code formats; H picks
+# up every residue class the kernels branch on (multiple of the group, of 8
+# only, odd), and T ragged or not.
+def _random_shapes(n=18, seed=20260):
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n):
+        group = int(rng.choice([32, 64, 128]))
+        kind = i % 3
+        H = int(rng.integers(1, 2500))
+        if kind == 0:
+            H = max(group, H - H % group)  # a multiple of the group
+        elif kind == 1:
+            H = max(8, H - H % 8)          # a multiple of 8
+        T = int(rng.integers(1, 2500))
+        shapes.append((T, H, group, bool(i % 2)))
+    return shapes
+
+
+@pytest.mark.parametrize("T,H,group,fp8", _random_shapes())
+def test_random_shapes(T, H, group, fp8):
+    print("case random", T, H, group, fp8, flush=True)
+    x, dy = random_inputs(T, H, device=DEV, seed=T * 7919 + H)
+    check_group(x, dy, group, "random T=%d H=%d group=%d fp8=%d" % (T, H, group, fp8), fp8=fp8)
+
+
 def test_hip_graph_capture_and_replay():
     # Each entry point is one kernel launch on the caller's stream, so once the
     # sigmoid table exists the calls can be captured in a HIP graph.  The graph
