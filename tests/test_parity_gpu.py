@@ -205,11 +205,13 @@ def test_ragged_token_counts(T, H):
     assert sum(rep.values()) == 0
 
 
-@pytest.mark.parametrize("T,H", [(32768, 4224), (8192 + 128, 4224)])
+@pytest.mark.parametrize("T,H", [(32768, 4224), (8192 + 128, 4224), (8192, 8192), (4096, 2048)])
 def test_tile_walk_orders(T, H):
     # rows of 33 tiles (longer than an XCD's share of 256 workgroups) over
     # 256 tile rows: the XCDs take interleaved tile rows with their own column
-    # phase; over 65 tile rows (not a multiple of 8) only the phase applies
+    # phase; over 65 tile rows (not a multiple of 8) only the phase applies;
+    # rows of 64 and 16 tiles that deal out evenly: runs of 4 tiles (at 256
+    # workgroups; other device sizes take the walks above)
     print("case walk T=%d H=%d" % (T, H), flush=True)
     x, dy = random_inputs(T, H, device=DEV, seed=T + H)
     assert sum(check(x, dy, "walk T=%d H=%d" % (T, H)).values()) == 0
