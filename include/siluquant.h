@@ -85,7 +85,9 @@ enum siluquant_status {
  *   tiled kernel; other multiples of 8 above 128 a tiled kernel that walks
  *   runs of channel blocks and hands each block's d_up to the shifted d_up
  *   groups (below 128, two work items per tile); H not a multiple of 8 (rows
- *   then start off 16 bytes) a slower path with 2-byte loads.
+ *   then start off 16 bytes) a tiled kernel over 128-position tiles of the
+ *   2H-long row [d_gate | d_up] that loads aligned 16-byte pieces and shifts
+ *   them across lanes (slower: d_up is computed in tiles of its own).
  * Ownership: the caller allocates and owns every buffer; the library keeps no
  *   pointer after the call returns.  Buffers must not overlap.
  * Asynchrony: the work is enqueued on `stream` and the call returns without

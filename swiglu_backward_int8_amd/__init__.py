@@ -110,7 +110,7 @@ def silu_dot_fwd_bwd_quant_fuse(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_
     and of y^T (groups of group_size tokens) into the given output tensors.
     group_size is 128 (the default), 64 or 32; any H: when it is not a multiple
     of group_size one group straddles d_gate and d_up, and when it is not a
-    multiple of 8 a slower path with 2-byte loads runs.
+    multiple of 8 (rows off 16 bytes) a slower tiled path runs.
     Enqueued on the current stream of x's device; returns None."""
     _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size, fp8=False)
 

@@ -1926,6 +1926,446 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// H not a multiple of 8 (silu_quant_bwd_narrow_kernel): rows of x, grad_y and
+// grad_input_q start at any even byte offset, so no row piece is 16-byte
+// aligned in general.  The pass runs over position tiles of the 2H-long row
+// [d_gate | d_up]: tile hb holds positions 128 hb + [0, 128) of 128 tokens,
+// so every row group lies in one tile (the group divides 128).  With
+// nA = floor(H / 128) and r = H - 128 nA (1 .. 127):
+//   * kind 0, hb < nA: d_gate at channels 128 hb + [0, 128), and y^T for the
+//     same channels (both from that tile's gate, up and grad_y);
+//   * kind 1, hb == nA: the tile that holds position H: d_gate's last r
+//     channels, then d_up's first 128 - r; y^T for the last r channels.
+//     Its values are read two bytes at a time (one such tile per token block);
+//   * kind 2, hb > nA: d_up at channels 128 hb - H + [0, 128), from gate and
+//     grad_y alone.
+// Loads: lane p of a row reads the aligned 16 bytes at or below its eight
+// channels, takes the next aligned 16 bytes from lane p + 1 (lane 15 from
+// dwords that lanes 0..3 read just past the row's 16 pieces) and shifts the
+// pair down by the row's offset within 16 bytes.  A kind-2 tile re-reads
+// gate and grad_y lines a kind-0 tile has just read: each token block's tiles
+// are walked in the order 0, nA, 1, nA + 1, 2, nA + 2, ... (D_k, channels
+// 128 (k + 1) - r .., right after the channel tile k + 1 it overlaps), and
+// the loads are plain, so that those lines are still in L2.
+// Stores: lane pairs put a row's 16 code bytes together (as in the aligned
+// kernel), take the previous pair's 16 bytes (row_ror:2) and shift the two
+// into the aligned 16-byte piece of the output row that the pair covers; at
+// both ends of a tile's row only the tile's own bytes are written (2- and
+// 4-byte stores), so neighbouring tiles never write the same byte.
+
+// Bytes [s, s + 16) of the 32 bytes lo | hi (lo first), s in [0, 16).
+// (Plain values, not arrays: a select between two array elements can become
+// a select between their addresses, which keeps the array in memory.)
+__device__ __forceinline__ uint4 funnel16(uint4 lo, uint4 hi, uint32_t s) {
+  const bool two = (s & 8u) != 0, one = (s & 4u) != 0;
+  // dwords s/4 .. s/4 + 4 of lo | hi: first down by 2 if s & 8, then by 1 if s & 4
+  const uint32_t q0 = two ? lo.z : lo.x, q1 = two ? lo.w : lo.y, q2 = two ? hi.x : lo.z, q3 = two ? hi.y : lo.w,
+                 q4 = two ? hi.z : hi.x, q5 = two ? hi.w : hi.y;
+  const uint32_t r0 = one ? q1 : q0, r1 = one ? q2 : q1, r2 = one ? q3 : q2, r3 = one ? q4 : q3,
+                 r4 = one ? q5 : q4;
+  const uint32_t b = s & 3u;
+  return make_uint4(__builtin_amdgcn_alignbyte(r1, r0, b), __builtin_amdgcn_alignbyte(r2, r1, b),
+                    __builtin_amdgcn_alignbyte(r3, r2, b), __builtin_amdgcn_alignbyte(r4, r3, b));
+}
+
+// row_ror:n (kCtrl = 0x120 + n): lane p of each 16-lane row takes the value of
+// lane p - n (mod 16).
+template <int kCtrl>
+__device__ __forceinline__ uint32_t row_ror(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kCtrl, 0xf, 0xf, false);
+}
+
+// What a lane reads for one row of one tensor: the aligned 16 bytes at or
+// below the row's byte `at` plus 16 p, and (lanes 0..3) dword p of the
+// aligned 16 bytes 256 bytes further, which lane 15 needs.
+struct NarrowRaw {
+  uint4 g[kRows], u[kRows], d[kRows];
+  uint32_t eg[kRows], eu[kRows], ed[kRows];
+};
+
+__device__ __forceinline__ void load_piece(__amdgpu_buffer_rsrc_t buf, uint32_t at, int p, uint4& v, uint32_t& e) {
+  const uint32_t a = at & ~15u;
+  v = load_buf<0>(buf, a + 16u * (uint32_t)p);
+  e = p < 4 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(buf, a + 256u + 4u * (uint32_t)p, 0, 0) : 0u;
+}
+
+// The eight bf16 values at the row's byte `at` plus 16 p.  Every lane of the
+// wave takes part (the moves read the other lanes of its row).
+__device__ __forceinline__ uint4 piece_values(uint4 v, uint32_t e, uint32_t at, int p) {
+  const bool last = p == 15;
+  const uint32_t n0 = row_ror<0x12F>(v.x), f0 = row_ror<0x12F>(e);  // from lane p + 1 / lane 15 from lane 0
+  const uint32_t n1 = row_ror<0x12F>(v.y), f1 = row_ror<0x12E>(e);  // lane 15 from lane 1
+  const uint32_t n2 = row_ror<0x12F>(v.z), f2 = row_ror<0x12D>(e);  // lane 15 from lane 2
+  const uint32_t n3 = row_ror<0x12F>(v.w), f3 = row_ror<0x12C>(e);  // lane 15 from lane 3
+  const uint4 next = make_uint4(last ? f0 : n0, last ? f1 : n1, last ? f2 : n2, last ? f3 : n3);
+  return funnel16(v, next, at & 15u);
+}
+
+// Bytes [lo, hi) of a 16-byte piece stored at `off` (lo and hi even): the
+// whole piece in one store, else 4- and 2-byte parts.
+__device__ __forceinline__ void store_range16(__amdgpu_buffer_rsrc_t buf, uint32_t off, uint4 v, int lo, int hi) {
+  if (lo == 0 && hi == 16) {
+    __builtin_amdgcn_raw_buffer_store_b128((u32x4){v.x, v.y, v.z, v.w}, buf, off, 0, 0);
+    return;
+  }
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int b0 = 4 * k;
+    if (b0 >= lo && b0 + 4 <= hi) {
+      __builtin_amdgcn_raw_buffer_store_b32(w[k], buf, off + b0, 0, 0);
+    } else {
+      if (b0 >= lo && b0 < hi)
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[k] & 0xffffu), buf, off + b0, 0, 0);
+      if (b0 + 2 >= lo && b0 + 2 < hi)
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[k] >> 16), buf, off + b0 + 2, 0, 0);
+    }
+  }
+}
+
+struct NarrowItem {
+  int kind;     // 0: d_gate and y^T, 1: the tile holding position H, 2: d_up
+  int rows;     // tokens that exist (< 128 only in the last token block)
+  int len;      // positions of the tile that exist (< 128 only in the row's last tile)
+  uint32_t c0;  // first channel (kind 0: 128 hb; kind 2: 128 hb - H; kind 1: 128 hb)
+  int64_t t0, pos0;
+};
+
+// Item -> tile: token block item / nP; within it the position tiles in the
+// order 0, nA, 1, nA + 1, 2, nA + 2, ..., then the remaining d_up tiles.
+__device__ __forceinline__ NarrowItem narrow_item(int item, int nA, int nP, int64_t T, int64_t H) {
+  const int tb = item / nP, j = item - tb * nP;
+  int hb;
+  if (nA == 0 || j >= 2 * nA)
+    hb = j;
+  else if (j == 0)
+    hb = 0;
+  else if (j == 1)
+    hb = nA;
+  else
+    hb = (j & 1) == 0 ? j / 2 : nA + (j - 1) / 2;
+  NarrowItem it;
+  it.kind = hb < nA ? 0 : hb == nA ? 1 : 2;
+  it.t0 = (int64_t)tb * kTile;
+  it.pos0 = (int64_t)hb * kTile;
+  it.rows = T - it.t0 < kTile ? (int)(T - it.t0) : kTile;
+  it.len = 2 * H - it.pos0 < kTile ? (int)(2 * H - it.pos0) : kTile;
+  it.c0 = (uint32_t)(it.kind == 2 ? it.pos0 - H : it.pos0);
+  return it;
+}
+
+// Word mask of the halves (elements 2k, 2k + 1) below n.
+__device__ __forceinline__ uint32_t halves_below(int k, int n) {
+  return (2 * k < n ? 0x0000ffffu : 0u) | (2 * k + 1 < n ? 0xffff0000u : 0u);
+}
+
+template <Fmt F, int kG>
+__global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void silu_quant_bwd_narrow_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ grad_y, int8_t* __restrict__ grad_input_q,
+    float* __restrict__ grad_input_s, int8_t* __restrict__ y_q_t, float* __restrict__ y_s_t, int64_t T, int64_t H,
+    int nA, int nP, int items) {
+  static_assert(kG == 32 || kG == 64 || kG == 128, "group sizes that divide the tile");
+  constexpr int kSub = kTile / kG;
+  constexpr int kRowGroups = kTile * kSub, kColGroups = kTile * kSub;
+  constexpr int kLanesPerRowGroup = kG / 8;
+  constexpr int kPairsPerColGroup = kG / kRows;
+  static_assert(kRowGroups + kColGroups <= kInvFloats, "inverse slots");
+
+  __shared__ __align__(16) float lds[kLdsFloats];
+  __shared__ __align__(16) float2 s_qtab[128];
+  float* s_tab = lds;
+  float* s_rowpart = lds + kSigEntries;
+  float* s_colpart = s_rowpart + kRowPartFloats;
+  float* s_inv = s_colpart + kColPartFloats;
+  char* s_yqt = reinterpret_cast<char*>(s_rowpart);
+  int* s_flag = reinterpret_cast<int*>(s_inv + kInvFloats);
+
+  const int tid = threadIdx.x;
+  const int p = tid & 15;
+  const int q = tid >> 4;
+  const bool odd = p & 1;
+
+  const uint32_t H2 = (uint32_t)(2 * H), H4 = (uint32_t)(4 * H);
+  const int64_t row_groups = (2 * H + kG - 1) / kG, col_groups = (T + kG - 1) / kG;
+  const int yq_align = (T & 15) == 0 ? 16 : (T & 3) == 0 ? 4 : 1;
+  // the lane's rows (tokens kRows q + i of a tile), byte offsets from the
+  // tile's first row of x and grad_y
+  uint32_t xrow[kRows], dyrow[kRows];
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    xrow[i] = (uint32_t)(kRows * q + i) * H4;
+    dyrow[i] = (uint32_t)(kRows * q + i) * H2;
+  }
+  // the row and pair whose 16 code bytes this lane stores
+  const int rho = kRows * q + (p & 1), pair = p >> 1;
+  const uint32_t gq_row = (uint32_t)rho * H2;
+  constexpr int kOutSteps = kTile * kTile / 16 / kThreads;
+  uint32_t lane_yq[kOutSteps];
+#pragma unroll
+  for (int step = 0; step < kOutSteps; ++step) {
+    const int id = tid + step * kThreads;
+    lane_yq[step] = (uint32_t)((id >> 3) * T + 16 * (id & 7));
+  }
+  const int sub_row = p / kLanesPerRowGroup, sub_col = q / kPairsPerColGroup;
+
+  // each XCD walks a contiguous eighth of the items
+  int item, end, stride;
+  if ((gridDim.x & 7) == 0) {
+    const int per_xcd = gridDim.x >> 3, xcd = blockIdx.x & 7;
+    const int begin = (int)(((int64_t)items * xcd) >> 3);
+    end = (int)(((int64_t)items * (xcd + 1)) >> 3);
+    item = begin + (int)(blockIdx.x >> 3);
+    stride = per_xcd;
+  } else {
+    item = blockIdx.x;
+    end = items;
+    stride = gridDim.x;
+  }
+
+  const char* xb = reinterpret_cast<const char*>(x);
+  const char* dyb = reinterpret_cast<const char*>(grad_y);
+  // tile bases and buffers: a token block's rows of x and grad_y (rounded up
+  // to 16 bytes, so that an aligned piece holding the last bytes is in range)
+  auto x_buf = [&](const NarrowItem& it) {
+    return buffer_of(const_cast<char*>(xb + it.t0 * (int64_t)H4), ((uint32_t)it.rows * H4 + 15u) & ~15u);
+  };
+  auto dy_buf = [&](const NarrowItem& it) {
+    return buffer_of(const_cast<char*>(dyb + it.t0 * (int64_t)H2), ((uint32_t)it.rows * H2 + 15u) & ~15u);
+  };
+  // aligned pieces of an item of kind 0 or 2 (nothing for kind 1)
+  auto load_raw = [&](NarrowRaw& raw, const NarrowItem& it) {
+    const __amdgpu_buffer_rsrc_t xbuf = x_buf(it), dbuf = dy_buf(it);
+    const uint32_t c2 = 2u * it.c0;
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      raw.g[i] = raw.u[i] = raw.d[i] = make_uint4(0, 0, 0, 0);
+      raw.eg[i] = raw.eu[i] = raw.ed[i] = 0u;
+      if (it.kind != 1 && kRows * q + i < it.rows) {
+        load_piece(xbuf, xrow[i] + c2, p, raw.g[i], raw.eg[i]);
+        load_piece(dbuf, dyrow[i] + c2, p, raw.d[i], raw.ed[i]);
+        if (it.kind == 0) load_piece(xbuf, xrow[i] + H2 + c2, p, raw.u[i], raw.eu[i]);
+      }
+    }
+  };
+
+  NarrowRaw raw, raw_next;
+  NarrowItem cur = narrow_item(item < end ? item : 0, nA, nP, T, H);
+  if (item < end) load_raw(raw, cur);
+  {
+    const float4* src = reinterpret_cast<const float4*>(g_sigma_tab);
+    float4* dst = reinterpret_cast<float4*>(s_tab);
+    for (int i = tid; i < kSigEntries / 4; i += kThreads) dst[i] = src[i];
+    fill_scale_table(s_qtab, tid);
+  }
+  __syncthreads();
+
+  while (item < end) {
+    // ---- the tile's values: gate, up and grad_y per lane row ---------------
+    // (taken from the raw pieces before the next tile's loads are issued, so
+    // that the two sets of raw registers are never live together)
+    TileIn in;
+    const uint32_t c2 = 2u * cur.c0;
+    if (cur.kind != 1) {
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) {
+        in.g[i] = piece_values(raw.g[i], raw.eg[i], xrow[i] + c2, p);
+        in.d[i] = piece_values(raw.d[i], raw.ed[i], dyrow[i] + c2, p);
+      }
+      if (cur.kind == 0) {
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) in.u[i] = piece_values(raw.u[i], raw.eu[i], xrow[i] + H2 + c2, p);
+      } else {
+        // d_up = grad_y * silu(gate) is the product y = silu(gate) * u with
+        // grad_y in place of up (the multiplication commutes exactly)
+        if (cur.len < kTile) {
+          // positions past 2H read as zeros
+          const int n = cur.len - 8 * p;
+#pragma unroll
+          for (int i = 0; i < kRows; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const uint32_t mk = halves_below(k, n);
+              (&in.g[i].x)[k] &= mk;
+              (&in.d[i].x)[k] &= mk;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) in.u[i] = in.d[i];
+      }
+    } else {
+      // position pos of the row: d_gate at channel pos below H, else d_up at
+      // channel pos - H (grad_y in the up slot, as for kind 2); two-byte loads
+      const __amdgpu_buffer_rsrc_t xbuf = x_buf(cur), dbuf = dy_buf(cur);
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) {
+        uint32_t gw[4], uw[4], dw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) gw[k] = uw[k] = dw[k] = 0u;
+        if (kRows * q + i < cur.rows) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int64_t pos = cur.pos0 + 8 * p + e;
+            if (pos < 2 * H) {
+              const uint32_t ch = (uint32_t)(pos < H ? pos : pos - H);
+              const uint32_t gv = __builtin_amdgcn_raw_buffer_load_b16(xbuf, xrow[i] + 2u * ch, 0, 0);
+              const uint32_t dv = __builtin_amdgcn_raw_buffer_load_b16(dbuf, dyrow[i] + 2u * ch, 0, 0);
+              const uint32_t uv = pos < H ? __builtin_amdgcn_raw_buffer_load_b16(xbuf, xrow[i] + H2 + 2u * ch, 0, 0)
+                                          : dv;
+              const int sh = 16 * (e & 1);
+              gw[e >> 1] |= gv << sh;
+              uw[e >> 1] |= uv << sh;
+              dw[e >> 1] |= dv << sh;
+            }
+          }
+        }
+        in.g[i] = make_uint4(gw[0], gw[1], gw[2], gw[3]);
+        in.u[i] = make_uint4(uw[0], uw[1], uw[2], uw[3]);
+        in.d[i] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+      }
+    }
+
+    const int next = item + stride;
+    const NarrowItem nxt = narrow_item(next < end ? next : item, nA, nP, T, H);
+    if (next < end) load_raw(raw_next, nxt);
+
+    // ---- elementwise: the row values V, y, partial maxima -----------------
+    // One path for every kind: y = silu * u is d_up where u holds grad_y, and
+    // the lane's positions below H take d_gate.
+    uint32_t Yp[kRows][4], Vp[kRows][4];
+    float rv[kRows], cm[8];
+    {
+      uint32_t Gp[kRows][4], Up[kRows][4];
+      float rg[kRows], ru[kRows];
+      elementwise<false>(in, s_tab, Yp, Gp, Up, rg, ru, cm);
+      const int n = cur.kind == 0 ? 8 : (int)(H - cur.pos0) - 8 * p;  // the lane's positions below H
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) {
+        float m = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t mk = halves_below(k, n);
+          Vp[i][k] = (Gp[i][k] & mk) | (Yp[i][k] & ~mk);
+          m = amax3(m, bf16_lo(Vp[i][k]), bf16_hi(Vp[i][k]));
+        }
+        rv[i] = cur.kind == 0 ? rg[i] : m;
+      }
+    }
+    if (tid == 0) s_flag[0] = 0;
+    const bool has_y = cur.kind != 2;
+    {
+      float* rp = s_rowpart + p * kRowPartStride + kRows * q;
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) rp[i] = rv[i];
+      if (has_y) {
+        float4* cp = reinterpret_cast<float4*>(s_colpart + q * kTile + 4 * p);
+        cp[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
+        cp[16] = make_float4(cm[4], cm[5], cm[6], cm[7]);
+      }
+    }
+    __syncthreads();
+
+    // ---- one thread per group ----------------------------------------------
+    const int cols = has_y ? (H - cur.pos0 < kTile ? (int)(H - cur.pos0) : kTile) : 0;  // channels of y^T
+    const int groups = kRowGroups + (has_y ? kColGroups : 0);
+    for (int id = tid; id < groups; id += kThreads) {
+      float m = 0.0f;
+      if (id < kRowGroups) {
+        const int row = id & (kTile - 1), sub = id >> 7;
+#pragma unroll
+        for (int pp = 0; pp < kLanesPerRowGroup; ++pp)
+          m = fmaxf(m, s_rowpart[(sub * kLanesPerRowGroup + pp) * kRowPartStride + row]);
+      } else {
+        const int cid = id - kRowGroups, c = cid & (kTile - 1), sub = cid >> 7;
+        const int idx = ((c >> 2) & 1) * 64 + (c >> 3) * 4 + (c & 3);
+#pragma unroll 8
+        for (int qq = 0; qq < kPairsPerColGroup; ++qq)
+          m = fmaxf(m, s_colpart[(sub * kPairsPerColGroup + qq) * kTile + idx]);
+      }
+      float scale, inv;
+      if constexpr (F == Fmt::kInt8) {
+        scale_and_inverse(m, s_qtab, scale, inv);
+      } else {
+        scale = group_scale<F>(m);
+        inv = 1.0f / scale;
+      }
+      s_inv[id] = inv;
+      if (inv == __builtin_huge_valf()) s_flag[0] = 1;
+      if (id < kRowGroups) {
+        const int row = id & (kTile - 1), sub = id >> 7;
+        // groups past the row's 2H positions and rows past T do not exist
+        if (row < cur.rows && sub * kG < cur.len)
+          grad_input_s[(cur.t0 + row) * row_groups + cur.pos0 / kG + sub] = scale;
+      } else {
+        const int cid = id - kRowGroups, c = cid & (kTile - 1), sub = cid >> 7;
+        if (c < cols && sub * kG < cur.rows) y_s_t[(cur.pos0 + c) * col_groups + cur.t0 / kG + sub] = scale;
+      }
+    }
+    __syncthreads();
+
+    // ---- codes: the row's pieces straight out, y via the LDS transpose -----
+    {
+      float iv[kRows], iy[8];
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) iv[i] = s_inv[sub_row * kTile + kRows * q + i];
+      if (has_y) {
+        const float* inv_col = s_inv + kRowGroups + sub_col * kTile + 8 * p;
+        const float4 a = *reinterpret_cast<const float4*>(inv_col);
+        const float4 b = *reinterpret_cast<const float4*>(inv_col + 4);
+        iy[0] = a.x, iy[1] = a.y, iy[2] = a.z, iy[3] = a.w, iy[4] = b.x, iy[5] = b.y, iy[6] = b.z, iy[7] = b.w;
+      }
+      const bool safe = s_flag[0] != 0;  // some group's inverse overflowed: the clamped rule
+      uint2 c[kRows];
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) c[i] = safe ? codes8<true, F>(Vp[i], iv[i]) : codes8<false, F>(Vp[i], iv[i]);
+      const uint4 piece = pair_rows16(c[0], c[1], odd);
+      const uint4 prev = make_uint4(row_ror<0x122>(piece.x), row_ror<0x122>(piece.y), row_ror<0x122>(piece.z),
+                                    row_ror<0x122>(piece.w));
+      if (rho < cur.rows) {
+        const __amdgpu_buffer_rsrc_t gq_buf = buffer_of(grad_input_q + cur.t0 * (int64_t)H2, (uint32_t)cur.rows * H2);
+        const uint32_t S = gq_row + (uint32_t)cur.pos0, m = S & 15u, a0 = S - m;
+        const int len = cur.len, mi = (int)m;
+        const uint4 chunk = m == 0 ? piece : funnel16(prev, piece, 16u - m);
+        const int lo = pair == 0 ? mi : 0, hi = min(16, len + mi - 16 * pair);
+        if (hi > lo) store_range16(gq_buf, a0 + 16u * pair, chunk, lo, hi);
+        if (pair == 7 && m != 0) {
+          const int hi8 = min(16, len + mi - 128);
+          if (hi8 > 0) store_range16(gq_buf, a0 + 128u, funnel16(piece, make_uint4(0, 0, 0, 0), 16u - m), 0, hi8);
+        }
+      }
+      if (has_y) {
+        if (safe)
+          stage_y_codes<F, true>(Yp, iy, s_yqt, p, q);
+        else
+          stage_y_codes<F, false>(Yp, iy, s_yqt, p, q);
+      }
+      __syncthreads();
+    }
+
+    // ---- transposed codes out ----------------------------------------------
+    if (has_y) {
+      const __amdgpu_buffer_rsrc_t yq_buf =
+          buffer_of(y_q_t + (cur.pos0 * T + cur.t0), (uint32_t)(cols * T));  // rows past H lie past the records
+#pragma unroll
+      for (int step = 0; step < kOutSteps; ++step) {
+        const int id = tid + step * kThreads;
+        const int h = id >> 3;
+        const int phys = (id & 7) ^ ((h >> 3) & 7);
+        const uint4 v = *reinterpret_cast<const uint4*>(s_yqt + h * kTile + phys * 16);
+        if (cur.rows == kTile && yq_align == 16)
+          store_yq(yq_buf, lane_yq[step], v);
+        else
+          store_yq_piece(yq_buf, lane_yq[step], v, min(16, max(0, cur.rows - 16 * (id & 7))), yq_align);
+      }
+    }
+
+    raw = raw_next;
+    item = next;
+    cur = nxt;
+    if (item < end) __syncthreads();  // the transpose buffer is read before it is rewritten
+  }
+}
+
 // Diagnostics: the fused kernel's own sigmoid lookup and elementwise helpers,
 // run on their own so tests can compare them bit for bit.  Element i takes the
 // low half of the packed index path when i is even and the high half when odd,
@@ -1937,11 +2377,10 @@ __device__ __forceinline__ float sigma_of(uint32_t gb, int64_t i) {
 }
 
 // ---------------------------------------------------------------------------
-// H not a multiple of 8: rows start off 16 bytes, so the tiled kernels' wide
-// loads do not apply.  A plain path with the same arithmetic: 2-byte loads,
-// byte stores, the sigmoid from the device table, a wave per 128 positions of
-// a row and a lane per channel for the token groups.  Grid-stride loops cover
-// any size.
+// The forward quantiser with H not a multiple of 8: rows start off 16 bytes,
+// so the tiled kernel's wide loads do not apply.  A plain path with the same
+// arithmetic: 2-byte loads, byte stores, the sigmoid from the device table, a
+// wave per 128 positions of a row.  A grid-stride loop covers any size.
 
 // One code of a value with inverse scale inv (the low byte).
 template <Fmt F, bool kSafe>
@@ -1977,106 +2416,6 @@ __device__ __forceinline__ void narrow_groups(const float (&a)[2], float (&scale
     scale[k] = group_scale<F>(m[k]);
     const int64_t c = c0 + lane + 64 * k;
     if ((kG < 128 || k == 0) && lane % (kG < 64 ? kG : 64) == 0 && c < n_row) scale_row[c / kG] = scale[k];
-  }
-}
-
-// Row groups of the 2H-long row [d_gate | d_up].
-template <Fmt F, int kG>
-__global__ __launch_bounds__(256) void silu_quant_rows_narrow_kernel(const uint16_t* __restrict__ x,
-                                                                     const uint16_t* __restrict__ grad_y,
-                                                                     uint8_t* __restrict__ grad_input_q,
-                                                                     float* __restrict__ grad_input_s, int64_t T,
-                                                                     int64_t H) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row_groups = (2 * H + kG - 1) / kG, units = (2 * H + 127) / 128;
-  const int64_t waves = (int64_t)gridDim.x * 4;
-  for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < T * units; w += waves) {
-    const int64_t t = w / units, c0 = (w - t * units) * 128;
-    float v[2], a[2], scale[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int64_t c = c0 + lane + 64 * k, h = c < H ? c : c - H;
-      v[k] = a[k] = 0.0f;
-      if (c < 2 * H) {
-        const uint32_t gb = x[t * 2 * H + h];
-        float y, dg, du;
-        pair_f32(sigma_of(gb, 0), bf16_lo(gb), bf16_lo(x[t * 2 * H + H + h]), bf16_lo(grad_y[t * H + h]), y, dg,
-                 du);
-        const float val = c < H ? dg : du;
-        a[k] = fabsf(val);
-        v[k] = bf16_lo(pack_bf16(val, 0.0f));
-      }
-    }
-    narrow_groups<F, kG>(a, scale, grad_input_s + t * row_groups, c0, 2 * H, lane);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int64_t c = c0 + lane + 64 * k;
-      const float inv = 1.0f / scale[k];
-      if (c < 2 * H)
-        grad_input_q[t * 2 * H + c] =
-            (uint8_t)(inv == __builtin_huge_valf() ? code1<F, true>(v[k], inv) : code1<F, false>(v[k], inv));
-    }
-  }
-}
-
-// Token groups of y^T: lane l of a 64-thread workgroup takes channel
-// 64 b + l of group g for work item (b, g); the group's kG values of y stay
-// in registers between the maximum and the codes.
-template <Fmt F, int kG>
-__global__ __launch_bounds__(64) void silu_quant_cols_narrow_kernel(const uint16_t* __restrict__ x,
-                                                                    uint8_t* __restrict__ y_q_t,
-                                                                    float* __restrict__ y_s_t, int64_t T,
-                                                                    int64_t H) {
-  const int64_t col_groups = (T + kG - 1) / kG, hblocks = (H + 63) / 64;
-  for (int64_t item = blockIdx.x; item < col_groups * hblocks; item += gridDim.x) {
-    const int64_t g = item / hblocks, h = (item - g * hblocks) * 64 + threadIdx.x, t0 = g * kG;
-    if (h >= H) continue;
-    const int n = T - t0 < kG ? (int)(T - t0) : kG;
-    uint32_t yb[kG / 2];
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kG; ++i) {
-      float yv = 0.0f;
-      if (i < n) {
-        const uint32_t gb = x[(t0 + i) * 2 * H + h];
-        const float silu = bf16_lo(gb) * sigma_of(gb, 0);
-        yv = silu * bf16_lo(x[(t0 + i) * 2 * H + H + h]);
-        m = fmaxf(m, fabsf(yv));
-      }
-      const uint32_t b = pack_bf16(yv, 0.0f) & 0xffffu;
-      yb[i / 2] = (i & 1) ? (yb[i / 2] | (b << 16)) : b;
-    }
-    const float scale = group_scale<F>(m);
-    const float inv = 1.0f / scale;
-    const bool safe = inv == __builtin_huge_valf();
-    uint8_t* row = y_q_t + h * T + t0;
-    if ((T & 15) == 0 && n == kG) {
-      // rows of y^T start on 16 bytes: the lane's kG codes as 16-byte pieces
-#pragma unroll
-      for (int q = 0; q < kG / 16; ++q) {
-        uint32_t wd[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wd[e] = 0;
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            const int i = 16 * q + 4 * e + bb;
-            const float yv = (i & 1) ? bf16_hi(yb[i / 2]) : bf16_lo(yb[i / 2]);
-            wd[e] |= (safe ? code1<F, true>(yv, inv) : code1<F, false>(yv, inv)) << (8 * bb);
-          }
-        }
-        *reinterpret_cast<uint4*>(row + 16 * q) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kG; ++i) {
-        if (i < n) {
-          const float yv = (i & 1) ? bf16_hi(yb[i / 2]) : bf16_lo(yb[i / 2]);
-          row[i] = (uint8_t)(safe ? code1<F, true>(yv, inv) : code1<F, false>(yv, inv));
-        }
-      }
-    }
-    y_s_t[h * col_groups + g] = scale;
   }
 }
 
@@ -2207,21 +2546,17 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
   const uint16_t* xs = static_cast<const uint16_t*>(x);
   const uint16_t* dys = static_cast<const uint16_t*>(grad_y);
   if (H % 8 != 0) {
-    // rows off 16 bytes: the plain path, a kernel per quantisation axis
-    const int64_t row_waves = T * ((2 * H + 127) / 128);
-    const int64_t col_items = ((T + group - 1) / group) * ((H + 63) / 64);
-    const int64_t rows_grid = std::min<int64_t>((row_waves + 3) / 4, (int64_t)cus * 16);
-    const int64_t cols_grid = std::min<int64_t>(col_items, (int64_t)cus * 64);
-    auto rows = group == 128 ? silu_quant_rows_narrow_kernel<F, 128>
-                : group == 64 ? silu_quant_rows_narrow_kernel<F, 64>
-                              : silu_quant_rows_narrow_kernel<F, 32>;
-    hipLaunchKernelGGL(rows, dim3((unsigned)rows_grid), dim3(256), 0, s, xs, dys,
-                       static_cast<uint8_t*>(grad_input_q), grad_input_s, T, H);
-    auto cols = group == 128 ? silu_quant_cols_narrow_kernel<F, 128>
-                : group == 64 ? silu_quant_cols_narrow_kernel<F, 64>
-                              : silu_quant_cols_narrow_kernel<F, 32>;
-    hipLaunchKernelGGL(cols, dim3((unsigned)cols_grid), dim3(64), 0, s, xs, static_cast<uint8_t*>(y_q_t), y_s_t, T,
-                       H);
+    // rows off 16 bytes: position tiles of [d_gate | d_up], 2 per 128 channels
+    const int nA = (int)(H / kTile), nP = (int)((2 * H + kTile - 1) / kTile);
+    const int64_t items = tiles_t * nP;  // at most 2 * tiles_t * tiles_h64, checked above
+    int ngrid = cus * kWorkgroupsPerCU;
+    ngrid = ngrid >= 8 ? ngrid - ngrid % 8 : ngrid;
+    if (items < ngrid) ngrid = (int)items;
+    auto kernel = group == 128  ? silu_quant_bwd_narrow_kernel<F, 128>
+                  : group == 64 ? silu_quant_bwd_narrow_kernel<F, 64>
+                                : silu_quant_bwd_narrow_kernel<F, 32>;
+    hipLaunchKernelGGL(kernel, dim3(ngrid), dim3(kThreads), 0, s, xs, dys, static_cast<int8_t*>(grad_input_q),
+                       grad_input_s, static_cast<int8_t*>(y_q_t), y_s_t, T, H, nA, nP, (int)items);
     return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;
   }
   const int tiles_h = (int)tiles_h64;

@@ -173,7 +173,7 @@ def test_straddling_kernel_at_the_token_limit():
 
 
 def test_narrow_kernels_at_the_token_limit():
-    # T = 2^23, H = 3 (not a multiple of 8: the 2-byte-load kernels), group
+    # T = 2^23, H = 3 (not a multiple of 8: the position-tile kernel), group
     # 32: every row is one partial group of 6; y_q_t rows are 8 MiB long
     T, H, G = 1 << 23, 3, 32
     print("case narrow T=2^23 H=3", flush=True)

@@ -433,14 +433,46 @@ def test_hip_graph_capture_and_replay():
         assert np.all(np.abs(C.cpu().numpy() - want) <= (2 * H // 128 + 2) * 2.0**-24 * want_abs)
 
 
-# H not a multiple of 8: rows start off 16 bytes and a plain path with 2-byte
-# loads and byte stores runs; groups still straddle d_gate and d_up.
+# H not a multiple of 8: rows start off 16 bytes (loads take aligned pieces and
+# shift them, code stores write aligned pieces and the tile's own bytes at both
+# ends); groups still straddle d_gate and d_up.
 @pytest.mark.parametrize("T,H,group", [(256, 100, 128), (129, 1, 32), (64, 3, 128), (300, 1001, 64),
                                        (1000, 2050, 128), (77, 13, 32), (4096, 1410, 128), (1, 250, 64)])
 def test_h_not_a_multiple_of_8(T, H, group):
     print("case narrow", T, H, group, flush=True)
     x, dy = random_inputs(T, H, device=DEV, seed=7 * T + H + group)
     check_group(x, dy, group, "narrow T=%d H=%d group=%d" % (T, H, group))
+
+
+# The tiled path over position tiles of [d_gate | d_up]: the tile that holds
+# position H with r = H mod 128 of 1, 63, 65 and 127 (a last tile of less or
+# more than half a tile), a row of 86 channel tiles, and seeded random shapes.
+@pytest.mark.parametrize("T,H,group", [(300, 129, 128), (260, 255, 64), (130, 191, 32), (129, 193, 128),
+                                       (2048, 11001, 128), (512, 11003, 32)])
+def test_h_not_a_multiple_of_8_position_tiles(T, H, group):
+    print("case narrow tiles", T, H, group, flush=True)
+    x, dy = random_inputs(T, H, device=DEV, seed=3 * T + H + group)
+    check_group(x, dy, group, "narrow tiles T=%d H=%d group=%d" % (T, H, group))
+
+
+def _random_narrow_shapes(n=12, seed=8081):
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n):
+        group = int(rng.choice([32, 64, 128]))
+        H = int(rng.integers(1, 3000))
+        if H % 8 == 0:
+            H += int(rng.integers(1, 8))
+        T = int(rng.integers(1, 1500))
+        shapes.append((T, H, group, bool(i % 2)))
+    return shapes
+
+
+@pytest.mark.parametrize("T,H,group,fp8", _random_narrow_shapes())
+def test_h_not_a_multiple_of_8_random(T, H, group, fp8):
+    print("case narrow random", T, H, group, fp8, flush=True)
+    x, dy = random_inputs(T, H, device=DEV, seed=T * 31 + H)
+    check_group(x, dy, group, "narrow random T=%d H=%d group=%d fp8=%d" % (T, H, group, fp8), fp8=fp8)
 
 
 @pytest.mark.parametrize("T,H,group", [(256, 100, 128), (300, 1001, 32)])
