@@ -38,6 +38,7 @@
 // sigmoid and elementwise helpers on their own for the tests.
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include <algorithm>
@@ -1943,11 +1944,14 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
 // Loads: lane p of a row reads the aligned 16 bytes at or below its eight
 // channels, takes the next aligned 16 bytes from lane p + 1 (lane 15 from
 // dwords that lanes 0..3 read just past the row's 16 pieces) and shifts the
-// pair down by the row's offset within 16 bytes.  A kind-2 tile re-reads
-// gate and grad_y lines a kind-0 tile has just read: each token block's tiles
-// are walked in the order 0, nA, 1, nA + 1, 2, nA + 2, ... (D_k, channels
-// 128 (k + 1) - r .., right after the channel tile k + 1 it overlaps), and
-// the loads are plain, so that those lines are still in L2.
+// pair down by the row's offset within 16 bytes.
+// Two teams per XCD, each in a loop of its own (one loop for every kind needs
+// more than the 128 registers a lane has): team A takes the tiles 0 .. nA of
+// the XCD's token blocks, team D the d_up tiles, which need only
+// d_up = grad_y * silu(gate).  The teams walk their eighths of the two item
+// lists at about the same pace, so a d_up tile's gate and grad_y lines (read
+// by the two channel tiles it overlaps) are often still in L2; the loads are
+// plain for that.
 // Stores: lane pairs put a row's 16 code bytes together (as in the aligned
 // kernel), take the previous pair's 16 bytes (row_ror:2) and shift the two
 // into the aligned 16-byte piece of the output row that the pair covers; at
@@ -2032,19 +2036,13 @@ struct NarrowItem {
   int64_t t0, pos0;
 };
 
-// Item -> tile: token block item / nP; within it the position tiles in the
-// order 0, nA, 1, nA + 1, 2, nA + 2, ..., then the remaining d_up tiles.
+// Item -> tile for the two teams: team A takes the tiles 0 .. nA of each
+// token block (kind 0, then kind 1 at nA), team D the tiles after nA (kind 2).
+template <bool kTeamD>
 __device__ __forceinline__ NarrowItem narrow_item(int item, int nA, int nP, int64_t T, int64_t H) {
-  const int tb = item / nP, j = item - tb * nP;
-  int hb;
-  if (nA == 0 || j >= 2 * nA)
-    hb = j;
-  else if (j == 0)
-    hb = 0;
-  else if (j == 1)
-    hb = nA;
-  else
-    hb = (j & 1) == 0 ? j / 2 : nA + (j - 1) / 2;
+  const int per = kTeamD ? nP - nA - 1 : nA + 1;
+  const int tb = item / per, j = item - tb * per;
+  const int hb = kTeamD ? nA + 1 + j : j;
   NarrowItem it;
   it.kind = hb < nA ? 0 : hb == nA ? 1 : 2;
   it.t0 = (int64_t)tb * kTile;
@@ -2064,7 +2062,7 @@ template <Fmt F, int kG>
 __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void silu_quant_bwd_narrow_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ grad_y, int8_t* __restrict__ grad_input_q,
     float* __restrict__ grad_input_s, int8_t* __restrict__ y_q_t, float* __restrict__ y_s_t, int64_t T, int64_t H,
-    int nA, int nP, int items) {
+    int nA, int nP, int items_a, int items_d, int team_a) {
   static_assert(kG == 32 || kG == 64 || kG == 128, "group sizes that divide the tile");
   constexpr int kSub = kTile / kG;
   constexpr int kRowGroups = kTile * kSub, kColGroups = kTile * kSub;
@@ -2109,19 +2107,14 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
   }
   const int sub_row = p / kLanesPerRowGroup, sub_col = q / kPairsPerColGroup;
 
-  // each XCD walks a contiguous eighth of the items
-  int item, end, stride;
-  if ((gridDim.x & 7) == 0) {
-    const int per_xcd = gridDim.x >> 3, xcd = blockIdx.x & 7;
-    const int begin = (int)(((int64_t)items * xcd) >> 3);
-    end = (int)(((int64_t)items * (xcd + 1)) >> 3);
-    item = begin + (int)(blockIdx.x >> 3);
-    stride = per_xcd;
-  } else {
-    item = blockIdx.x;
-    end = items;
-    stride = gridDim.x;
-  }
+  // The first team_a workgroups of each XCD form team A, the others team D;
+  // each walks its XCD's contiguous eighth of its own items.
+  const int per_xcd = gridDim.x >> 3, xcd = blockIdx.x & 7, wg = blockIdx.x >> 3;
+  const bool team_d = wg >= team_a;
+  const int items = team_d ? items_d : items_a;
+  const int end = (int)(((int64_t)items * (xcd + 1)) >> 3);
+  const int stride = team_d ? per_xcd - team_a : team_a;
+  int item = (int)(((int64_t)items * xcd) >> 3) + (team_d ? wg - team_a : wg);
 
   const char* xb = reinterpret_cast<const char*>(x);
   const char* dyb = reinterpret_cast<const char*>(grad_y);
@@ -2133,7 +2126,8 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
   auto dy_buf = [&](const NarrowItem& it) {
     return buffer_of(const_cast<char*>(dyb + it.t0 * (int64_t)H2), ((uint32_t)it.rows * H2 + 15u) & ~15u);
   };
-  // aligned pieces of an item of kind 0 or 2 (nothing for kind 1)
+  // aligned pieces of a tile of kind 0 (gate, up, grad_y) or 2 (gate,
+  // grad_y); nothing for kind 1
   auto load_raw = [&](NarrowRaw& raw, const NarrowItem& it) {
     const __amdgpu_buffer_rsrc_t xbuf = x_buf(it), dbuf = dy_buf(it);
     const uint32_t c2 = 2u * it.c0;
@@ -2149,36 +2143,35 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
     }
   };
 
-  NarrowRaw raw, raw_next;
-  NarrowItem cur = narrow_item(item < end ? item : 0, nA, nP, T, H);
-  if (item < end) load_raw(raw, cur);
   {
     const float4* src = reinterpret_cast<const float4*>(g_sigma_tab);
     float4* dst = reinterpret_cast<float4*>(s_tab);
     for (int i = tid; i < kSigEntries / 4; i += kThreads) dst[i] = src[i];
     fill_scale_table(s_qtab, tid);
   }
-  __syncthreads();
 
-  while (item < end) {
-    // ---- the tile's values: gate, up and grad_y per lane row ---------------
-    // (taken from the raw pieces before the next tile's loads are issued, so
-    // that the two sets of raw registers are never live together)
-    TileIn in;
-    const uint32_t c2 = 2u * cur.c0;
-    if (cur.kind != 1) {
+  // One team's loop (kD: team D).
+  auto walk = [&](auto team) {
+    constexpr bool kD = decltype(team)::value;
+    NarrowRaw raw, raw_next;
+    NarrowItem cur = narrow_item<kD>(item < end ? item : 0, nA, nP, T, H);
+    if (item < end) load_raw(raw, cur);
+    __syncthreads();
+
+    while (item < end) {
+      // ---- the tile's values: gate, up and grad_y per lane row -------------
+      // (taken from the raw pieces before the next tile's loads are issued,
+      // so that the two sets of raw registers are never live together)
+      TileIn in;
+      const uint32_t c2 = 2u * cur.c0;
+      if (kD || cur.kind == 0) {
 #pragma unroll
-      for (int i = 0; i < kRows; ++i) {
-        in.g[i] = piece_values(raw.g[i], raw.eg[i], xrow[i] + c2, p);
-        in.d[i] = piece_values(raw.d[i], raw.ed[i], dyrow[i] + c2, p);
-      }
-      if (cur.kind == 0) {
-#pragma unroll
-        for (int i = 0; i < kRows; ++i) in.u[i] = piece_values(raw.u[i], raw.eu[i], xrow[i] + H2 + c2, p);
-      } else {
-        // d_up = grad_y * silu(gate) is the product y = silu(gate) * u with
-        // grad_y in place of up (the multiplication commutes exactly)
-        if (cur.len < kTile) {
+        for (int i = 0; i < kRows; ++i) {
+          in.g[i] = piece_values(raw.g[i], raw.eg[i], xrow[i] + c2, p);
+          in.d[i] = piece_values(raw.d[i], raw.ed[i], dyrow[i] + c2, p);
+          in.u[i] = kD ? make_uint4(0, 0, 0, 0) : piece_values(raw.u[i], raw.eu[i], xrow[i] + H2 + c2, p);
+        }
+        if (kD && cur.len < kTile) {
           // positions past 2H read as zeros
           const int n = cur.len - 8 * p;
 #pragma unroll
@@ -2190,180 +2183,186 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
               (&in.d[i].x)[k] &= mk;
             }
         }
+      } else {
+        // kind 1, position pos of the row: d_gate at channel pos below H, else
+        // d_up at channel pos - H, for which grad_y goes in the up slot
+        // (y = silu(gate) * u is then d_up: the product commutes exactly);
+        // two-byte loads
+        const __amdgpu_buffer_rsrc_t xbuf = x_buf(cur), dbuf = dy_buf(cur);
 #pragma unroll
-        for (int i = 0; i < kRows; ++i) in.u[i] = in.d[i];
-      }
-    } else {
-      // position pos of the row: d_gate at channel pos below H, else d_up at
-      // channel pos - H (grad_y in the up slot, as for kind 2); two-byte loads
-      const __amdgpu_buffer_rsrc_t xbuf = x_buf(cur), dbuf = dy_buf(cur);
+        for (int i = 0; i < kRows; ++i) {
+          uint32_t gw[4], uw[4], dw[4];
 #pragma unroll
-      for (int i = 0; i < kRows; ++i) {
-        uint32_t gw[4], uw[4], dw[4];
+          for (int k = 0; k < 4; ++k) gw[k] = uw[k] = dw[k] = 0u;
+          if (kRows * q + i < cur.rows) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) gw[k] = uw[k] = dw[k] = 0u;
-        if (kRows * q + i < cur.rows) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int64_t pos = cur.pos0 + 8 * p + e;
-            if (pos < 2 * H) {
-              const uint32_t ch = (uint32_t)(pos < H ? pos : pos - H);
-              const uint32_t gv = __builtin_amdgcn_raw_buffer_load_b16(xbuf, xrow[i] + 2u * ch, 0, 0);
-              const uint32_t dv = __builtin_amdgcn_raw_buffer_load_b16(dbuf, dyrow[i] + 2u * ch, 0, 0);
-              const uint32_t uv = pos < H ? __builtin_amdgcn_raw_buffer_load_b16(xbuf, xrow[i] + H2 + 2u * ch, 0, 0)
-                                          : dv;
-              const int sh = 16 * (e & 1);
-              gw[e >> 1] |= gv << sh;
-              uw[e >> 1] |= uv << sh;
-              dw[e >> 1] |= dv << sh;
+            for (int e = 0; e < 8; ++e) {
+              const int64_t pos = cur.pos0 + 8 * p + e;
+              if (pos < 2 * H) {
+                const uint32_t ch = (uint32_t)(pos < H ? pos : pos - H);
+                const uint32_t gv = __builtin_amdgcn_raw_buffer_load_b16(xbuf, xrow[i] + 2u * ch, 0, 0);
+                const uint32_t dv = __builtin_amdgcn_raw_buffer_load_b16(dbuf, dyrow[i] + 2u * ch, 0, 0);
+                const uint32_t uv =
+                    pos < H ? __builtin_amdgcn_raw_buffer_load_b16(xbuf, xrow[i] + H2 + 2u * ch, 0, 0) : dv;
+                const int sh = 16 * (e & 1);
+                gw[e >> 1] |= gv << sh;
+                uw[e >> 1] |= uv << sh;
+                dw[e >> 1] |= dv << sh;
+              }
             }
           }
-        }
-        in.g[i] = make_uint4(gw[0], gw[1], gw[2], gw[3]);
-        in.u[i] = make_uint4(uw[0], uw[1], uw[2], uw[3]);
-        in.d[i] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
-      }
-    }
-
-    const int next = item + stride;
-    const NarrowItem nxt = narrow_item(next < end ? next : item, nA, nP, T, H);
-    if (next < end) load_raw(raw_next, nxt);
-
-    // ---- elementwise: the row values V, y, partial maxima -----------------
-    // One path for every kind: y = silu * u is d_up where u holds grad_y, and
-    // the lane's positions below H take d_gate.
-    uint32_t Yp[kRows][4], Vp[kRows][4];
-    float rv[kRows], cm[8];
-    {
-      uint32_t Gp[kRows][4], Up[kRows][4];
-      float rg[kRows], ru[kRows];
-      elementwise<false>(in, s_tab, Yp, Gp, Up, rg, ru, cm);
-      const int n = cur.kind == 0 ? 8 : (int)(H - cur.pos0) - 8 * p;  // the lane's positions below H
-#pragma unroll
-      for (int i = 0; i < kRows; ++i) {
-        float m = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t mk = halves_below(k, n);
-          Vp[i][k] = (Gp[i][k] & mk) | (Yp[i][k] & ~mk);
-          m = amax3(m, bf16_lo(Vp[i][k]), bf16_hi(Vp[i][k]));
-        }
-        rv[i] = cur.kind == 0 ? rg[i] : m;
-      }
-    }
-    if (tid == 0) s_flag[0] = 0;
-    const bool has_y = cur.kind != 2;
-    {
-      float* rp = s_rowpart + p * kRowPartStride + kRows * q;
-#pragma unroll
-      for (int i = 0; i < kRows; ++i) rp[i] = rv[i];
-      if (has_y) {
-        float4* cp = reinterpret_cast<float4*>(s_colpart + q * kTile + 4 * p);
-        cp[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
-        cp[16] = make_float4(cm[4], cm[5], cm[6], cm[7]);
-      }
-    }
-    __syncthreads();
-
-    // ---- one thread per group ----------------------------------------------
-    const int cols = has_y ? (H - cur.pos0 < kTile ? (int)(H - cur.pos0) : kTile) : 0;  // channels of y^T
-    const int groups = kRowGroups + (has_y ? kColGroups : 0);
-    for (int id = tid; id < groups; id += kThreads) {
-      float m = 0.0f;
-      if (id < kRowGroups) {
-        const int row = id & (kTile - 1), sub = id >> 7;
-#pragma unroll
-        for (int pp = 0; pp < kLanesPerRowGroup; ++pp)
-          m = fmaxf(m, s_rowpart[(sub * kLanesPerRowGroup + pp) * kRowPartStride + row]);
-      } else {
-        const int cid = id - kRowGroups, c = cid & (kTile - 1), sub = cid >> 7;
-        const int idx = ((c >> 2) & 1) * 64 + (c >> 3) * 4 + (c & 3);
-#pragma unroll 8
-        for (int qq = 0; qq < kPairsPerColGroup; ++qq)
-          m = fmaxf(m, s_colpart[(sub * kPairsPerColGroup + qq) * kTile + idx]);
-      }
-      float scale, inv;
-      if constexpr (F == Fmt::kInt8) {
-        scale_and_inverse(m, s_qtab, scale, inv);
-      } else {
-        scale = group_scale<F>(m);
-        inv = 1.0f / scale;
-      }
-      s_inv[id] = inv;
-      if (inv == __builtin_huge_valf()) s_flag[0] = 1;
-      if (id < kRowGroups) {
-        const int row = id & (kTile - 1), sub = id >> 7;
-        // groups past the row's 2H positions and rows past T do not exist
-        if (row < cur.rows && sub * kG < cur.len)
-          grad_input_s[(cur.t0 + row) * row_groups + cur.pos0 / kG + sub] = scale;
-      } else {
-        const int cid = id - kRowGroups, c = cid & (kTile - 1), sub = cid >> 7;
-        if (c < cols && sub * kG < cur.rows) y_s_t[(cur.pos0 + c) * col_groups + cur.t0 / kG + sub] = scale;
-      }
-    }
-    __syncthreads();
-
-    // ---- codes: the row's pieces straight out, y via the LDS transpose -----
-    {
-      float iv[kRows], iy[8];
-#pragma unroll
-      for (int i = 0; i < kRows; ++i) iv[i] = s_inv[sub_row * kTile + kRows * q + i];
-      if (has_y) {
-        const float* inv_col = s_inv + kRowGroups + sub_col * kTile + 8 * p;
-        const float4 a = *reinterpret_cast<const float4*>(inv_col);
-        const float4 b = *reinterpret_cast<const float4*>(inv_col + 4);
-        iy[0] = a.x, iy[1] = a.y, iy[2] = a.z, iy[3] = a.w, iy[4] = b.x, iy[5] = b.y, iy[6] = b.z, iy[7] = b.w;
-      }
-      const bool safe = s_flag[0] != 0;  // some group's inverse overflowed: the clamped rule
-      uint2 c[kRows];
-#pragma unroll
-      for (int i = 0; i < kRows; ++i) c[i] = safe ? codes8<true, F>(Vp[i], iv[i]) : codes8<false, F>(Vp[i], iv[i]);
-      const uint4 piece = pair_rows16(c[0], c[1], odd);
-      const uint4 prev = make_uint4(row_ror<0x122>(piece.x), row_ror<0x122>(piece.y), row_ror<0x122>(piece.z),
-                                    row_ror<0x122>(piece.w));
-      if (rho < cur.rows) {
-        const __amdgpu_buffer_rsrc_t gq_buf = buffer_of(grad_input_q + cur.t0 * (int64_t)H2, (uint32_t)cur.rows * H2);
-        const uint32_t S = gq_row + (uint32_t)cur.pos0, m = S & 15u, a0 = S - m;
-        const int len = cur.len, mi = (int)m;
-        const uint4 chunk = m == 0 ? piece : funnel16(prev, piece, 16u - m);
-        const int lo = pair == 0 ? mi : 0, hi = min(16, len + mi - 16 * pair);
-        if (hi > lo) store_range16(gq_buf, a0 + 16u * pair, chunk, lo, hi);
-        if (pair == 7 && m != 0) {
-          const int hi8 = min(16, len + mi - 128);
-          if (hi8 > 0) store_range16(gq_buf, a0 + 128u, funnel16(piece, make_uint4(0, 0, 0, 0), 16u - m), 0, hi8);
+          in.g[i] = make_uint4(gw[0], gw[1], gw[2], gw[3]);
+          in.u[i] = make_uint4(uw[0], uw[1], uw[2], uw[3]);
+          in.d[i] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
         }
       }
-      if (has_y) {
-        if (safe)
-          stage_y_codes<F, true>(Yp, iy, s_yqt, p, q);
-        else
-          stage_y_codes<F, false>(Yp, iy, s_yqt, p, q);
+
+      const int next = item + stride;
+      const NarrowItem nxt = narrow_item<kD>(next < end ? next : item, nA, nP, T, H);
+      if (next < end) load_raw(raw_next, nxt);
+
+      // ---- elementwise: the row values V, y, partial maxima ---------------
+      // Team D: d_up alone.  Team A: y and d_gate; in the tile holding
+      // position H the lane's positions from H on take y, which is d_up there.
+      uint32_t Yp[kRows][4], Vp[kRows][4];
+      float rv[kRows], cm[8];
+      if constexpr (kD) {
+        elementwise_window<false>(in, false, s_tab, Vp, rv);
+      } else {
+        uint32_t Gp[kRows][4], Up[kRows][4];
+        float rg[kRows], ru[kRows];
+        elementwise<false>(in, s_tab, Yp, Gp, Up, rg, ru, cm);
+        const int n = cur.kind == 0 ? 8 : (int)(H - cur.pos0) - 8 * p;  // the lane's positions below H
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+          float m = 0.0f;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t mk = halves_below(k, n);
+            Vp[i][k] = (Gp[i][k] & mk) | (Yp[i][k] & ~mk);
+            m = amax3(m, bf16_lo(Vp[i][k]), bf16_hi(Vp[i][k]));
+          }
+          rv[i] = cur.kind == 0 ? rg[i] : m;
+        }
+      }
+      if (tid == 0) s_flag[0] = 0;
+      {
+        float* rp = s_rowpart + p * kRowPartStride + kRows * q;
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) rp[i] = rv[i];
+        if (!kD) {
+          float4* cp = reinterpret_cast<float4*>(s_colpart + q * kTile + 4 * p);
+          cp[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
+          cp[16] = make_float4(cm[4], cm[5], cm[6], cm[7]);
+        }
       }
       __syncthreads();
-    }
 
-    // ---- transposed codes out ----------------------------------------------
-    if (has_y) {
-      const __amdgpu_buffer_rsrc_t yq_buf =
-          buffer_of(y_q_t + (cur.pos0 * T + cur.t0), (uint32_t)(cols * T));  // rows past H lie past the records
+      // ---- one thread per group --------------------------------------------
+      const int cols = kD ? 0 : (H - cur.pos0 < kTile ? (int)(H - cur.pos0) : kTile);  // channels of y^T
+      for (int id = tid; id < kRowGroups + (kD ? 0 : kColGroups); id += kThreads) {
+        float m = 0.0f;
+        if (id < kRowGroups) {
+          const int row = id & (kTile - 1), sub = id >> 7;
 #pragma unroll
-      for (int step = 0; step < kOutSteps; ++step) {
-        const int id = tid + step * kThreads;
-        const int h = id >> 3;
-        const int phys = (id & 7) ^ ((h >> 3) & 7);
-        const uint4 v = *reinterpret_cast<const uint4*>(s_yqt + h * kTile + phys * 16);
-        if (cur.rows == kTile && yq_align == 16)
-          store_yq(yq_buf, lane_yq[step], v);
-        else
-          store_yq_piece(yq_buf, lane_yq[step], v, min(16, max(0, cur.rows - 16 * (id & 7))), yq_align);
+          for (int pp = 0; pp < kLanesPerRowGroup; ++pp)
+            m = fmaxf(m, s_rowpart[(sub * kLanesPerRowGroup + pp) * kRowPartStride + row]);
+        } else {
+          const int cid = id - kRowGroups, c = cid & (kTile - 1), sub = cid >> 7;
+          const int idx = ((c >> 2) & 1) * 64 + (c >> 3) * 4 + (c & 3);
+#pragma unroll 8
+          for (int qq = 0; qq < kPairsPerColGroup; ++qq)
+            m = fmaxf(m, s_colpart[(sub * kPairsPerColGroup + qq) * kTile + idx]);
+        }
+        float scale, inv;
+        if constexpr (F == Fmt::kInt8) {
+          scale_and_inverse(m, s_qtab, scale, inv);
+        } else {
+          scale = group_scale<F>(m);
+          inv = 1.0f / scale;
+        }
+        s_inv[id] = inv;
+        if (inv == __builtin_huge_valf()) s_flag[0] = 1;
+        if (id < kRowGroups) {
+          const int row = id & (kTile - 1), sub = id >> 7;
+          // groups past the row's 2H positions and rows past T do not exist
+          if (row < cur.rows && sub * kG < cur.len)
+            grad_input_s[(cur.t0 + row) * row_groups + cur.pos0 / kG + sub] = scale;
+        } else {
+          const int cid = id - kRowGroups, c = cid & (kTile - 1), sub = cid >> 7;
+          if (c < cols && sub * kG < cur.rows) y_s_t[(cur.pos0 + c) * col_groups + cur.t0 / kG + sub] = scale;
+        }
       }
-    }
+      __syncthreads();
 
-    raw = raw_next;
-    item = next;
-    cur = nxt;
-    if (item < end) __syncthreads();  // the transpose buffer is read before it is rewritten
-  }
+      // ---- codes: the row's pieces straight out, y via the LDS transpose ---
+      {
+        float iv[kRows], iy[8];
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) iv[i] = s_inv[sub_row * kTile + kRows * q + i];
+        if (!kD) {
+          const float* inv_col = s_inv + kRowGroups + sub_col * kTile + 8 * p;
+          const float4 a = *reinterpret_cast<const float4*>(inv_col);
+          const float4 b = *reinterpret_cast<const float4*>(inv_col + 4);
+          iy[0] = a.x, iy[1] = a.y, iy[2] = a.z, iy[3] = a.w, iy[4] = b.x, iy[5] = b.y, iy[6] = b.z, iy[7] = b.w;
+        }
+        const bool safe = s_flag[0] != 0;  // some group's inverse overflowed: the clamped rule
+        uint2 c[kRows];
+#pragma unroll
+        for (int i = 0; i < kRows; ++i)
+          c[i] = safe ? codes8<true, F>(Vp[i], iv[i]) : codes8<false, F>(Vp[i], iv[i]);
+        const uint4 piece = pair_rows16(c[0], c[1], odd);
+        const uint4 prev = make_uint4(row_ror<0x122>(piece.x), row_ror<0x122>(piece.y), row_ror<0x122>(piece.z),
+                                      row_ror<0x122>(piece.w));
+        if (rho < cur.rows) {
+          const __amdgpu_buffer_rsrc_t gq_buf =
+              buffer_of(grad_input_q + cur.t0 * (int64_t)H2, (uint32_t)cur.rows * H2);
+          const uint32_t S = gq_row + (uint32_t)cur.pos0, m = S & 15u, a0 = S - m;
+          const int len = cur.len, mi = (int)m;
+          const uint4 chunk = m == 0 ? piece : funnel16(prev, piece, 16u - m);
+          const int lo = pair == 0 ? mi : 0, hi = min(16, len + mi - 16 * pair);
+          if (hi > lo) store_range16(gq_buf, a0 + 16u * pair, chunk, lo, hi);
+          if (pair == 7 && m != 0) {
+            const int hi8 = min(16, len + mi - 128);
+            if (hi8 > 0) store_range16(gq_buf, a0 + 128u, funnel16(piece, make_uint4(0, 0, 0, 0), 16u - m), 0, hi8);
+          }
+        }
+        if (!kD) {
+          if (safe)
+            stage_y_codes<F, true>(Yp, iy, s_yqt, p, q);
+          else
+            stage_y_codes<F, false>(Yp, iy, s_yqt, p, q);
+        }
+        __syncthreads();
+      }
+
+      // ---- transposed codes out --------------------------------------------
+      if (!kD) {
+        const __amdgpu_buffer_rsrc_t yq_buf =
+            buffer_of(y_q_t + (cur.pos0 * T + cur.t0), (uint32_t)(cols * T));  // rows past H lie past the records
+#pragma unroll
+        for (int step = 0; step < kOutSteps; ++step) {
+          const int id = tid + step * kThreads;
+          const int h = id >> 3;
+          const int phys = (id & 7) ^ ((h >> 3) & 7);
+          const uint4 v = *reinterpret_cast<const uint4*>(s_yqt + h * kTile + phys * 16);
+          if (cur.rows == kTile && yq_align == 16)
+            store_yq(yq_buf, lane_yq[step], v);
+          else
+            store_yq_piece(yq_buf, lane_yq[step], v, min(16, max(0, cur.rows - 16 * (id & 7))), yq_align);
+        }
+      }
+
+      raw = raw_next;
+      item = next;
+      cur = nxt;
+      if (item < end) __syncthreads();  // the transpose buffer is read before it is rewritten
+    }
+  };
+  if (team_d)
+    walk(std::true_type{});
+  else
+    walk(std::false_type{});
 }
 
 // Diagnostics: the fused kernel's own sigmoid lookup and elementwise helpers,
@@ -2546,17 +2545,36 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
   const uint16_t* xs = static_cast<const uint16_t*>(x);
   const uint16_t* dys = static_cast<const uint16_t*>(grad_y);
   if (H % 8 != 0) {
-    // rows off 16 bytes: position tiles of [d_gate | d_up], 2 per 128 channels
+    // rows off 16 bytes: position tiles of [d_gate | d_up], two teams per XCD
     const int nA = (int)(H / kTile), nP = (int)((2 * H + kTile - 1) / kTile);
-    const int64_t items = tiles_t * nP;  // at most 2 * tiles_t * tiles_h64, checked above
+    const int64_t items_a = tiles_t * (nA + 1), items_d = tiles_t * (nP - nA - 1);  // < 2^31, checked above
     int ngrid = cus * kWorkgroupsPerCU;
-    ngrid = ngrid >= 8 ? ngrid - ngrid % 8 : ngrid;
-    if (items < ngrid) ngrid = (int)items;
+    ngrid = ngrid < 16 ? 16 : ngrid - ngrid % 8;  // a multiple of 8, two workgroups per XCD at least
+    const int per_xcd = ngrid / 8;
+    // Team sizes: the split whose slower team needs the fewest rounds over
+    // its eighth of the items, a d_gate tile (three inputs, y^T as well)
+    // counting as 1.7 d_up tiles (measured 1.6-2.2); among equal round
+    // counts, the split whose teams' shares of work are closest.
+    int team_a = per_xcd;
+    if (items_d > 0) {
+      const int64_t xa = (items_a + 7) / 8, xd = (items_d + 7) / 8;
+      double best = 0.0;
+      for (int a = 1; a < per_xcd; ++a) {
+        const double ra = 1.7 * (double)((xa + a - 1) / a), rd = (double)((xd + per_xcd - a - 1) / (per_xcd - a));
+        const double wa = 1.7 * (double)xa / a, wd = (double)xd / (per_xcd - a);
+        const double cost = (ra > rd ? ra : rd) + 0.01 * (wa > wd ? wa : wd);
+        if (a == 1 || cost < best) {
+          best = cost;
+          team_a = a;
+        }
+      }
+    }
     auto kernel = group == 128  ? silu_quant_bwd_narrow_kernel<F, 128>
                   : group == 64 ? silu_quant_bwd_narrow_kernel<F, 64>
                                 : silu_quant_bwd_narrow_kernel<F, 32>;
     hipLaunchKernelGGL(kernel, dim3(ngrid), dim3(kThreads), 0, s, xs, dys, static_cast<int8_t*>(grad_input_q),
-                       grad_input_s, static_cast<int8_t*>(y_q_t), y_s_t, T, H, nA, nP, (int)items);
+                       grad_input_s, static_cast<int8_t*>(y_q_t), y_s_t, T, H, nA, nP, (int)items_a, (int)items_d,
+                       team_a);
     return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;
   }
   const int tiles_h = (int)tiles_h64;
