@@ -1707,6 +1707,89 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
 }
 
 // ---------------------------------------------------------------------------
+// Rows that start at any even byte offset (H not a multiple of 8): a lane's
+// 16 bytes of a row come from the aligned piece at or below them and the next
+// one, held by the neighbouring lane of the 16-lane DPP row; outputs go out as
+// aligned pieces put together the same way.
+
+// Bytes [s, s + 16) of the 32 bytes lo | hi (lo first), s in [0, 16).
+// (Plain values, not arrays: a select between two array elements can become
+// a select between their addresses, which keeps the array in memory.)
+__device__ __forceinline__ uint4 funnel16(uint4 lo, uint4 hi, uint32_t s) {
+  const bool two = (s & 8u) != 0, one = (s & 4u) != 0;
+  // dwords s/4 .. s/4 + 4 of lo | hi: first down by 2 if s & 8, then by 1 if s & 4
+  const uint32_t q0 = two ? lo.z : lo.x, q1 = two ? lo.w : lo.y, q2 = two ? hi.x : lo.z, q3 = two ? hi.y : lo.w,
+                 q4 = two ? hi.z : hi.x, q5 = two ? hi.w : hi.y;
+  const uint32_t r0 = one ? q1 : q0, r1 = one ? q2 : q1, r2 = one ? q3 : q2, r3 = one ? q4 : q3,
+                 r4 = one ? q5 : q4;
+  const uint32_t b = s & 3u;
+  return make_uint4(__builtin_amdgcn_alignbyte(r1, r0, b), __builtin_amdgcn_alignbyte(r2, r1, b),
+                    __builtin_amdgcn_alignbyte(r3, r2, b), __builtin_amdgcn_alignbyte(r4, r3, b));
+}
+
+// row_ror:n (kCtrl = 0x120 + n): lane p of each 16-lane row takes the value of
+// lane p - n (mod 16).
+template <int kCtrl>
+__device__ __forceinline__ uint32_t row_ror(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kCtrl, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ void load_piece(__amdgpu_buffer_rsrc_t buf, uint32_t at, int p, uint4& v, uint32_t& e) {
+  const uint32_t a = at & ~15u;
+  v = load_buf<0>(buf, a + 16u * (uint32_t)p);
+  e = p < 4 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(buf, a + 256u + 4u * (uint32_t)p, 0, 0) : 0u;
+}
+
+// The eight bf16 values at the row's byte `at` plus 16 p.  Every lane of the
+// wave takes part (the moves read the other lanes of its row).
+__device__ __forceinline__ uint4 piece_values(uint4 v, uint32_t e, uint32_t at, int p) {
+  const bool last = p == 15;
+  const uint32_t n0 = row_ror<0x12F>(v.x), f0 = row_ror<0x12F>(e);  // from lane p + 1 / lane 15 from lane 0
+  const uint32_t n1 = row_ror<0x12F>(v.y), f1 = row_ror<0x12E>(e);  // lane 15 from lane 1
+  const uint32_t n2 = row_ror<0x12F>(v.z), f2 = row_ror<0x12D>(e);  // lane 15 from lane 2
+  const uint32_t n3 = row_ror<0x12F>(v.w), f3 = row_ror<0x12C>(e);  // lane 15 from lane 3
+  const uint4 next = make_uint4(last ? f0 : n0, last ? f1 : n1, last ? f2 : n2, last ? f3 : n3);
+  return funnel16(v, next, at & 15u);
+}
+
+// Bytes [lo, hi) of a 16-byte piece stored at `off`: the whole piece in one
+// store, else 4- and 2-byte parts, and with kOddEnds single bytes where lo or
+// hi is odd (without it both must be even).
+template <bool kOddEnds = false>
+__device__ __forceinline__ void store_range16(__amdgpu_buffer_rsrc_t buf, uint32_t off, uint4 v, int lo, int hi) {
+  if (lo == 0 && hi == 16) {
+    __builtin_amdgcn_raw_buffer_store_b128((u32x4){v.x, v.y, v.z, v.w}, buf, off, 0, 0);
+    return;
+  }
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int b0 = 4 * k;
+    if (b0 >= lo && b0 + 4 <= hi) {
+      __builtin_amdgcn_raw_buffer_store_b32(w[k], buf, off + b0, 0, 0);
+      continue;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c0 = b0 + 2 * h;
+      if (c0 >= lo && c0 + 2 <= hi) {
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[k] >> (16 * h)), buf, off + c0, 0, 0);
+      } else if (kOddEnds) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          if (c0 + e >= lo && c0 + e < hi)
+            __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(w[k] >> (16 * h + 8 * e)), buf, off + c0 + e, 0, 0);
+      }
+    }
+  }
+}
+
+// Word mask of the halves (elements 2k, 2k + 1) below n.
+__device__ __forceinline__ uint32_t halves_below(int k, int n) {
+  return (2 * k < n ? 0x0000ffffu : 0u) | (2 * k + 1 < n ? 0xffff0000u : 0u);
+}
+
+// ---------------------------------------------------------------------------
 // Forward quantiser: y = bf16((silu(gate) * up) * w[t]), quantised per row in
 // groups of kG = 128, 64 or 32 channels (y_q [T, H], y_s [T, ceil(H/kG)]),
 // optionally also the bf16 y itself.  The fused launch shape follows the page
@@ -1745,6 +1828,7 @@ __device__ __forceinline__ float group_lanes_max(float v) {
 
 struct FwdIn {
   uint4 g, u;
+  uint32_t eg, eu;  // with kShift: lanes 0..3 read past the row's 16 pieces
 };
 
 // Sum of the eight signed bytes of two words: a dot product with bytes of 1.
@@ -1771,7 +1855,13 @@ __device__ __forceinline__ uint32_t f16_bits(float v) { return __builtin_bit_cas
 // and sum (fl32(scale * sum of the codes)), then the 32 codes.  y_q then
 // points at the blocks (4-byte aligned) and y_s is unused.  y_bf16, if not
 // null, receives the rounded y [T, H] in either layout.
-template <int kG, bool kQ81 = false, bool kWeighted = false>
+// kShift serves x = [gate | up] with H not a multiple of 8, whose rows start
+// at any even byte offset: each lane loads the aligned 16 bytes at or below
+// its channels and the next ones come from the neighbouring lane, as in
+// silu_quant_bwd_narrow_kernel; the code and y rows are stored as aligned
+// pieces put together from neighbouring lanes, with only the unit's own bytes
+// written at both ends of a row.
+template <int kG, bool kQ81 = false, bool kWeighted = false, bool kShift = false>
 __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
     const uint16_t* __restrict__ gate, const uint16_t* __restrict__ up, int64_t in_row,
     const float* __restrict__ row_weight, int8_t* __restrict__ y_q, float* __restrict__ y_s,
@@ -1822,8 +1912,25 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
     }
   };
   auto rows_of = [&](const Unit& c) { return T - 4 * c.rb < 4 ? (uint32_t)(T - 4 * c.rb) : 4u; };
+  // kShift: byte offsets of the lane's row of gate and of up from the unit's
+  // first row of x (x = [gate | up]: up lies 2H bytes further)
+  auto at_gate = [&](const Unit& c) { return r * x_row + 2 * (uint32_t)(c.hb * kTile); };
+  const uint32_t up_bytes = (uint32_t)(2 * H);
   auto load = [&](FwdIn& in, const Unit& c) {
     const int64_t t0 = 4 * c.rb, h0 = c.hb * kTile;
+    if constexpr (kShift) {
+      // the unit's rows of x, rounded up to 16 bytes (the row start t0 * 4H is
+      // a multiple of 16)
+      const __amdgpu_buffer_rsrc_t xb =
+          buffer_of(const_cast<uint16_t*>(gate) + t0 * in_row, (rows_of(c) * x_row + 15u) & ~15u);
+      in.g = in.u = make_uint4(0, 0, 0, 0);
+      in.eg = in.eu = 0u;
+      if ((uint32_t)r < rows_of(c)) {
+        load_piece(xb, at_gate(c), p, in.g, in.eg);
+        load_piece(xb, at_gate(c) + up_bytes, p, in.u, in.eu);
+      }
+      return;
+    }
     // records up to the last channel of the unit's last row
     const uint32_t bytes = (rows_of(c) - 1) * x_row + 2 * (uint32_t)(H - h0);
     const __amdgpu_buffer_rsrc_t gb = buffer_of(const_cast<uint16_t*>(gate) + (t0 * in_row + h0), bytes);
@@ -1853,8 +1960,17 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
                                          buffer_of(const_cast<float*>(row_weight) + t0, 4 * rows), 4 * r, 0, 0));
     uint32_t Yp[4];
     float m = 0.0f;
-    const uint32_t gw[4] = {in.g.x, in.g.y, in.g.z, in.g.w};
-    const uint32_t uw[4] = {in.u.x, in.u.y, in.u.z, in.u.w};
+    uint4 g4 = in.g, u4 = in.u;
+    if constexpr (kShift) {
+      g4 = piece_values(in.g, in.eg, at_gate(cur), p);
+      u4 = piece_values(in.u, in.eu, at_gate(cur) + up_bytes, p);
+      // channels past H read as zeros
+      const int n = (int)(H - h0) - 8 * p;
+      g4 = make_uint4(g4.x & halves_below(0, n), g4.y & halves_below(1, n), g4.z & halves_below(2, n),
+                      g4.w & halves_below(3, n));
+    }
+    const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w};
+    const uint32_t uw[4] = {u4.x, u4.y, u4.z, u4.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       uint32_t olo, ohi;
@@ -1903,14 +2019,58 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
       // Non-temporal code stores: for this write-light pass they measured
       // faster than the system-scope policy the backward pass uses.
       const uint2 other = make_uint2(swap_neighbour(c.x), swap_neighbour(c.y));
+      if constexpr (kShift) {
+        // The unit's rows of y_q and y_bf16 from an aligned base at or below
+        // row t0; a row starts S bytes after it, m = S mod 16 past an aligned
+        // piece.  Even lanes hold 16 codes (their own and the odd lane's),
+        // the previous pair's from row_ror:2; every lane's 16 bytes of y, the
+        // previous lane's from row_ror:1.
+        const int len = H - h0 < kTile ? (int)(H - h0) : kTile;  // channels of the unit's rows
+        const int64_t qb0 = (t0 * H) & ~(int64_t)15;
+        const uint4 piece = make_uint4(c.x, c.y, other.x, other.y);
+        const uint4 prev = make_uint4(row_ror<0x122>(piece.x), row_ror<0x122>(piece.y), row_ror<0x122>(piece.z),
+                                      row_ror<0x122>(piece.w));
+        const uint4 cur16 = make_uint4(Yp[0], Yp[1], Yp[2], Yp[3]);
+        const uint4 prev16 = make_uint4(row_ror<0x121>(cur16.x), row_ror<0x121>(cur16.y), row_ror<0x121>(cur16.z),
+                                        row_ror<0x121>(cur16.w));
+        if ((uint32_t)r < rows) {
+          const __amdgpu_buffer_rsrc_t qb = buffer_of(y_q + qb0, (uint32_t)(t0 * H + rows * H - qb0));
+          const uint32_t S = (uint32_t)(t0 * H - qb0) + r * (uint32_t)H + (uint32_t)h0, mq = S & 15u, a0 = S - mq;
+          const int mi = (int)mq, j = p >> 1;
+          if (!odd) {
+            const uint4 chunk = mq == 0 ? piece : funnel16(prev, piece, 16u - mq);
+            const int lo = j == 0 ? mi : 0, hi = min(16, len + mi - 16 * j);
+            if (hi > lo) store_range16<true>(qb, a0 + 16u * j, chunk, lo, hi);
+            if (j == 7 && mq != 0) {
+              const int hi8 = min(16, len + mi - 128);
+              if (hi8 > 0) store_range16<true>(qb, a0 + 128u, funnel16(piece, make_uint4(0, 0, 0, 0), 16u - mq), 0, hi8);
+            }
+          }
+          if (y_bf16 != nullptr) {
+            const int64_t bb0 = (t0 * H) & ~(int64_t)7;  // 8 bf16 values = 16 bytes
+            const __amdgpu_buffer_rsrc_t yb = buffer_of(y_bf16 + bb0, (uint32_t)(2 * (t0 * H + rows * H - bb0)));
+            const uint32_t Sb = 2 * ((uint32_t)(t0 * H - bb0) + r * (uint32_t)H + (uint32_t)h0), mb = Sb & 15u,
+                           b0 = Sb - mb;
+            const int mbi = (int)mb;
+            const uint4 chunk = mb == 0 ? cur16 : funnel16(prev16, cur16, 16u - mb);
+            const int lo = p == 0 ? mbi : 0, hi = min(16, 2 * len + mbi - 16 * p);
+            if (hi > lo) store_range16(yb, b0 + 16u * p, chunk, lo, hi);
+            if (p == 15 && mb != 0) {
+              const int hi16 = min(16, 2 * len + mbi - 256);
+              if (hi16 > 0) store_range16(yb, b0 + 256u, funnel16(cur16, make_uint4(0, 0, 0, 0), 16u - mb), 0, hi16);
+            }
+          }
+        }
+      }
       const __amdgpu_buffer_rsrc_t qb = buffer_of(y_q + (t0 * H + h0), rows * q_row - (uint32_t)h0);
       const uint32_t off = live ? lane_q : kOut;
-      if (pair_stores) {
+      if constexpr (kShift) {
+      } else if (pair_stores) {
         if (!odd) __builtin_amdgcn_raw_buffer_store_b128((u32x4){c.x, c.y, other.x, other.y}, qb, off, 0, 2);
       } else {
         __builtin_amdgcn_raw_buffer_store_b64((u32x2){c.x, c.y}, qb, off, 0, 2);
       }
-      if (y_bf16 != nullptr)
+      if (!kShift && y_bf16 != nullptr)
         __builtin_amdgcn_raw_buffer_store_b128((u32x4){Yp[0], Yp[1], Yp[2], Yp[3]},
                                                buffer_of(y_bf16 + (t0 * H + h0), 2 * (rows * q_row - (uint32_t)h0)),
                                                live ? lane_h : kOut, 0, 2);
@@ -1958,28 +2118,6 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
 // both ends of a tile's row only the tile's own bytes are written (2- and
 // 4-byte stores), so neighbouring tiles never write the same byte.
 
-// Bytes [s, s + 16) of the 32 bytes lo | hi (lo first), s in [0, 16).
-// (Plain values, not arrays: a select between two array elements can become
-// a select between their addresses, which keeps the array in memory.)
-__device__ __forceinline__ uint4 funnel16(uint4 lo, uint4 hi, uint32_t s) {
-  const bool two = (s & 8u) != 0, one = (s & 4u) != 0;
-  // dwords s/4 .. s/4 + 4 of lo | hi: first down by 2 if s & 8, then by 1 if s & 4
-  const uint32_t q0 = two ? lo.z : lo.x, q1 = two ? lo.w : lo.y, q2 = two ? hi.x : lo.z, q3 = two ? hi.y : lo.w,
-                 q4 = two ? hi.z : hi.x, q5 = two ? hi.w : hi.y;
-  const uint32_t r0 = one ? q1 : q0, r1 = one ? q2 : q1, r2 = one ? q3 : q2, r3 = one ? q4 : q3,
-                 r4 = one ? q5 : q4;
-  const uint32_t b = s & 3u;
-  return make_uint4(__builtin_amdgcn_alignbyte(r1, r0, b), __builtin_amdgcn_alignbyte(r2, r1, b),
-                    __builtin_amdgcn_alignbyte(r3, r2, b), __builtin_amdgcn_alignbyte(r4, r3, b));
-}
-
-// row_ror:n (kCtrl = 0x120 + n): lane p of each 16-lane row takes the value of
-// lane p - n (mod 16).
-template <int kCtrl>
-__device__ __forceinline__ uint32_t row_ror(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kCtrl, 0xf, 0xf, false);
-}
-
 // What a lane reads for one row of one tensor: the aligned 16 bytes at or
 // below the row's byte `at` plus 16 p, and (lanes 0..3) dword p of the
 // aligned 16 bytes 256 bytes further, which lane 15 needs.
@@ -1987,46 +2125,6 @@ struct NarrowRaw {
   uint4 g[kRows], u[kRows], d[kRows];
   uint32_t eg[kRows], eu[kRows], ed[kRows];
 };
-
-__device__ __forceinline__ void load_piece(__amdgpu_buffer_rsrc_t buf, uint32_t at, int p, uint4& v, uint32_t& e) {
-  const uint32_t a = at & ~15u;
-  v = load_buf<0>(buf, a + 16u * (uint32_t)p);
-  e = p < 4 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(buf, a + 256u + 4u * (uint32_t)p, 0, 0) : 0u;
-}
-
-// The eight bf16 values at the row's byte `at` plus 16 p.  Every lane of the
-// wave takes part (the moves read the other lanes of its row).
-__device__ __forceinline__ uint4 piece_values(uint4 v, uint32_t e, uint32_t at, int p) {
-  const bool last = p == 15;
-  const uint32_t n0 = row_ror<0x12F>(v.x), f0 = row_ror<0x12F>(e);  // from lane p + 1 / lane 15 from lane 0
-  const uint32_t n1 = row_ror<0x12F>(v.y), f1 = row_ror<0x12E>(e);  // lane 15 from lane 1
-  const uint32_t n2 = row_ror<0x12F>(v.z), f2 = row_ror<0x12D>(e);  // lane 15 from lane 2
-  const uint32_t n3 = row_ror<0x12F>(v.w), f3 = row_ror<0x12C>(e);  // lane 15 from lane 3
-  const uint4 next = make_uint4(last ? f0 : n0, last ? f1 : n1, last ? f2 : n2, last ? f3 : n3);
-  return funnel16(v, next, at & 15u);
-}
-
-// Bytes [lo, hi) of a 16-byte piece stored at `off` (lo and hi even): the
-// whole piece in one store, else 4- and 2-byte parts.
-__device__ __forceinline__ void store_range16(__amdgpu_buffer_rsrc_t buf, uint32_t off, uint4 v, int lo, int hi) {
-  if (lo == 0 && hi == 16) {
-    __builtin_amdgcn_raw_buffer_store_b128((u32x4){v.x, v.y, v.z, v.w}, buf, off, 0, 0);
-    return;
-  }
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int b0 = 4 * k;
-    if (b0 >= lo && b0 + 4 <= hi) {
-      __builtin_amdgcn_raw_buffer_store_b32(w[k], buf, off + b0, 0, 0);
-    } else {
-      if (b0 >= lo && b0 < hi)
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[k] & 0xffffu), buf, off + b0, 0, 0);
-      if (b0 + 2 >= lo && b0 + 2 < hi)
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[k] >> 16), buf, off + b0 + 2, 0, 0);
-    }
-  }
-}
 
 struct NarrowItem {
   int kind;     // 0: d_gate and y^T, 1: the tile holding position H, 2: d_up
@@ -2053,10 +2151,6 @@ __device__ __forceinline__ NarrowItem narrow_item(int item, int nA, int nP, int6
   return it;
 }
 
-// Word mask of the halves (elements 2k, 2k + 1) below n.
-__device__ __forceinline__ uint32_t halves_below(int k, int n) {
-  return (2 * k < n ? 0x0000ffffu : 0u) | (2 * k + 1 < n ? 0xffff0000u : 0u);
-}
 
 template <Fmt F, int kG>
 __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void silu_quant_bwd_narrow_kernel(
@@ -2375,89 +2469,6 @@ __device__ __forceinline__ float sigma_of(uint32_t gb, int64_t i) {
   return __uint_as_float(g_sigma_tab[((i & 1) ? hi : lo) >> 2]);
 }
 
-// ---------------------------------------------------------------------------
-// The forward quantiser with H not a multiple of 8: rows start off 16 bytes,
-// so the tiled kernel's wide loads do not apply.  A plain path with the same
-// arithmetic: 2-byte loads, byte stores, the sigmoid from the device table, a
-// wave per 128 positions of a row.  A grid-stride loop covers any size.
-
-// One code of a value with inverse scale inv (the low byte).
-template <Fmt F, bool kSafe>
-__device__ __forceinline__ uint32_t code1(float v, float inv) {
-  if constexpr (F == Fmt::kInt8)
-    return code_word<kSafe>(v, inv) & 0xffu;
-  else
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fp8_input<kSafe>(v, inv), 0.0f, 0, false) & 0xffu;
-}
-
-// Maximum over the lanes of a group: all 64, or each 32-lane half for
-// groups of 32.
-template <int kWidth>
-__device__ __forceinline__ float lanes_max(float m) {
-#pragma unroll
-  for (int off = kWidth / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  return m;
-}
-
-// A wave takes 128 consecutive positions of a row (128 / kG groups): lane l
-// the positions l and l + 64, whose groups are reduced over the lanes that
-// share them.  Returns the scale of the lane's group for each of its two
-// positions; a group's first lane stores it at scale_row[group].
-template <Fmt F, int kG>
-__device__ __forceinline__ void narrow_groups(const float (&a)[2], float (&scale)[2], float* scale_row, int64_t c0,
-                                              int64_t n_row, int lane) {
-  float m[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) m[k] = kG == 32 ? lanes_max<32>(a[k]) : lanes_max<64>(a[k]);
-  if (kG == 128) m[0] = m[1] = fmaxf(m[0], m[1]);
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    scale[k] = group_scale<F>(m[k]);
-    const int64_t c = c0 + lane + 64 * k;
-    if ((kG < 128 || k == 0) && lane % (kG < 64 ? kG : 64) == 0 && c < n_row) scale_row[c / kG] = scale[k];
-  }
-}
-
-// The forward quantiser's rows (H-long), 128 positions per wave as above.
-template <int kG>
-__global__ __launch_bounds__(256) void silu_fwd_quant_narrow_kernel(const uint16_t* __restrict__ x,
-                                                                    const float* __restrict__ row_weight,
-                                                                    int8_t* __restrict__ y_q, float* __restrict__ y_s,
-                                                                    uint16_t* __restrict__ y_bf16, int64_t T,
-                                                                    int64_t H) {
-  const int lane = threadIdx.x & 63;
-  const int64_t groups = (H + kG - 1) / kG, units = (H + 127) / 128;
-  const int64_t waves = (int64_t)gridDim.x * 4;
-  for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < T * units; w += waves) {
-    const int64_t t = w / units, c0 = (w - t * units) * 128;
-    const float wt = row_weight != nullptr ? row_weight[t] : 1.0f;
-    uint32_t b[2];
-    float a[2], scale[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int64_t h = c0 + lane + 64 * k;
-      float yv = 0.0f;
-      if (h < H) {
-        const uint32_t gb = x[t * 2 * H + h];
-        yv = (bf16_lo(gb) * sigma_of(gb, 0)) * bf16_lo(x[t * 2 * H + H + h]);
-        if (row_weight != nullptr) yv = yv * wt;
-      }
-      a[k] = fabsf(yv);
-      b[k] = pack_bf16(yv, 0.0f) & 0xffffu;
-    }
-    narrow_groups<Fmt::kInt8, kG>(a, scale, y_s + t * groups, c0, H, lane);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int64_t h = c0 + lane + 64 * k;
-      const float inv = 1.0f / scale[k], yv = bf16_lo(b[k]);
-      if (h < H) {
-        y_q[t * H + h] = (int8_t)(inv == __builtin_huge_valf() ? code1<Fmt::kInt8, true>(yv, inv)
-                                                               : code1<Fmt::kInt8, false>(yv, inv));
-        if (y_bf16 != nullptr) y_bf16[t * H + h] = (uint16_t)b[k];
-      }
-    }
-  }
-}
 
 __global__ void eval_sigmoid_kernel(const uint16_t* __restrict__ gate, float* __restrict__ s, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -2754,21 +2765,15 @@ __attribute__((visibility("default"))) int silu_fwd_quant(const void* x, const f
   for (int i = 0; i < 5; ++i)
     for (int j = i + 1; j < 5; ++j)
       if (bufs[i] && bufs[j] && overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
-  if (H % 8 != 0) {
-    // rows off 16 bytes (x, y_bf16) and 8 bytes (y_q): the plain path
-    int cus = 0;
-    int rc = device_cus(&cus);
-    if (rc != SILUQUANT_OK) return rc;
-    const int64_t waves = T * ((H + 127) / 128);
-    const int64_t grid = std::min<int64_t>((waves + 3) / 4, (int64_t)cus * 16);
-    auto kernel = group == 128 ? silu_fwd_quant_narrow_kernel<128>
-                  : group == 64 ? silu_fwd_quant_narrow_kernel<64>
-                                : silu_fwd_quant_narrow_kernel<32>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(x), row_weight, y_q, y_s, static_cast<uint16_t*>(y_bf16), T, H);
-    return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;
-  }
   const bool w = row_weight != nullptr;
+  if (H % 8 != 0) {
+    // rows off 16 bytes (x, y_bf16) and 8 bytes (y_q): shifted pieces
+    auto kernel = group == 128  ? (w ? silu_fwd_quant_kernel<128, false, true, true> : silu_fwd_quant_kernel<128, false, false, true>)
+                  : group == 64 ? (w ? silu_fwd_quant_kernel<64, false, true, true> : silu_fwd_quant_kernel<64, false, false, true>)
+                                : (w ? silu_fwd_quant_kernel<32, false, true, true> : silu_fwd_quant_kernel<32, false, false, true>);
+    return launch_forward(kernel, x, static_cast<const uint16_t*>(x) + H, 2 * H, row_weight, y_q, y_s, y_bf16, T, H,
+                          stream);
+  }
   auto kernel = group == 128 ? (w ? silu_fwd_quant_kernel<128, false, true> : silu_fwd_quant_kernel<128>)
                 : group == 64 ? (w ? silu_fwd_quant_kernel<64, false, true> : silu_fwd_quant_kernel<64>)
                               : (w ? silu_fwd_quant_kernel<32, false, true> : silu_fwd_quant_kernel<32>);

@@ -142,13 +142,49 @@ def test_forward_groups_workload(group):
     check(x, label="outliers group=%d" % group, group=group)
 
 
-# H not a multiple of 8: the plain path (2-byte loads, byte stores).
-@pytest.mark.parametrize("T,H,group", [(100, 100, 128), (64, 5, 32), (300, 1001, 64), (17, 1, 128), (129, 2050, 32)])
+# H not a multiple of 8: rows off 16 bytes, so the tiled kernel loads aligned
+# pieces and shifts them across lanes, and stores y_q and y_bf16 as aligned
+# pieces with only the unit's own bytes at both ends of a row (rows of 4
+# tokens start at every offset class; T ragged at 4).
+@pytest.mark.parametrize("T,H,group", [(100, 100, 128), (64, 5, 32), (300, 1001, 64), (17, 1, 128), (129, 2050, 32),
+                                       (9, 129, 128), (7, 255, 64), (31, 4095, 32), (2048, 11001, 128),
+                                       (65, 11003, 64), (3, 127, 32)])
 def test_forward_h_not_a_multiple_of_8(T, H, group):
     x, _ = random_inputs(T, H, device=DEV, seed=5 * T + H + group)
     w = torch.rand(T, device=DEV, generator=torch.Generator(device=DEV).manual_seed(T)) * 4 - 2
     check(x, label="narrow T=%d H=%d group=%d" % (T, H, group), group=group)
     check(x, w=w, want_bf16=True, label="narrow T=%d H=%d group=%d weighted" % (T, H, group), group=group)
+
+
+def _random_narrow_shapes(n=10, seed=9091):
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n):
+        H = int(rng.integers(1, 3000))
+        if H % 8 == 0:
+            H += int(rng.integers(1, 8))
+        shapes.append((int(rng.integers(1, 700)), H, int(rng.choice([32, 64, 128]))))
+    return shapes
+
+
+@pytest.mark.parametrize("T,H,group", _random_narrow_shapes())
+def test_forward_h_not_a_multiple_of_8_random(T, H, group):
+    x, _ = random_inputs(T, H, device=DEV, seed=11 * T + H)
+    w = torch.rand(T, device=DEV, generator=torch.Generator(device=DEV).manual_seed(H)) * 4 - 2
+    check(x, w=w, want_bf16=True, label="narrow random T=%d H=%d group=%d weighted" % (T, H, group), group=group)
+
+
+@pytest.mark.parametrize("group", [128, 64, 32])
+def test_forward_tiny_group_maxima_h_not_a_multiple_of_8(group):
+    # as below, with H = 251: the clamped rule on the shifted path
+    T, H = 40, 251
+    t = torch.arange(T, dtype=torch.float64).unsqueeze(1)
+    j = torch.arange(H, dtype=torch.float64).unsqueeze(0)
+    up = ((1 + (j % 64) / 64) * torch.pow(2.0, -110 - t)).to(torch.float32)
+    x = torch.cat([torch.full((T, H), 20.0), up], dim=1).to(torch.bfloat16).to(DEV)
+    check(x, label="tiny maxima H=251 group=%d" % group, group=group)
+    w = torch.full((T,), 0.75, dtype=torch.float32, device=DEV)
+    check(x, w=w, want_bf16=True, label="tiny maxima H=251 weighted group=%d" % group, group=group)
 
 
 @pytest.mark.parametrize("group", [128, 64, 32])

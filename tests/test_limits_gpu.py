@@ -103,6 +103,41 @@ def test_forward_at_the_channel_limit():
     torch.cuda.empty_cache()
 
 
+def test_forward_h_not_a_multiple_of_8_at_the_limits():
+    # the shifted tiled path at H = 2^22 - 1 (T = 64: the last unit of a row is
+    # 127 channels) and at T = 2^25 with H = 3 (every unit one partial
+    # group; the aligned bases of y_q and y_bf16 lie below rows far past 2^32
+    # bytes of x)
+    for T, H, G, rows, cols in ((64, (1 << 22) - 1, 128, None, (0, (1 << 22) - 1 - 300)),
+                                (1 << 25, 3, 32, (0, (1 << 24) + 5, (1 << 25) - 300), None)):
+        print("case forward narrow T=%d H=%d" % (T, H), flush=True)
+        x, _ = _inputs(T, H, 9)
+        yq = torch.empty((T, H), dtype=torch.int8, device=DEV)
+        ys = torch.empty((T, -(-H // G)), dtype=torch.float32, device=DEV)
+        yb = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+        sq.silu_fwd_quant(x, yq, ys, y_bf16=yb, group_size=G)
+        torch.cuda.synchronize()
+        if cols is not None:
+            for h0 in cols:  # whole groups: h0 multiple of G, or the row's last 300 channels from a group start
+                h0 = h0 - h0 % G
+                n = min(H - h0, 384)
+                xs = torch.cat([x[:, h0:h0 + n], x[:, H + h0:H + h0 + n]], dim=1)
+                wq, ws, wb = oracle.silu_fwd_quant(_bits(xs), group_size=G, want_bf16=True)
+                assert np.array_equal(yq[:, h0:h0 + n].cpu().numpy(), wq), h0
+                g0 = h0 // G
+                assert np.array_equal(ys[:, g0:g0 + ws.shape[1]].cpu().numpy().view(np.uint32), ws.view(np.uint32)), h0
+                assert np.array_equal(_bits(yb[:, h0:h0 + n]), wb), h0
+        else:
+            for t0 in rows:
+                xs = x[t0:t0 + 300]
+                wq, ws, wb = oracle.silu_fwd_quant(_bits(xs), group_size=G, want_bf16=True)
+                assert np.array_equal(yq[t0:t0 + 300].cpu().numpy(), wq), t0
+                assert np.array_equal(ys[t0:t0 + 300].cpu().numpy().view(np.uint32), ws.view(np.uint32)), t0
+                assert np.array_equal(_bits(yb[t0:t0 + 300]), wb), t0
+        del x, yq, ys, yb
+        torch.cuda.empty_cache()
+
+
 def test_gemm_at_the_k_limit():
     # K = 2^22 (the largest K): a tile's rows of A span 2^29 bytes of one buffer
     M, N, K = 256, 256, 1 << 22
