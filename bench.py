@@ -154,6 +154,22 @@ def step_series(ms):
             "min": min(us) if us else None, "all": us}
 
 
+def kernel_label(op, H, group=128):
+    """The kernel that does the work of one call at channel count H (group
+    128): the aligned tiled kernels, or the ones for H not a multiple of the
+    group or of 8 (shapes given with --shape)."""
+    if op == "forward_q8_1":
+        return "silu_fwd_quant_kernel<32, q8_1>"
+    if op == "forward":
+        return "silu_fwd_quant_kernel" + (" (shifted pieces)" if H % 8 else "")
+    fmt = "Fmt::kFp8" if op == "fp8" else "Fmt::kInt8"
+    if H % 8:
+        return "silu_quant_bwd_narrow_kernel<%s>" % fmt
+    if H % group:
+        return "silu_quant_bwd_%s_kernel<%s>" % ("carry" if H > 128 else "straddle", fmt)
+    return "silu_quant_bwd_kernel<%s>" % fmt
+
+
 def settle(call, ms: float) -> dict:
     """Run the measured op on an independent batch of the same shape (not the
     timed batch) until ms milliseconds have passed.  On MI355X the pass takes
@@ -494,8 +510,7 @@ def main():
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": measured_traffic({"forward": "forward:", "forward_q8_1": "forward_q8_1:", "fp8": "fp8:"}.get(
                 args.op, "") + w.name),
-            "kernel": {"forward": "silu_fwd_quant_kernel", "forward_q8_1": "silu_fwd_quant_kernel<32, q8_1>",
-                       "fp8": "silu_quant_bwd_kernel<Fmt::kFp8>"}.get(args.op, "silu_quant_bwd_kernel<Fmt::kInt8>"),
+            "kernel": kernel_label(args.op, w.H),
             "avg_launch_us": round(per_launch_s * 1e6, 3),
         },
         "settle": settle_info,
