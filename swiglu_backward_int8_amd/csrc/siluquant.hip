@@ -1734,10 +1734,14 @@ __device__ __forceinline__ uint32_t row_ror(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kCtrl, 0xf, 0xf, false);
 }
 
+// (Every lane issues the dword load, lane p that of lane p mod 4: a load
+// under a lane condition would leave the compiler unable to count the loads
+// in flight, and it would then wait for all of them, stores included, before
+// using any.)
 __device__ __forceinline__ void load_piece(__amdgpu_buffer_rsrc_t buf, uint32_t at, int p, uint4& v, uint32_t& e) {
   const uint32_t a = at & ~15u;
   v = load_buf<0>(buf, a + 16u * (uint32_t)p);
-  e = p < 4 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(buf, a + 256u + 4u * (uint32_t)p, 0, 0) : 0u;
+  e = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(buf, a + 256u + 4u * (uint32_t)(p & 3), 0, 0);
 }
 
 // The eight bf16 values at the row's byte `at` plus 16 p.  Every lane of the
@@ -1828,7 +1832,7 @@ __device__ __forceinline__ float group_lanes_max(float v) {
 
 struct FwdIn {
   uint4 g, u;
-  uint32_t eg, eu;  // with kShift: lanes 0..3 read past the row's 16 pieces
+  uint32_t eg, eu;  // with kShift: a dword past the row's 16 pieces (lane 15 takes lanes 0..3's)
 };
 
 // Sum of the eight signed bytes of two words: a dot product with bytes of 1.
@@ -2119,8 +2123,8 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
 // 4-byte stores), so neighbouring tiles never write the same byte.
 
 // What a lane reads for one row of one tensor: the aligned 16 bytes at or
-// below the row's byte `at` plus 16 p, and (lanes 0..3) dword p of the
-// aligned 16 bytes 256 bytes further, which lane 15 needs.
+// below the row's byte `at` plus 16 p, and dword p mod 4 of the aligned 16
+// bytes 256 bytes further, which lane 15 takes from lanes 0..3.
 struct NarrowRaw {
   uint4 g[kRows], u[kRows], d[kRows];
   uint32_t eg[kRows], eu[kRows], ed[kRows];

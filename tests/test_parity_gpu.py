@@ -433,6 +433,46 @@ def test_hip_graph_capture_and_replay():
         assert np.all(np.abs(C.cpu().numpy() - want) <= (2 * H // 128 + 2) * 2.0**-24 * want_abs)
 
 
+@pytest.mark.parametrize("H", [1376, 1001])
+def test_hip_graph_replay_of_the_other_kernels(H):
+    # The kernels for H not a multiple of the group (1376: runs of blocks) and
+    # of 8 (1001: the two-team position tiles; the forward quantiser's shifted
+    # pieces) captured with the pass's entry points and replayed on new inputs.
+    T = 640
+    x, dy = random_inputs(T, H, device=DEV, seed=47)
+    outs = sq.empty_outputs(T, H, DEV)
+    yq = torch.empty((T, H), dtype=torch.int8, device=DEV)
+    ys = torch.empty((T, -(-H // 128)), dtype=torch.float32, device=DEV)
+    yb = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+
+    def calls():
+        sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *outs)
+        sq.silu_fwd_quant(x, yq, ys, y_bf16=yb)
+
+    s = torch.cuda.Stream(device=DEV)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for seed in (48, 49, 50):
+        x2, dy2 = random_inputs(T, H, device=DEV, seed=seed)
+        x.copy_(x2)
+        dy.copy_(dy2)
+        for o in outs + (yq, ys, yb):
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        compare([o.cpu().numpy() for o in outs], oracle.silu_dot_fwd_bwd_quant_fuse(_bits(x2), _bits(dy2)),
+                "graph replay H=%d %d" % (H, seed))
+        wq, ws, wb = oracle.silu_fwd_quant(_bits(x2), want_bf16=True)
+        assert np.array_equal(yq.cpu().numpy(), wq) and np.array_equal(ys.cpu().numpy(), ws)
+        assert np.array_equal(_bits(yb), wb)
+
+
 # H not a multiple of 8: rows start off 16 bytes (loads take aligned pieces and
 # shift them, code stores write aligned pieces and the tile's own bytes at both
 # ends); groups still straddle d_gate and d_up.
