@@ -1756,36 +1756,51 @@ __device__ __forceinline__ uint4 piece_values(uint4 v, uint32_t e, uint32_t at, 
   return funnel16(v, next, at & 15u);
 }
 
-// Bytes [lo, hi) of a 16-byte piece stored at `off`: the whole piece in one
-// store, else 4- and 2-byte parts, and with kOddEnds single bytes where lo or
-// hi is odd (without it both must be even).
-template <bool kOddEnds = false>
-__device__ __forceinline__ void store_range16(__amdgpu_buffer_rsrc_t buf, uint32_t off, uint4 v, int lo, int hi) {
-  if (lo == 0 && hi == 16) {
-    __builtin_amdgcn_raw_buffer_store_b128((u32x4){v.x, v.y, v.z, v.w}, buf, off, 0, 0);
-    return;
+// Bytes [lo, hi) of the 16-byte piece that lane `src` of this lane's 16-lane
+// DPP row holds, stored at `off`: the piece is spread over the row with
+// ds_bpermute and lane k (k = `at` of the lane) stores the kUnit bytes at
+// kUnit * k that fall in the range, so a partial piece takes one store
+// instruction instead of a chain of 4-, 2- and 1-byte parts on one lane.  All
+// lanes of the wave run it (the spread reads other lanes); `live` masks the
+// store.
+template <int kUnit>
+__device__ __forceinline__ void store_spread(__amdgpu_buffer_rsrc_t buf, uint32_t off, uint4 v, int src, int lo, int hi,
+                                             int at, bool live) {
+  const int addr = 4 * ((int)(threadIdx.x & 48u) + src);  // the source lane within the wave, in bytes
+  const uint32_t w0 = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.x);
+  const uint32_t w1 = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.y);
+  const uint32_t w2 = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.z);
+  const uint32_t w3 = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.w);
+  const int b = kUnit * at;
+  const uint32_t word = (b & 8) ? ((b & 4) ? w3 : w2) : ((b & 4) ? w1 : w0);
+  const uint32_t val = word >> (8 * (b & 3));
+  if (live && b < 16 && b >= lo && b + kUnit <= hi) {
+    if constexpr (kUnit == 1)
+      __builtin_amdgcn_raw_buffer_store_b8((unsigned char)val, buf, off + b, 0, 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)val, buf, off + b, 0, 0);
   }
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int b0 = 4 * k;
-    if (b0 >= lo && b0 + 4 <= hi) {
-      __builtin_amdgcn_raw_buffer_store_b32(w[k], buf, off + b0, 0, 0);
-      continue;
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c0 = b0 + 2 * h;
-      if (c0 >= lo && c0 + 2 <= hi) {
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[k] >> (16 * h)), buf, off + c0, 0, 0);
-      } else if (kOddEnds) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          if (c0 + e >= lo && c0 + e < hi)
-            __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(w[k] >> (16 * h + 8 * e)), buf, off + c0 + e, 0, 0);
-      }
-    }
-  }
+}
+
+// A row segment of `len` bytes starting `m` bytes into the aligned piece at
+// `a0` (m = the start mod 16), whose aligned pieces this lane holds as
+// `chunk` (piece j = the lane's slot) and, for the last slot, `extra` (the
+// piece after it): whole pieces as 16-byte stores from their slots, the
+// partial first and last pieces spread over the row.  kUnit: 1 for byte rows,
+// 2 when m and len are even; slot_lane(j) is the lane that holds piece j,
+// `at` the lane's place in its row for the spread.
+template <int kUnit, int kSlots, typename SlotLane>
+__device__ __forceinline__ void store_segment(__amdgpu_buffer_rsrc_t buf, uint32_t a0, int m, int len, uint4 chunk,
+                                              uint4 extra, int slot, bool holds, SlotLane slot_lane, int at,
+                                              bool live) {
+  const int end = m + len;        // bytes from a0 to the segment's end
+  const int jl = (end - 1) >> 4;  // the piece holding the last byte (at most kSlots)
+  if (live && holds && (slot > 0 || m == 0) && 16 * slot + 16 <= end)
+    __builtin_amdgcn_raw_buffer_store_b128((u32x4){chunk.x, chunk.y, chunk.z, chunk.w}, buf, a0 + 16u * slot, 0, 0);
+  store_spread<kUnit>(buf, a0, chunk, slot_lane(0), m, min(16, end), at, live && (m != 0 || end < 16));
+  const uint4 last = (slot == kSlots - 1 && jl == kSlots) ? extra : chunk;
+  store_spread<kUnit>(buf, a0 + 16u * jl, last, slot_lane(min(jl, kSlots - 1)), 0, end - 16 * jl, at,
+                      live && jl > 0 && (end & 15) != 0);
 }
 
 // Word mask of the halves (elements 2k, 2k + 1) below n.
@@ -2037,33 +2052,23 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
         const uint4 cur16 = make_uint4(Yp[0], Yp[1], Yp[2], Yp[3]);
         const uint4 prev16 = make_uint4(row_ror<0x121>(cur16.x), row_ror<0x121>(cur16.y), row_ror<0x121>(cur16.z),
                                         row_ror<0x121>(cur16.w));
-        if ((uint32_t)r < rows) {
-          const __amdgpu_buffer_rsrc_t qb = buffer_of(y_q + qb0, (uint32_t)(t0 * H + rows * H - qb0));
-          const uint32_t S = (uint32_t)(t0 * H - qb0) + r * (uint32_t)H + (uint32_t)h0, mq = S & 15u, a0 = S - mq;
-          const int mi = (int)mq, j = p >> 1;
-          if (!odd) {
-            const uint4 chunk = mq == 0 ? piece : funnel16(prev, piece, 16u - mq);
-            const int lo = j == 0 ? mi : 0, hi = min(16, len + mi - 16 * j);
-            if (hi > lo) store_range16<true>(qb, a0 + 16u * j, chunk, lo, hi);
-            if (j == 7 && mq != 0) {
-              const int hi8 = min(16, len + mi - 128);
-              if (hi8 > 0) store_range16<true>(qb, a0 + 128u, funnel16(piece, make_uint4(0, 0, 0, 0), 16u - mq), 0, hi8);
-            }
-          }
-          if (y_bf16 != nullptr) {
-            const int64_t bb0 = (t0 * H) & ~(int64_t)7;  // 8 bf16 values = 16 bytes
-            const __amdgpu_buffer_rsrc_t yb = buffer_of(y_bf16 + bb0, (uint32_t)(2 * (t0 * H + rows * H - bb0)));
-            const uint32_t Sb = 2 * ((uint32_t)(t0 * H - bb0) + r * (uint32_t)H + (uint32_t)h0), mb = Sb & 15u,
-                           b0 = Sb - mb;
-            const int mbi = (int)mb;
-            const uint4 chunk = mb == 0 ? cur16 : funnel16(prev16, cur16, 16u - mb);
-            const int lo = p == 0 ? mbi : 0, hi = min(16, 2 * len + mbi - 16 * p);
-            if (hi > lo) store_range16(yb, b0 + 16u * p, chunk, lo, hi);
-            if (p == 15 && mb != 0) {
-              const int hi16 = min(16, 2 * len + mbi - 256);
-              if (hi16 > 0) store_range16(yb, b0 + 256u, funnel16(cur16, make_uint4(0, 0, 0, 0), 16u - mb), 0, hi16);
-            }
-          }
+        const bool row_live = (uint32_t)r < rows;
+        const __amdgpu_buffer_rsrc_t qb = buffer_of(y_q + qb0, (uint32_t)(t0 * H + rows * H - qb0));
+        const uint32_t S = (uint32_t)(t0 * H - qb0) + r * (uint32_t)H + (uint32_t)h0, mq = S & 15u;
+        const uint4 chunk = mq == 0 ? piece : funnel16(prev, piece, 16u - mq);
+        const uint4 extra = funnel16(piece, make_uint4(0, 0, 0, 0), (16u - mq) & 15u);
+        // pieces j = 0..8 of the row: piece j from even lane 2j (the extra one from lane 14)
+        store_segment<1, 8>(qb, S - mq, (int)mq, len, chunk, extra, p >> 1, !odd, [](int j) { return 2 * j; }, p,
+                            row_live);
+        if (y_bf16 != nullptr) {
+          const int64_t bb0 = (t0 * H) & ~(int64_t)7;  // 8 bf16 values = 16 bytes
+          const __amdgpu_buffer_rsrc_t yb = buffer_of(y_bf16 + bb0, (uint32_t)(2 * (t0 * H + rows * H - bb0)));
+          const uint32_t Sb = 2 * ((uint32_t)(t0 * H - bb0) + r * (uint32_t)H + (uint32_t)h0), mb = Sb & 15u;
+          const uint4 chunk16 = mb == 0 ? cur16 : funnel16(prev16, cur16, 16u - mb);
+          const uint4 extra16 = funnel16(cur16, make_uint4(0, 0, 0, 0), (16u - mb) & 15u);
+          // pieces j = 0..16: piece j from lane j (the extra one from lane 15)
+          store_segment<2, 16>(yb, Sb - mb, (int)mb, 2 * len, chunk16, extra16, p, true, [](int j) { return j; }, p,
+                               row_live);
         }
       }
       const __amdgpu_buffer_rsrc_t qb = buffer_of(y_q + (t0 * H + h0), rows * q_row - (uint32_t)h0);
@@ -2412,18 +2417,17 @@ __global__ __launch_bounds__(kThreads, kWorkgroupsPerCU * kThreads / 256) void s
         const uint4 piece = pair_rows16(c[0], c[1], odd);
         const uint4 prev = make_uint4(row_ror<0x122>(piece.x), row_ror<0x122>(piece.y), row_ror<0x122>(piece.z),
                                       row_ror<0x122>(piece.w));
-        if (rho < cur.rows) {
+        {
           const __amdgpu_buffer_rsrc_t gq_buf =
               buffer_of(grad_input_q + cur.t0 * (int64_t)H2, (uint32_t)cur.rows * H2);
-          const uint32_t S = gq_row + (uint32_t)cur.pos0, m = S & 15u, a0 = S - m;
-          const int len = cur.len, mi = (int)m;
+          const uint32_t S = gq_row + (uint32_t)cur.pos0, m = S & 15u;
           const uint4 chunk = m == 0 ? piece : funnel16(prev, piece, 16u - m);
-          const int lo = pair == 0 ? mi : 0, hi = min(16, len + mi - 16 * pair);
-          if (hi > lo) store_range16(gq_buf, a0 + 16u * pair, chunk, lo, hi);
-          if (pair == 7 && m != 0) {
-            const int hi8 = min(16, len + mi - 128);
-            if (hi8 > 0) store_range16(gq_buf, a0 + 128u, funnel16(piece, make_uint4(0, 0, 0, 0), 16u - m), 0, hi8);
-          }
+          const uint4 extra = funnel16(piece, make_uint4(0, 0, 0, 0), (16u - m) & 15u);
+          // the lane's row: pieces j = 0..8 from lanes 2j + (p & 1) (the
+          // extra one from lane 14 or 15), stored 2 bytes per lane of the row
+          const int par = p & 1;
+          store_segment<2, 8>(gq_buf, S - m, (int)m, cur.len, chunk, extra, pair, true,
+                              [par](int j) { return 2 * j + par; }, pair, rho < cur.rows);
         }
         if (!kD) {
           if (safe)
