@@ -2572,15 +2572,17 @@ int launch_backward(const void* x, const void* grad_y, void* grad_input_q, float
     const int per_xcd = ngrid / 8;
     // Team sizes: the split whose slower team needs the fewest rounds over
     // its eighth of the items, a d_gate tile (three inputs, y^T as well)
-    // counting as 1.7 d_up tiles (measured 1.6-2.2); among equal round
-    // counts, the split whose teams' shares of work are closest.
+    // counting as 1.9 d_up tiles (21 of 32 workgroups per XCD where the two
+    // lists are equally long; 20 and 22 measured slower, 22 by up to 90% when
+    // team D falls behind); among equal round counts, the split whose teams'
+    // shares of work are closest.
     int team_a = per_xcd;
     if (items_d > 0) {
       const int64_t xa = (items_a + 7) / 8, xd = (items_d + 7) / 8;
       double best = 0.0;
       for (int a = 1; a < per_xcd; ++a) {
-        const double ra = 1.7 * (double)((xa + a - 1) / a), rd = (double)((xd + per_xcd - a - 1) / (per_xcd - a));
-        const double wa = 1.7 * (double)xa / a, wd = (double)xd / (per_xcd - a);
+        const double ra = 1.9 * (double)((xa + a - 1) / a), rd = (double)((xd + per_xcd - a - 1) / (per_xcd - a));
+        const double wa = 1.9 * (double)xa / a, wd = (double)xd / (per_xcd - a);
         const double cost = (ra > rd ? ra : rd) + 0.01 * (wa > wd ? wa : wd);
         if (a == 1 || cost < best) {
           best = cost;
