@@ -161,6 +161,8 @@ def kernel_label(op, H, group=128):
     if op == "forward_q8_1":
         return "silu_fwd_quant_kernel<32, q8_1>"
     if op == "forward":
+        if H % 8 and H >= 1024 and 100 * (-(-H // 512) * 512) <= 103 * (-(-H // 128) * 128):
+            return "silu_fwd_quant_wide_kernel (rows of 512-channel units, shifted pieces)"
         return "silu_fwd_quant_kernel" + (" (shifted pieces)" if H % 8 else "")
     fmt = "Fmt::kFp8" if op == "fp8" else "Fmt::kInt8"
     if H % 8:

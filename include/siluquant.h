@@ -143,7 +143,8 @@ int silu_dot_fwd_bwd_quant_fuse_fp8(const void* x, const void* grad_y, void* gra
  * Sizes: any T >= 0 (T <= 2^31), any H >= 0 (H <= 2^22); the last group of a
  *   row has the H % group channels that remain when H is not a multiple of
  *   the group.  H not a multiple of 8 (rows off 16 bytes) loads aligned
- *   pieces and shifts them across lanes, and is slower.
+ *   pieces and shifts them across lanes, and is slower; long rows of that
+ *   kind go a token row x 512 channels per wave.
  * Same ownership, asynchrony and error conventions as above.
  */
 int silu_fwd_quant(const void* x, const float* row_weight, int8_t* y_q, float* y_s, void* y_bf16, int64_t T,

@@ -1763,10 +1763,12 @@ __device__ __forceinline__ uint4 piece_values(uint4 v, uint32_t e, uint32_t at, 
 // instruction instead of a chain of 4-, 2- and 1-byte parts on one lane.  All
 // lanes of the wave run it (the spread reads other lanes); `live` masks the
 // store.
-template <int kUnit>
+// With kWave the row is the whole wave: `src` is a lane of the wave.
+template <int kUnit, bool kWave = false>
 __device__ __forceinline__ void store_spread(__amdgpu_buffer_rsrc_t buf, uint32_t off, uint4 v, int src, int lo, int hi,
                                              int at, bool live) {
-  const int addr = 4 * ((int)(threadIdx.x & 48u) + src);  // the source lane within the wave, in bytes
+  // the source lane within the wave, in bytes
+  const int addr = kWave ? 4 * src : 4 * ((int)(threadIdx.x & 48u) + src);
   const uint32_t w0 = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.x);
   const uint32_t w1 = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.y);
   const uint32_t w2 = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.z);
@@ -1789,7 +1791,7 @@ __device__ __forceinline__ void store_spread(__amdgpu_buffer_rsrc_t buf, uint32_
 // partial first and last pieces spread over the row.  kUnit: 1 for byte rows,
 // 2 when m and len are even; slot_lane(j) is the lane that holds piece j,
 // `at` the lane's place in its row for the spread.
-template <int kUnit, int kSlots, typename SlotLane>
+template <int kUnit, int kSlots, bool kWave = false, typename SlotLane>
 __device__ __forceinline__ void store_segment(__amdgpu_buffer_rsrc_t buf, uint32_t a0, int m, int len, uint4 chunk,
                                               uint4 extra, int slot, bool holds, SlotLane slot_lane, int at,
                                               bool live) {
@@ -1797,9 +1799,9 @@ __device__ __forceinline__ void store_segment(__amdgpu_buffer_rsrc_t buf, uint32
   const int jl = (end - 1) >> 4;  // the piece holding the last byte (at most kSlots)
   if (live && holds && (slot > 0 || m == 0) && 16 * slot + 16 <= end)
     __builtin_amdgcn_raw_buffer_store_b128((u32x4){chunk.x, chunk.y, chunk.z, chunk.w}, buf, a0 + 16u * slot, 0, 0);
-  store_spread<kUnit>(buf, a0, chunk, slot_lane(0), m, min(16, end), at, live && (m != 0 || end < 16));
+  store_spread<kUnit, kWave>(buf, a0, chunk, slot_lane(0), m, min(16, end), at, live && (m != 0 || end < 16));
   const uint4 last = (slot == kSlots - 1 && jl == kSlots) ? extra : chunk;
-  store_spread<kUnit>(buf, a0 + 16u * jl, last, slot_lane(min(jl, kSlots - 1)), 0, end - 16 * jl, at,
+  store_spread<kUnit, kWave>(buf, a0 + 16u * jl, last, slot_lane(min(jl, kSlots - 1)), 0, end - 16 * jl, at,
                       live && jl > 0 && (end & 15) != 0);
 }
 
@@ -2089,6 +2091,161 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
             buffer_of(y_s + (t0 * groups + h0 / kG), 4 * (rows * (uint32_t)groups - (uint32_t)(h0 / kG))),
             live ? lane_s : kOut, 0, 0);
     }
+    in = in_next;
+    in_next = in_next2;
+    cur = nxt;
+    nxt = nxt2;
+  }
+}
+
+// The forward quantiser for long rows that start at any even byte offset (H
+// not a multiple of 8, x = [gate | up]): a wave owns one row x 512 channels
+// per unit, 16-lane DPP row k holding channels 128 k .. 128 k + 127 of the
+// unit (lane p of it 8 channels, loaded as in the kShift form above).  A
+// unit's codes and y then leave as one run of aligned pieces, each piece put
+// together from the lane that holds it and the one before it in the wave, so
+// a 128-byte line of y_q or y_bf16 is split between two units only at every
+// fourth channel block, where the 4-row units of the kShift form split one at
+// every block of every row.
+template <int kG, bool kWeighted>
+__global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_wide_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ row_weight, int8_t* __restrict__ y_q,
+    float* __restrict__ y_s, uint16_t* __restrict__ y_bf16, int64_t T, int64_t H, int tiles_w) {
+  __shared__ __align__(16) float s_tab[kSigEntries];
+  __shared__ __align__(16) float2 s_qtab[128];
+  const int tid = threadIdx.x;
+  {
+    const float4* src = reinterpret_cast<const float4*>(g_sigma_tab);
+    float4* dst = reinterpret_cast<float4*>(s_tab);
+    for (int i = tid; i < kSigEntries / 4; i += kFwdThreads) dst[i] = src[i];
+    fill_scale_table(s_qtab, tid);
+  }
+  __syncthreads();
+
+  const int lane = tid & 63;
+  const int k = lane >> 4, p = lane & 15;
+  const bool odd = p & 1;
+  constexpr int kWide = 4 * kTile;  // channels per unit
+  const int64_t waves = (int64_t)gridDim.x * (kFwdThreads / 64);
+  const int64_t first = (int64_t)blockIdx.x * (kFwdThreads / 64) + __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t units = T * tiles_w;
+  const int64_t step_t = waves / tiles_w, step_w = waves - step_t * tiles_w;
+  const int64_t groups = (H + kG - 1) / kG;
+  const uint32_t up_bytes = (uint32_t)(2 * H);
+  // unit (t, w): row t, channels kWide w .. kWide w + kWide - 1; units are
+  // walked row-major, w, w + waves, ... per wave
+  struct Unit {
+    int64_t t, w;
+  };
+  auto advance = [&](Unit& c) {
+    c.t += step_t;
+    c.w += step_w;
+    if (c.w >= tiles_w) {
+      c.w -= tiles_w;
+      ++c.t;
+    }
+  };
+  // Row t of x starts at byte 4 H t, which need not be a multiple of 16: the
+  // buffer starts at the aligned byte at or below it and ends at the row's
+  // end rounded up to 16 bytes (the piece that holds the last byte, which
+  // cannot cross a page); the lane's channels start at byte `at` of it.
+  auto row_skew = [&](const Unit& c) { return (uint32_t)((4 * H * c.t) & 15); };
+  auto at_gate = [&](const Unit& c) { return row_skew(c) + 2 * (uint32_t)(c.w * kWide + kTile * k); };
+  auto load = [&](FwdIn& in, const Unit& c) {
+    const int64_t row0 = 4 * H * c.t;  // bytes
+    const __amdgpu_buffer_rsrc_t xb =
+        buffer_of(reinterpret_cast<char*>(const_cast<uint16_t*>(x)) + (row0 & ~(int64_t)15),
+                  (row_skew(c) + (uint32_t)(4 * H) + 15u) & ~15u);
+    load_piece(xb, at_gate(c), p, in.g, in.eg);
+    load_piece(xb, at_gate(c) + up_bytes, p, in.u, in.eu);
+  };
+
+  Unit cur = {first / tiles_w, first - (first / tiles_w) * tiles_w};
+  FwdIn in, in_next, in_next2;
+  Unit nxt = cur;
+  advance(nxt);
+  if (first < units) load(in, cur);
+  if (first + waves < units) load(in_next, nxt);
+  for (int64_t u = first; u < units; u += waves) {
+    Unit nxt2 = nxt;
+    advance(nxt2);
+    if (u + 2 * waves < units) load(in_next2, nxt2);
+    const int64_t t = cur.t, h0 = cur.w * kWide + kTile * k;  // the lane's DPP row starts at channel h0
+    const int len = H - cur.w * kWide < kWide ? (int)(H - cur.w * kWide) : kWide;  // channels of the unit
+    float wt = 1.0f;
+    if constexpr (kWeighted) wt = row_weight[t];
+    uint4 g4 = piece_values(in.g, in.eg, at_gate(cur), p);
+    const uint4 u4 = piece_values(in.u, in.eu, at_gate(cur) + up_bytes, p);
+    // channels past H read as zeros
+    const int n = (int)(H - h0) - 8 * p;
+    g4 = make_uint4(g4.x & halves_below(0, n), g4.y & halves_below(1, n), g4.z & halves_below(2, n),
+                    g4.w & halves_below(3, n));
+    const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w};
+    const uint32_t uw[4] = {u4.x, u4.y, u4.z, u4.w};
+    uint32_t Yp[4];
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t olo, ohi;
+      sigma_offsets2(gw[e], olo, ohi);
+      const float s0 = lds_f32(s_tab, olo), s1 = lds_f32(s_tab, ohi);
+      float y0 = (bf16_lo(gw[e]) * s0) * bf16_lo(uw[e]);
+      float y1 = (bf16_hi(gw[e]) * s1) * bf16_hi(uw[e]);
+      if constexpr (kWeighted) {
+        y0 = y0 * wt;
+        y1 = y1 * wt;
+      }
+      Yp[e] = pack_bf16(y0, y1);
+      m = amax3(m, y0, y1);
+    }
+    m = group_lanes_max<kG>(m);
+    float scale, inv;
+    scale_and_inverse(m, s_qtab, scale, inv);
+    uint2 c;
+    if (__builtin_expect(inv == __builtin_huge_valf(), 0))
+      c = codes8<true>(Yp, inv);
+    else
+      c = codes8<false>(Yp, inv);
+    const uint2 other = make_uint2(swap_neighbour(c.x), swap_neighbour(c.y));
+    // Pieces of the unit's codes: even lane 2j holds piece j (its own 8 codes
+    // and the odd lane's), the previous piece comes from lane 2j - 2 of the
+    // wave.  The unit's codes start m_q bytes into the aligned piece at
+    // q_base; stores reach no further than the row's end.
+    const int64_t sq = t * H + cur.w * kWide;  // the unit's first code
+    const int64_t q_base = sq & ~(int64_t)15;
+    const uint32_t mq = (uint32_t)(sq & 15);
+    const __amdgpu_buffer_rsrc_t qb = buffer_of(y_q + q_base, (uint32_t)(t * H + H - q_base));
+    const uint4 piece = make_uint4(c.x, c.y, other.x, other.y);
+    const int from2 = 4 * ((lane + 62) & 63), from1 = 4 * ((lane + 63) & 63);
+    const uint4 prev = make_uint4(
+        (uint32_t)__builtin_amdgcn_ds_bpermute(from2, (int)piece.x), (uint32_t)__builtin_amdgcn_ds_bpermute(from2, (int)piece.y),
+        (uint32_t)__builtin_amdgcn_ds_bpermute(from2, (int)piece.z), (uint32_t)__builtin_amdgcn_ds_bpermute(from2, (int)piece.w));
+    const uint4 chunk = mq == 0 ? piece : funnel16(prev, piece, 16u - mq);
+    const uint4 extra = funnel16(piece, make_uint4(0, 0, 0, 0), (16u - mq) & 15u);
+    // pieces j = 0..32: piece j from even lane 2j (the extra one from lane 62)
+    store_segment<1, 32, true>(qb, 0, (int)mq, len, chunk, extra, lane >> 1, !odd, [](int j) { return 2 * j; }, lane,
+                               true);
+    if (y_bf16 != nullptr) {
+      // lane j holds piece j of the unit's y (8 values), the previous one
+      // comes from lane j - 1
+      const int64_t b_base = sq & ~(int64_t)7;  // 8 bf16 values = 16 bytes
+      const uint32_t mb = 2 * (uint32_t)(sq & 7);
+      const __amdgpu_buffer_rsrc_t yb = buffer_of(y_bf16 + b_base, (uint32_t)(2 * (t * H + H - b_base)));
+      const uint4 cur16 = make_uint4(Yp[0], Yp[1], Yp[2], Yp[3]);
+      const uint4 prev16 = make_uint4(
+          (uint32_t)__builtin_amdgcn_ds_bpermute(from1, (int)cur16.x), (uint32_t)__builtin_amdgcn_ds_bpermute(from1, (int)cur16.y),
+          (uint32_t)__builtin_amdgcn_ds_bpermute(from1, (int)cur16.z), (uint32_t)__builtin_amdgcn_ds_bpermute(from1, (int)cur16.w));
+      const uint4 chunk16 = mb == 0 ? cur16 : funnel16(prev16, cur16, 16u - mb);
+      const uint4 extra16 = funnel16(cur16, make_uint4(0, 0, 0, 0), (16u - mb) & 15u);
+      // pieces j = 0..64: piece j from lane j (the extra one from lane 63)
+      store_segment<2, 64, true>(yb, 0, (int)mb, 2 * len, chunk16, extra16, lane, true, [](int j) { return j; }, lane,
+                                 true);
+    }
+    // the group's scale from its first lane
+    const bool live = h0 + 8 * p < H;
+    if (p % (kG / 8) == 0)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(scale), buffer_of(y_s + t * groups, 4 * (uint32_t)groups),
+                                            live ? 4 * (uint32_t)((h0 + 8 * p) / kG) : 0x80000000u, 0, 0);
     in = in_next;
     in_next = in_next2;
     cur = nxt;
@@ -2702,6 +2859,35 @@ int launch_forward(ForwardKernel kernel, const void* gate, const void* up, int64
   return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;
 }
 
+// The wide forward kernel serves H not a multiple of 8 from this many channels
+// on, when its 512-channel units pad a row by at most 3% more than 128-channel
+// ones: a unit's idle lanes cost more than its whole lines save (T = 16384:
+// H = 11001, padded 2.3% more, 229 against 236 us; H = 2753 and 1377, 9% more,
+// 1-2% slower; H = 1025, 33% more, 14% slower).
+constexpr int64_t kFwdWideMinH = 1024;
+bool forward_wide(int64_t H) {
+  const int64_t wide = (H + 4 * kTile - 1) / (4 * kTile) * (4 * kTile), narrow = (H + kTile - 1) / kTile * kTile;
+  return H % 8 != 0 && H >= kFwdWideMinH && 100 * wide <= 103 * narrow;
+}
+
+int launch_forward_wide(bool weighted, int64_t group, const void* x, const float* row_weight, int8_t* y_q,
+                        float* y_s, void* y_bf16, int64_t T, int64_t H, hipStream_t stream) {
+  int cus = 0;
+  int rc = device_cus(&cus);
+  if (rc != SILUQUANT_OK) return rc;
+  const int tiles_w = (int)((H + 4 * kTile - 1) / (4 * kTile));
+  const int64_t units = T * tiles_w;
+  int64_t grid = (int64_t)cus * kFwdWorkgroupsPerCU;
+  const int64_t wg_needed = (units + kFwdThreads / 64 - 1) / (kFwdThreads / 64);
+  if (wg_needed < grid) grid = wg_needed;
+  auto kernel = group == 128  ? (weighted ? silu_fwd_quant_wide_kernel<128, true> : silu_fwd_quant_wide_kernel<128, false>)
+                : group == 64 ? (weighted ? silu_fwd_quant_wide_kernel<64, true> : silu_fwd_quant_wide_kernel<64, false>)
+                              : (weighted ? silu_fwd_quant_wide_kernel<32, true> : silu_fwd_quant_wide_kernel<32, false>);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kFwdThreads), 0, stream, static_cast<const uint16_t*>(x),
+                     row_weight, y_q, y_s, static_cast<uint16_t*>(y_bf16), T, H, tiles_w);
+  return hipGetLastError() == hipSuccess ? SILUQUANT_OK : SILUQUANT_ERR_LAUNCH_FAILED;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2776,6 +2962,8 @@ __attribute__((visibility("default"))) int silu_fwd_quant(const void* x, const f
     for (int j = i + 1; j < 5; ++j)
       if (bufs[i] && bufs[j] && overlaps(bufs[i], sizes[i], bufs[j], sizes[j])) return SILUQUANT_ERR_OVERLAP;
   const bool w = row_weight != nullptr;
+  if (forward_wide(H))
+    return launch_forward_wide(w, group, x, row_weight, y_q, y_s, y_bf16, T, H, stream);
   if (H % 8 != 0) {
     // rows off 16 bytes (x, y_bf16) and 8 bytes (y_q): shifted pieces
     auto kernel = group == 128  ? (w ? silu_fwd_quant_kernel<128, false, true, true> : silu_fwd_quant_kernel<128, false, false, true>)

@@ -174,6 +174,40 @@ def test_forward_h_not_a_multiple_of_8_random(T, H, group):
     check(x, w=w, want_bf16=True, label="narrow random T=%d H=%d group=%d weighted" % (T, H, group), group=group)
 
 
+def _takes_wide_rows(H):
+    # the library's choice for H not a multiple of 8: rows of 512-channel units
+    # when H >= 1024 and they pad a row by at most 3% more than 128-channel units
+    wide, narrow = -(-H // 512) * 512, -(-H // 128) * 128
+    return H % 8 != 0 and H >= 1024 and 100 * wide <= 103 * narrow
+
+
+# Long rows take units of one token x 512 channels, each unit's codes and y
+# stored as one run of aligned pieces: rows that fill their units, a last unit
+# of 511 channels or of one channel, every offset class of a row's start.
+@pytest.mark.parametrize("T,H,group", [(5, 1535, 128), (9, 2047, 64), (3, 4607, 32), (5, 33281, 128), (130, 3583, 128),
+                                       (66, 6143, 64), (7, 1531, 32), (17, 12287, 128)])
+def test_forward_wide_rows(T, H, group):
+    assert _takes_wide_rows(H)
+    x, _ = random_inputs(T, H, device=DEV, seed=7 * T + H + group)
+    w = torch.rand(T, device=DEV, generator=torch.Generator(device=DEV).manual_seed(H + 1)) * 4 - 2
+    check(x, label="wide rows T=%d H=%d group=%d" % (T, H, group), group=group)
+    check(x, w=w, want_bf16=True, label="wide rows T=%d H=%d group=%d weighted" % (T, H, group), group=group)
+
+
+@pytest.mark.parametrize("group", [128, 64, 32])
+def test_forward_tiny_group_maxima_wide_rows(group):
+    # as below, with H = 1535 (units of 512 channels): the clamped rule there
+    T, H = 40, 1535
+    assert _takes_wide_rows(H)
+    t = torch.arange(T, dtype=torch.float64).unsqueeze(1)
+    j = torch.arange(H, dtype=torch.float64).unsqueeze(0)
+    up = ((1 + (j % 64) / 64) * torch.pow(2.0, -110 - t)).to(torch.float32)
+    x = torch.cat([torch.full((T, H), 20.0), up], dim=1).to(torch.bfloat16).to(DEV)
+    check(x, label="tiny maxima H=1535 group=%d" % group, group=group)
+    w = torch.full((T,), 0.75, dtype=torch.float32, device=DEV)
+    check(x, w=w, want_bf16=True, label="tiny maxima H=1535 weighted group=%d" % group, group=group)
+
+
 @pytest.mark.parametrize("group", [128, 64, 32])
 def test_forward_tiny_group_maxima_h_not_a_multiple_of_8(group):
     # as below, with H = 251: the clamped rule on the shifted path
