@@ -22,12 +22,14 @@
 //
 // Kernel: 256 threads (4 waves in a 2 x 2 grid) per 128 x 128 tile of C, and
 // two workgroups per CU, so that one's loads and promotion overlap the other's
-// MFMAs.  Each wave owns 64 x 64 = 2 x 2 MFMA blocks of 32 x 32.  Per group,
-// the A and B tiles (128 x 128 bytes each) and their scales are staged in LDS,
-// double buffered: the next group is loaded into registers while the matrix
-// cores work on this one.  Tiles are handed out in groups of 4 tile-rows, and
-// each XCD takes a contiguous range of that order, so that the workgroups
-// resident on one XCD share A and B tiles in its L2.
+// MFMAs.  Each wave owns 64 x 64 = 2 x 2 MFMA blocks of 32 x 32.  Per stage of
+// 128 along K, the A and B tiles (128 x 128 bytes each) and the scales of the
+// stage's groups go from memory straight into LDS (buffer loads with the lds
+// flag: no staging registers, no LDS write instructions), double buffered:
+// the next stage is in flight while the matrix cores work on this one.  Tiles
+// are handed out in groups of 4 tile-rows, and each XCD takes a contiguous
+// range of that order, so that the workgroups resident on one XCD share A and
+// B tiles in its L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,27 +39,26 @@
 
 namespace {
 
-constexpr int kBK = 128;                  // the K step: one group
+constexpr int kBK = 128;                  // the K stage
 constexpr int kWavesM = 2, kWavesN = 2;   // wave grid of a workgroup
 constexpr int kBM = 64 * kWavesM, kBN = 64 * kWavesN;  // tile of C: 128 x 128
 constexpr int kGemmThreads = 64 * kWavesM * kWavesN;   // 256
+constexpr int kWaves = kGemmThreads / 64;
 constexpr int kGroupM = 4;                // tile-rows per raster group (2, 6, 8, 16, 32 measured slower)
-constexpr int kStageBytes = (kBM + kBN) * kBK;         // A and B tiles of one group
-constexpr int kChunksPerThread = kStageBytes / 16 / kGemmThreads;  // 16-byte chunks staged per thread
-constexpr int kAChunks = kBM * kBK / 16;  // chunk ids below this are A's, the rest B's
-static_assert(kStageBytes % (16 * kGemmThreads) == 0, "whole chunks per thread");
-static_assert(kAChunks % kGemmThreads == 0, "a thread's chunks are all A or all B per step");
-static_assert(kBM + kBN <= kGemmThreads, "one scale per thread");
+constexpr int kOpBytes = kBM * kBK;       // one operand's stage: 16 KB
+constexpr int kStageBytes = 2 * kOpBytes; // A, then B
+constexpr int kRowsPerLoad = 8;           // a wave-wide 16-byte-per-lane load covers 8 rows of 128 bytes
+constexpr int kLoadsPerWave = kBM / kRowsPerLoad / kWaves;  // per operand and stage: 4
+static_assert(kBM == kBN && kBM + kBN == kGemmThreads, "one scale per thread; A and B share row offsets");
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 // LDS layout of a tile: rows of 128 bytes, whose eight 16-byte chunks are
-// stored at positions XOR-permuted by the row.  Staging writes (eight lanes
-// per row, one chunk each) and MFMA operand reads (32 consecutive rows, one
-// chunk each) then both fall on distinct banks, for 32 or 64 banks.  Byte
-// offset of logical chunk c (0..7) of row r:
-__device__ __forceinline__ int lds_at(int r, int c) { return r * kBK + 16 * (c ^ ((r ^ (r >> 3)) & 7)); }
+// stored at positions XOR-permuted by the row.  MFMA operand reads (32
+// consecutive rows, one chunk each) then fall on distinct banks, for 32 or 64
+// banks.  Logical chunk c of row r sits at physical chunk c ^ swz(r):
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -65,30 +66,49 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+// Buffer resource words: base, 32-bit record count (loads at or past it read
+// as zeros), raw addressing.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return (i32x4){(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xFFFF, (int)bytes, 0x00020000};
 }
 
-// One stage (128 of K) in flight: kChunksPerThread 16-byte chunks and the
-// thread's scale of each of the stage's kSub groups.
-template <int kSub>
-struct Stage {
-  i32x4 v[kChunksPerThread];
-  float sc[kSub], sb[kSub];
-};
+// Loads into LDS: each lane reads 16 (or 4) bytes at voffset + soffset of the
+// buffer (voffset is range-checked against the record count) and the wave
+// writes them, lane by lane, to consecutive LDS bytes from address lds (M0)
+// on.  They are written as asm so that the compiler, which cannot tell which
+// LDS bytes they write, does not wait for all of them before every LDS read;
+// the kernel waits for them itself (wait_vm) before the barrier that
+// publishes a stage.  The instructions have no register result.
+__device__ __forceinline__ void lds_load16(i32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+__device__ __forceinline__ void lds_load4(i32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("buffer_load_dword %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
 
-// kBlockScale: B's scale rows cover 128 rows (constant over a wave's 64
-// columns).  kG: the group size along K (128, 64 or 32); a stage of 128 of K
-// holds kSub = 128 / kG groups, each promoted on its own.
+// kBlockScale: B's scale rows cover 128 rows (one scale per tile and group).
+// kG: the group size along K (128, 64 or 32); a stage holds kSub = 128 / kG
+// groups, each promoted on its own.
 template <bool kBf16Out, bool kBlockScale, int kG>
 __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* __restrict__ A,
                                                                   const float* __restrict__ sA,
                                                                   const int8_t* __restrict__ B,
                                                                   const float* __restrict__ sB, void* __restrict__ C,
-                                                                  int64_t M, int64_t N, int64_t K, int b_rows,
-                                                                  int tiles_m, int tiles_n, int per_xcd) {
+                                                                  int64_t M, int64_t N, int64_t K, int tiles_m,
+                                                                  int tiles_n, int per_xcd) {
+  constexpr int kSub = kBK / kG, kStepsPerGroup = kG / 32;  // MFMA k-steps (32 of K) per group
   __shared__ __attribute__((aligned(16))) char s_tile[2][kStageBytes];
-  constexpr int kSub = kBK / kG, kStepsPerGroup = 4 / kSub;  // MFMA k-steps (32 of K) per group
+  // scales of the stage's groups: [buffer][group in stage][A rows, then B rows]
   __shared__ __attribute__((aligned(16))) float s_scale[2][kSub][kBM + kBN];
 
   const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -101,67 +121,60 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
   const int tm = first_m + in_group % gsz, tn = in_group / gsz;
   const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = (wave / kWavesN) * 64, wn = (wave % kWavesN) * 64;  // the wave's 64 x 64 corner
   // K is a multiple of kG; with kG < 128 the last stage may hold fewer than
-  // kSub groups, and its chunks past K read as zeros (see load_stage).
+  // kSub groups, and its chunks past K read as zeros.
   const int stages = (int)((K + kBK - 1) / kBK), groups = (int)(K / kG);
 
-  // Rows past M or N read as zeros: the buffer's record count ends at the last row.
+  // Rows past M or N read as zeros: the record count ends at the tile's last
+  // row, and every row offset is in the range-checked lane offset.
   const int a_rows = M - m0 < kBM ? (int)(M - m0) : kBM;
   const int b_rows_here = N - n0 < kBN ? (int)(N - n0) : kBN;
-  const __amdgpu_buffer_rsrc_t ra = rsrc(A + m0 * K, (int64_t)a_rows * K);
-  const __amdgpu_buffer_rsrc_t rb = rsrc(B + n0 * K, (int64_t)b_rows_here * K);
-  // this thread's scale: A rows for tid < kBM, then B rows
-  const bool sc_is_a = tid < kBM;
-  const int sc_row = sc_is_a ? tid : tid - kBM;
-  const bool sc_live = tid < kBM + kBN && (sc_is_a ? sc_row < a_rows : sc_row < b_rows_here);
-  const float* sc_ptr = sc_is_a ? sA + (m0 + sc_row) * groups : sB + ((n0 + sc_row) / b_rows) * groups;
-  // with block scales one B scale covers the whole tile (n0 is a multiple of
-  // 128): it is folded into the A scales when they are staged
-  const float* sb_blk = sB + (n0 / kBN) * groups;
+  const i32x4 ra = rsrc_words(A + m0 * K, (int64_t)a_rows * K);
+  const i32x4 rb = rsrc_words(B + n0 * K, (int64_t)b_rows_here * K);
+  // Scales: waves 0-1 load the tile's A rows, waves 2-3 its B rows (with
+  // block scales, the tile's one B scale into every B slot).
+  const bool sc_a = wave < 2;
+  const i32x4 rsc = sc_a ? rsrc_words(sA + m0 * groups, (int64_t)a_rows * groups * 4)
+                    : kBlockScale ? rsrc_words(sB + (n0 / kBN) * groups, (int64_t)groups * 4)
+                                  : rsrc_words(sB + n0 * groups, (int64_t)b_rows_here * groups * 4);
+  const uint32_t sc_voff = (!sc_a && kBlockScale) ? 0u : (uint32_t)((64 * (wave & 1) + lane) * groups * 4);
 
-  // Chunk i of this thread is row (tid >> 3) + d of A or of B (d a multiple
-  // of 32), 16-byte chunk tid & 7: one byte offset per thread, the row step in
-  // the scalar offset.  In LDS, row r + d (r < 32 or d a multiple of 64) has
-  // the swizzle of row r XOR (d / 8) mod 8, so the store offsets are the
-  // thread's offset XOR a constant plus a constant.
-  constexpr int kAPer = kAChunks / kGemmThreads;  // A chunks per thread
-  const int g_off = (tid >> 3) * (int)K + 16 * (tid & 7);
-  // In a last stage that K ends inside (a multiple of 32 bytes), the chunks
-  // past K take an offset past the record count and read as zeros; so do
-  // their groups' scales, which do not exist.
+  // Load j of this wave per operand covers rows R0 = 8 (4 w + j) + [0, 8):
+  // lane L writes LDS row R0 + L / 8 at physical chunk L % 8, so it reads
+  // logical chunk (L % 8) ^ swz(row) of that row.
+  uint32_t voff[kLoadsPerWave], voff_last[kLoadsPerWave];
   const int k_last = (stages - 1) * kBK;
-  const int g_off_last = 16 * (tid & 7) < K - k_last ? g_off : (int)0x80000000;
-  const int l_off = lds_at(tid >> 3, tid & 7);
-  auto load_stage = [&](int g, Stage<kSub>& st) {
-    const int k0 = g * kBK;
-    const int off = g == stages - 1 ? g_off_last : g_off;
 #pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      const int row_step = (i < kAPer ? i : i - kAPer) * (kGemmThreads / 8);
-      st.v[i] = __builtin_bit_cast(
-          i32x4, __builtin_amdgcn_raw_buffer_load_b128(i < kAPer ? ra : rb, off, k0 + row_step * (int)K, 0));
+  for (int j = 0; j < kLoadsPerWave; ++j) {
+    const int R = kRowsPerLoad * (kLoadsPerWave * wave + j) + (lane >> 3);
+    const int c = (lane & 7) ^ swz(R);
+    voff[j] = (uint32_t)(R * K + 16 * c);
+    // in a last stage that K ends inside (a multiple of 32 bytes), chunks
+    // past K read as zeros
+    voff_last[j] = 16 * c < K - k_last ? voff[j] : 0x80000000u;
+  }
+  const uint32_t lds_tile = (uint32_t)reinterpret_cast<uintptr_t>(&s_tile[0][0]);
+  const uint32_t lds_scale = (uint32_t)reinterpret_cast<uintptr_t>(&s_scale[0][0][0]);
+
+  // Stage s into buffer s % 2: the scales of its groups, then the A and B rows.
+  auto issue = [&](int s) {
+    const int buf = s & 1;
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
+      const int g = s * kSub + u;
+      if (g < groups)
+        lds_load4(rsc, lds_scale + 4 * ((buf * kSub + u) * (kBM + kBN) + 64 * wave), sc_voff, (uint32_t)(4 * g));
     }
+    const bool last = s == stages - 1;
+    const uint32_t k0 = (uint32_t)(s * kBK);
 #pragma unroll
-    for (int j = 0; j < kSub; ++j) {
-      const bool live = g * kSub + j < groups;
-      st.sc[j] = sc_live && live ? sc_ptr[g * kSub + j] : 0.0f;
-      if constexpr (kBlockScale) st.sb[j] = live ? sb_blk[g * kSub + j] : 0.0f;
-    }
-  };
-  auto store_stage = [&](int buf, const Stage<kSub>& st) {
-#pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      const int row_step = (i < kAPer ? i : i - kAPer) * (kGemmThreads / 8);
-      *reinterpret_cast<i32x4*>(&s_tile[buf][(i < kAPer ? 0 : kBM * kBK) + row_step * kBK +
-                                            (l_off ^ (16 * ((row_step >> 3) & 7)))]) = st.v[i];
-    }
-#pragma unroll
-    for (int j = 0; j < kSub; ++j) {
-      float sc = st.sc[j];
-      if constexpr (kBlockScale) sc = sc_is_a ? sc * st.sb[j] : 0.0f;
-      if (tid < kBM + kBN) s_scale[buf][j][tid] = sc;
+    for (int j = 0; j < kLoadsPerWave; ++j) {
+      const uint32_t at = lds_tile + buf * kStageBytes + kRowsPerLoad * (kLoadsPerWave * wave + j) * kBK;
+      lds_load16(ra, at, last ? voff_last[j] : voff[j], k0);
+      lds_load16(rb, at + kOpBytes, last ? voff_last[j] : voff[j], k0);
     }
   };
 
@@ -179,43 +192,42 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
   // multiples of 64 and lrow < 32, the swizzled chunk position of block i is
   // that of block 0 with bit 2 flipped, and k-step s flips bits 1-2 by s: the
   // offset of (i, s) is the (0, 0) offset XOR 32 s XOR 64 i, plus 4096 i.
-  const int a_base = lds_at(wm + lrow, lhalf);
-  const int b_base = kBM * kBK + lds_at(wn + lrow, lhalf);
+  const int a_base = (wm + lrow) * kBK + 16 * (lhalf ^ swz(wm + lrow));
+  const int b_base = kOpBytes + (wn + lrow) * kBK + 16 * (lhalf ^ swz(wn + lrow));
   auto off = [](int base, int blk, int s) { return (base ^ (32 * s) ^ (64 * blk)) + 32 * kBK * blk; };
 
-  // One group from LDS buffer buf: 4 k-steps of 2 x 2 MFMAs into exact int32
-  // sums, then acc += float(I) * (sA[m] * sB[n]).  The lane's rows are
-  // 8 q + 4 lhalf + e (q = r / 4, e = r % 4) of each 32-row block, its column
-  // lrow of each 32-column block.  With block scales the staged A scale
-  // already holds the product.
-  auto compute = [&](int buf) {
+  // One stage from LDS buffer buf: per group, its k-steps of 2 x 2 MFMAs into
+  // exact int32 sums, then acc += float(I) * (sA[m] * sB[n]).  The lane's
+  // rows are 8 q + 4 lhalf + e (q = r / 4, e = r % 4) of each 32-row block,
+  // its column lrow of each 32-column block.
+  auto compute = [&](int s) {
+    const int buf = s & 1;
     const char* t = s_tile[buf];
     // With several groups per stage the loop over them stays rolled, so that
     // one group's int32 sums are promoted before the next group's MFMAs start
     // (unrolled, the scheduler overlaps them and runs out of registers).
 #pragma unroll 1
     for (int j = 0; j < kSub; ++j) {
+      if (s * kSub + j >= groups) break;  // a last stage that K ends inside
       i32x16 I[2][2];
 #pragma unroll
-      for (int s = j * kStepsPerGroup; s < (j + 1) * kStepsPerGroup; ++s) {
+      for (int ks = j * kStepsPerGroup; ks < (j + 1) * kStepsPerGroup; ++ks) {
         i32x4 fa[2], fb[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const i32x4*>(t + off(a_base, i, s));
+        for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const i32x4*>(t + off(a_base, i, ks));
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) fb[jj] = *reinterpret_cast<const i32x4*>(t + off(b_base, jj, s));
+        for (int jj = 0; jj < 2; ++jj) fb[jj] = *reinterpret_cast<const i32x4*>(t + off(b_base, jj, ks));
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj)
             I[i][jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[jj],
-                                                             s == j * kStepsPerGroup ? (i32x16){} : I[i][jj], 0, 0, 0);
+                                                             ks == j * kStepsPerGroup ? (i32x16){} : I[i][jj], 0, 0, 0);
       }
       const float* scl = s_scale[buf][j];
       float sb[2];
-      if constexpr (!kBlockScale) {
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) sb[jj] = scl[kBM + wn + 32 * jj + lrow];
-      }
+      for (int jj = 0; jj < 2; ++jj) sb[jj] = kBlockScale ? scl[kBM] : scl[kBM + wn + 32 * jj + lrow];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -225,9 +237,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * q + e;
+            const float sc0 = sav[e] * sb[0];
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
-              const float sc = kBlockScale ? sav[e] : sav[e] * sb[jj];
+              const float sc = kBlockScale ? sc0 : sav[e] * sb[jj];
               acc[i][jj][r] = __builtin_fmaf((float)I[i][jj][r], sc, acc[i][jj][r]);
             }
           }
@@ -236,24 +249,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void i8_gemm_kernel(const int8_t* 
     }
   };
 
-  // The next group's operands are loaded into registers while this group is
-  // computed from LDS, then written to the other LDS buffer.
-  Stage<kSub> st;
-  if (stages > 0) {
-    load_stage(0, st);
-    store_stage(0, st);
-  }
-  __syncthreads();
-  // The fence keeps the LDS writes (which wait for the loads) after the whole
-  // group's compute, so that the loads have that long to arrive.
-  auto group_step = [&](int g, int buf) {
-    if (g + 1 < stages) load_stage(g + 1, st);
-    compute(buf);
-    __builtin_amdgcn_sched_barrier(0);
-    if (g + 1 < stages) store_stage(buf ^ 1, st);
+  // Stage s: wait for this thread's loads of it, then the barrier publishes
+  // them to every wave and tells that every wave is done with the other
+  // buffer, into which stage s + 1 then goes while s is computed.
+  if (stages > 0) issue(0);
+  for (int s = 0; s < stages; ++s) {
+    wait_vm_all();
     __syncthreads();
-  };
-  for (int g = 0; g < stages; ++g) group_step(g, g & 1);
+    if (s + 1 < stages) issue(s + 1);
+    compute(s);
+  }
 
   // epilogue: row m0 + wm + 32 i + 8 q + 4 lhalf + e, column n0 + wn + 32 j + lrow
 #pragma unroll
@@ -314,7 +319,7 @@ __attribute__((visibility("default"))) int i8_gemm_group_scaled(const int8_t* A,
   hipStream_t s = stream;
   const bool bf16 = c_dtype == SILUQUANT_GEMM_OUT_BF16, blk = b_rows_per_scale == kBN;
   using KernelFn = void (*)(const int8_t*, const float*, const int8_t*, const float*, void*, int64_t, int64_t, int64_t,
-                            int, int, int, int);
+                            int, int, int);
   auto pick = [&](auto g_tag) -> KernelFn {
     constexpr int kG = decltype(g_tag)::value;
     return bf16 ? (blk ? i8_gemm_kernel<true, true, kG> : i8_gemm_kernel<true, false, kG>)
@@ -323,8 +328,7 @@ __attribute__((visibility("default"))) int i8_gemm_group_scaled(const int8_t* A,
   const KernelFn kernel = group == 128 ? pick(std::integral_constant<int, 128>{})
                           : group == 64 ? pick(std::integral_constant<int, 64>{})
                                         : pick(std::integral_constant<int, 32>{});
-  hipLaunchKernelGGL(kernel, grid, block, 0, s, A, sA, B, sB, C, M, N, K, (int)b_rows_per_scale, (int)tiles_m,
-                     (int)tiles_n, per_xcd);
+  hipLaunchKernelGGL(kernel, grid, block, 0, s, A, sA, B, sB, C, M, N, K, (int)tiles_m, (int)tiles_n, per_xcd);
   if (hipGetLastError() != hipSuccess) return SILUQUANT_ERR_LAUNCH_FAILED;
   return SILUQUANT_OK;
 }
