@@ -78,17 +78,20 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, int64_t bytes) {
 // writes them, lane by lane, to consecutive LDS bytes from address lds (M0)
 // on.  They are written as asm so that the compiler, which cannot tell which
 // LDS bytes they write, does not wait for all of them before every LDS read;
-// the kernel waits for them itself (wait_vm) before the barrier that
-// publishes a stage.  The instructions have no register result.
+// the kernel waits for them itself (wait_vm_all) before the barrier that
+// publishes a stage.  The instructions have no register result.  A load that
+// takes its LDS address from M0 needs one wait state after M0 is written; the
+// compiler writes M0 right before the asm and does not look inside it, so the
+// asm starts with an s_nop.
 __device__ __forceinline__ void lds_load16(i32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
                : "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(soff)),
                  "{m0}"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
 }
 __device__ __forceinline__ void lds_load4(i32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff) {
-  asm volatile("buffer_load_dword %0, %1, %2 offen lds"
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
                :
                : "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(soff)),
                  "{m0}"(__builtin_amdgcn_readfirstlane(lds))
