@@ -58,5 +58,23 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def device_asm(src: str) -> str:
+    """gfx950 assembly of one HIP source, compiled with the library's flags
+    (for checks of the generated instructions)."""
+    from swiglu_backward_int8_amd import sigmoid_table
+    import tempfile
+
+    sigmoid_table.write(os.path.join(GEN, "sigmoid_table.inc"))
+    flags = [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "k.s")
+        cmd = [hipcc()] + flags + ["--cuda-device-only", "-S", "-I" + INCLUDE, "-I" + GEN, src, "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc -S failed (%d):\n%s" % (r.returncode, r.stderr))
+        with open(out) as f:
+            return f.read()
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -1868,6 +1868,15 @@ __device__ __forceinline__ int quad_sum(int v) {
 // subnormals kept).
 __device__ __forceinline__ uint32_t f16_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
 
+// An fp32 result the compiler must produce as such.  A product converted to
+// binary16 right away is otherwise fused into v_fma_mixlo_f16, which rounds
+// the exact product once: on gfx950 that differs from fl32 then binary16 for
+// some (scale, code sum) pairs of the q8_1 blocks.
+__device__ __forceinline__ float as_fp32(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Row t of gate starts at gate + t * in_row and row t of up at up + t * in_row
 // (bf16 elements): x = [gate | up] gives up = gate + H and in_row = 2H, the
 // page's separate gate and up arrays in_row = H.
@@ -2030,7 +2039,7 @@ __global__ __launch_bounds__(kFwdThreads) void silu_fwd_quant_kernel(
       __builtin_amdgcn_raw_buffer_store_b32(c.x, qb, off, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b32(c.y, qb, off + 4, 0, 0);
       if ((p & 3) == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(f16_bits(scale) | (f16_bits(scale * (float)qsum) << 16), qb,
+        __builtin_amdgcn_raw_buffer_store_b32(f16_bits(scale) | (f16_bits(as_fp32(scale * (float)qsum)) << 16), qb,
                                               off - 4, 0, 0);
       if (y_bf16 != nullptr)
         __builtin_amdgcn_raw_buffer_store_b128((u32x4){Yp[0], Yp[1], Yp[2], Yp[3]},

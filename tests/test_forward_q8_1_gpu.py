@@ -52,6 +52,30 @@ def test_workloads(name):
     check(x, label=name)
 
 
+def test_block_sums_rounded_through_fp32():
+    # A block's sum is fl32(scale * code sum) rounded to binary16.  Rounding
+    # the exact product to binary16 once (what v_fma_mixlo_f16 does when the
+    # compiler fuses the multiply into the conversion) gives another value for
+    # some (scale, code sum) pairs, all with large code sums, which zero-mean
+    # rows rarely reach.  Here every row is positive: a gate of 20 makes
+    # silu(g) = g exactly, up is uniform in [0.1, 1) times a power of two per
+    # row.  The oracle's codes and scales show how many blocks tell the two
+    # roundings apart; the GPU must match the oracle's byte for byte.
+    g = torch.Generator().manual_seed(11)
+    T, H = 256, 4096
+    up = (torch.rand(T, H, generator=g) * 0.9 + 0.1) * (2.0 ** torch.randint(-12, 4, (T, 1), generator=g).float())
+    x = torch.cat([torch.full((T, H), 20.0), up], 1).bfloat16()
+    q, s = oracle.silu_fwd_quant(_bits(x), group_size=32)[:2]
+    qs = q.reshape(T, -1, 32).astype(np.int64).sum(-1)
+    s = s.astype(np.float32)
+    twice = (s * qs.astype(np.float32)).astype(np.float32).astype(np.float16).view(np.uint16)
+    once = (s.astype(np.float64) * qs).astype(np.float16).view(np.uint16)
+    differ = int((twice != once).sum())
+    print("blocks whose sum depends on the rounding:", differ, flush=True)
+    assert differ >= 20
+    check(x.to(DEV), label="positive rows, T=%d H=%d" % (T, H))
+
+
 @pytest.mark.parametrize("T,H", [(1, 32), (5, 96), (1000, 160), (129, 4096), (77, 2080)])
 def test_shapes_with_and_without_weights(T, H):
     x, _ = random_inputs(T, H, device=DEV, seed=T + H)
