@@ -5,13 +5,17 @@ compiles the sources to assembly with the library's flags; nothing runs).
   any kernel: the build turns the feature off, and the values must come from
   scalar fp32 operations in the written order.
 * In the fused pass and the forward quantisers every fused multiply-add
-  (v_fma_f32, v_fmac_f32, v_fma_mix*) belongs to an IEEE division sequence
-  (v_div_scale_f32 ... v_div_fixup_f32, the scale and inverse of a group
-  whose maximum is below 2^-119): the elementwise formulas, the bf16 round
-  trips and the code rounding are separate multiplies and adds, which is what
-  the oracle computes (evaluation order of d_gate, rounding of the fp32
-  product v * inv).  "Belongs" is checked as: within 20 instructions of a
-  division instruction.  The GEMM is exempt: its promotion is a stated fma.
+  (v_fma_f32, v_fmac_f32, v_fmamk/fmaak_f32, v_fma_mix*) belongs either to an
+  IEEE division sequence (v_div_scale_f32 ... v_div_fixup_f32, the scale and
+  inverse of a group whose maximum is below 2^-119) or to the compiler's
+  expansion of a 64-bit integer division in the index arithmetic (it scales by
+  2^32, the literal 0x4f800000 or 0xcf800000): the elementwise formulas, the
+  bf16 round trips, the code rounding and the q8_1 sums are separate
+  multiplies, adds and conversions, which is what the oracle computes
+  (evaluation order of d_gate, rounding of the fp32 product v * inv, fl32 of
+  a block's scale times its code sum before binary16).  "Belongs to a
+  division sequence" is checked as: within 20 instructions of a division
+  instruction.  The GEMM is exempt: its promotion is a stated fma.
 * The aligned pass, the forward quantisers and the GEMM spill no registers
   and use no scratch memory.  (The straddling-group carry kernel is known to
   spill 2-8 registers at some group sizes and is not held to this.)
@@ -30,7 +34,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_build.hipcc()) and shutil.wh
 
 SRC = {name: os.path.join(_build.PKG, "csrc", name) for name in ("siluquant.hip", "i8gemm.hip")}
 PACKED = re.compile(r"\bv_pk_(fma|mul|add)_f32\b")
-FMA = re.compile(r"\bv_(fma_f32|fmac_f32|fma_mix\w*)\b")
+FMA = re.compile(r"\bv_(fma_f32|fmac_f32|fmamk_f32|fmaak_f32|fma_mix\w*|mad_f32|mac_f32|madmk_f32|madak_f32|mad_mix\w*)\b")
+INT_DIV = re.compile(r"0x[4c]f800000\b")  # 2^32 scaling in the compiler's 64-bit integer division
 DIV = re.compile(r"\bv_div_(scale|fmas|fixup)_f32\b")
 
 
@@ -89,7 +94,7 @@ def test_pass_and_forward_fmas_only_in_divisions(asm):
             continue
         divs = [i for i, l in enumerate(body) if DIV.search(l)]
         for i, l in enumerate(body):
-            if FMA.search(l):
+            if FMA.search(l) and not INT_DIV.search(l):
                 assert any(abs(i - d) <= 20 for d in divs), "%s: '%s' outside a division" % (name, l)
                 checked += 1
     assert checked > 0  # the division fallbacks exist and were seen
