@@ -121,7 +121,44 @@ def silu_dot_fwd_bwd_quant_fuse_fp8(x, grad_y, grad_input_q, grad_input_s, y_q_t
     _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size, fp8=True)
 
 
+def bind_backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size: int = GROUP, fp8: bool = False):
+    """Check the six tensors once, as silu_dot_fwd_bwd_quant_fuse(_fp8) does,
+    and return a function of no arguments that enqueues the pass on them (on
+    the current stream of x's device at each call) without checking them
+    again: for loops that run the pass many times on the same buffers, where
+    the checks would otherwise cost host time on every call.  The function
+    holds the tensors; they must not be resized while it is in use."""
+    import torch
+
+    T, H = _validate_backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size, fp8)
+    dev = x.device
+    tensors = (x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t)
+    ptrs = tuple(t.data_ptr() for t in tensors)
+    what = "silu_dot_fwd_bwd_quant_fuse_fp8" if fp8 else "silu_dot_fwd_bwd_quant_fuse"
+
+    def run():
+        with torch.cuda.device(dev):
+            code = raw_call(*ptrs, T, H, group_size, torch.cuda.current_stream(dev).cuda_stream, fp8=fp8)
+        _check(code, what)
+
+    run.tensors = tensors
+    return run
+
+
 def _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size: int, fp8: bool):
+    import torch
+
+    T, H = _validate_backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size, fp8)
+    dev = x.device
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        code = raw_call(x.data_ptr(), grad_y.data_ptr(), grad_input_q.data_ptr(), grad_input_s.data_ptr(),
+                        y_q_t.data_ptr(), y_s_t.data_ptr(), T, H, group_size, stream, fp8=fp8)
+    _check(code, "silu_dot_fwd_bwd_quant_fuse_fp8" if fp8 else "silu_dot_fwd_bwd_quant_fuse")
+
+
+def _validate_backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size: int, fp8: bool):
+    """The binding's checks of the pass's tensors; returns (T, H)."""
     import torch
 
     code_types = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)) if fp8 else (torch.int8,)
@@ -151,11 +188,7 @@ def _backward(x, grad_y, grad_input_q, grad_input_s, y_q_t, y_s_t, group_size: i
             raise ValueError("%s must be contiguous" % name)
         if tuple(t.shape) != tuple(shape):
             raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
-    with torch.cuda.device(dev):
-        stream = torch.cuda.current_stream(dev).cuda_stream
-        code = raw_call(x.data_ptr(), grad_y.data_ptr(), grad_input_q.data_ptr(), grad_input_s.data_ptr(),
-                        y_q_t.data_ptr(), y_s_t.data_ptr(), T, H, group_size, stream, fp8=fp8)
-    _check(code, "silu_dot_fwd_bwd_quant_fuse_fp8" if fp8 else "silu_dot_fwd_bwd_quant_fuse")
+    return T, H
 
 
 def silu_fwd_quant(x, y_q, y_s, row_weight=None, y_bf16=None, group_size: int = GROUP):

@@ -265,6 +265,10 @@ def test_binding_rejects_bad_tensors_before_any_call():
         sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *outs, group_size=16)
     with pytest.raises(ValueError):  # tensors on the host
         sq.silu_dot_fwd_bwd_quant_fuse(x, dy, *outs)
+    with pytest.raises(ValueError):  # the bound form checks the same way, once
+        sq.bind_backward(x, dy, *outs)
+    with pytest.raises(ValueError):
+        sq.bind_backward(x[:, :15], dy, *outs)
     with pytest.raises(ValueError):
         sq.silu_fwd_quant(x, outs[0][:, :8], outs[1])
     with pytest.raises(ValueError):
