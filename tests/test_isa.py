@@ -100,6 +100,15 @@ def test_pass_and_forward_fmas_only_in_divisions(asm):
     assert checked > 0  # the division fallbacks exist and were seen
 
 
+def test_pass_and_forward_use_no_fused_conversions(asm):
+    # conversions that multiply by a scale, or dot products of fp values,
+    # would round a product once where the oracle rounds it to fp32 first
+    fused = re.compile(r"\bv_(cvt_scalef32\w*|dot2\w*_f32\w*|dot2c_f32\w*)\b")
+    for name, body in kernels(asm["siluquant.hip"]).items():
+        bad = [l for l in body if fused.search(l)]
+        assert not bad, "%s: %s" % (name, bad[:3])
+
+
 def test_hot_kernels_do_not_spill(asm):
     meta = {**metadata(asm["siluquant.hip"]), **metadata(asm["i8gemm.hip"])}
     hot = [n for n in meta if re.search(r"silu_quant_bwd_kernel|silu_fwd_quant_kernel|silu_fwd_quant_wide_kernel|"
